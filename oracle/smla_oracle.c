@@ -1,0 +1,329 @@
+/*
+ * smla_oracle.c — CPU oracle (TEST INFRASTRUCTURE ONLY; see smla_oracle.h for the definitions
+ * and the passages they follow). Every quantity is computed straight from its definition:
+ * integer indexer scores in int64, a full sort for top-k, and fp64 softmax attention over the
+ * dequantised rows. Worker threads split the listed query tokens; they never reorder the
+ * arithmetic inside one token.
+ */
+#include "smla_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+int32_t smla_oracle_default_threads(void) {
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  if (n < 1) n = 1;
+  if (n > 256) n = 256;
+  return (int32_t)n;
+}
+
+/* OCP 8-bit floating point, E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+ * Exponent field 0 is subnormal: (m/8) * 2^(1-7). S.1111.111 is NaN; there is no infinity. */
+double smla_oracle_e4m3(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double mag;
+  if (e == 0xF && m == 0x7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, 1 - 7);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double smla_oracle_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+int smla_oracle_dequant_row(const uint8_t* row, int32_t fmt, int32_t D_qk, double* out) {
+  if (!row || !out) return -1;
+  if (fmt == 0) {
+    for (int d = 0; d < D_qk; ++d) out[d] = smla_oracle_bf16((uint16_t)(row[2 * d] | (row[2 * d + 1] << 8)));
+    return 0;
+  }
+  if (fmt != 1 || D_qk != 576) return -1;
+  /* 656-byte row: [512 e4m3 codes][4 fp32 block scales][64 bf16 rope values] */
+  float scale[4];
+  memcpy(scale, row + 512, 16);
+  for (int d = 0; d < 512; ++d) out[d] = smla_oracle_e4m3(row[d]) * (double)scale[d / 128];
+  for (int d = 0; d < 64; ++d) {
+    const uint8_t* b = row + 528 + 2 * d;
+    out[512 + d] = smla_oracle_bf16((uint16_t)(b[0] | (b[1] << 8)));
+  }
+  return 0;
+}
+
+int smla_oracle_indexer_scores(const int8_t* q_tok, const int8_t* keys, const int32_t* w,
+                               int32_t H_I, int32_t D_I, int64_t n, int64_t* out) {
+  /* |q_d * k_d| <= 2^14, so a dot product over D_I <= 2^16 dims is exact in int32 */
+  if (D_I < 1 || D_I > 65536 || H_I < 1) return -1;
+  int bad = 0;
+  for (int64_t s = 0; s < n; ++s) {
+    const int8_t* k = keys + s * D_I;
+    int64_t score = 0;
+    for (int h = 0; h < H_I; ++h) {
+      const int8_t* qh = q_tok + (int64_t)h * D_I;
+      int32_t dot = 0;
+      for (int d = 0; d < D_I; ++d) dot += (int32_t)qh[d] * (int32_t)k[d];
+      int64_t relu = dot > 0 ? dot : 0;
+      score += (int64_t)w[h] * relu;
+    }
+    if (score < 0 || score > 2147483647LL) bad = 1;
+    out[s] = score;
+  }
+  return bad ? -1 : 0;
+}
+
+typedef struct {
+  int64_t score;
+  int64_t s;
+} cand_t;
+
+/* Total order of the selection: larger score first; among equal scores, lower index first. */
+static int cmp_cand(const void* a, const void* b) {
+  const cand_t* x = (const cand_t*)a;
+  const cand_t* y = (const cand_t*)b;
+  if (x->score != y->score) return x->score > y->score ? -1 : 1;
+  return x->s < y->s ? -1 : (x->s > y->s ? 1 : 0);
+}
+
+int smla_oracle_topk(const int64_t* scores, int64_t n, int32_t top_k, int32_t* idx,
+                     int32_t* score) {
+  if (n < 0 || top_k < 1) return -1;
+  cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+  if (!c) return -1;
+  for (int64_t s = 0; s < n; ++s) {
+    c[s].score = scores[s];
+    c[s].s = s;
+  }
+  qsort(c, (size_t)n, sizeof(cand_t), cmp_cand);
+  for (int32_t j = 0; j < top_k; ++j) {
+    if (j < n) {
+      idx[j] = (int32_t)c[j].s;
+      if (score) score[j] = (int32_t)c[j].score;
+    } else {
+      idx[j] = -1;
+      if (score) score[j] = -1;
+    }
+  }
+  free(c);
+  return 0;
+}
+
+int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,
+                       int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
+                       double sm_scale, double* out, double* lse) {
+  int32_t nsel = 0;
+  for (int32_t i = 0; i < top_k; ++i) nsel += idx[i] >= 0;
+  if (nsel == 0) return -1;
+  double* v = (double*)malloc(sizeof(double) * (size_t)nsel * (size_t)D_qk);
+  double* q = (double*)malloc(sizeof(double) * (size_t)D_qk);
+  double* l = (double*)malloc(sizeof(double) * (size_t)nsel);
+  if (!v || !q || !l) { free(v); free(q); free(l); return -1; }
+  /* dequantise each selected row once; every head reads the same rows */
+  int32_t r = 0;
+  for (int32_t i = 0; i < top_k; ++i) {
+    if (idx[i] < 0) continue;
+    if (smla_oracle_dequant_row(rows + (int64_t)idx[i] * row_bytes, fmt, D_qk, v + (int64_t)r * D_qk)) {
+      free(v); free(q); free(l);
+      return -1;
+    }
+    ++r;
+  }
+  for (int32_t h = 0; h < H; ++h) {
+    for (int d = 0; d < D_qk; ++d) q[d] = smla_oracle_bf16(q_tok[(int64_t)h * D_qk + d]);
+    double m = -INFINITY;
+    for (int32_t i = 0; i < nsel; ++i) {
+      const double* vi = v + (int64_t)i * D_qk;
+      double dot = 0.0;
+      for (int d = 0; d < D_qk; ++d) dot += q[d] * vi[d];
+      l[i] = sm_scale * dot;
+      if (l[i] > m) m = l[i];
+    }
+    double Z = 0.0;
+    for (int32_t i = 0; i < nsel; ++i) {
+      l[i] = exp(l[i] - m); /* l now holds e_i */
+      Z += l[i];
+    }
+    if (out) {
+      double* o = out + (int64_t)h * D_v;
+      for (int d = 0; d < D_v; ++d) o[d] = 0.0;
+      for (int32_t i = 0; i < nsel; ++i) {
+        const double p = l[i] / Z;
+        const double* vi = v + (int64_t)i * D_qk;
+        for (int d = 0; d < D_v; ++d) o[d] += p * vi[d];
+      }
+    }
+    if (lse) lse[h] = m + log(Z);
+  }
+  free(v);
+  free(q);
+  free(l);
+  return 0;
+}
+
+/* ---- batched drivers -------------------------------------------------------------------- */
+
+typedef struct {
+  int32_t batch;
+  const int32_t* n_q;
+  const int64_t* kv_len;
+  int64_t* q0; /* [batch+1] token prefix */
+  int64_t* r0; /* [batch+1] row prefix */
+} layout_t;
+
+static int layout_init(layout_t* L, int32_t batch, const int32_t* n_q, const int64_t* kv_len) {
+  L->batch = batch;
+  L->n_q = n_q;
+  L->kv_len = kv_len;
+  L->q0 = (int64_t*)calloc((size_t)batch + 1, sizeof(int64_t));
+  L->r0 = (int64_t*)calloc((size_t)batch + 1, sizeof(int64_t));
+  if (!L->q0 || !L->r0) return -1;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (n_q[b] < 0 || kv_len[b] < n_q[b]) return -1;
+    L->q0[b + 1] = L->q0[b] + n_q[b];
+    L->r0[b + 1] = L->r0[b] + kv_len[b];
+  }
+  return 0;
+}
+
+static void layout_free(layout_t* L) {
+  free(L->q0);
+  free(L->r0);
+}
+
+/* request, position and first row of global token t; -1 if t is out of range */
+static int32_t locate(const layout_t* L, int64_t t, int64_t* p, int64_t* row0) {
+  for (int32_t b = 0; b < L->batch; ++b)
+    if (t >= L->q0[b] && t < L->q0[b + 1]) {
+      *p = L->kv_len[b] - L->n_q[b] + (t - L->q0[b]);
+      *row0 = L->r0[b];
+      return b;
+    }
+  return -1;
+}
+
+typedef struct {
+  const layout_t* L;
+  const int8_t* q_idx; const int8_t* k_idx; const int32_t* w;
+  int32_t H_I, D_I, top_k;
+  const uint16_t* q; const uint8_t* kv; int32_t fmt, row_bytes, H, D_qk, D_v;
+  const int32_t* idx; double sm_scale;
+  const int64_t* tokens; int64_t i0, i1;
+  int32_t* idx_out; int32_t* score_out; double* out; double* lse;
+  int rc;
+} job_t;
+
+static void* topk_worker(void* arg) {
+  job_t* j = (job_t*)arg;
+  int64_t* sc = NULL;
+  int64_t cap = 0;
+  for (int64_t i = j->i0; i < j->i1; ++i) {
+    int64_t p, row0;
+    int64_t t = j->tokens[i];
+    if (locate(j->L, t, &p, &row0) < 0) { j->rc = -1; break; }
+    int64_t n = p + 1;
+    if (n > cap) {
+      free(sc);
+      sc = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+      cap = n;
+      if (!sc) { j->rc = -1; break; }
+    }
+    if (smla_oracle_indexer_scores(j->q_idx + t * (int64_t)j->H_I * j->D_I, j->k_idx + row0 * j->D_I,
+                                   j->w, j->H_I, j->D_I, n, sc))
+      j->rc = -1;
+    if (smla_oracle_topk(sc, n, j->top_k, j->idx_out + i * j->top_k,
+                         j->score_out ? j->score_out + i * j->top_k : NULL))
+      j->rc = -1;
+  }
+  free(sc);
+  return NULL;
+}
+
+static void* mla_worker(void* arg) {
+  job_t* j = (job_t*)arg;
+  for (int64_t i = j->i0; i < j->i1; ++i) {
+    int64_t p, row0;
+    int64_t t = j->tokens[i];
+    if (locate(j->L, t, &p, &row0) < 0) { j->rc = -1; break; }
+    /* every selected index must be a row this token may see */
+    const int32_t* ix = j->idx + t * j->top_k;
+    for (int32_t k = 0; k < j->top_k; ++k)
+      if (ix[k] > p) j->rc = -1;
+    if (j->rc) break;
+    if (smla_oracle_attend(j->q + t * (int64_t)j->H * j->D_qk, j->kv + row0 * j->row_bytes, j->fmt,
+                           j->row_bytes, j->H, j->D_qk, j->D_v, ix, j->top_k, j->sm_scale,
+                           j->out ? j->out + i * (int64_t)j->H * j->D_v : NULL,
+                           j->lse ? j->lse + i * (int64_t)j->H : NULL))
+      j->rc = -1;
+  }
+  return NULL;
+}
+
+static int run_jobs(job_t* proto, int64_t n_tokens, int32_t nthreads, void* (*fn)(void*)) {
+  int nt = nthreads > 0 ? nthreads : smla_oracle_default_threads();
+  if (nt > 256) nt = 256;
+  if (nt > n_tokens) nt = (int)(n_tokens > 0 ? n_tokens : 1);
+  job_t jobs[256];
+  pthread_t th[256];
+  for (int i = 0; i < nt; ++i) {
+    jobs[i] = *proto;
+    jobs[i].i0 = n_tokens * i / nt;
+    jobs[i].i1 = n_tokens * (i + 1) / nt;
+    jobs[i].rc = 0;
+  }
+  for (int i = 1; i < nt; ++i) pthread_create(&th[i], NULL, fn, &jobs[i]);
+  fn(&jobs[0]);
+  int rc = jobs[0].rc;
+  for (int i = 1; i < nt; ++i) {
+    pthread_join(th[i], NULL);
+    if (jobs[i].rc) rc = jobs[i].rc;
+  }
+  return rc;
+}
+
+int smla_oracle_indexer_topk_batch(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                                   const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                                   int32_t H_I, int32_t D_I, int32_t top_k, const int64_t* tokens,
+                                   int64_t n_tokens, int32_t* idx_out, int32_t* score_out,
+                                   int32_t nthreads) {
+  if (batch < 1 || !n_q || !kv_len || !q_idx || !k_idx || !w || !tokens || !idx_out || top_k < 1)
+    return -1;
+  layout_t L;
+  if (layout_init(&L, batch, n_q, kv_len)) { layout_free(&L); return -1; }
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.L = &L; proto.q_idx = q_idx; proto.k_idx = k_idx; proto.w = w;
+  proto.H_I = H_I; proto.D_I = D_I; proto.top_k = top_k; proto.tokens = tokens;
+  proto.idx_out = idx_out; proto.score_out = score_out;
+  int rc = run_jobs(&proto, n_tokens, nthreads, topk_worker);
+  layout_free(&L);
+  return rc;
+}
+
+int smla_oracle_sparse_mla_batch(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                                 const uint16_t* q, const uint8_t* kv, int32_t fmt,
+                                 int32_t row_bytes, int32_t H, int32_t D_qk, int32_t D_v,
+                                 const int32_t* idx, int32_t top_k, double sm_scale,
+                                 const int64_t* tokens, int64_t n_tokens, double* out, double* lse,
+                                 int32_t nthreads) {
+  if (batch < 1 || !n_q || !kv_len || !q || !kv || !idx || !tokens || top_k < 1) return -1;
+  layout_t L;
+  if (layout_init(&L, batch, n_q, kv_len)) { layout_free(&L); return -1; }
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.L = &L; proto.q = q; proto.kv = kv; proto.fmt = fmt; proto.row_bytes = row_bytes;
+  proto.H = H; proto.D_qk = D_qk; proto.D_v = D_v; proto.idx = idx; proto.top_k = top_k;
+  proto.sm_scale = sm_scale; proto.tokens = tokens; proto.out = out; proto.lse = lse;
+  int rc = run_jobs(&proto, n_tokens, nthreads, mla_worker);
+  layout_free(&L);
+  return rc;
+}

@@ -1,0 +1,83 @@
+/*
+ * smla_oracle.h — CPU oracle for the indexer -> top-k -> sparse-MLA path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only tests, the package's smoke check and the benchmark's CPU
+ * baseline may load this library. It shares no code with the GPU library.
+ *
+ * Plain, slow, obviously correct definitions:
+ *  - Indexer score of query token t (at position p) against earlier token s <= p:
+ *      score(t, s) = sum_h w_h * max(0, sum_d q_I[t,h,d] * k_I[s,d])   (int64, exact)
+ *    The pages: an indexer scores every earlier token for every query to choose the 2,048 tokens
+ *    sparse MLA attends ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why DP8 and
+ *    TP8 fall short"); the formula itself is the workload definition of the tiny causal prefill.
+ *  - Top-k: the min(k, p+1) tokens with the largest scores; ties go to the lower index; every
+ *    s <= p is taken when p+1 <= k. Implemented as a sort by (score desc, s asc).
+ *  - Sparse MLA (MQA form: all heads read the same selected latent rows; QK over 576 dims, PV
+ *    over the first 512; section "Why the numbers work"): for each head h,
+ *      l_i = sm_scale * sum_{d<D_qk} q[h,d] v_i[d],  m = max_i l_i,  e_i = exp(l_i - m),
+ *      Z = sum_i e_i,  o[h,d] = sum_i (e_i / Z) v_i[d] for d < D_v,  lse[h] = m + log Z
+ *    in fp64 over the dequantised rows.
+ *  - Row dequantisation: bf16 rows decode exactly; 656-byte rows decode
+ *      v[d] = e4m3(code[d]) * scale[d / 128] for d < 512 and v[d] = bf16(rope[d - 512]) otherwise.
+ */
+#ifndef SMLA_ORACLE_H
+#define SMLA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* OCP E4M3 ("FN") code -> value; NaN for S.1111.111. */
+double smla_oracle_e4m3(uint8_t code);
+/* bfloat16 bit pattern -> value. */
+double smla_oracle_bf16(uint16_t bits);
+/* Dequantise one latent row of `fmt` (0 bf16, 1 fp8-656) into D_qk doubles. */
+int smla_oracle_dequant_row(const uint8_t* row, int32_t fmt, int32_t D_qk, double* out);
+
+/* Scores of one query token (q_tok [H_I, D_I]) against keys [n, D_I]; out [n] int64.
+ * Returns -1 when a score leaves [0, 2^31 - 1]. */
+int smla_oracle_indexer_scores(const int8_t* q_tok, const int8_t* keys, const int32_t* w,
+                               int32_t H_I, int32_t D_I, int64_t n, int64_t* out);
+
+/* Exact top-k of scores[0..n) by (score desc, index asc). idx/score [top_k], in that order;
+ * slots past min(n, top_k) hold idx -1 and score -1. */
+int smla_oracle_topk(const int64_t* scores, int64_t n, int32_t top_k, int32_t* idx,
+                     int32_t* score);
+
+/* Attention of one query token q_tok [H, D_qk] (bf16 bits) over rows[idx[i]] (row_bytes each),
+ * skipping idx < 0; out [H, D_v], lse [H] (either may be NULL). Returns -1 if no row is valid. */
+int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,
+                       int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
+                       double sm_scale, double* out, double* lse);
+
+/*
+ * Batched drivers over a list of query tokens, `nthreads` worker threads (<= 0: all cores).
+ * Batch layout: request b owns query tokens [Q_b, Q_b + n_q[b]) and rows [R_b, R_b + kv_len[b])
+ * with Q_b, R_b exclusive prefix sums of n_q and kv_len; its query j sits at position
+ * p = kv_len[b] - n_q[b] + j and sees rows s <= p (s is local to the request).
+ * Outputs are packed per listed token: idx_out/score_out [n_tokens, top_k],
+ * out [n_tokens, H, D_v], lse [n_tokens, H]. `idx` for sparse MLA is [total_q, top_k] indexed by
+ * the global token id.
+ */
+int smla_oracle_indexer_topk_batch(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                                   const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                                   int32_t H_I, int32_t D_I, int32_t top_k, const int64_t* tokens,
+                                   int64_t n_tokens, int32_t* idx_out, int32_t* score_out,
+                                   int32_t nthreads);
+
+int smla_oracle_sparse_mla_batch(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                                 const uint16_t* q, const uint8_t* kv, int32_t fmt,
+                                 int32_t row_bytes, int32_t H, int32_t D_qk, int32_t D_v,
+                                 const int32_t* idx, int32_t top_k, double sm_scale,
+                                 const int64_t* tokens, int64_t n_tokens, double* out, double* lse,
+                                 int32_t nthreads);
+
+/* Worker threads used for nthreads <= 0. */
+int32_t smla_oracle_default_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

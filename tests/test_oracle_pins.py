@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Each test checks one oracle function against a library routine (torch's e4m3 and bf16 casts,
+numpy integer matmuls and lexsort, torch's scaled-dot-product attention), a closed form, an
+invariant, or a hand-worked example, chosen so that a dropped term, a wrong sign or index, or a
+transposed operand in the oracle fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indexer_amd import workload as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16_bits(x) -> np.ndarray:
+    return torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_vals(bits) -> np.ndarray:
+    return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+
+
+# ---- storage decodes ---------------------------------------------------------------------
+
+def test_e4m3_all_codes_match_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x38] == 1.0
+
+
+def test_bf16_all_patterns_match_torch():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_vals(bits)
+    got = np.array([oracle.bf16(int(b)) for b in bits[::97]] + [oracle.bf16(0x3F80), oracle.bf16(0xC000)])
+    exp = np.concatenate([ref[::97], [1.0, -2.0]])
+    same = (got == exp) | (np.isnan(got) & np.isnan(exp))
+    assert same.all()
+
+
+def test_fp8_row_layout_hand_built():
+    # codes: dim 0 -> 1.0 (0x38), dim 130 -> -2.0 (0xC0), dim 511 -> 448 (0x7E); block scales
+    # 2, 3, 0.5, 4; rope dim 512 -> bf16 1.0, rope dim 575 -> bf16 -3.0
+    row = np.zeros(656, np.uint8)
+    row[0], row[130], row[511] = 0x38, 0xC0, 0x7E
+    row[512:528] = np.array([2.0, 3.0, 0.5, 4.0], np.float32).view(np.uint8)
+    rope = np.zeros(64, np.uint16)
+    rope[0], rope[63] = 0x3F80, 0xC040
+    row[528:656] = rope.view(np.uint8)
+    v = oracle.dequant_row(row, W.KV_FP8_656, 576)
+    exp = np.zeros(576)
+    exp[0], exp[130], exp[511], exp[512], exp[575] = 2.0, -6.0, 448.0 * 4.0, 1.0, -3.0
+    assert np.array_equal(v, exp)
+
+
+def test_fp8_rows_within_e4m3_rounding_of_generated_latents():
+    d = W.small_big_dims(n_q=4, cached=60)
+    x = W.generate(d, parts=("kv",))
+    lat = W.latent_f64(d, x.seed, 0, d.total_rows)
+    for r in range(d.total_rows):
+        v = oracle.dequant_row(x.kv[r], W.KV_FP8_656, 576)
+        scales = x.kv[r, 512:528].view(np.float32).astype(np.float64)
+        for b in range(4):
+            sl = slice(128 * b, 128 * b + 128)
+            amax = np.abs(lat[r, sl]).max()
+            assert scales[b] == np.float32(amax / 448.0)
+            y = lat[r, sl] / scales[b]
+            # RNE on the e4m3 grid: error <= half a step; step 2^(e-3) for |y| in [2^e, 2^(e+1)),
+            # 2^-9 below 2^-6
+            e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6)))
+            bound = 0.5 * 2.0 ** (e - 3) * scales[b] * (1 + 1e-9) + 1e-300
+            assert np.all(np.abs(v[sl] - lat[r, sl]) <= bound)
+        rope_err = np.abs(v[512:] - lat[r, 512:])
+        assert np.all(rope_err <= np.abs(lat[r, 512:]) * (2.0 ** -8) + 1e-30)
+
+
+# ---- indexer -----------------------------------------------------------------------------
+
+def _rand_indexer(rng, H, D, n, lo=-8, hi=7):
+    q = rng.integers(lo, hi + 1, size=(H, D), dtype=np.int64).astype(np.int8)
+    k = rng.integers(lo, hi + 1, size=(n, D), dtype=np.int64).astype(np.int8)
+    w = rng.integers(1, 5, size=H).astype(np.int32)
+    return q, k, w
+
+
+@pytest.mark.parametrize("H,D,n", [(4, 32, 50), (64, 128, 300), (3, 7, 20)])
+def test_indexer_nonnegative_inputs_is_integer_gemv(H, D, n):
+    # with q, k >= 0 every dot is >= 0, so ReLU is the identity and the score is (w^T Q) . k
+    rng = np.random.default_rng(H * 1000 + D)
+    q, k, w = _rand_indexer(rng, H, D, n, 0, 7)
+    ref = k.astype(np.int64) @ (w.astype(np.int64) @ q.astype(np.int64))
+    assert np.array_equal(oracle.indexer_scores(q, k, w), ref)
+
+
+def test_indexer_antisymmetric_heads_gives_weighted_abs():
+    # heads h and h + H/2 carry q and -q with equal weights: relu(x) + relu(-x) = |x|
+    rng = np.random.default_rng(7)
+    half, D, n = 16, 128, 200
+    qh, k, wh = _rand_indexer(rng, half, D, n)
+    qh = np.clip(qh, -7, 7)  # keep -q in int8 range
+    q = np.concatenate([qh, -qh]).astype(np.int8)
+    w = np.concatenate([wh, wh]).astype(np.int32)
+    dots = k.astype(np.int64) @ qh.astype(np.int64).T  # [n, half]
+    ref = np.abs(dots) @ wh.astype(np.int64)
+    assert np.array_equal(oracle.indexer_scores(q, k, w), ref)
+
+
+def test_indexer_all_negative_dots_score_zero():
+    rng = np.random.default_rng(3)
+    q, k, w = _rand_indexer(rng, 8, 32, 64, 0, 7)
+    k = (-np.abs(k.astype(np.int16))).astype(np.int8)
+    assert not oracle.indexer_scores(q, k, w).any()
+
+
+def test_indexer_overflow_is_reported():
+    q = np.full((64, 128), -128, np.int8)
+    k = np.full((2, 128), -128, np.int8)
+    w = np.full(64, 16, np.int32)  # 64 * 16 * 2^21 = 2^31
+    with pytest.raises(OverflowError):
+        oracle.indexer_scores(q, k, w)
+
+
+def _golden_indexer():
+    rec = {"k": [], "topk": []}
+    with open(os.path.join(GOLDEN, "indexer_hand.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tag, *rest = line.split()
+            if tag in ("w", "q", "scores"):
+                rec[tag] = [int(v) for v in rest]
+            elif tag == "k":
+                rec["k"].append([int(v) for v in rest])
+            elif tag == "topk":
+                p = int(rest[0].split("=")[1])
+                kk = int(rest[1].split("=")[1])
+                pairs = [tuple(int(x) for x in e.split(":")) for e in rest[2:]]
+                rec["topk"].append((p, kk, pairs))
+    return rec
+
+
+def test_indexer_and_topk_hand_worked_example():
+    g = _golden_indexer()
+    q = np.array(g["q"], np.int8).reshape(2, 3)
+    k = np.array(g["k"], np.int8)
+    w = np.array(g["w"], np.int32)
+    assert oracle.indexer_scores(q, k, w).tolist() == g["scores"]
+    for p, kk, pairs in g["topk"]:
+        idx, sc = oracle.topk(oracle.indexer_scores(q, k[: p + 1], w), kk)
+        assert list(zip(idx.tolist(), sc.tolist())) == pairs
+
+
+# ---- top-k -------------------------------------------------------------------------------
+
+def test_topk_short_prefix_takes_everything():
+    s = np.array([5, 1, 9], np.int64)
+    idx, sc = oracle.topk(s, 8)
+    assert sorted(idx[:3].tolist()) == [0, 1, 2] and (idx[3:] == -1).all() and (sc[3:] == -1).all()
+
+
+def test_topk_all_equal_scores_take_lowest_indices():
+    idx, _ = oracle.topk(np.zeros(5000, np.int64), 2048)
+    assert sorted(idx.tolist()) == list(range(2048))
+
+
+def test_topk_monotone_scores():
+    n, kk = 3000, 100
+    idx, _ = oracle.topk(np.arange(n, dtype=np.int64), kk)
+    assert sorted(idx.tolist()) == list(range(n - kk, n))
+    idx, _ = oracle.topk(-np.arange(n, dtype=np.int64), kk)
+    assert sorted(idx.tolist()) == list(range(kk))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_tie_heavy_matches_numpy_lexsort(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 5000))
+    kk = int(rng.integers(1, 300))
+    s = rng.integers(0, 6, size=n).astype(np.int64)  # many ties
+    order = np.lexsort((np.arange(n), -s))  # primary: score desc, secondary: index asc
+    idx, sc = oracle.topk(s, kk)
+    m = min(n, kk)
+    assert idx[:m].tolist() == order[:m].tolist()
+    assert sc[:m].tolist() == s[order[:m]].tolist()
+    # invariant: every selected score >= every unselected; ties at the cut favour lower indices
+    if n > kk:
+        sel = np.zeros(n, bool)
+        sel[idx] = True
+        assert s[sel].min() >= s[~sel].max()
+        t = s[sel].min()
+        assert np.arange(n)[sel & (s == t)].max() < np.arange(n)[~sel & (s == t)].min(initial=n)
+
+
+def test_batch_layout_positions_and_rows():
+    # score(t, s) = s + 1 (one head, one dim, q = w = 1, key value s + 1), so each token's
+    # top-k is the k highest visible positions; this pins p = kv_len - n_q + j and the row base.
+    n_q = np.array([3, 1, 2], np.int32)
+    kv_len = np.array([10, 4, 7], np.int64)
+    rows = []
+    for b in range(3):
+        rows += [s + 1 for s in range(kv_len[b])]
+    k_idx = np.array(rows, np.int8).reshape(-1, 1)
+    q_idx = np.ones((n_q.sum(), 1, 1), np.int8)
+    w = np.ones(1, np.int32)
+    tokens = np.arange(n_q.sum())
+    idx, sc = oracle.indexer_topk_batch(n_q, kv_len, q_idx, k_idx, w, 3, tokens, nthreads=2)
+    exp_p = [7, 8, 9, 3, 5, 6]
+    for t, p in enumerate(exp_p):
+        assert idx[t].tolist() == [p, p - 1, p - 2]
+        assert sc[t].tolist() == [p + 1, p, p - 1]
+
+
+def test_batch_driver_matches_single_token_calls():
+    d = W.custom_dims(batch=2, n_q=5, cached=40, H=8, D_qk=80, D_v=64, H_I=4, D_I=32, top_k=16,
+                      kv_format=W.KV_BF16)
+    x = W.generate(d)
+    tokens = np.arange(d.total_q)
+    idx, sc = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, 16, tokens)
+    for t in tokens:
+        b, j = divmod(int(t), d.n_q)
+        p = d.cached + j
+        keys = x.k_idx[b * d.max_kv: b * d.max_kv + p + 1]
+        i1, s1 = oracle.topk(oracle.indexer_scores(x.q_idx[t], keys, x.w), 16)
+        assert idx[t].tolist() == i1.tolist() and sc[t].tolist() == s1.tolist()
+
+
+# ---- attention ---------------------------------------------------------------------------
+
+def _sdpa_causal(qv, kv_vals, D_v, sm_scale, positions):
+    """torch scaled-dot-product attention in fp64 on the CPU: qv [T, H, D], kv_vals [n, D]."""
+    T, H, D = qv.shape
+    n = kv_vals.shape[0]
+    q = torch.from_numpy(qv).permute(1, 0, 2).unsqueeze(0)  # [1, H, T, D]
+    k = torch.from_numpy(kv_vals).expand(1, H, n, D)
+    v = torch.from_numpy(kv_vals[:, :D_v].copy()).expand(1, H, n, D_v)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= np.asarray(positions)[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=sm_scale)
+    logits = (q @ k.transpose(-1, -2)) * sm_scale
+    logits = logits.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)
+    return out[0].permute(1, 0, 2).numpy(), lse[0].permute(1, 0).numpy()
+
+
+def test_sparse_equals_dense_causal_when_k_covers_prefix_bf16_rows():
+    d = W.config_dims(0)  # tiny: k = 64, tokens 0..63 take every s <= p
+    x = W.generate(d)
+    T = 64
+    idx, _ = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, d.top_k, np.arange(T))
+    full = np.zeros((d.total_q, d.top_k), np.int32)
+    full[:T] = idx
+    out, lse = oracle.sparse_mla_batch(x.n_q, x.kv_len, x.q, x.kv, W.KV_BF16, d.D_v, full, d.sm_scale,
+                                       np.arange(T))
+    rows = bf16_vals(x.kv[:T].view(np.uint16))
+    qv = bf16_vals(x.q[:T])
+    ref, ref_lse = _sdpa_causal(qv, rows, d.D_v, d.sm_scale, np.arange(T))
+    assert np.abs(out - ref).max() < 1e-12
+    assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+def test_sparse_equals_dense_causal_fp8_rows():
+    d = W.small_big_dims(n_q=6, cached=20, top_k=64)
+    x = W.generate(d)
+    tokens = np.arange(d.total_q)
+    idx, _ = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, 64, tokens)
+    out, lse = oracle.sparse_mla_batch(x.n_q, x.kv_len, x.q, x.kv, W.KV_FP8_656, 512, idx, d.sm_scale,
+                                       tokens)
+    # dequantise with torch's e4m3 cast and the stored scales (independent of the oracle)
+    codes = torch.from_numpy(x.kv[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()
+    scales = x.kv[:, 512:528].copy().view(np.float32).astype(np.float64)
+    vals = np.concatenate([codes * np.repeat(scales, 128, axis=1),
+                           bf16_vals(x.kv[:, 528:656].copy().view(np.uint16))], axis=1)
+    qv = bf16_vals(x.q)
+    ref, ref_lse = _sdpa_causal(qv, vals, 512, d.sm_scale, d.cached + np.arange(d.n_q))
+    assert np.abs(out - ref).max() < 1e-12
+    assert np.abs(lse - ref_lse).max() < 1e-12
+
+
+def _rows_bf16(vals):
+    return bf16_bits(vals).view(np.uint8).reshape(len(vals), -1)
+
+
+def test_attention_two_rows_closed_form():
+    q = bf16_bits([[1.0, 0.0]])
+    rows = _rows_bf16(np.array([[0.0, 2.0], [1.0, 4.0]]))
+    out, lse = oracle.attend(q, rows, W.KV_BF16, 2, np.array([0, 1, -1]), 1.0)
+    e = math.e
+    assert np.allclose(out[0], [e / (1 + e), (2 + 4 * e) / (1 + e)], rtol=0, atol=1e-15)
+    assert abs(lse[0] - math.log(1 + e)) < 1e-15
+    # scale enters the logits: with sm_scale = 0.5 the weights are 1 : e^0.5
+    out, _ = oracle.attend(q, rows, W.KV_BF16, 2, np.array([0, 1]), 0.5)
+    r = math.exp(0.5)
+    assert np.allclose(out[0], [r / (1 + r), (2 + 4 * r) / (1 + r)], rtol=0, atol=1e-15)
+
+
+def test_attention_weights_sum_to_one():
+    rng = np.random.default_rng(1)
+    q = bf16_bits(rng.standard_normal((4, 16)))
+    rows = _rows_bf16(np.full((30, 16), 1.5))
+    out, _ = oracle.attend(q, rows, W.KV_BF16, 8, rng.permutation(30)[:20].astype(np.int32), 0.25)
+    assert np.abs(out - 1.5).max() < 1e-13
+
+
+def test_attention_single_row_and_zero_query():
+    rng = np.random.default_rng(2)
+    vals = rng.standard_normal((10, 12))
+    rows = _rows_bf16(vals)
+    vb = bf16_vals(bf16_bits(vals))
+    q = bf16_bits(rng.standard_normal((3, 12)))
+    out, lse = oracle.attend(q, rows, W.KV_BF16, 6, np.array([-1, 7, -1]), 0.3)
+    assert np.array_equal(out, np.tile(vb[7, :6], (3, 1)))
+    assert np.allclose(lse, 0.3 * (bf16_vals(q) @ vb[7]), atol=1e-13)
+    sel = np.array([1, 4, 9, 2])
+    out, lse = oracle.attend(np.zeros((3, 12), np.uint16), rows, W.KV_BF16, 6, sel, 0.3)
+    assert np.allclose(out, np.tile(vb[sel, :6].mean(0), (3, 1)), atol=1e-14)
+    assert np.allclose(lse, math.log(4), atol=1e-14)
+
+
+def test_attention_permutation_invariant_and_lse_merge():
+    rng = np.random.default_rng(4)
+    vals = rng.standard_normal((50, 20))
+    rows = _rows_bf16(vals)
+    q = bf16_bits(rng.standard_normal((5, 20)))
+    sel = rng.permutation(50)[:32].astype(np.int32)
+    o1, l1 = oracle.attend(q, rows, W.KV_BF16, 16, sel, 0.2)
+    o2, l2 = oracle.attend(q, rows, W.KV_BF16, 16, sel[::-1].copy(), 0.2)
+    assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+    # partial results over disjoint row sets merge exactly by log-sum-exp
+    oa, la = oracle.attend(q, rows, W.KV_BF16, 16, sel[:13], 0.2)
+    ob, lb = oracle.attend(q, rows, W.KV_BF16, 16, sel[13:], 0.2)
+    lm = np.logaddexp(la, lb)
+    om = np.exp(la - lm)[:, None] * oa + np.exp(lb - lm)[:, None] * ob
+    assert np.allclose(om, o1, atol=1e-13) and np.allclose(lm, l1, atol=1e-13)
