@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of one layer of the hot path (indexer scores -> exact top-k -> sparse MLA) on one
+MI355X, in query tokens per second, with the dominant kernel's roofline fraction and the CPU
+oracle timed on the host beside it.
+
+A step is one pass of the whole path over one batch of seeded synthetic inputs resident in HBM:
+smla_indexer_scores_topk then smla_sparse_mla_decode (decode workloads) or _prefill. The default
+workload is the decode batch: 32 requests x 1 query token over 65,536 cached tokens each.
+
+    python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query-tokens/s per layer (indexer+top-k+sparse MLA); % of MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+DECODE_CONFIGS = (1, 4)
+STAGES = ("indexer", "topk", "mla", "combine")
+
+
+def workload_name(d):
+    return (f"{d.batch} request(s) x {d.n_q} query token(s) after {d.cached} cached tokens; "
+            f"{d.H} heads, {d.D_qk}/{d.D_v} dims, "
+            f"{'656-byte FP8' if d.kv_format == 1 else 'bf16'} latent rows, "
+            f"{d.H_I}x{d.D_I} int8 indexer, top-k {d.top_k}")
+
+
+class HipEvents:
+    """hipEvent_t handles via the HIP runtime (timing on the library's own launch stream)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.rt.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.rt.hipEventDestroy(e)
+
+
+def algorithmic(d, positions):
+    """Algorithmic work of one step (unique bytes; FLOPs/ops), per stage."""
+    import numpy as np
+
+    rows_sel = np.minimum(positions + 1, d.top_k)
+    pairs = float(np.sum(positions + 1))
+    return {
+        # every key read once per request, every query once, the weights
+        "indexer_bytes": d.total_rows * d.D_I + d.total_q * d.H_I * d.D_I + 4 * d.H_I,
+        "indexer_ops": 2.0 * d.H_I * d.D_I * pairs,
+        # the pages' accounting per query: selected rows (656 B + 4 B index) + bf16 q and out
+        "mla_bytes": float(np.sum(rows_sel)) * (d.row_bytes + 4) + d.total_q * d.H * 2 * (d.D_qk + d.D_v),
+        "mla_flops": float(np.sum(rows_sel)) * d.H * 2.0 * (d.D_qk + d.D_v),
+    }
+
+
+def cpu_baseline(x, d, sample_tokens):
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    tokens = np.asarray(sample_tokens, np.int64)
+    t0 = time.perf_counter()
+    idx, _ = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, d.top_k, tokens,
+                                       nthreads=threads)
+    full = np.full((d.total_q, d.top_k), -1, np.int32)
+    full[tokens] = idx
+    oracle.sparse_mla_batch(x.n_q, x.kv_len, x.q, x.kv, d.kv_format, d.D_v, full, d.sm_scale, tokens,
+                            nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens.size / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{tokens.size} of {d.total_q} query tokens of the same workload "
+                      f"(indexer + top-k + fp64 attention), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_indexer_amd import _lib, ops
+    from sparse_mla_attention_indexer_amd import workload as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    d = W.config_dims(args.config)
+    decode = args.config in DECODE_CONFIGS
+    print(f"[bench] generating workload {args.config} ({W.CONFIG_NAMES[args.config]})", file=sys.stderr, flush=True)
+    x = W.generate(d)
+    plan = ops.BatchPlan(x.n_q, x.kv_len, dev)
+    q = torch.from_numpy(x.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    if d.kv_format == W.KV_FP8_656:
+        kv = torch.from_numpy(x.kv).to(dev)
+    else:
+        kv = torch.from_numpy(x.kv.view(np.int16).reshape(d.total_rows, d.D_qk)).view(torch.bfloat16).to(dev)
+    q_idx = torch.from_numpy(x.q_idx).to(dev)
+    k_idx = torch.from_numpy(x.k_idx).to(dev)
+    w = torch.from_numpy(x.w).to(dev)
+    idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
+    out = torch.empty((d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((d.total_q, d.H), dtype=torch.float32, device=dev)
+    ws_topk = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
+    ws_mla = ops.mla_workspace(plan, d.H, d.D_v, d.top_k, decode)
+    torch.cuda.synchronize()
+
+    def step():
+        ops.indexer_topk(plan, q_idx, k_idx, w, d.top_k, with_scores=False, idx=idx,
+                         workspace=ws_topk)
+        ops.sparse_mla(plan, q, kv, d.kv_format, d.D_v, idx, d.sm_scale, decode=decode, out=out,
+                       lse=lse, workspace=ws_mla)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    L = _lib.lib()
+    ev = [[(hip.create(), hip.create()) for _ in STAGES] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        begin = (ctypes.c_void_p * len(STAGES))(*[e[0] for e in ev[k]])
+        end = (ctypes.c_void_p * len(STAGES))(*[e[1] for e in ev[k]])
+        _lib.check("smla_set_stage_events", L.smla_set_stage_events(begin, end, len(STAGES)))
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.smla_set_stage_events(None, None, 0)
+
+    stage_ms = {}
+    for s, name in enumerate(STAGES):
+        if name == "combine" and not (decode and ws_mla.numel() > 256):
+            continue
+        stage_ms[name] = sum(hip.elapsed_ms(*ev[k][s]) for k in range(args.steps)) / args.steps
+    for row in ev:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = d.total_q / (ms_per_step * 1e-3)
+    alg = algorithmic(d, plan.positions)
+    idx_gbs = alg["indexer_bytes"] / (stage_ms["indexer"] * 1e-3) / 1e9
+    idx_tops = alg["indexer_ops"] / (stage_ms["indexer"] * 1e-3) / 1e12
+    mla_ms = stage_ms["mla"] + stage_ms.get("combine", 0.0)
+    mla_gbs = alg["mla_bytes"] / (mla_ms * 1e-3) / 1e9
+    mla_tflops = alg["mla_flops"] / (mla_ms * 1e-3) / 1e12
+    # the indexer dominates the step; it is HBM-bound when its ops per key byte fall below the
+    # int8 ridge (5.0 POP/s / 8 TB/s = 625)
+    idx_hbm = alg["indexer_ops"] / alg["indexer_bytes"] < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if idx_hbm:
+        roof = {"bound": "hbm", "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(idx_tops, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s (int8)", "frac": round(idx_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
+    mla_hbm = alg["mla_flops"] / alg["mla_bytes"] < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mla_roof = ({"bound": "hbm", "achieved": round(mla_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(mla_gbs / HBM_PEAK_GBS, 4)} if mla_hbm else
+                {"bound": "mfma", "achieved": round(mla_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(mla_tflops / BF16_PEAK_TFLOPS, 4)})
+    mla_roof["kernel_ms"] = round(mla_ms, 4)
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "dtypes": {"indexer": "int8 x int8 -> int32", "kv": "fp8 e4m3 + fp32 block scales",
+                   "attention": "bf16 MFMA, fp32 accumulate"},
+        "data": "synthetic",
+        "config": {"workload": workload_name(d), "config_id": args.config, "batch": d.batch,
+                   "query_tokens": d.total_q, "cached_tokens": d.cached, "heads": d.H,
+                   "top_k": d.top_k, "decode_entry": decode},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roof,
+        "mla_roofline": mla_roof,
+    }
+    if not args.no_cpu_baseline:
+        sample = np.arange(d.total_q) if d.total_q <= 32 else np.linspace(0, d.total_q - 1, 32).astype(np.int64)
+        print(f"[bench] oracle on {sample.size} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, d, sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

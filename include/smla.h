@@ -1,0 +1,157 @@
+/*
+ * smla.h — C ABI of the MI355X (gfx950) library for sparse Multi-head Latent Attention with a
+ * lightning indexer: indexer scoring -> per-query exact top-k -> sparse MLA over a shared
+ * latent KV cache.
+ *
+ * What the pages define ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse on 16 H200", sections
+ * "Why DP8 and TP8 fall short", "PCP: split tokens, not heads", "Why the numbers work"):
+ *  - an indexer scores every earlier token for every query token and the 2,048 best are kept;
+ *    its cost grows with the square of the prompt, sparse MLA's only linearly;
+ *  - MLA's latent KV row is shared by all 64 heads, so one gathered row serves every head;
+ *  - QK runs over 576 dims and PV over 512; queries and outputs are BF16; a KV row is 656 bytes
+ *    of FP8 plus a 4-byte index;
+ *  - partial attention results over disjoint row sets merge by log-sum-exp (section "DCP").
+ * The indexer's formula is score(t, s) = sum_h w_h * ReLU(q_I[t,h] . k_I[s]) over s <= p(t),
+ * on int8 inputs with exact int32 results; ties go to the lower token index.
+ *
+ * Conventions for every entry point
+ *  - Pointers marked (device) are HIP device memory; (host) are host memory. The caller owns
+ *    every buffer; the library keeps no pointer after a call returns.
+ *  - GPU entry points are asynchronous on `stream` (a hipStream_t; NULL is the default stream)
+ *    and never synchronise; buffers must stay valid until the stream reaches the work.
+ *  - The library allocates no device memory: scratch comes from a caller workspace sized by the
+ *    matching *_workspace_bytes function.
+ *  - Return SMLA_OK (0) or a negative smla_status. Arguments are validated on the host before
+ *    anything is enqueued; on error nothing is enqueued and smla_last_error() describes why.
+ *  - Device pointers must be 16-byte aligned (q, kv, q_idx, k_idx, out, workspace: 256 bytes).
+ *
+ * Batch layout (all entry points): request b owns query tokens [Q_b, Q_b + n_q[b]) and latent
+ * rows / indexer keys [R_b, R_b + kv_len[b]), Q and R being exclusive prefix sums. Query j of
+ * request b sits at position p = kv_len[b] - n_q[b] + j (its own row is already in the cache)
+ * and may use rows s <= p; s is local to the request.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum smla_status {
+  SMLA_OK = 0,
+  SMLA_E_INVALID = -1,     /* null pointer, bad size, misaligned pointer, inconsistent batch */
+  SMLA_E_UNSUPPORTED = -2, /* shape outside the supported families (see each entry point) */
+  SMLA_E_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes */
+  SMLA_E_HIP = -4,         /* a HIP runtime call failed */
+} smla_status;
+
+typedef enum smla_kv_format {
+  SMLA_KV_BF16 = 0,    /* row = D_qk bfloat16 values (2*D_qk bytes) */
+  SMLA_KV_FP8_656 = 1, /* row = 656 bytes: [512 e4m3 (OCP E4M3FN) codes of dims 0..511]
+                          [4 x fp32 scale, one per 128-dim block][64 x bf16 dims 512..575];
+                          value = e4m3(code) * scale[d / 128]. Requires D_qk = 576, D_v = 512. */
+} smla_kv_format;
+
+/* Host-side summary of a batch; `table` points at the device table smla_batch_build wrote. */
+typedef struct smla_batch {
+  int32_t batch;      /* B >= 1 */
+  int32_t total_q;    /* sum of n_q */
+  int32_t max_q;      /* max n_q */
+  int32_t n_items;    /* indexer work items in the table */
+  int64_t max_kv;     /* max kv_len */
+  int64_t total_rows; /* sum of kv_len */
+  int64_t total_cand; /* sum over query tokens of (p + 1) */
+  const void* table;  /* (device) table written by smla_batch_build */
+  size_t table_bytes;
+} smla_batch;
+
+/* Device bytes smla_batch_build needs for a batch of `batch` requests and `total_q` tokens
+ * (an upper bound that holds for any lengths). */
+size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv);
+
+/*
+ * Validate a batch and write its device table. n_q (host) [batch], kv_len (host) [batch] with
+ * 1 <= n_q[b] <= kv_len[b] < 2^31 and total rows < 2^40. `table` (device, table_bytes from
+ * smla_batch_table_bytes) receives the per-request, per-token and indexer work-item tables.
+ * Blocking: returns after the table is on the device. `out` is filled on success.
+ */
+int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
+                     size_t table_bytes, void* stream, smla_batch* out);
+
+/*
+ * Indexer scores, full matrix (parity and debugging; O(total_q * max_kv) memory).
+ * q_idx (device) [total_q, H_I, D_I] int8; k_idx (device) [total_rows, D_I] int8;
+ * w (device) [H_I] int32 with w_h >= 0 and sum_h w_h * 2^14 * D_I < 2^31 (so no score can
+ * overflow; a violation gives wrong scores, never a fault).
+ * scores (device) [total_q, max_kv] int32: score(t, s) for s <= p, -1 for p < s < max_kv.
+ * Supported (H_I, D_I): (64, 128) on int8 MFMA, and H_I <= 16 with D_I a multiple of 4 up to
+ * 256 on a generic kernel.
+ */
+int smla_indexer_scores(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
+                        const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores, void* stream);
+
+/* Workspace for smla_indexer_scores_topk. */
+size_t smla_indexer_topk_workspace_bytes(const smla_batch* b, int32_t H_I, int32_t D_I,
+                                         int32_t top_k);
+
+/*
+ * Indexer scores followed by the exact per-query top-k (same inputs as smla_indexer_scores).
+ * idx (device) [total_q, top_k] int32: the min(top_k, p+1) local row indices with the largest
+ * scores, ties to the lower index (all s <= p when p+1 <= top_k), in ascending index order,
+ * then -1 padding. score (device, optional) [total_q, top_k] int32: the score of each selected
+ * index, -1 on padding. 1 <= top_k <= 2048.
+ */
+int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
+                             const int32_t* w, int32_t H_I, int32_t D_I, int32_t top_k,
+                             int32_t* idx, int32_t* score, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Workspace for the sparse-MLA entry points (decode needs split partials; prefill none). */
+size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v,
+                                       int32_t top_k, int32_t decode);
+
+/*
+ * Sparse MLA in MQA form: every head attends over the same selected rows.
+ * q (device) [total_q, H, D_qk] bf16; kv (device) [total_rows] rows of `kv_format`;
+ * idx (device) [total_q, top_k] int32 local row indices (any order; -1 entries are skipped;
+ * indices above the token's position p are treated like -1, so no row past p is ever read);
+ * out (device) [total_q, H, D_v] bf16; lse (device, optional) [total_q, H] fp32 natural-log
+ * log-sum-exp of the scaled logits (-inf and zero output for a token with no valid index).
+ * logit_i = sm_scale * q_h . v_i over D_qk dims; output = softmax-weighted sum of v_i[0:D_v].
+ * Supported: FP8_656 with (H, D_qk, D_v) = (64, 576, 512) on bf16 MFMA; BF16 rows with H <= 16,
+ * D_qk <= 256, D_v <= D_qk on a generic kernel. top_k <= 2048.
+ * _prefill runs one workgroup per query token; _decode also splits each token's rows across
+ * workgroups and merges the partials by log-sum-exp (for few query tokens).
+ */
+int smla_sparse_mla_prefill(const smla_batch* b, const void* q, const void* kv, int32_t kv_format,
+                            int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx,
+                            int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, int32_t kv_format,
+                           int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx,
+                           int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Optional per-stage timing for benchmarks and profilers: while set, the GPU entry points record
+ * begin[s] before and end[s] after the launches of stage s on the call's stream, for
+ * s = 0 indexer scores, 1 top-k select, 2 sparse MLA, 3 split-KV combine (decode only).
+ * begin/end (host arrays of n hipEvent_t, caller-owned; entries may be NULL) are read at each
+ * call; pass n = 0 to stop. Process-wide setting: set it only while no other thread calls the
+ * library.
+ */
+int smla_set_stage_events(void* const* begin, void* const* end, int32_t n);
+
+/* Status name and the calling thread's last error message ("" if none). */
+const char* smla_status_str(int status);
+const char* smla_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMLA_H */

@@ -1,0 +1,345 @@
+// api.cpp — host side of the C ABI (include/smla.h): argument validation, the batch table and
+// indexer work plan, workspace sizing and kernel launches. Every check runs before anything is
+// enqueued; failures set a thread-local message and return a negative status.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SMLA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_batch(const smla_batch* b) {
+  if (!b) return fail(SMLA_E_INVALID, "batch is NULL");
+  if (b->batch < 1 || b->total_q < 1 || b->max_q < 1 || b->max_kv < 1 || b->total_rows < 1 ||
+      b->n_items < 0 || !b->table)
+    return fail(SMLA_E_INVALID, "batch descriptor is not initialised (call smla_batch_build)");
+  if (!aligned(b->table, 16)) return fail(SMLA_E_INVALID, "batch table is not 16-byte aligned");
+  return SMLA_OK;
+}
+
+int check_indexer_args(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
+                       const int32_t* w, int32_t H_I, int32_t D_I, bool* mfma) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!q_idx || !k_idx || !w) return fail(SMLA_E_INVALID, "q_idx, k_idx and w must be non-NULL");
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(w, 4))
+    return fail(SMLA_E_INVALID, "q_idx and k_idx must be 16-byte aligned, w 4-byte aligned");
+  if (H_I == 64 && D_I == 128) {
+    *mfma = true;
+    return SMLA_OK;
+  }
+  if (H_I >= 1 && H_I <= 16 && D_I >= 4 && D_I <= 256 && D_I % 4 == 0) {
+    *mfma = false;
+    return SMLA_OK;
+  }
+  return fail(SMLA_E_UNSUPPORTED,
+              "indexer shape H_I=%d D_I=%d unsupported (64x128, or H_I<=16 with D_I%%4==0<=256)",
+              H_I, D_I);
+}
+
+int check_mla_args(const smla_batch* b, const void* q, const void* kv, int32_t fmt, int32_t H,
+                   int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k, const void* out,
+                   bool* fp8) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!q || !kv || !idx || !out) return fail(SMLA_E_INVALID, "q, kv, idx and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4) || !aligned(out, 16))
+    return fail(SMLA_E_INVALID, "q, kv and out must be 16-byte aligned, idx 4-byte aligned");
+  if (top_k < 1 || top_k > smla::TOPK_MAX_K)
+    return fail(SMLA_E_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, smla::TOPK_MAX_K);
+  if (fmt == SMLA_KV_FP8_656) {
+    if (H != 64 || D_qk != 576 || D_v != 512)
+      return fail(SMLA_E_UNSUPPORTED, "FP8_656 rows need H=64, D_qk=576, D_v=512 (got %d, %d, %d)",
+                  H, D_qk, D_v);
+    *fp8 = true;
+    return SMLA_OK;
+  }
+  if (fmt == SMLA_KV_BF16) {
+    if (H < 1 || H > 16 || D_qk < 1 || D_qk > 256 || D_v < 1 || D_v > D_qk)
+      return fail(SMLA_E_UNSUPPORTED, "BF16 rows need H<=16, D_qk<=256, D_v<=D_qk (got %d, %d, %d)",
+                  H, D_qk, D_v);
+    *fp8 = false;
+    return SMLA_OK;
+  }
+  return fail(SMLA_E_INVALID, "unknown kv_format %d", fmt);
+}
+
+// Indexer work plan: query tiles of up to QT tokens, tile i paired with tile n-1-i, each pair's
+// combined key range (front tile's keys, then back tile's) cut into KEY_CHUNK-key items.
+void plan_items(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                const std::vector<int32_t>& q_start, std::vector<smla::Item>* items) {
+  using smla::Item;
+  using smla::Seg;
+  const int64_t C = smla::KEY_CHUNK;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t base = kv_len[b] - n_q[b];
+    const int32_t nt = (n_q[b] + smla::QT - 1) / smla::QT;
+    auto tile = [&](int32_t i, int64_t* extent, int32_t* q0, int32_t* nq) {
+      const int32_t lo = i * smla::QT;
+      const int32_t hi = std::min<int32_t>(n_q[b], lo + smla::QT);
+      *q0 = q_start[b] + lo;
+      *nq = hi - lo;
+      *extent = base + hi;  // keys [0, extent) cover every position of the tile
+    };
+    for (int32_t i = 0; i < (nt + 1) / 2; ++i) {
+      const int32_t j = nt - 1 - i;
+      int64_t ea, eb = 0;
+      int32_t qa, na, qb = 0, nb = 0;
+      tile(i, &ea, &qa, &na);
+      if (j != i) tile(j, &eb, &qb, &nb);
+      const int64_t E = ea + eb;
+      for (int64_t c0 = 0; c0 < E; c0 += C) {
+        const int64_t c1 = std::min(E, c0 + C);
+        Seg segs[2];
+        int ns = 0;
+        if (c0 < ea) segs[ns++] = Seg{qa, na, (int32_t)c0, (int32_t)std::min(c1, ea)};
+        if (c1 > ea && nb > 0)
+          segs[ns++] = Seg{qb, nb, (int32_t)(std::max(c0, ea) - ea), (int32_t)(c1 - ea)};
+        Item it;
+        it.a = segs[0];
+        it.b = ns > 1 ? segs[1] : Seg{0, 0, 0, 0};
+        items->push_back(it);
+      }
+    }
+  }
+}
+
+size_t table_layout(int32_t batch, int32_t total_q, int64_t n_items) {
+  return smla::align_up(sizeof(smla::Req) * batch, 256) +
+         smla::align_up(sizeof(smla::Tok) * (size_t)total_q, 256) +
+         smla::align_up(sizeof(smla::Item) * (size_t)(n_items > 0 ? n_items : 1), 256);
+}
+
+hipEvent_t g_stage_begin[smla::N_STAGES] = {};
+hipEvent_t g_stage_end[smla::N_STAGES] = {};
+
+}  // namespace
+
+void smla::mark_stage(int s, bool end, hipStream_t st) {
+  hipEvent_t e = end ? g_stage_end[s] : g_stage_begin[s];
+  if (e) (void)hipEventRecord(e, st);
+}
+
+extern "C" {
+
+int smla_set_stage_events(void* const* begin, void* const* end, int32_t n) {
+  g_err.clear();
+  if (n < 0 || n > smla::N_STAGES || (n > 0 && (!begin || !end)))
+    return fail(SMLA_E_INVALID, "stage events: 0 <= n <= %d with non-NULL arrays", smla::N_STAGES);
+  for (int s = 0; s < smla::N_STAGES; ++s) {
+    g_stage_begin[s] = s < n ? static_cast<hipEvent_t>(begin[s]) : nullptr;
+    g_stage_end[s] = s < n ? static_cast<hipEvent_t>(end[s]) : nullptr;
+  }
+  return SMLA_OK;
+}
+
+size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv) {
+  if (batch < 1 || total_q < 1 || max_kv < 1) return 0;
+  // every tile pair contributes at most ceil(E / C) <= E / C + 1 items, E <= 2 * max_kv
+  const int64_t tiles = (int64_t)total_q / smla::QT + batch;
+  const int64_t items = tiles * (max_kv / smla::KEY_CHUNK + 2);
+  return table_layout(batch, total_q, items);
+}
+
+int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
+                     size_t table_bytes, void* stream, smla_batch* out) {
+  g_err.clear();
+  if (batch < 1 || !n_q || !kv_len || !table || !out)
+    return fail(SMLA_E_INVALID, "batch >= 1 and non-NULL n_q, kv_len, table, out required");
+  if (!aligned(table, 256)) return fail(SMLA_E_INVALID, "table must be 256-byte aligned");
+  int64_t total_q = 0, total_rows = 0, max_kv = 0, total_cand = 0;
+  int32_t max_q = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (n_q[b] < 1 || kv_len[b] < n_q[b] || kv_len[b] >= (int64_t(1) << 31))
+      return fail(SMLA_E_INVALID, "request %d: need 1 <= n_q (%d) <= kv_len (%lld) < 2^31", b, n_q[b],
+                  (long long)kv_len[b]);
+    total_q += n_q[b];
+    total_rows += kv_len[b];
+    max_kv = std::max<int64_t>(max_kv, kv_len[b]);
+    max_q = std::max(max_q, n_q[b]);
+    // positions kv_len - n_q .. kv_len - 1 see (p + 1) candidates each
+    total_cand += (int64_t)n_q[b] * (2 * kv_len[b] - n_q[b] + 1) / 2;
+  }
+  if (total_q >= (int64_t(1) << 31)) return fail(SMLA_E_INVALID, "too many query tokens");
+  if (total_rows >= (int64_t(1) << 40)) return fail(SMLA_E_INVALID, "too many rows");
+  std::vector<smla::Req> req(batch);
+  std::vector<smla::Tok> tok((size_t)total_q);
+  std::vector<int32_t> q_start(batch);
+  int64_t q0 = 0, r0 = 0, cand = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    q_start[b] = (int32_t)q0;
+    req[b] = smla::Req{r0, kv_len[b], (int32_t)q0, n_q[b], 0};
+    for (int32_t j = 0; j < n_q[b]; ++j) {
+      const int64_t p = kv_len[b] - n_q[b] + j;
+      tok[(size_t)(q0 + j)] = smla::Tok{r0, cand, (int32_t)p, b, 0};
+      cand += p + 1;
+    }
+    q0 += n_q[b];
+    r0 += kv_len[b];
+  }
+  std::vector<smla::Item> items;
+  plan_items(batch, n_q, kv_len, q_start, &items);
+  const size_t need = table_layout(batch, (int32_t)total_q, (int64_t)items.size());
+  if (table_bytes < need)
+    return fail(SMLA_E_WORKSPACE, "table needs %zu bytes, got %zu", need, table_bytes);
+  std::vector<unsigned char> host(need, 0);
+  const size_t off_tok = smla::align_up(sizeof(smla::Req) * batch, 256);
+  const size_t off_item = off_tok + smla::align_up(sizeof(smla::Tok) * (size_t)total_q, 256);
+  memcpy(host.data(), req.data(), sizeof(smla::Req) * batch);
+  memcpy(host.data() + off_tok, tok.data(), sizeof(smla::Tok) * (size_t)total_q);
+  if (!items.empty()) memcpy(host.data() + off_item, items.data(), sizeof(smla::Item) * items.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(table, host.data(), need, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(batch table)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(batch table)");
+  out->batch = batch;
+  out->total_q = (int32_t)total_q;
+  out->max_q = max_q;
+  out->n_items = (int32_t)items.size();
+  out->max_kv = max_kv;
+  out->total_rows = total_rows;
+  out->total_cand = total_cand;
+  out->table = table;
+  out->table_bytes = need;
+  return SMLA_OK;
+}
+
+int smla_indexer_scores(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
+                        const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores, void* stream) {
+  g_err.clear();
+  bool mfma = false;
+  int rc = check_indexer_args(b, q_idx, k_idx, w, H_I, D_I, &mfma);
+  if (rc) return rc;
+  if (!scores || !aligned(scores, 16)) return fail(SMLA_E_INVALID, "scores must be non-NULL, 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = smla::launch_fill_i32(scores, (int64_t)b->total_q * b->max_kv, -1, s);
+  if (e == hipSuccess)
+    e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 0, s)
+             : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 0, s);
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "indexer launch");
+}
+
+size_t smla_indexer_topk_workspace_bytes(const smla_batch* b, int32_t /*H_I*/, int32_t /*D_I*/,
+                                         int32_t top_k) {
+  if (!b || b->total_q < 1) return 0;
+  return smla::align_up(sizeof(int32_t) * (size_t)b->total_cand, 256) +
+         smla::topk_workspace_bytes(*b, top_k);
+}
+
+int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
+                             const int32_t* w, int32_t H_I, int32_t D_I, int32_t top_k,
+                             int32_t* idx, int32_t* score, void* ws, size_t ws_bytes,
+                             void* stream) {
+  g_err.clear();
+  bool mfma = false;
+  int rc = check_indexer_args(b, q_idx, k_idx, w, H_I, D_I, &mfma);
+  if (rc) return rc;
+  if (top_k < 1 || top_k > smla::TOPK_MAX_K)
+    return fail(SMLA_E_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, smla::TOPK_MAX_K);
+  if (!idx || !aligned(idx, 4) || (score && !aligned(score, 4)))
+    return fail(SMLA_E_INVALID, "idx must be non-NULL; idx and score 4-byte aligned");
+  const size_t need = smla_indexer_topk_workspace_bytes(b, H_I, D_I, top_k);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(SMLA_E_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* scores = static_cast<int32_t*>(ws);
+  void* tws = static_cast<char*>(ws) + smla::align_up(sizeof(int32_t) * (size_t)b->total_cand, 256);
+  smla::mark_stage(smla::STAGE_INDEXER, false, s);
+  hipError_t e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 1, s)
+                      : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 1, s);
+  smla::mark_stage(smla::STAGE_INDEXER, true, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  smla::mark_stage(smla::STAGE_TOPK, false, s);
+  e = smla::launch_topk(*b, scores, top_k, idx, score, tws, s);
+  smla::mark_stage(smla::STAGE_TOPK, true, s);
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k launch");
+}
+
+size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v, int32_t top_k,
+                                       int32_t decode) {
+  if (!b || b->total_q < 1 || top_k < 1) return 0;
+  return smla::mla_workspace_bytes(*b, H, D_v, top_k, decode);
+}
+
+static int sparse_mla(const smla_batch* b, const void* q, const void* kv, int32_t kv_format,
+                      int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
+                      float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                      void* stream, int decode) {
+  g_err.clear();
+  bool fp8 = false;
+  int rc = check_mla_args(b, q, kv, kv_format, H, D_qk, D_v, idx, top_k, out, &fp8);
+  if (rc) return rc;
+  if (lse && !aligned(lse, 4)) return fail(SMLA_E_INVALID, "lse must be 4-byte aligned");
+  if (!(sm_scale > 0.f) || sm_scale > 1e30f) return fail(SMLA_E_INVALID, "sm_scale must be positive and finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (fp8) {
+    const size_t need = smla::mla_workspace_bytes(*b, H, D_v, top_k, decode);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, 256)))
+      return fail(SMLA_E_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+    e = smla::launch_mla_fp8(*b, q, kv, idx, top_k, sm_scale, out, lse, ws, decode, s);
+  } else {
+    smla::mark_stage(smla::STAGE_MLA, false, s);
+    e = smla::launch_mla_generic(*b, q, kv, H, D_qk, D_v, idx, top_k, sm_scale, out, lse, s);
+    smla::mark_stage(smla::STAGE_MLA, true, s);
+  }
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "sparse MLA launch");
+}
+
+int smla_sparse_mla_prefill(const smla_batch* b, const void* q, const void* kv, int32_t kv_format,
+                            int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx,
+                            int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return sparse_mla(b, q, kv, kv_format, H, D_qk, D_v, idx, top_k, sm_scale, out, lse, ws,
+                    ws_bytes, stream, 0);
+}
+
+int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, int32_t kv_format,
+                           int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx,
+                           int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return sparse_mla(b, q, kv, kv_format, H, D_qk, D_v, idx, top_k, sm_scale, out, lse, ws,
+                    ws_bytes, stream, 1);
+}
+
+const char* smla_status_str(int status) {
+  switch (status) {
+    case SMLA_OK: return "SMLA_OK";
+    case SMLA_E_INVALID: return "SMLA_E_INVALID";
+    case SMLA_E_UNSUPPORTED: return "SMLA_E_UNSUPPORTED";
+    case SMLA_E_WORKSPACE: return "SMLA_E_WORKSPACE";
+    case SMLA_E_HIP: return "SMLA_E_HIP";
+    default: return "SMLA_E_UNKNOWN";
+  }
+}
+
+const char* smla_last_error(void) { return g_err.c_str(); }
+
+int32_t smla_version(void) { return 100; }
+
+}  // extern "C"

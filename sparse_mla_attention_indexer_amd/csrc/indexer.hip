@@ -1,0 +1,175 @@
+// indexer.hip — lightning-indexer scores on gfx950.
+//
+// score(t, s) = sum_h w_h * ReLU(q_I[t,h] . k_I[s]) for every earlier token s <= p(t): the
+// indexer that scores every earlier token so sparse MLA can keep the best 2,048 ("Serving
+// GLM-5.3 ... PCP, DCP, Hybrid HiSparse", sections "Why DP8 and TP8 fall short" and "PCP:
+// split tokens, not heads"; the formula is the workload definition of the tiny causal prefill).
+//
+// 64 heads x 128 dims: a dense int8 contraction per (query, key) pair, run on
+// v_mfma_i32_32x32x32_i8 with the heads of one query token as the M dimension (two 32-row
+// tiles) and 32 keys as N. Keys go straight from HBM into B-operand registers: the contraction
+// order over the 128 dims is permuted so every lane reads 64 contiguous bytes of its key (lane
+// half h covers dims [64h, 64h+64)), and the query fragments use the same permutation. The
+// ReLU * w head reduction runs in the accumulator registers, then across the two lane halves.
+//
+// Work is planned on the host (smla_batch_build): query tiles of up to 4 tokens are paired
+// front with back (tile i with tile n-1-i), the pages' load-balanced chunk pairing applied to
+// causal query tiles on one GPU, and each pair's combined key range is cut into equal chunks.
+#include "smla_internal.h"
+
+namespace smla {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+namespace {
+
+constexpr int IDX_H = 64;
+constexpr int IDX_D = 128;
+
+// One wave: query token t against key tiles s = s_begin, s_begin + step, ... < s_end, s <= p.
+__device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
+                                             int step, const int8_t* __restrict__ q_idx,
+                                             const int8_t* __restrict__ k_idx,
+                                             const int (&wl)[2][16], int32_t* __restrict__ out_row) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int p = tk.pos;
+  // A fragments: head 32*mt + col, dims [64*half + 16*j, +16)
+  v4i qa[2][4];
+  const int8_t* qbase = q_idx + t * (IDX_H * IDX_D);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
+
+  const int8_t* kbase = k_idx + tk.row_start * IDX_D + 64 * half;
+  const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
+  for (int s = s_begin; s <= last; s += step) {
+    int key = s + col;
+    const int kr = key < last ? key : last;  // clamp: never read past the visible rows
+    const v4i* kp = reinterpret_cast<const v4i*>(kbase + (int64_t)kr * IDX_D);
+    v4i kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = kp[j];
+    v16i acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+    }
+    // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them
+    uint32_t sum = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sum += (uint32_t)max(acc0[r], 0) * (uint32_t)wl[0][r];
+      sum += (uint32_t)max(acc1[r], 0) * (uint32_t)wl[1][r];
+    }
+    sum += (uint32_t)__shfl_xor((int)sum, 32);
+    if (half == 0 && key <= last) out_row[key] = (int32_t)sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void indexer_mfma_kernel(const Item* __restrict__ items,
+                                                           const Tok* __restrict__ toks,
+                                                           const int8_t* __restrict__ q_idx,
+                                                           const int8_t* __restrict__ k_idx,
+                                                           const int32_t* __restrict__ w,
+                                                           int32_t* __restrict__ scores,
+                                                           int64_t stride) {
+  const Item it = items[blockIdx.x];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  int wl[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wl[mt][r] = w[32 * mt + 8 * (r >> 2) + 4 * half + (r & 3)];
+
+#pragma unroll 1
+  for (int sgi = 0; sgi < 2; ++sgi) {
+    const Seg sg = sgi == 0 ? it.a : it.b;
+    if (sg.nq <= 0) continue;
+    // waves per query: 4 for a single query (they split the key tiles), 2 for two, else 1
+    const int qpw = sg.nq == 1 ? 4 : (sg.nq == 2 ? 2 : 1);
+    const int qi = wave / qpw;
+    if (qi >= sg.nq) continue;
+    const int phase = wave - qi * qpw;
+    const int64_t t = sg.q0 + qi;
+    const Tok tk = toks[t];
+    int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
+    indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row);
+  }
+}
+
+// Generic small-shape indexer: one thread per (query, key); H_I <= 16, D_I % 4 == 0, <= 256.
+__global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restrict__ toks,
+                                                              const int8_t* __restrict__ q_idx,
+                                                              const int8_t* __restrict__ k_idx,
+                                                              const int32_t* __restrict__ w,
+                                                              int H_I, int D_I,
+                                                              int32_t* __restrict__ scores,
+                                                              int64_t stride) {
+  __shared__ int qs[16 * 64];
+  __shared__ int ws[16];
+  const int64_t t = blockIdx.x;
+  const Tok tk = toks[t];
+  const int nw = D_I / 4;
+  const int* qsrc = reinterpret_cast<const int*>(q_idx + t * H_I * D_I);
+  for (int i = threadIdx.x; i < H_I * nw; i += blockDim.x) qs[i] = qsrc[i];
+  if (threadIdx.x < H_I) ws[threadIdx.x] = w[threadIdx.x];
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+  if (s > tk.pos) return;
+  const int* kr = reinterpret_cast<const int*>(k_idx + (tk.row_start + s) * D_I);
+  uint32_t score = 0;
+  for (int h = 0; h < H_I; ++h) {
+    int dot = 0;
+    for (int i = 0; i < nw; ++i) dot = __builtin_amdgcn_sdot4(qs[h * nw + i], kr[i], dot, false);
+    score += (uint32_t)max(dot, 0) * (uint32_t)ws[h];
+  }
+  int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
+  out_row[s] = (int32_t)score;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
+                               const int32_t* w, int32_t* scores, int compact, hipStream_t s) {
+  if (b.n_items <= 0) return hipSuccess;
+  TableView tv = table_view(b.table, b.batch, b.total_q);
+  const int64_t stride = compact ? 0 : b.max_kv;
+  hipLaunchKernelGGL(indexer_mfma_kernel, dim3(b.n_items), dim3(256), 0, s, tv.item, tv.tok,
+                     q_idx, k_idx, w, scores, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
+                                  const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores,
+                                  int compact, hipStream_t s) {
+  TableView tv = table_view(b.table, b.batch, b.total_q);
+  const int64_t stride = compact ? 0 : b.max_kv;
+  dim3 grid((unsigned)b.total_q, (unsigned)((b.max_kv + 255) / 256));
+  hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), 0, s, tv.tok, q_idx, k_idx, w, H_I,
+                     D_I, scores, stride);
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,0 +1,104 @@
+// smla_internal.h — layouts and constants shared by the library's host code and its gfx950
+// kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smla.h"
+
+namespace smla {
+
+// ---- device batch table (written by smla_batch_build, read by every kernel) --------------
+// Layout inside the caller's table buffer: [Req x batch][Tok x total_q][Item x n_items].
+struct alignas(16) Req {
+  int64_t row_start;  // first row of the request in k_idx / kv
+  int64_t kv_len;     // rows of the request (cached + its own queries)
+  int32_t q_start;    // first global query token
+  int32_t n_q;        // query tokens
+  int64_t _pad;
+};
+struct alignas(16) Tok {
+  int64_t row_start;  // row_start of the token's request
+  int64_t cand_off;   // offset of the token's causal score row in compact layout
+  int32_t pos;        // position p: rows s <= p are visible
+  int32_t req;        // request id
+  int64_t _pad;
+};
+// One indexer workgroup's work: up to two segments (a front query tile and a back query tile
+// of the same request), each `nq` consecutive query tokens from global token `q0` against the
+// keys [s0, s1) of their request.
+struct alignas(16) Seg {
+  int32_t q0, nq, s0, s1;
+};
+struct alignas(32) Item {
+  Seg a, b;
+};
+
+// Indexer planning: query tiles of up to QT tokens; each front/back pair of tiles is cut into
+// chunks of KEY_CHUNK keys of combined work.
+constexpr int QT = 4;
+constexpr int KEY_CHUNK = 4096;
+
+// Top-k: rows with n <= TOPK_LDS_MAX candidates are selected by one workgroup in LDS; longer
+// rows go through histogram / filter / resolve over segments of TOPK_SEG candidates.
+constexpr int TOPK_MAX_K = 2048;
+constexpr int TOPK_LDS_MAX = 32768;
+constexpr int TOPK_SEG = 8192;
+constexpr int TOPK_BINS = 4096;
+constexpr int TOPK_CAND_CAP = 16384;
+
+// Sparse MLA (big shape): heads, dims, rows per tile, decode splits.
+constexpr int MLA_H = 64;
+constexpr int MLA_DQK = 576;
+constexpr int MLA_DV = 512;
+constexpr int MLA_ROW_BYTES = 656;
+constexpr int MLA_TILE = 64;
+
+inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct TableView {
+  const Req* req;
+  const Tok* tok;
+  const Item* item;
+};
+
+inline __host__ __device__ TableView table_view(const void* base, int32_t batch, int32_t total_q) {
+  const char* p = static_cast<const char*>(base);
+  TableView v;
+  v.req = reinterpret_cast<const Req*>(p);
+  v.tok = reinterpret_cast<const Tok*>(p + align_up(sizeof(Req) * batch, 256));
+  v.item = reinterpret_cast<const Item*>(p + align_up(sizeof(Req) * batch, 256) +
+                                         align_up(sizeof(Tok) * (size_t)total_q, 256));
+  return v;
+}
+
+// ---- optional per-stage events (smla_set_stage_events) -------------------------------------
+enum Stage { STAGE_INDEXER = 0, STAGE_TOPK = 1, STAGE_MLA = 2, STAGE_COMBINE = 3, N_STAGES = 4 };
+// Record the begin (end = false) or end event of stage s on stream st, if one is set.
+void mark_stage(int s, bool end, hipStream_t st);
+
+// ---- kernel launchers (defined in the .hip files) -----------------------------------------
+// Each returns hipSuccess or the launch error; arguments were validated by the caller.
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
+
+hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
+                               const int32_t* w, int32_t* scores, int compact, hipStream_t s);
+hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
+                                  const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores,
+                                  int compact, hipStream_t s);
+
+size_t topk_workspace_bytes(const smla_batch& b, int32_t top_k);
+hipError_t launch_topk(const smla_batch& b, const int32_t* scores_compact, int32_t top_k,
+                       int32_t* idx, int32_t* score, void* ws, hipStream_t s);
+
+size_t mla_workspace_bytes(const smla_batch& b, int32_t H, int32_t D_v, int32_t top_k, int decode);
+int mla_decode_splits(const smla_batch& b, int32_t top_k);
+hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, const int32_t* idx,
+                          int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
+                          int decode, hipStream_t s);
+hipError_t launch_mla_generic(const smla_batch& b, const void* q, const void* kv, int32_t H,
+                              int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
+                              float sm_scale, void* out, float* lse, hipStream_t s);
+
+}  // namespace smla

@@ -1,0 +1,171 @@
+"""Torch-facing wrappers over the C ABI (argument marshalling and host-side shape checks only).
+
+torch provides device memory and the current HIP stream; every step of the path runs in the
+library's gfx950 kernels. Shapes are checked here against the batch plan before any launch, so a
+kernel never sees buffers smaller than its grid assumes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import KV_BF16, KV_FP8_656, Batch, check, lib
+
+__all__ = ["BatchPlan", "indexer_scores", "indexer_topk", "sparse_mla", "KV_BF16", "KV_FP8_656"]
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _req(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+class BatchPlan:
+    """Device batch table for requests with `n_q[b]` query tokens and `kv_len[b]` cached rows
+    (queries are the last n_q rows of their request). Built once, reused by every call."""
+
+    def __init__(self, n_q, kv_len, device="cuda:0"):
+        self.device = torch.device(device)
+        self.n_q = np.ascontiguousarray(n_q, np.int32).reshape(-1)
+        self.kv_len = np.ascontiguousarray(kv_len, np.int64).reshape(-1)
+        if self.n_q.size != self.kv_len.size or self.n_q.size < 1:
+            raise ValueError("n_q and kv_len must be non-empty and of equal length")
+        B = int(self.n_q.size)
+        total_q = int(self.n_q.sum())
+        max_kv = int(self.kv_len.max())
+        nbytes = int(lib().smla_batch_table_bytes(B, total_q, max_kv))
+        if nbytes == 0:
+            raise ValueError("invalid batch sizes")
+        self.table = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.desc = Batch()
+        with torch.cuda.device(self.device):
+            check("smla_batch_build",
+                  lib().smla_batch_build(B, self.n_q.ctypes.data, self.kv_len.ctypes.data,
+                                         self.table.data_ptr(), nbytes, _stream(self.device),
+                                         ctypes.byref(self.desc)))
+        self.batch = B
+        self.total_q = total_q
+        self.total_rows = int(self.kv_len.sum())
+        self.max_kv = max_kv
+        self.positions = np.concatenate(
+            [np.arange(k - n, k) for n, k in zip(self.n_q, self.kv_len)]).astype(np.int64)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def _check_indexer(plan: BatchPlan, q_idx, k_idx, w):
+    d = plan.device
+    if q_idx.dim() != 3:
+        raise ValueError("q_idx must be [total_q, H_I, D_I]")
+    H_I, D_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    _req(q_idx, "q_idx", torch.int8, (plan.total_q, H_I, D_I), d)
+    if k_idx.dim() != 2 or k_idx.shape[0] < plan.total_rows:
+        raise ValueError(f"k_idx must be [>= {plan.total_rows}, D_I]")
+    _req(k_idx, "k_idx", torch.int8, (k_idx.shape[0], D_I), d)
+    _req(w, "w", torch.int32, (H_I,), d)
+    return H_I, D_I
+
+
+def indexer_scores(plan: BatchPlan, q_idx, k_idx, w, out=None):
+    """Full score matrix [total_q, max_kv] int32 (-1 where s > p)."""
+    H_I, D_I = _check_indexer(plan, q_idx, k_idx, w)
+    if out is None:
+        out = torch.empty((plan.total_q, plan.max_kv), dtype=torch.int32, device=plan.device)
+    _req(out, "out", torch.int32, (plan.total_q, plan.max_kv), plan.device)
+    with torch.cuda.device(plan.device):
+        check("smla_indexer_scores",
+              lib().smla_indexer_scores(plan.ref, q_idx.data_ptr(), k_idx.data_ptr(), w.data_ptr(),
+                                        H_I, D_I, out.data_ptr(), _stream(plan.device)))
+    return out
+
+
+def topk_workspace(plan: BatchPlan, H_I: int, D_I: int, top_k: int) -> torch.Tensor:
+    n = int(lib().smla_indexer_topk_workspace_bytes(plan.ref, H_I, D_I, top_k))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)
+
+
+def indexer_topk(plan: BatchPlan, q_idx, k_idx, w, top_k: int, with_scores=True, idx=None,
+                 score=None, workspace=None):
+    """Exact top-k per query token: idx [total_q, top_k] ascending, -1 padded; optional scores."""
+    H_I, D_I = _check_indexer(plan, q_idx, k_idx, w)
+    shape = (plan.total_q, top_k)
+    if idx is None:
+        idx = torch.empty(shape, dtype=torch.int32, device=plan.device)
+    _req(idx, "idx", torch.int32, shape, plan.device)
+    if with_scores and score is None:
+        score = torch.empty(shape, dtype=torch.int32, device=plan.device)
+    if score is not None:
+        _req(score, "score", torch.int32, shape, plan.device)
+    if workspace is None:
+        workspace = topk_workspace(plan, H_I, D_I, top_k)
+    with torch.cuda.device(plan.device):
+        check("smla_indexer_scores_topk",
+              lib().smla_indexer_scores_topk(plan.ref, q_idx.data_ptr(), k_idx.data_ptr(),
+                                             w.data_ptr(), H_I, D_I, top_k, idx.data_ptr(),
+                                             score.data_ptr() if score is not None else None,
+                                             workspace.data_ptr(), workspace.numel(),
+                                             _stream(plan.device)))
+    return idx, score
+
+
+def mla_workspace(plan: BatchPlan, H: int, D_v: int, top_k: int, decode: bool) -> torch.Tensor:
+    n = int(lib().smla_sparse_mla_workspace_bytes(plan.ref, H, D_v, top_k, int(decode)))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)
+
+
+def sparse_mla(plan: BatchPlan, q, kv, kv_format: int, D_v: int, idx, sm_scale: float,
+               decode=False, with_lse=True, out=None, lse=None, workspace=None):
+    """Sparse MLA over the selected rows: out [total_q, H, D_v] bf16 (+ lse [total_q, H] fp32).
+
+    q is [total_q, H, D_qk] bf16; kv is [>= total_rows, row_bytes] uint8 (656-byte FP8 rows) or
+    [>= total_rows, D_qk] bf16; idx is [total_q, top_k] int32."""
+    d = plan.device
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, H, D_qk]")
+    H, D_qk = int(q.shape[1]), int(q.shape[2])
+    _req(q, "q", torch.bfloat16, (plan.total_q, H, D_qk), d)
+    if kv_format == KV_FP8_656:
+        if kv.dim() != 2 or kv.shape[0] < plan.total_rows:
+            raise ValueError(f"kv must be [>= {plan.total_rows}, 656] uint8")
+        _req(kv, "kv", torch.uint8, (kv.shape[0], 656), d)
+    elif kv_format == KV_BF16:
+        if kv.dim() != 2 or kv.shape[0] < plan.total_rows:
+            raise ValueError(f"kv must be [>= {plan.total_rows}, {D_qk}] bf16")
+        _req(kv, "kv", torch.bfloat16, (kv.shape[0], D_qk), d)
+    else:
+        raise ValueError(f"unknown kv_format {kv_format}")
+    if idx.dim() != 2:
+        raise ValueError("idx must be [total_q, top_k]")
+    top_k = int(idx.shape[1])
+    _req(idx, "idx", torch.int32, (plan.total_q, top_k), d)
+    if out is None:
+        out = torch.empty((plan.total_q, H, D_v), dtype=torch.bfloat16, device=d)
+    _req(out, "out", torch.bfloat16, (plan.total_q, H, D_v), d)
+    if with_lse and lse is None:
+        lse = torch.empty((plan.total_q, H), dtype=torch.float32, device=d)
+    if lse is not None:
+        _req(lse, "lse", torch.float32, (plan.total_q, H), d)
+    if workspace is None:
+        workspace = mla_workspace(plan, H, D_v, top_k, decode)
+    fn = "smla_sparse_mla_decode" if decode else "smla_sparse_mla_prefill"
+    with torch.cuda.device(d):
+        check(fn, getattr(lib(), fn)(plan.ref, q.data_ptr(), kv.data_ptr(), kv_format, H, D_qk, D_v,
+                                     idx.data_ptr(), top_k, float(sm_scale), out.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     workspace.data_ptr(), workspace.numel(), _stream(d)))
+    return out, lse

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/smla.h
+declares, and rejects bad arguments on the host before touching the device. Also checks that the
+product never reaches the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_mla_attention_indexer_amd import _build, _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions(name):
+    text = open(os.path.join(ROOT, "include", name)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        _build.build_hip()
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _header_functions("smla.h")
+    assert set(declared) == set(_lib.EXPORTS)
+    for fn in declared:
+        assert hasattr(L, fn), fn
+
+
+def test_workload_library_exports_declared_symbols():
+    from sparse_mla_attention_indexer_amd import workload as W
+
+    L = W.lib()
+    for fn in _header_functions("smla_workload.h"):
+        assert hasattr(L, fn), fn
+
+
+def _fake_batch(**kw):
+    b = _lib.Batch()
+    b.batch, b.total_q, b.max_q, b.n_items = 1, 4, 4, 1
+    b.max_kv, b.total_rows, b.total_cand = 100, 100, 394
+    b.table, b.table_bytes = 0x10000, 4096
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+FAKE = 0x20000  # aligned, never dereferenced: validation fails before any launch
+
+
+def test_batch_build_rejects_bad_lengths(L):
+    out = _lib.Batch()
+    n_q = np.array([2, 5], np.int32)
+    kv = np.array([10, 4], np.int64)  # n_q > kv_len in request 1
+    rc = L.smla_batch_build(2, n_q.ctypes.data, kv.ctypes.data, FAKE, 1 << 20, None, ctypes.byref(out))
+    assert rc == _lib.SMLA_E_INVALID and "request 1" in _lib.last_error()
+    rc = L.smla_batch_build(0, n_q.ctypes.data, kv.ctypes.data, FAKE, 1 << 20, None, ctypes.byref(out))
+    assert rc == _lib.SMLA_E_INVALID
+    rc = L.smla_batch_build(1, n_q.ctypes.data, kv.ctypes.data, FAKE + 8, 1 << 20, None, ctypes.byref(out))
+    assert rc == _lib.SMLA_E_INVALID and "aligned" in _lib.last_error()
+    kv_ok = np.array([10, 9], np.int64)
+    rc = L.smla_batch_build(2, n_q.ctypes.data, kv_ok.ctypes.data, FAKE, 64, None, ctypes.byref(out))
+    assert rc == _lib.SMLA_E_WORKSPACE
+
+
+def test_table_bytes_bounds(L):
+    assert L.smla_batch_table_bytes(0, 1, 1) == 0
+    assert L.smla_batch_table_bytes(1, 32768, 32768) > 0
+
+
+def test_indexer_validation(L):
+    b = _fake_batch()
+    rc = L.smla_indexer_scores(None, FAKE, FAKE, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID
+    rc = L.smla_indexer_scores(ctypes.byref(b), FAKE, FAKE, FAKE, 48, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_UNSUPPORTED
+    rc = L.smla_indexer_scores(ctypes.byref(b), FAKE + 4, FAKE, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID
+    rc = L.smla_indexer_scores(ctypes.byref(b), FAKE, FAKE, FAKE, 64, 128, None, None)
+    assert rc == _lib.SMLA_E_INVALID
+    uninit = _lib.Batch()
+    rc = L.smla_indexer_scores(ctypes.byref(uninit), FAKE, FAKE, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID and "smla_batch_build" in _lib.last_error()
+
+
+def test_topk_validation(L):
+    b = _fake_batch()
+    for k in (0, 2049):
+        rc = L.smla_indexer_scores_topk(ctypes.byref(b), FAKE, FAKE, FAKE, 64, 128, k, FAKE, None,
+                                        FAKE, 1 << 30, None)
+        assert rc == _lib.SMLA_E_UNSUPPORTED
+    need = L.smla_indexer_topk_workspace_bytes(ctypes.byref(b), 64, 128, 2048)
+    assert need >= 394 * 4
+    rc = L.smla_indexer_scores_topk(ctypes.byref(b), FAKE, FAKE, FAKE, 64, 128, 2048, FAKE, None,
+                                    FAKE, need - 1, None)
+    assert rc == _lib.SMLA_E_WORKSPACE
+    rc = L.smla_indexer_scores_topk(ctypes.byref(b), FAKE, FAKE, FAKE, 64, 128, 2048, None, None,
+                                    FAKE, need, None)
+    assert rc == _lib.SMLA_E_INVALID
+
+
+def test_mla_validation(L):
+    b = _fake_batch()
+    args = dict(H=64, D_qk=576, D_v=512)
+
+    def call(fn="smla_sparse_mla_prefill", fmt=1, H=64, D_qk=576, D_v=512, k=2048, scale=0.04,
+             q=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return getattr(L, fn)(ctypes.byref(b), q, FAKE, fmt, H, D_qk, D_v, FAKE, k, scale, FAKE,
+                              None, ws, ws_bytes, None)
+
+    assert call(H=32) == _lib.SMLA_E_UNSUPPORTED
+    assert call(D_qk=512) == _lib.SMLA_E_UNSUPPORTED
+    assert call(fmt=7) == _lib.SMLA_E_INVALID
+    assert call(fmt=0, H=64) == _lib.SMLA_E_UNSUPPORTED  # bf16 rows only on the small-head kernel
+    assert call(k=0) == _lib.SMLA_E_UNSUPPORTED
+    assert call(scale=0.0) == _lib.SMLA_E_INVALID
+    assert call(q=FAKE + 2) == _lib.SMLA_E_INVALID
+    need = L.smla_sparse_mla_workspace_bytes(ctypes.byref(b), 64, 512, 2048, 1)
+    assert need > 0  # 4 tokens split across workgroups
+    assert call("smla_sparse_mla_decode", ws_bytes=need - 1) == _lib.SMLA_E_WORKSPACE
+    assert L.smla_sparse_mla_workspace_bytes(ctypes.byref(b), 64, 512, 2048, 0) == 0
+    del args
+
+
+def test_status_strings(L):
+    assert _lib.status_str(0) == "SMLA_OK"
+    assert _lib.status_str(-3) == "SMLA_E_WORKSPACE"
+    assert L.smla_version() >= 100
+
+
+def test_product_never_reaches_the_oracle():
+    pkg = os.path.join(ROOT, "sparse_mla_attention_indexer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h", ".c")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "smla_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "smla_internal" not in text and "hip" not in text.lower().replace("ship", ""), f
