@@ -64,6 +64,7 @@ typedef struct smla_batch {
   int64_t max_kv;     /* max kv_len */
   int64_t total_rows; /* sum of kv_len */
   int64_t total_cand; /* sum over query tokens of (p + 1) */
+  int64_t min_cand;   /* min over query tokens of (p + 1) */
   const void* table;  /* (device) table written by smla_batch_build */
   size_t table_bytes;
 } smla_batch;

@@ -46,6 +46,7 @@ class Batch(ctypes.Structure):
         ("max_kv", ctypes.c_int64),
         ("total_rows", ctypes.c_int64),
         ("total_cand", ctypes.c_int64),
+        ("min_cand", ctypes.c_int64),
         ("table", ctypes.c_void_p),
         ("table_bytes", ctypes.c_size_t),
     ]

@@ -35,7 +35,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int check_batch(const smla_batch* b) {
   if (!b) return fail(SMLA_E_INVALID, "batch is NULL");
   if (b->batch < 1 || b->total_q < 1 || b->max_q < 1 || b->max_kv < 1 || b->total_rows < 1 ||
-      b->n_items < 0 || !b->table)
+      b->n_items < 0 || b->min_cand < 1 || !b->table)
     return fail(SMLA_E_INVALID, "batch descriptor is not initialised (call smla_batch_build)");
   if (!aligned(b->table, 16)) return fail(SMLA_E_INVALID, "batch table is not 16-byte aligned");
   return SMLA_OK;
@@ -171,7 +171,7 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
   if (batch < 1 || !n_q || !kv_len || !table || !out)
     return fail(SMLA_E_INVALID, "batch >= 1 and non-NULL n_q, kv_len, table, out required");
   if (!aligned(table, 256)) return fail(SMLA_E_INVALID, "table must be 256-byte aligned");
-  int64_t total_q = 0, total_rows = 0, max_kv = 0, total_cand = 0;
+  int64_t total_q = 0, total_rows = 0, max_kv = 0, total_cand = 0, min_cand = INT64_MAX;
   int32_t max_q = 0;
   for (int32_t b = 0; b < batch; ++b) {
     if (n_q[b] < 1 || kv_len[b] < n_q[b] || kv_len[b] >= (int64_t(1) << 31))
@@ -183,6 +183,7 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
     max_q = std::max(max_q, n_q[b]);
     // positions kv_len - n_q .. kv_len - 1 see (p + 1) candidates each
     total_cand += (int64_t)n_q[b] * (2 * kv_len[b] - n_q[b] + 1) / 2;
+    min_cand = std::min<int64_t>(min_cand, kv_len[b] - n_q[b] + 1);
   }
   if (total_q >= (int64_t(1) << 31)) return fail(SMLA_E_INVALID, "too many query tokens");
   if (total_rows >= (int64_t(1) << 40)) return fail(SMLA_E_INVALID, "too many rows");
@@ -224,6 +225,7 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
   out->max_kv = max_kv;
   out->total_rows = total_rows;
   out->total_cand = total_cand;
+  out->min_cand = min_cand;
   out->table = table;
   out->table_bytes = need;
   return SMLA_OK;
@@ -239,8 +241,8 @@ int smla_indexer_scores(const smla_batch* b, const int8_t* q_idx, const int8_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = smla::launch_fill_i32(scores, (int64_t)b->total_q * b->max_kv, -1, s);
   if (e == hipSuccess)
-    e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 0, s)
-             : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 0, s);
+    e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 0, nullptr, s)
+             : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 0, nullptr, s);
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "indexer launch");
 }
 
@@ -269,13 +271,16 @@ int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* scores = static_cast<int32_t*>(ws);
   void* tws = static_cast<char*>(ws) + smla::align_up(sizeof(int32_t) * (size_t)b->total_cand, 256);
+  const smla::TopkWs tw = smla::topk_workspace(*b, tws);
+  hipError_t e = smla::topk_prepare(*b, tw, s);
+  if (e != hipSuccess) return hip_fail(e, "top-k workspace init");
   smla::mark_stage(smla::STAGE_INDEXER, false, s);
-  hipError_t e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 1, s)
-                      : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 1, s);
+  e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 1, tw.hist, s)
+           : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 1, tw.hist, s);
   smla::mark_stage(smla::STAGE_INDEXER, true, s);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
   smla::mark_stage(smla::STAGE_TOPK, false, s);
-  e = smla::launch_topk(*b, scores, top_k, idx, score, tws, s);
+  e = smla::launch_topk(*b, scores, top_k, idx, score, tw, s);
   smla::mark_stage(smla::STAGE_TOPK, true, s);
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k launch");
 }

@@ -42,10 +42,12 @@ constexpr int IDX_H = 64;
 constexpr int IDX_D = 128;
 
 // One wave: query token t against key tiles s = s_begin, s_begin + step, ... < s_end, s <= p.
+// `lhist` (LDS, optional) receives the histogram code of every score the wave writes.
 __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
                                              int step, const int8_t* __restrict__ q_idx,
                                              const int8_t* __restrict__ k_idx,
-                                             const int (&wl)[2][16], int32_t* __restrict__ out_row) {
+                                             const int (&wl)[2][16], int32_t* __restrict__ out_row,
+                                             int* lhist) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -61,13 +63,18 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
 
   const int8_t* kbase = k_idx + tk.row_start * IDX_D + 64 * half;
   const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
-  for (int s = s_begin; s <= last; s += step) {
-    int key = s + col;
-    const int kr = key < last ? key : last;  // clamp: never read past the visible rows
+  auto load_keys = [&](int s, v4i (&kb)[4]) {
+    const int kr = min(s + col, last);  // clamp: never read past the visible rows
     const v4i* kp = reinterpret_cast<const v4i*>(kbase + (int64_t)kr * IDX_D);
-    v4i kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kp[j];
+  };
+  if (s_begin > last) return;
+  v4i kb[4];
+  load_keys(s_begin, kb);
+  for (int s = s_begin; s <= last; s += step) {
+    v4i kn[4];
+    load_keys(s + step, kn);  // next tile in flight while this one computes
     v16i acc0 = {}, acc1 = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -82,7 +89,13 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
       sum += (uint32_t)max(acc1[r], 0) * (uint32_t)wl[1][r];
     }
     sum += (uint32_t)__shfl_xor((int)sum, 32);
-    if (half == 0 && key <= last) out_row[key] = (int32_t)sum;
+    const int key = s + col;
+    if (half == 0 && key <= last) {
+      out_row[key] = (int32_t)sum;
+      if (lhist) atomicAdd(&lhist[topk_bin(sum)], 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = kn[j];
   }
 }
 
@@ -92,7 +105,8 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(const Item* __restric
                                                            const int8_t* __restrict__ k_idx,
                                                            const int32_t* __restrict__ w,
                                                            int32_t* __restrict__ scores,
-                                                           int64_t stride) {
+                                                           int64_t stride, int* __restrict__ hist) {
+  __shared__ int lhist[QT][TOPK_BINS];
   const Item it = items[blockIdx.x];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -106,16 +120,36 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(const Item* __restric
 #pragma unroll 1
   for (int sgi = 0; sgi < 2; ++sgi) {
     const Seg sg = sgi == 0 ? it.a : it.b;
-    if (sg.nq <= 0) continue;
+    if (sg.nq <= 0) continue;  // uniform over the workgroup
+    // rows longer than the LDS top-k path also get their score histogram (the last token of the
+    // tile has the longest row)
+    const bool hist_on = hist != nullptr && toks[sg.q0 + sg.nq - 1].pos + 1 > TOPK_LDS_MAX;
+    if (hist_on) {
+      for (int i = threadIdx.x; i < QT * TOPK_BINS; i += 256) (&lhist[0][0])[i] = 0;
+      __syncthreads();
+    }
     // waves per query: 4 for a single query (they split the key tiles), 2 for two, else 1
     const int qpw = sg.nq == 1 ? 4 : (sg.nq == 2 ? 2 : 1);
     const int qi = wave / qpw;
-    if (qi >= sg.nq) continue;
-    const int phase = wave - qi * qpw;
-    const int64_t t = sg.q0 + qi;
-    const Tok tk = toks[t];
-    int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
-    indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row);
+    if (qi < sg.nq) {
+      const int phase = wave - qi * qpw;
+      const int64_t t = sg.q0 + qi;
+      const Tok tk = toks[t];
+      int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
+      int* lh = hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
+      indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row, lh);
+    }
+    if (hist_on) {
+      __syncthreads();
+      for (int q = 0; q < sg.nq; ++q) {
+        const int64_t t = sg.q0 + q;
+        if (toks[t].pos + 1 <= TOPK_LDS_MAX) continue;
+        int* g = hist + t * TOPK_BINS;
+        for (int i = threadIdx.x; i < TOPK_BINS; i += 256)
+          if (lhist[q][i]) atomicAdd(&g[i], lhist[q][i]);
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -126,7 +160,7 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restr
                                                               const int32_t* __restrict__ w,
                                                               int H_I, int D_I,
                                                               int32_t* __restrict__ scores,
-                                                              int64_t stride) {
+                                                              int64_t stride, int* __restrict__ hist) {
   __shared__ int qs[16 * 64];
   __shared__ int ws[16];
   const int64_t t = blockIdx.x;
@@ -147,28 +181,30 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restr
   }
   int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
   out_row[s] = (int32_t)score;
+  if (hist && tk.pos + 1 > TOPK_LDS_MAX) atomicAdd(&hist[t * TOPK_BINS + topk_bin(score)], 1);
 }
 
 }  // namespace
 
 hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
-                               const int32_t* w, int32_t* scores, int compact, hipStream_t s) {
+                               const int32_t* w, int32_t* scores, int compact, int* hist,
+                               hipStream_t s) {
   if (b.n_items <= 0) return hipSuccess;
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const int64_t stride = compact ? 0 : b.max_kv;
   hipLaunchKernelGGL(indexer_mfma_kernel, dim3(b.n_items), dim3(256), 0, s, tv.item, tv.tok,
-                     q_idx, k_idx, w, scores, stride);
+                     q_idx, k_idx, w, scores, stride, hist);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
                                   const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores,
-                                  int compact, hipStream_t s) {
+                                  int compact, int* hist, hipStream_t s) {
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const int64_t stride = compact ? 0 : b.max_kv;
   dim3 grid((unsigned)b.total_q, (unsigned)((b.max_kv + 255) / 256));
   hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), 0, s, tv.tok, q_idx, k_idx, w, H_I,
-                     D_I, scores, stride);
+                     D_I, scores, stride, hist);
   return hipGetLastError();
 }
 

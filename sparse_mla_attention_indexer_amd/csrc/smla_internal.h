@@ -44,9 +44,37 @@ constexpr int KEY_CHUNK = 4096;
 // rows go through histogram / filter / resolve over segments of TOPK_SEG candidates.
 constexpr int TOPK_MAX_K = 2048;
 constexpr int TOPK_LDS_MAX = 32768;
+constexpr int TOPK_ROW_MAX = 73728;  // 1024 threads x 72 scores in registers
 constexpr int TOPK_SEG = 8192;
-constexpr int TOPK_BINS = 4096;
-constexpr int TOPK_CAND_CAP = 16384;
+constexpr int TOPK_BINS = 2048;
+constexpr int TOPK_CAND_CAP = 4096;
+constexpr int TOPK_REC = 8;  // per row: cand count, done count, b*, -, cut prefix (2), mask (2)
+
+// Monotone 11-bit code of a non-negative score: values below 64 map to themselves, larger
+// values to (leading-one position - 5) * 64 + the 6 bits below the leading one. Shared by the
+// indexer (which accumulates the histogram of long rows while scoring) and the top-k kernels.
+__device__ __forceinline__ int topk_bin(uint32_t s) {
+  if (s < 64u) return (int)s;
+  const int e = 31 - __builtin_clz(s);  // 6..31
+  return 64 * (e - 5) + (int)((s >> (e - 6)) & 63u);
+}
+
+// Smallest score whose code is b (the inverse of topk_bin on bin boundaries), as a 64-bit
+// value so that the bound past the last bin is representable.
+__device__ __forceinline__ uint64_t topk_bin_lo(int b) {
+  if (b < 64) return (uint64_t)b;
+  const int e = b / 64 + 5;
+  return (uint64_t)(64 + b % 64) << (e - 6);
+}
+
+// Top-k workspace for rows longer than TOPK_LDS_MAX.
+struct TopkWs {
+  int* hist;       // [total_q][TOPK_BINS] score histogram of each row (indexer fills it)
+  int* rec;        // [total_q][TOPK_REC]
+  int* seg;        // [total_q][nseg] per-segment counts, then output offsets
+  uint64_t* cand;  // [total_q][TOPK_CAND_CAP] keys of the b* candidates
+  int64_t nseg;
+};
 
 // Sparse MLA (big shape): heads, dims, rows per tile, decode splits.
 constexpr int MLA_H = 64;
@@ -82,15 +110,20 @@ void mark_stage(int s, bool end, hipStream_t st);
 // Each returns hipSuccess or the launch error; arguments were validated by the caller.
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
 
+// `hist` (optional, TopkWs::hist): histogram of every row longer than TOPK_LDS_MAX.
 hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
-                               const int32_t* w, int32_t* scores, int compact, hipStream_t s);
+                               const int32_t* w, int32_t* scores, int compact, int* hist,
+                               hipStream_t s);
 hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
                                   const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores,
-                                  int compact, hipStream_t s);
+                                  int compact, int* hist, hipStream_t s);
 
 size_t topk_workspace_bytes(const smla_batch& b, int32_t top_k);
+TopkWs topk_workspace(const smla_batch& b, void* ws);
+// Zero the histogram and counters (before the indexer accumulates into the histogram).
+hipError_t topk_prepare(const smla_batch& b, const TopkWs& w, hipStream_t s);
 hipError_t launch_topk(const smla_batch& b, const int32_t* scores_compact, int32_t top_k,
-                       int32_t* idx, int32_t* score, void* ws, hipStream_t s);
+                       int32_t* idx, int32_t* score, const TopkWs& w, hipStream_t s);
 
 size_t mla_workspace_bytes(const smla_batch& b, int32_t H, int32_t D_v, int32_t top_k, int decode);
 int mla_decode_splits(const smla_batch& b, int32_t top_k);

@@ -7,19 +7,20 @@
 // rows). Partial results over disjoint row sets merge by log-sum-exp (section "DCP").
 //
 // FP8 kernel (64 heads, 576/512 dims, 656-byte rows), one workgroup of 4 waves per (token,
-// split), 64-row tiles:
-//  1. all 256 threads gather the tile's rows (each wave instruction reads 512 contiguous bytes
-//     of one row), dequantise e4m3 * block scale to bf16 and store the tile twice in LDS:
-//     row-major K[row][576] for QK^T and transposed V^T[512][row] for PV (16-byte chunks
-//     XOR-swizzled so both the writes and the MFMA operand reads are bank-conflict free);
-//  2. wave (g, r) holds Q of heads [32g, 32g+32) in registers and computes S^T for rows
-//     [32r, 32r+32) on v_mfma_f32_32x32x16_bf16 with the rows as M and the heads as N, so each
-//     lane owns one head's logits;
-//  3. the two waves of a head group share the tile maximum through LDS and keep one running
-//     maximum per head; O is rescaled only when the maximum grows by more than 2^8 (so P stays
-//     <= 256 and a bf16 P loses nothing);
-//  4. P goes to LDS and wave (g, r) accumulates O^T for dims [256r, 256r+256) of its 32 heads as
-//     V^T * P^T over all 64 rows (the same lane-owns-a-head layout as S^T).
+// split), 32-row tiles, double-buffered in LDS:
+//  1. all 256 threads gather the next tile's rows while the current one computes (each wave
+//     instruction reads 512 contiguous bytes of one row), then dequantise e4m3 * block scale to
+//     bf16 into a row-major K[row][576] tile (16-byte chunks XOR-swizzled by row);
+//  2. wave (g, h) holds Q of heads [32g, 32g+32) over dims [288h, 288h+288) and computes that
+//     half of S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (rows as M, heads as N, so each lane owns
+//     one head); the two waves of a head group add their halves through LDS;
+//  3. one running maximum per head; O is rescaled only when the maximum grows by more than 2^8
+//     (so P <= 256 and a bf16 P loses nothing);
+//  4. P stays in registers: its accumulator layout is reused as the B operand of
+//     O^T = V^T P^T (the contraction runs over rows in the order the accumulator holds them);
+//     V^T comes straight from the row-major tile through transposing LDS reads
+//     (ds_read_b64_tr_b16), so no second copy of the tile is stored. Wave (g, h) accumulates
+//     O^T for dims [256h, 256h+256) of its 32 heads.
 // Decode splits a token's rows across workgroups and merges the partials by log-sum-exp.
 #include "smla_internal.h"
 
@@ -27,7 +28,7 @@ namespace smla {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -35,31 +36,23 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int NT = 256;
-constexpr int TILE = MLA_TILE;           // 64 rows
-constexpr int KCH = MLA_DQK / 8;         // 72 16-byte chunks per K row
-constexpr int K_BYTES = TILE * MLA_DQK * 2;     // 73728
-constexpr int VT_BYTES = MLA_DV * TILE * 2;     // 65536
-constexpr int P_BYTES = MLA_H * TILE * 2;       // 8192
+constexpr int TILE = 32;                   // rows per tile
+constexpr int KCH = MLA_DQK / 8;           // 72 16-byte chunks per K row
+constexpr int K_BYTES = TILE * MLA_DQK * 2;  // 36864 per buffer
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.0f;
 
 struct __align__(16) MlaSmem {
-  unsigned char k[K_BYTES];   // K[row][chunk ^ (row & 7)] (16-byte chunks of 8 bf16)
-  unsigned char vt[VT_BYTES]; // V^T[dim][chunk ^ ((dim + dim/8) & 7)] (chunks of 8 rows)
-  unsigned char p[P_BYTES];   // P[head][chunk ^ (head & 7)] (chunks of 8 rows)
-  float scale[TILE][4];
-  int rowidx[TILE];
-  float tmax[2][2][32];
+  unsigned char k[2][K_BYTES];  // K[row][chunk ^ swz(row)], two tiles
+  float sx[4][4][64][4];        // per wave: its half of S^T, [i/4][lane][i%4]
+  int idx[TOPK_MAX_K];          // the split's row indices (-1: skip)
   float lsum[2][2][32];
 };
 
-__device__ __forceinline__ int k_off(int row, int chunk) { return (row * KCH + (chunk ^ (row & 7))) * 16; }
-__device__ __forceinline__ int vt_off(int dim, int chunk) {
-  return (dim * (TILE / 8) + (chunk ^ ((dim + (dim >> 3)) & 7))) * 16;
-}
-__device__ __forceinline__ int p_off(int head, int chunk) {
-  return (head * (TILE / 8) + (chunk ^ (head & 7))) * 16;
-}
+// Row swizzle of 16-byte chunks: a bijection on row & 7 that keeps the 8 consecutive rows of an
+// MFMA operand read and the 4-row pairs of a transposing read on distinct banks.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int k_off(int row, int chunk) { return (row * KCH + (chunk ^ swz(row))) * 16; }
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   v2f x = {a, b};
@@ -68,76 +61,60 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, y);
 }
 
-// Gather + dequantise one tile into LDS. Rows whose index is < 0 are stored as zeros.
-__device__ void load_tile(MlaSmem& sm, const unsigned char* __restrict__ kv_req,
-                          const int32_t* __restrict__ idx_row, int r0, int r1, int pos) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  if (tid < TILE) {
-    const int j = r0 + tid;
-    int ix = j < r1 ? idx_row[j] : -1;
-    if (ix > pos) ix = -1;  // rows past the token's position are never read
-    sm.rowidx[tid] = ix;
-    float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ix >= 0) sc = *reinterpret_cast<const float4*>(kv_req + (int64_t)ix * MLA_ROW_BYTES + 512);
-    sm.scale[tid][0] = sc.x;
-    sm.scale[tid][1] = sc.y;
-    sm.scale[tid][2] = sc.z;
-    sm.scale[tid][3] = sc.w;
-  }
-  __syncthreads();
-  // rope dims 512..575 (bf16 as stored): thread -> row 16*wave + lane/4, 32 bytes
-  {
-    const int row = 16 * wave + (lane >> 2), part = lane & 3;
-    const int ix = sm.rowidx[row];
-    v4u a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (ix >= 0) {
-      const v4u* src = reinterpret_cast<const v4u*>(kv_req + (int64_t)ix * MLA_ROW_BYTES + 528 + 32 * part);
-      a = src[0];
-      b = src[1];
-    }
-    *reinterpret_cast<v4u*>(sm.k + k_off(row, 64 + 2 * part)) = a;
-    *reinterpret_cast<v4u*>(sm.k + k_off(row, 64 + 2 * part + 1)) = b;
-  }
-  // value dims 0..511: lane -> dims [8*lane, 8*lane + 8); wave -> two blocks of 8 rows
-  const int c = lane;
-  const int blk = c >> 4;  // 128-dim scale block
-#pragma unroll 1
-  for (int rb = 0; rb < 2; ++rb) {
-    const int rbase = 16 * wave + 8 * rb;
-    v2u raw[8];
+// Raw bytes of one tile for this thread: 8 rows x 8 value dims, one 16-byte piece of rope, and
+// the 8 rows' block scales.
+struct TileRegs {
+  v2u val[8];
+  v4u rope;
+  float scale[8];
+};
+
+__device__ __forceinline__ void tile_load(TileRegs& r, const int* sidx, int tr0,
+                                          const unsigned char* __restrict__ kv_req) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ix = sm.rowidx[rbase + i];
-      raw[i] = ix >= 0 ? *reinterpret_cast<const v2u*>(kv_req + (int64_t)ix * MLA_ROW_BYTES + 8 * c)
-                       : v2u{0u, 0u};
-    }
-    const int rchunk = rbase >> 3;
-    // four dims at a time (one dword of codes per row) keeps the live set small
+  for (int i = 0; i < 8; ++i) {
+    const int ix = sidx[tr0 + 8 * wave + i];
+    const unsigned char* rowp = kv_req + (int64_t)ix * MLA_ROW_BYTES;
+    r.val[i] = ix >= 0 ? *reinterpret_cast<const v2u*>(rowp + 8 * lane) : v2u{0u, 0u};
+    r.scale[i] = ix >= 0 ? *reinterpret_cast<const float*>(rowp + 512 + 4 * (lane >> 4)) : 0.f;
+  }
+  const int ix = sidx[tr0 + (tid >> 3)];
+  r.rope = ix >= 0 ? *reinterpret_cast<const v4u*>(kv_req + (int64_t)ix * MLA_ROW_BYTES + 528 + 16 * (tid & 7))
+                   : v4u{0u, 0u, 0u, 0u};
+}
+
+// LDS offsets a thread stores its part of a tile to: 8 value chunks (rows 8*wave + i, chunk =
+// lane) and one rope chunk; the same for every tile.
+struct StoreOffsets {
+  int val[8];
+  int rope;
+};
+
+__device__ __forceinline__ StoreOffsets store_offsets() {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  StoreOffsets so;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) so.val[i] = k_off(8 * wave + i, lane);
+  so.rope = k_off(tid >> 3, 64 + (tid & 7));
+  return so;
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& r, unsigned char* kb, const StoreOffsets& so) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float s = r.scale[i];
+    unsigned pk[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float f[8][4];  // [row][dim]
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float s = sm.scale[rbase + i][blk];
-        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[i][h], false);
-        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[i][h], true);
-        f[i][0] = lo[0] * s;
-        f[i][1] = lo[1] * s;
-        f[i][2] = hi[0] * s;
-        f[i][3] = hi[1] * s;
-        v2u o = {pack_bf16(f[i][0], f[i][1]), pack_bf16(f[i][2], f[i][3])};
-        *reinterpret_cast<v2u*>(sm.k + k_off(rbase + i, c) + 8 * h) = o;
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        v4u o = {pack_bf16(f[0][d], f[1][d]), pack_bf16(f[2][d], f[3][d]), pack_bf16(f[4][d], f[5][d]),
-                 pack_bf16(f[6][d], f[7][d])};
-        *reinterpret_cast<v4u*>(sm.vt + vt_off(8 * c + 4 * h + d, rchunk)) = o;
-      }
+      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.val[i][h], false);
+      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.val[i][h], true);
+      pk[2 * h] = pack_bf16(lo[0] * s, lo[1] * s);
+      pk[2 * h + 1] = pack_bf16(hi[0] * s, hi[1] * s);
     }
+    *reinterpret_cast<v4u*>(kb + so.val[i]) = v4u{pk[0], pk[1], pk[2], pk[3]};
   }
-  __syncthreads();
+  *reinterpret_cast<v4u*>(kb + so.rope) = r.rope;
 }
 
 // One (token, split): rows idx_row[r_begin, r_end) of the token's request.
@@ -158,7 +135,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const int nsplit = gridDim.y;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int hg = wave >> 1, rr = wave & 1;
+  const int hg = wave >> 1, kh = wave & 1;
   const int col = lane & 31, half = lane >> 5;
   const int head = 32 * hg + col;
 
@@ -167,74 +144,118 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const int32_t* idx_row = idx + t * top_k;
   const int r_begin = split * rows_per_split;
   const int r_end = min(top_k, r_begin + rows_per_split);
+  const int nrows = max(0, r_end - r_begin);
 
-  // Q^T fragments: head `head`, dims [8*half + 16*ks, +8)
-  v8bf qf[MLA_DQK / 16];
+  // the split's indices; rows past the token's position are never read
+  __shared__ int last_valid;
+  if (tid == 0) last_valid = -1;
+  __syncthreads();
   {
-    const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 8 * half;
+    constexpr int PER = TOPK_MAX_K / NT;
+    int ixs[PER];
 #pragma unroll
-    for (int ks = 0; ks < MLA_DQK / 16; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qh + 16 * ks);
+    for (int u = 0; u < PER; ++u) {  // all loads in flight before any is used
+      const int j = u * NT + tid;
+      ixs[u] = j < nrows ? idx_row[r_begin + j] : -1;
+    }
+    int lv = -1;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = u * NT + tid;
+      int ix = ixs[u] > tk.pos ? -1 : ixs[u];
+      if (j < TOPK_MAX_K) sm.idx[j] = ix;
+      if (ix >= 0) lv = j;
+    }
+    if (lv >= 0) atomicMax(&last_valid, lv);
+  }
+  __syncthreads();
+  const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
+
+  // Q^T fragments: head `head`, dims [288*kh + 16*ks + 8*half, +8)
+  v8bf qf[18];
+  {
+    const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 288 * kh + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qh + 16 * ks);
   }
   v16f o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = v16f{};
-  // Per-lane LDS bases. The XOR swizzles only touch the low three chunk bits, so every
-  // operand read is one of a few bases plus a compile-time offset.
-  const unsigned char* kbase[4];  // K row 32*rr + col, chunks half + 2u (+ 8 per 64 dims)
-  {
-    const int row = 32 * rr + col;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kbase[u] = sm.k + k_off(row, half + 2 * u);
-  }
-  const unsigned char* vbase[4][2];  // V^T dims 256*rr + 32*m + col, m = 0 or 1; chunk half + 2ks
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) vbase[ks][m] = sm.vt + vt_off(256 * rr + 32 * m + col, half + 2 * ks);
-  const unsigned char* pbase[4];  // P of `head`, chunk half + 2ks
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) pbase[ks] = sm.p + p_off(head, half + 2 * ks);
   float m_run = -INFINITY;  // running max of this lane's head, log2 units
   float l_run = 0.f;        // this lane's share of the softmax denominator
   const float c = sm_scale * LOG2E;
 
-#pragma unroll 1
-  for (int r0 = r_begin; r0 < r_end; r0 += TILE) {
-    load_tile(sm, kv_req, idx_row, r0, r_end, tk.pos);
-    bool any_valid = false;
-    {
-      const int ix = sm.rowidx[lane];
-      any_valid = __any(ix >= 0);
-    }
-    if (!any_valid) {
-      __syncthreads();
-      continue;
-    }
-    // S^T for rows [32*rr, 32*rr + 32) of the tile x heads [32*hg, +32)
-    v16f s = v16f{};
+  // per-lane LDS offsets: S operand (K row `col`, chunk 36*kh + 2u + half (+ 8m)), and the
+  // transposing V reads (16-lane group g: dims +16*(g&1); 4 rows from 4*(g>>1) + lane%16 / 4)
+  int koff[4];
 #pragma unroll
-    for (int kc = 0; kc < MLA_DQK / 64; ++kc) {
+  for (int u = 0; u < 4; ++u) koff[u] = k_off(col, 36 * kh + 2 * u + half);
+  const int grp = lane >> 4, gl = lane & 15;
+  const int vrow = 4 * (grp >> 1) + (gl >> 2);          // + 16*ks (+8 for the second read)
+  const int vdim = 256 * kh + 16 * (grp & 1) + 4 * (gl & 3);  // + 32*mt
+  // The transposing V reads of (ks, second half, mt = 2m + par) sit at voff[ks][hi][par] + 128m:
+  // the chunk of dim vdim + 32mt is (vdim >> 3) + 4par + 8m and the swizzle leaves bit 3 up alone.
+  int voff[2][2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        voff[ks][hi][par] = k_off(16 * ks + 8 * hi + vrow, (vdim >> 3) + 4 * par) + 2 * (vdim & 7);
+  const StoreOffsets so = store_offsets();
+
+  TileRegs R;
+  if (ntiles > 0) {
+    tile_load(R, sm.idx, 0, kv_req);
+    tile_store(R, sm.k[0], so);
+    if (ntiles > 1) tile_load(R, sm.idx, TILE, kv_req);
+  }
+  __syncthreads();
+
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    const unsigned char* kb = sm.k[it & 1];
+    // half of S^T over this wave's dims, as two independent accumulation chains
+    v16f s = v16f{}, s2 = v16f{};
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+      const int nu = m < 4 ? 4 : 2;
       v8bf a[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) a[u] = *reinterpret_cast<const v8bf*>(kbase[u] + 128 * kc);
+      for (int u = 0; u < nu; ++u) a[u] = *reinterpret_cast<const v8bf*>(kb + koff[u] + 128 * m);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], qf[4 * kc + u], s, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < nu; u += 2) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], qf[4 * m + u], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u + 1], qf[4 * m + u + 1], s2, 0, 0, 0);
+      }
     }
-    // lane holds head `head`, rows 32*rr + 8*(i/4) + 4*half + i%4
+    s += s2;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<float4*>(&sm.sx[wave][g4][lane][0]) =
+          make_float4(s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]);
+    __syncthreads();
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 o4 = *reinterpret_cast<const float4*>(&sm.sx[wave ^ 1][g4][lane][0]);
+      s[4 * g4] += o4.x;
+      s[4 * g4 + 1] += o4.y;
+      s[4 * g4 + 2] += o4.z;
+      s[4 * g4 + 3] += o4.w;
+    }
+    // lane holds head `head`, rows 8*(i/4) + 4*half + i%4 of the tile
+    const uint64_t valid = __ballot(sm.idx[it * TILE + col] >= 0);  // bit r: row r is valid
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = 32 * rr + 8 * (i >> 2) + 4 * half + (i & 3);
-      const float v = sm.rowidx[row] >= 0 ? s[i] * c : -INFINITY;
+      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+      const float v = (valid >> row) & 1 ? s[i] * c : -INFINITY;
       s[i] = v;
       tmax = fmaxf(tmax, v);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (half == 0) sm.tmax[hg][rr][col] = tmax;
-    __syncthreads();
-    tmax = fmaxf(tmax, sm.tmax[hg][rr ^ 1][col]);
-    // both waves of a head group see the same maxima and take the same decision
+    // both waves of a head group hold identical logits and take the same decision
     const float m_new = fmaxf(m_run, tmax);
     if (__any(m_new > m_run + RESCALE_LOG2)) {
       const float alpha = exp2f(m_run - m_new);
@@ -243,49 +264,47 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
       l_run *= alpha;
       m_run = m_new;
     }
-    // P = exp2(s - m_run) -> LDS as bf16, rows in groups of 4
+    // P in registers, packed as the B operand of the two 16-row k-steps
+    v8bf pb[2];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float p4[4];
+    for (int ks = 0; ks < 2; ++ks) {
+      float p8[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p4[i] = exp2f(s[4 * g4 + i] - m_run);
-        l_run += p4[i];
+      for (int j = 0; j < 8; ++j) {
+        p8[j] = exp2f(s[8 * ks + j] - m_run);
+        l_run += p8[j];
       }
-      const int row0 = 32 * rr + 8 * g4 + 4 * half;  // first of 4 consecutive rows
-      v2u pk = {pack_bf16(p4[0], p4[1]), pack_bf16(p4[2], p4[3])};
-      *reinterpret_cast<v2u*>(sm.p + p_off(head, row0 >> 3) + 8 * ((row0 >> 2) & 1)) = pk;
+      v4u pk = {pack_bf16(p8[0], p8[1]), pack_bf16(p8[2], p8[3]), pack_bf16(p8[4], p8[5]),
+                pack_bf16(p8[6], p8[7])};
+      pb[ks] = __builtin_bit_cast(v8bf, pk);
     }
-    __syncthreads();
-    // O^T[dims 256*rr + 32*mt + m][head] += V^T[dim][rows] * P^T[rows][head]
+    // O^T[dims 256*kh + 32*mt + m][head] += V^T[dim][rows] P^T[rows][head]
 #pragma unroll
-    for (int ks = 0; ks < TILE / 16; ++ks) {
-      const v8bf b = *reinterpret_cast<const v8bf*>(pbase[ks]);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int mh = 0; mh < 2; ++mh) {
-        v8bf a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int mt = 4 * mh + u;  // dims 256*rr + 32*mt + col; swizzle depends on mt & 1
-          a[u] = *reinterpret_cast<const v8bf*>(vbase[ks][mt & 1] + (mt >> 1) * (64 * TILE * 2));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[4 * mh + u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b, o[4 * mh + u], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int mt = 0; mt < 8; ++mt) {
+        const int par = mt & 1, m = mt >> 1;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(kb + voff[ks][0][par] + 128 * m));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(kb + voff[ks][1][par] + 128 * m));
+        const v8bf a = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[mt], 0, 0, 0);
       }
+    }
+    // next tile: store the rows gathered during this one, start gathering the one after
+    if (it + 1 < ntiles) {
+      tile_store(R, sm.k[(it + 1) & 1], so);
+      if (it + 2 < ntiles) tile_load(R, sm.idx, (it + 2) * TILE, kv_req);
     }
     __syncthreads();
   }
 
-  // denominator of each head: both lane halves and both row halves
+  // denominator of each head: both lane halves, both waves of the head group hold the same
   l_run += __shfl_xor(l_run, 32);
-  if (half == 0) sm.lsum[hg][rr][col] = l_run;
-  __syncthreads();
-  const float l_tot = l_run + sm.lsum[hg][rr ^ 1][col];
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  const float lse = empty ? -INFINITY : (m_run + log2f(l_tot)) * (1.0f / LOG2E);
+  const bool empty = !(l_run > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_run;
+  const float lse = empty ? -INFINITY : (m_run + log2f(l_run)) * (1.0f / LOG2E);
 
   if (part_o == nullptr) {
     __bf16* orow = out + (t * MLA_H + head) * MLA_DV;
@@ -293,24 +312,24 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int dim = 256 * rr + 32 * mt + 8 * g4 + 4 * half;
+        const int dim = 256 * kh + 32 * mt + 8 * g4 + 4 * half;
         v2u pk = {pack_bf16(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv),
                   pack_bf16(o[mt][4 * g4 + 2] * inv, o[mt][4 * g4 + 3] * inv)};
         *reinterpret_cast<v2u*>(orow + dim) = pk;
       }
-    if (lse_out && rr == 0 && half == 0) lse_out[t * MLA_H + head] = lse;
+    if (lse_out && kh == 0 && half == 0) lse_out[t * MLA_H + head] = lse;
   } else {
     float* prow = part_o + ((t * nsplit + split) * MLA_H + head) * MLA_DV;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int dim = 256 * rr + 32 * mt + 8 * g4 + 4 * half;
+        const int dim = 256 * kh + 32 * mt + 8 * g4 + 4 * half;
         float4 v = make_float4(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv, o[mt][4 * g4 + 2] * inv,
                                o[mt][4 * g4 + 3] * inv);
         *reinterpret_cast<float4*>(prow + dim) = v;
       }
-    if (rr == 0 && half == 0) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
+    if (kh == 0 && half == 0) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
   }
 }
 

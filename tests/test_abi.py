@@ -44,7 +44,7 @@ def test_workload_library_exports_declared_symbols():
 def _fake_batch(**kw):
     b = _lib.Batch()
     b.batch, b.total_q, b.max_q, b.n_items = 1, 4, 4, 1
-    b.max_kv, b.total_rows, b.total_cand = 100, 100, 394
+    b.max_kv, b.total_rows, b.total_cand, b.min_cand = 100, 100, 394, 97
     b.table, b.table_bytes = 0x10000, 4096
     for k, v in kw.items():
         setattr(b, k, v)

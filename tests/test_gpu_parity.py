@@ -100,20 +100,22 @@ def test_ragged_batch_both_topk_paths_and_decode():
         assert_attn_close(out, ref, lse, ref_lse, f"ragged decode={decode}")
 
 
-@pytest.mark.parametrize("pattern", ["zeros", "few_values"])
-def test_tie_stress_long_rows(pattern):
-    # > 32768 candidates per row with massive ties: every score equal (the candidate buffer
-    # overflows and the row is resolved from the scores directly) or only a few distinct values
-    d = W.small_big_dims(n_q=3, cached=40000)
+@pytest.mark.parametrize("cached", [40000, 300000])
+@pytest.mark.parametrize("pattern", ["zeros", "few_values", "random"])
+def test_tie_stress_long_rows(pattern, cached):
+    # rows longer than the LDS path (40,000: one workgroup per row; 300,000: the segmented
+    # three-kernel path) with massive ties: every score equal (the candidate buffer overflows and
+    # the row is resolved from the scores directly), a few distinct values, or random scores
+    d = W.small_big_dims(n_q=3, cached=cached)
     x = W.generate(d)
     if pattern == "zeros":
         x.k_idx[:] = 0
-    else:
+    elif pattern == "few_values":
         rng = np.random.default_rng(5)
         x.k_idx[:] = 0
         x.k_idx[:, 0] = rng.integers(0, 3, size=x.k_idx.shape[0])
         x.q_idx[:] = 1
-    say(f"[case] tie stress {pattern}")
+    say(f"[case] tie stress {pattern} cached={cached}")
     dev = Dev(x)
     tokens = np.arange(d.total_q)
     idx, sc = dev.topk()
