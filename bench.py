@@ -8,13 +8,21 @@ smla_indexer_scores_topk then smla_sparse_mla_decode (decode workloads) or _pref
 workload is the decode batch: 32 requests x 1 query token over 65,536 cached tokens each.
 
     python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
+    python bench.py --copy-calibration    # a plain 256 MiB device copy, for counter scaling
+
+HBM traffic of the dominant kernel comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters taken
+on this same command and scaled by what the counters read for the plain copy; the summary under
+profiles/ records the hash of the kernel's sources, and the figure is reported only while the
+sources still match.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +35,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 DECODE_CONFIGS = (1, 4)
+# file-name tags of the workloads in profiles/
+WORKLOAD_TAGS = {0: "tiny_1x512", 1: "decode_32x65536", 2: "chunk_2048after65536",
+                 3: "prefill_32768", 4: "decode_4x4after1048576"}
 STAGES = ("indexer", "topk", "mla", "combine")
 
 
@@ -66,6 +77,49 @@ class HipEvents:
         self.rt.hipEventDestroy(e)
 
 
+# sources whose code decides a kernel's memory traffic
+KERNEL_SOURCES = {
+    "indexer_mfma_kernel": ("sparse_mla_attention_indexer_amd/csrc/indexer.hip",
+                            "sparse_mla_attention_indexer_amd/csrc/smla_internal.h"),
+}
+
+
+def sources_sha256(kernel):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel, tag):
+    """HBM bytes per launch from the committed counter summary, or None when there is none or the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{tag}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^src_sha256:\s*([0-9a-f]{64})", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != sources_sha256(kernel):
+        return None
+    return float(val.group(1))
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 256 MiB, five times: the reference for counter scaling."""
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
 def algorithmic(d, positions):
     """Algorithmic work of one step (unique bytes; FLOPs/ops), per stage."""
     import numpy as np
@@ -89,17 +143,24 @@ def cpu_baseline(x, d, sample_tokens):
 
     threads = oracle.default_threads()
     tokens = np.asarray(sample_tokens, np.int64)
-    t0 = time.perf_counter()
-    idx, _ = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, d.top_k, tokens,
-                                       nthreads=threads)
-    full = np.full((d.total_q, d.top_k), -1, np.int32)
-    full[tokens] = idx
-    oracle.sparse_mla_batch(x.n_q, x.kv_len, x.q, x.kv, d.kv_format, d.D_v, full, d.sm_scale, tokens,
-                            nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": tokens.size / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{tokens.size} of {d.total_q} query tokens of the same workload "
-                      f"(indexer + top-k + fp64 attention), {dt:.2f} s wall"}
+    # whole passes over the sample until about a second of wall time (tens of CPU-seconds)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        idx, _ = oracle.indexer_topk_batch(x.n_q, x.kv_len, x.q_idx, x.k_idx, x.w, d.top_k, tokens,
+                                           nthreads=threads)
+        full = np.full((d.total_q, d.top_k), -1, np.int32)
+        full[tokens] = idx
+        oracle.sparse_mla_batch(x.n_q, x.kv_len, x.q, x.kv, d.kv_format, d.D_v, full, d.sm_scale,
+                                tokens, nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 1.0 or reps >= 50:
+            break
+    return {"value": reps * tokens.size / dt, "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} pass(es) over {tokens.size} of {d.total_q} query tokens of the same "
+                      f"workload (indexer + top-k + fp64 attention), {dt:.2f} s wall on "
+                      f"{threads} threads"}
 
 
 def main():
@@ -109,6 +170,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (counter scaling reference)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no collectives); "
@@ -124,6 +187,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     d = W.config_dims(args.config)
     decode = args.config in DECODE_CONFIGS
@@ -201,13 +267,16 @@ def main():
     # the indexer dominates the step; it is HBM-bound when its ops per key byte fall below the
     # int8 ridge (5.0 POP/s / 8 TB/s = 625)
     idx_hbm = alg["indexer_ops"] / alg["indexer_bytes"] < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = profiled_traffic("indexer_mfma_kernel", WORKLOAD_TAGS.get(args.config, ""))
     if idx_hbm:
         roof = {"bound": "hbm", "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(idx_tops, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s (int8)", "frac": round(idx_tops / INT8_PEAK_TOPS, 4), "traffic": None,
+                "unit": "TOP/s (int8)", "frac": round(idx_tops / INT8_PEAK_TOPS, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
     mla_hbm = alg["mla_flops"] / alg["mla_bytes"] < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     mla_roof = ({"bound": "hbm", "achieved": round(mla_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
