@@ -94,7 +94,13 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
 int smla_indexer_scores(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
                         const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores, void* stream);
 
-/* Workspace for smla_indexer_scores_topk. */
+/*
+ * Workspace for smla_indexer_scores_topk. Zero-fill it once after allocating it (for example
+ * with hipMemsetAsync): the per-row histograms and counters it holds must be zero when a call
+ * starts, and every call that returns SMLA_OK leaves them zero again, so the same workspace
+ * serves any later call whose size fits. After a call that failed on the device, zero it again.
+ * Calls that share one workspace must not overlap.
+ */
 size_t smla_indexer_topk_workspace_bytes(const smla_batch* b, int32_t H_I, int32_t D_I,
                                          int32_t top_k);
 
@@ -103,7 +109,8 @@ size_t smla_indexer_topk_workspace_bytes(const smla_batch* b, int32_t H_I, int32
  * idx (device) [total_q, top_k] int32: the min(top_k, p+1) local row indices with the largest
  * scores, ties to the lower index (all s <= p when p+1 <= top_k), in ascending index order,
  * then -1 padding. score (device, optional) [total_q, top_k] int32: the score of each selected
- * index, -1 on padding. 1 <= top_k <= 2048.
+ * index, -1 on padding. 1 <= top_k <= 2048; kv_len <= 8,388,608 (SMLA_E_UNSUPPORTED beyond).
+ * ws: a workspace of smla_indexer_topk_workspace_bytes, zero-filled before its first use.
  */
 int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int8_t* k_idx,
                              const int32_t* w, int32_t H_I, int32_t D_I, int32_t top_k,

@@ -263,6 +263,9 @@ int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int
   if (rc) return rc;
   if (top_k < 1 || top_k > smla::TOPK_MAX_K)
     return fail(SMLA_E_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, smla::TOPK_MAX_K);
+  if (b->max_kv > (int64_t)smla::TOPK_SEG * smla::TOPK_SEG_MAX)
+    return fail(SMLA_E_UNSUPPORTED, "kv_len %lld above the top-k limit %lld", (long long)b->max_kv,
+                (long long)smla::TOPK_SEG * smla::TOPK_SEG_MAX);
   if (!idx || !aligned(idx, 4) || (score && !aligned(score, 4)))
     return fail(SMLA_E_INVALID, "idx must be non-NULL; idx and score 4-byte aligned");
   const size_t need = smla_indexer_topk_workspace_bytes(b, H_I, D_I, top_k);
@@ -272,10 +275,8 @@ int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int
   int32_t* scores = static_cast<int32_t*>(ws);
   void* tws = static_cast<char*>(ws) + smla::align_up(sizeof(int32_t) * (size_t)b->total_cand, 256);
   const smla::TopkWs tw = smla::topk_workspace(*b, tws);
-  hipError_t e = smla::topk_prepare(*b, tw, s);
-  if (e != hipSuccess) return hip_fail(e, "top-k workspace init");
   smla::mark_stage(smla::STAGE_INDEXER, false, s);
-  e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 1, tw.hist, s)
+  hipError_t e = mfma ? smla::launch_indexer_mfma(*b, q_idx, k_idx, w, scores, 1, tw.hist, s)
            : smla::launch_indexer_generic(*b, q_idx, k_idx, w, H_I, D_I, scores, 1, tw.hist, s);
   smla::mark_stage(smla::STAGE_INDEXER, true, s);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");

@@ -41,14 +41,18 @@ constexpr int QT = 4;
 constexpr int KEY_CHUNK = 4096;
 
 // Top-k: rows with n <= TOPK_LDS_MAX candidates are selected by one workgroup in LDS; longer
-// rows go through histogram / filter / resolve over segments of TOPK_SEG candidates.
+// rows by one workgroup each (up to TOPK_ROW_MAX) or by count / resolve / emit kernels over
+// segments of TOPK_SEG candidates.
 constexpr int TOPK_MAX_K = 2048;
 constexpr int TOPK_LDS_MAX = 32768;
 constexpr int TOPK_ROW_MAX = 73728;  // 1024 threads x 72 scores in registers
-constexpr int TOPK_SEG = 8192;
+constexpr int TOPK_SEG = 4096;       // 256 threads x 16 scores in registers
+constexpr int TOPK_SEG_MAX = 2048;   // segments per row: rows of up to 8,388,608 candidates
+constexpr int TOPK_SEG_ALL_MAX_Q = 160;  // up to this many query tokens, all long rows segmented
 constexpr int TOPK_BINS = 2048;
 constexpr int TOPK_CAND_CAP = 4096;
-constexpr int TOPK_REC = 8;  // per row: cand count, done count, b*, -, cut prefix (2), mask (2)
+// per row: [0] candidate counter, [1] b*, [2] count above b*, [4..5] cut key (low, high word)
+constexpr int TOPK_REC = 8;
 
 // Monotone 11-bit code of a non-negative score: values below 64 map to themselves, larger
 // values to (leading-one position - 5) * 64 + the 6 bits below the leading one. Shared by the
@@ -67,11 +71,13 @@ __device__ __forceinline__ uint64_t topk_bin_lo(int b) {
   return (uint64_t)(64 + b % 64) << (e - 6);
 }
 
-// Top-k workspace for rows longer than TOPK_LDS_MAX.
+// Top-k workspace for rows longer than TOPK_LDS_MAX. The histogram and the candidate counters
+// must be zero when a call starts: the kernels that consume them clear them again, so a
+// workspace zero-filled once stays ready for every later call.
 struct TopkWs {
   int* hist;       // [total_q][TOPK_BINS] score histogram of each row (indexer fills it)
   int* rec;        // [total_q][TOPK_REC]
-  int* seg;        // [total_q][nseg] per-segment counts, then output offsets
+  int* seg;        // [total_q][nseg] per-segment counts above b*, then output offsets
   uint64_t* cand;  // [total_q][TOPK_CAND_CAP] keys of the b* candidates
   int64_t nseg;
 };
@@ -120,8 +126,6 @@ hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, cons
 
 size_t topk_workspace_bytes(const smla_batch& b, int32_t top_k);
 TopkWs topk_workspace(const smla_batch& b, void* ws);
-// Zero the histogram and counters (before the indexer accumulates into the histogram).
-hipError_t topk_prepare(const smla_batch& b, const TopkWs& w, hipStream_t s);
 hipError_t launch_topk(const smla_batch& b, const int32_t* scores_compact, int32_t top_k,
                        int32_t* idx, int32_t* score, const TopkWs& w, hipStream_t s);
 

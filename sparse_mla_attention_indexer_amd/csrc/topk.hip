@@ -11,10 +11,11 @@
 //     everything in higher bins is selected;
 //  2. inside b* an MSD radix select over 8-bit digits of the 64-bit key finds the exact cut.
 // Rows of up to 32,768 candidates are selected by one workgroup with the scores held in LDS.
-// Longer rows use the histogram the indexer kernel accumulated while scoring: rows of up to
-// 73,728 candidates are held in one workgroup's registers; longer rows are cut into
-// 8,192-candidate segments handled by three kernels (count, resolve, emit). Selected indices always come out in
-// ascending order, each written at its rank.
+// Longer rows use the histogram the indexer kernel accumulated while scoring: in batches with
+// many query tokens, rows of up to 73,728 candidates are held in one workgroup's registers;
+// otherwise (and for longer rows) rows are cut into 4,096-candidate segments handled by three
+// kernels (count, resolve, emit). Selected indices always come out in ascending order, each
+// written at its rank.
 #include "smla_internal.h"
 
 namespace smla {
@@ -335,9 +336,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
       wcnt);
 }
 
-// ---- path B: rows of n > TOPK_LDS_MAX ----------------------------------------------------
-constexpr int NT_B = 256;
-
+// ---- rows of n > TOPK_LDS_MAX: workspace layout ------------------------------------------
 __host__ __device__ inline TopkWs topk_ws(void* base, int64_t total_q, int64_t nseg) {
   char* p = static_cast<char*>(base);
   TopkWs w;
@@ -352,30 +351,30 @@ __host__ __device__ inline TopkWs topk_ws(void* base, int64_t total_q, int64_t n
   return w;
 }
 
-// ---- rows of TOPK_LDS_MAX < n <= TOPK_ROW_MAX: one 1024-thread workgroup per row ----------
-// The score histogram comes from the indexer, so b* is known at once. Each of the 16 waves owns a
-// contiguous chunk of the row and holds it in registers (72 scores per lane, every load issued
-// before any is used); a first pass over the registers counts the elements above b* and gathers
-// the b* candidates in LDS, one wave resolves the exact cut among them, and a second pass writes
-// every selected index at its rank. No state is shared across workgroups.
-constexpr int NT_R = 1024;
-constexpr int NW_R = NT_R / 64;
-constexpr int V_R = TOPK_ROW_MAX / NT_R;  // scores per lane
+// ---- register-resident passes shared by the row and segment kernels --------------------------
+// A lane holds V scores: element u is at index i0 + 64 u of the row, and it lies inside the row
+// (or segment) iff 64 u < rem. Masks are ballots of compares, so the per-element cost is one or
+// two vector compares; counting and rank arithmetic are scalar.
 
-// Loads the V_R elements row[ib + 64 u] of this lane. One buffer resource per group of 16 u
-// (1024 elements) keeps every per-load offset in the instruction's 12-bit immediate, so a single
-// address register serves all V_R loads; each resource's range is what is left of the row past
-// the group's base, and loads past the end return 0. aux: cache-policy bits.
-__device__ __forceinline__ void row_load(uint32_t (&v)[V_R], const int32_t* row, int n, int ib,
-                                         int aux) {
+__device__ __forceinline__ int lanes_below(uint64_t m) {  // set bits of m below this lane
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Loads v[u] = base[ib + 64 u] for u < V. One buffer resource per group of 16 u (1024 elements)
+// keeps every per-load offset in the instruction's 12-bit immediate, so a single address register
+// serves all loads; each resource's range is what is left of [0, len) past the group's base, so
+// loads past the end return 0 instead of faulting. aux: cache-policy bits.
+template <int V>
+__device__ __forceinline__ void lane_load(uint32_t (&v)[V], const int32_t* base, int len, int ib,
+                                          int aux) {
   const int voff = ib * 4;
 #pragma unroll
-  for (int g = 0; g < (V_R + 15) / 16; ++g) {
-    const int left = max(0, n - 1024 * g);
+  for (int g = 0; g < (V + 15) / 16; ++g) {
+    const int left = max(0, len - 1024 * g);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(row + 1024 * g), 0, left * 4, 0x00020000);
+        const_cast<int32_t*>(base + 1024 * g), 0, left * 4, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 16 && 16 * g + j < V_R; ++j) {
+    for (int j = 0; j < 16 && 16 * g + j < V; ++j) {
       if (aux)
         v[16 * g + j] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 256 * j, 0, 1);
       else
@@ -384,21 +383,16 @@ __device__ __forceinline__ void row_load(uint32_t (&v)[V_R], const int32_t* row,
   }
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t m) {  // set bits of m below this lane
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-}
-
-// Row pass 1 over one wave's register-resident chunk: count the elements above bin b* = [lo, hm1]
-// (returned, wave-uniform) and append the keys of the b* candidates to klo/khi. The masks are
-// ballots of compares, so the per-element work is two vector compares; everything else is scalar.
-// FULL: the whole chunk lies inside the row (no range mask).
-template <bool FULL>
-__device__ __forceinline__ int row_pass1(const uint32_t (&v)[V_R], int ib, int rem, uint32_t lo,
-                                         uint32_t hm1, uint32_t* klo, uint32_t* khi, int* nk) {
+// Counts the lane-group's elements above bin b* = [lo, hm1] (returned, wave-uniform) and appends
+// the keys of the b* candidates to klo/khi (slots from *nk, at most cap). FULL: no range mask.
+template <int V, bool FULL>
+__device__ __forceinline__ int pass_gather(const uint32_t (&v)[V], int i0, int rem, uint32_t lo,
+                                           uint32_t hm1, uint32_t* klo, uint32_t* khi, int* nk,
+                                           int cap) {
   const int lane = threadIdx.x & 63;
   int above = 0;
 #pragma unroll
-  for (int u = 0; u < V_R; ++u) {
+  for (int u = 0; u < V; ++u) {
     const uint32_t x = v[u];
     uint64_t ma = __ballot(x > hm1);
     uint64_t mc = __ballot(x >= lo) & ~ma;
@@ -414,8 +408,8 @@ __device__ __forceinline__ int row_pass1(const uint32_t (&v)[V_R], int ib, int r
       base = __builtin_amdgcn_readfirstlane(base);
       if ((mc >> lane) & 1) {
         const int slot = base + lanes_below(mc);
-        if (slot < TOPK_CAND_CAP) {
-          klo[slot] = 0xFFFFFFFFu - (uint32_t)(ib + 64 * u);
+        if (slot < cap) {
+          klo[slot] = 0xFFFFFFFFu - (uint32_t)(i0 + 64 * u);
           khi[slot] = x;
         }
       }
@@ -424,27 +418,42 @@ __device__ __forceinline__ int row_pass1(const uint32_t (&v)[V_R], int ib, int r
   return above;
 }
 
-// Row pass 2: write every element whose key (score, then lower index) is at least the cut key
-// (th, tl) at its rank, starting at `pos` (wave-uniform). Index comparisons happen only for
-// elements whose score equals the cut score.
+// Selected iff the key (score, then lower index) is at least the cut key (th, tl); the index
+// comparison only matters for elements whose score equals the cut score.
 template <bool FULL>
-__device__ __forceinline__ void row_pass2(const uint32_t (&v)[V_R], int ib, int rem, uint32_t th,
-                                          uint32_t tl, int pos, int top_k, int32_t* oi,
-                                          int32_t* os) {
+__device__ __forceinline__ uint64_t sel_mask(uint32_t x, int i, int u, int rem, uint32_t th,
+                                             uint32_t tl) {
+  uint64_t m = __ballot(x > th);
+  if (__ballot(x == th)) m |= __ballot((x == th) & (0xFFFFFFFFu - (uint32_t)i >= tl));
+  if (!FULL) m &= __ballot(64 * u < rem);
+  return m;
+}
+
+template <int V, bool FULL>
+__device__ __forceinline__ int pass_count(const uint32_t (&v)[V], int i0, int rem, uint32_t th,
+                                          uint32_t tl) {
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < V; ++u) c += __popcll(sel_mask<FULL>(v[u], i0 + 64 * u, u, rem, th, tl));
+  return c;
+}
+
+// Writes every selected element's index (and score) at its rank, from `pos` (wave-uniform).
+template <int V, bool FULL>
+__device__ __forceinline__ void pass_write(const uint32_t (&v)[V], int i0, int rem, uint32_t th,
+                                           uint32_t tl, int pos, int top_k, int32_t* oi,
+                                           int32_t* os) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < V_R; ++u) {
-    const uint32_t x = v[u];
-    const int i = ib + 64 * u;
-    uint64_t m = __ballot(x > th);
-    if (__ballot(x == th)) m |= __ballot((x == th) & (0xFFFFFFFFu - (uint32_t)i >= tl));
-    if (!FULL) m &= __ballot(64 * u < rem);
+  for (int u = 0; u < V; ++u) {
+    const int i = i0 + 64 * u;
+    const uint64_t m = sel_mask<FULL>(v[u], i, u, rem, th, tl);
     if (m) {
       if ((m >> lane) & 1) {
         const int p = pos + lanes_below(m);
         if (p < top_k) {  // exactly top_k are selected; the guard only bounds the writes
           oi[p] = i;
-          if (os) os[p] = (int32_t)x;
+          if (os) os[p] = (int32_t)v[u];
         }
       }
       pos += __popcll(m);
@@ -452,12 +461,65 @@ __device__ __forceinline__ void row_pass2(const uint32_t (&v)[V_R], int ib, int 
   }
 }
 
+// The cut key inside b*: keys are unique, so the selection is a threshold on the key. When every
+// candidate is taken the threshold is the bottom of b*.
+__device__ __forceinline__ uint64_t cut_key(uint64_t prefix, uint32_t lo) {
+  return max(prefix, (uint64_t)lo << 32);
+}
+
+__device__ __forceinline__ uint32_t bin_hm1(int b) {  // top score of bin b
+  return (uint32_t)min(topk_bin_lo(b + 1) - 1, (uint64_t)0xFFFFFFFFu);
+}
+
+// b* and the count above it from a row's global histogram, 2048 / NT bins per thread in
+// registers. Results in out[0] (bin) and out[1] (count above).
+template <int NT>
+__device__ void hist_cut(const int* __restrict__ gh, int k, int* red, int* out) {
+  constexpr int PER = TOPK_BINS / NT;
+  static_assert(PER * NT == TOPK_BINS, "bins per thread");
+  int h[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) h[j] = gh[threadIdx.x * PER + j];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) local += h[j];
+  if (threadIdx.x == 0) {
+    out[0] = 0;
+    out[1] = 0;
+  }
+  const int incl = block_incl_scan<NT>(local, red);
+  const int above = red[NT / 64] - incl;
+  if (above < k && above + local >= k) {
+    int c = above;
+#pragma unroll
+    for (int b = PER - 1; b >= 0; --b) {
+      if (c + h[b] >= k) {
+        out[0] = threadIdx.x * PER + b;
+        out[1] = c;
+        break;
+      }
+      c += h[b];
+    }
+  }
+  __syncthreads();
+}
+
+// ---- rows of TOPK_LDS_MAX < n <= TOPK_ROW_MAX: one 1024-thread workgroup per row ----------
+// For batches with many long rows. The score histogram comes from the indexer, so b* is known at
+// once. Each of the 16 waves owns a contiguous chunk of the row and holds it in registers (72
+// scores per lane); a first pass counts the elements above b* and gathers the b* candidates in
+// LDS, one wave resolves the exact cut among them, the selected candidates are credited to the
+// waves that hold them, and a second pass (reloading the chunk, by then in L2) writes every
+// selected index at its rank. The row's histogram is cleared once read.
+constexpr int NT_R = 1024;
+constexpr int NW_R = NT_R / 64;
+constexpr int V_R = TOPK_ROW_MAX / NT_R;  // scores per lane
+
 __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ toks,
                                                         const int32_t* __restrict__ scores,
                                                         int top_k, TopkWs ws,
                                                         int32_t* __restrict__ idx_out,
                                                         int32_t* __restrict__ score_out) {
-  __shared__ int hist[TOPK_BINS];
   // candidate keys as two planes (low words: ~index, high words: score) so the compiler never
   // pairs a score with an index into a 64-bit register
   __shared__ uint32_t klo[TOPK_CAND_CAP], khi[TOPK_CAND_CAP];
@@ -473,57 +535,50 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
   if (n <= TOPK_LDS_MAX || n > TOPK_ROW_MAX) return;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int32_t* row = scores + tk.cand_off;
-  // Element u of this lane is row[ib + 64 u]: wave w owns [w 64 V_R, (w + 1) 64 V_R). Buffer
-  // loads with the row length as the range return 0 past the end instead of faulting; the
-  // range mask drops those in the one wave whose chunk crosses the end. Each pass issues all
-  // V_R loads before using any.
   const int ib = wv * (64 * V_R) + lane;
   const int rem = n - ib;
   const bool full = n >= (wv + 1) * (64 * V_R);
   int32_t* oi = idx_out + t * top_k;
   int32_t* os = score_out ? score_out + t * top_k : nullptr;
+  int* gh = ws.hist + t * TOPK_BINS;
   int need, bstar;
   uint32_t lo;
   {
     uint32_t v[V_R];
-    row_load(v, row, n, ib, 0);
-    // while the row is in flight: the cut bin b* from the histogram the indexer accumulated
-    const int* gh = ws.hist + t * TOPK_BINS;
-    for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) hist[i] = gh[i];
+    lane_load<V_R>(v, row, n, ib, 0);
     if (threadIdx.x == 0) nk = 0;
-    __syncthreads();
-    find_cut<NT_R>(hist, TOPK_BINS, top_k, red, cut);
+    hist_cut<NT_R>(gh, top_k, red, cut);  // while the row is in flight
     bstar = cut[0];
     need = top_k - cut[1];
     lo = (uint32_t)topk_bin_lo(bstar);
-    const uint32_t hm1 = (uint32_t)min(topk_bin_lo(bstar + 1) - 1, (uint64_t)0xFFFFFFFFu);
-    const int above = full ? row_pass1<true>(v, ib, rem, lo, hm1, klo, khi, &nk)
-                           : row_pass1<false>(v, ib, rem, lo, hm1, klo, khi, &nk);
+    const uint32_t hm1 = bin_hm1(bstar);
+    const int above = full ? pass_gather<V_R, true>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP)
+                           : pass_gather<V_R, false>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP);
     if (lane == 0) wsel[wv] = above;
   }
+  // the histogram was read by every thread before hist_cut's last barrier: clear it for the next
+  // call
+  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) gh[i] = 0;
   __syncthreads();
 
   const int ncand = nk;
   if (ncand <= TOPK_CAND_CAP) {
     // pass 2's loads go out before the cut so their latency hides behind it
     uint32_t v[V_R];
-    row_load(v, row, n, ib, 1);  // glc: a distinct load the compiler cannot merge with pass 1
+    lane_load<V_R>(v, row, n, ib, 1);  // glc: a distinct load the compiler cannot merge with pass 1
     if (wv == 0) {
       uint64_t pf, mk;
       wave_radix_cut([&](int i) { return ((uint64_t)khi[i] << 32) | klo[i]; }, ncand, need, hist2,
                      &pf, &mk);
-      // Keys are unique, so the cut is a threshold: the selected elements are exactly those whose
-      // key (score, then lower index) is at least the cut key. When every candidate is taken the
-      // cut is the bottom of bin b*.
-      if (lane == 0) pm[0] = max(pf, (uint64_t)lo << 32);
+      if (lane == 0) pm[0] = cut_key(pf, lo);
       (void)mk;
     }
     __syncthreads();
-    const uint64_t cutkey = pm[0];
+    const uint64_t ck = pm[0];
     // selected candidates per owning wave (the index says which wave holds the score)
     for (int c = threadIdx.x; c < ncand; c += NT_R) {
       const uint64_t key = ((uint64_t)khi[c] << 32) | klo[c];
-      if (key >= cutkey) atomicAdd(&wsel[(int)(0xFFFFFFFFu - klo[c]) / (64 * V_R)], 1);
+      if (key >= ck) atomicAdd(&wsel[(int)(0xFFFFFFFFu - klo[c]) / (64 * V_R)], 1);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -534,26 +589,26 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
       }
     }
     __syncthreads();
-    const uint32_t th = (uint32_t)(cutkey >> 32), tl = (uint32_t)cutkey;
+    const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
     const int pos = __builtin_amdgcn_readfirstlane(woff[wv]);
     if (full)
-      row_pass2<true>(v, ib, rem, th, tl, pos, top_k, oi, os);
+      pass_write<V_R, true>(v, ib, rem, th, tl, pos, top_k, oi, os);
     else
-      row_pass2<false>(v, ib, rem, th, tl, pos, top_k, oi, os);
+      pass_write<V_R, false>(v, ib, rem, th, tl, pos, top_k, oi, os);
     return;
   }
   // more candidates than LDS holds (heavy ties): cut and emit straight from the score row
   radix_cut<NT_R>(
       n, need, [&](int i) { return sel_key(row[i], i); },
       [&](int i) { return score_bin((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
-  const uint64_t prefix = pm[0], mask = pm[1];
+  const uint64_t ck = cut_key(pm[0], lo);
+  const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
   const int c0 = wv * (64 * V_R);
   const int c1 = min(n, c0 + 64 * V_R);
   int cp = 0;
   for (int i = c0 + lane; i < c1; i += 64) {
-    const int x = row[i];
-    const int bn = score_bin((uint32_t)x);
-    cp += bn > bstar || (bn == bstar && (sel_key(x, i) & mask) >= prefix);
+    const uint32_t x = (uint32_t)row[i];
+    cp += x > th || (x == th && 0xFFFFFFFFu - (uint32_t)i >= tl);
   }
   for (int d = 32; d > 0; d >>= 1) cp += __shfl_xor(cp, d);
   if (lane == 0) wsel[wv] = cp;
@@ -569,204 +624,197 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
   int pos = woff[wv];
   for (int b0 = c0; b0 < c1; b0 += 64) {
     const int i = b0 + lane;
-    const int x = i < c1 ? row[i] : 0;
-    const int bn = i < c1 ? score_bin((uint32_t)x) : -1;
-    const bool f = bn > bstar || (bn == bstar && (sel_key(x, i) & mask) >= prefix);
+    const uint32_t x = i < c1 ? (uint32_t)row[i] : 0u;
+    const bool f = i < c1 && (x > th || (x == th && 0xFFFFFFFFu - (uint32_t)i >= tl));
     const uint64_t m = __ballot(f);
     if (f) {
-      const int p = pos + __popcll(m & ((1ull << lane) - 1));
+      const int p = pos + lanes_below(m);
       if (p < top_k) {
         oi[p] = i;
-        if (os) os[p] = x;
+        if (os) os[p] = (int32_t)x;
       }
     }
     pos += __popcll(m);
   }
 }
 
-// ---- rows of n > TOPK_ROW_MAX: segments of TOPK_SEG candidates over three kernels ---------
-// count: per segment, the elements above b* and the b* candidates (appended to the row's
-// candidate buffer); resolve: one workgroup per row finds the exact cut among the candidates and
-// turns the per-segment counts into output offsets; emit: each segment writes its selected
-// indices at their ranks. Kernel boundaries order the three, not device-wide fences.
-__global__ __launch_bounds__(NT_B) void topk_seg_count_kernel(const Tok* __restrict__ toks,
+// ---- segmented rows: count / resolve / emit over TOPK_SEG-candidate segments ---------------
+// For rows longer than TOPK_ROW_MAX, and for every row longer than TOPK_LDS_MAX when the batch has
+// few query tokens (one workgroup per row would leave most of the chip idle). Kernel boundaries
+// order the three kernels; no workgroup waits on another.
+//  count   (segment x row): b* from the row's histogram; the segment's elements above b* and its
+//          b* candidates (gathered in LDS, then appended to the row's candidate buffer with one
+//          atomic per workgroup).
+//  resolve (row): the exact cut key among the candidates (or, when they overflowed the buffer,
+//          by radix select over the row) and each segment's output offset; clears the row's
+//          histogram and candidate counter for the next call.
+//  emit    (segment x row): counts per wave, then writes each selected index at its rank.
+constexpr int NT_S = 256;
+constexpr int V_S = TOPK_SEG / NT_S;  // 16 per lane: wave w owns [1024 w, 1024 (w + 1))
+static_assert(V_S == 16, "one buffer resource per segment");
+
+__global__ __launch_bounds__(NT_S) void topk_seg_count_kernel(const Tok* __restrict__ toks,
                                                               const int32_t* __restrict__ scores,
-                                                              int top_k, TopkWs ws) {
-  __shared__ int hist[TOPK_BINS];
-  __shared__ int red[NT_B / 64 + 1];
+                                                              int top_k, int seg_min_n,
+                                                              TopkWs ws) {
+  __shared__ uint32_t klo[TOPK_SEG], khi[TOPK_SEG];
+  __shared__ int red[NT_S / 64 + 1];
   __shared__ int cut[2];
+  __shared__ int nk, gbase;
+  __shared__ int wab[NT_S / 64];
   const int64_t t = blockIdx.y;
+  const int g = blockIdx.x;
   const Tok tk = toks[t];
   const int n = tk.pos + 1;
-  const int g = blockIdx.x;
   const int s0 = g * TOPK_SEG;
-  if (n <= TOPK_ROW_MAX || s0 >= n) return;
-  const int s1 = min(n, s0 + TOPK_SEG);
-  const int* gh = ws.hist + t * TOPK_BINS;
-  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = gh[i];
-  __syncthreads();
-  find_cut<NT_B>(hist, TOPK_BINS, top_k, red, cut);
+  if (n <= seg_min_n || s0 >= n) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int len = min(n - s0, TOPK_SEG);
+  const int ib = wv * (64 * V_S) + lane;
+  const int rem = len - ib;
+  const bool full = len >= (wv + 1) * (64 * V_S);
+  uint32_t v[V_S];
+  lane_load<V_S>(v, scores + tk.cand_off + s0, len, ib, 0);
+  if (threadIdx.x == 0) nk = 0;
+  hist_cut<NT_S>(ws.hist + t * TOPK_BINS, top_k, red, cut);
   const int bstar = cut[0];
+  const uint32_t lo = (uint32_t)topk_bin_lo(bstar), hm1 = bin_hm1(bstar);
+  const int above = full ? pass_gather<V_S, true>(v, s0 + ib, rem, lo, hm1, klo, khi, &nk, TOPK_SEG)
+                         : pass_gather<V_S, false>(v, s0 + ib, rem, lo, hm1, klo, khi, &nk, TOPK_SEG);
+  if (lane == 0) wab[wv] = above;
+  __syncthreads();
   int* rec = ws.rec + t * TOPK_REC;
-  uint64_t* cand = ws.cand + t * TOPK_CAND_CAP;
-  const int32_t* row = scores + tk.cand_off;
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = TOPK_SEG / NT_B;
-  int vals[PER];
+  if (threadIdx.x == 0) {
+    int tot = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {  // every load of the segment in flight before any is used
-    const int i = s0 + j * NT_B + threadIdx.x;
-    vals[j] = i < s1 ? row[i] : 0;
-  }
-  int sel = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = s0 + j * NT_B + threadIdx.x;
-    const int bn = i < s1 ? score_bin((uint32_t)vals[j]) : -1;
-    sel += bn > bstar;
-    const uint64_t m = __ballot(bn == bstar);
-    if (m) {  // wave-aggregated append of this wave's b* candidates
-      int base = 0;
-      const int leader = __builtin_ctzll(m);
-      if (lane == leader) base = atomicAdd(&rec[0], __popcll(m));
-      base = __shfl(base, leader);
-      if (bn == bstar) {
-        const int slot = base + __popcll(m & ((1ull << lane) - 1));
-        if (slot < TOPK_CAND_CAP) cand[slot] = sel_key(vals[j], i);
-      }
+    for (int w = 0; w < NT_S / 64; ++w) tot += wab[w];
+    ws.seg[t * ws.nseg + g] = tot;
+    gbase = nk ? atomicAdd(&rec[0], nk) : 0;
+    if (g == 0) {
+      rec[1] = bstar;
+      rec[2] = cut[1];
     }
   }
-  block_incl_scan<NT_B>(sel, red);
-  if (threadIdx.x == 0) ws.seg[t * ws.nseg + g] = red[NT_B / 64];
+  __syncthreads();
+  const int nl = nk, base = gbase;
+  uint64_t* cand = ws.cand + t * TOPK_CAND_CAP;
+  for (int i = threadIdx.x; i < nl && base + i < TOPK_CAND_CAP; i += NT_S)
+    cand[base + i] = ((uint64_t)khi[i] << 32) | klo[i];
 }
 
-__global__ __launch_bounds__(NT_B) void topk_resolve_kernel(const Tok* __restrict__ toks,
-                                                            const int32_t* __restrict__ scores,
-                                                            int top_k, TopkWs ws) {
-  __shared__ int hist[TOPK_BINS];
-  __shared__ uint64_t keys[TOPK_CAND_CAP];
+__global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __restrict__ toks,
+                                                                const int32_t* __restrict__ scores,
+                                                                int top_k, int seg_min_n,
+                                                                TopkWs ws) {
+  __shared__ uint32_t klo[TOPK_CAND_CAP], khi[TOPK_CAND_CAP];
+  __shared__ int segc[TOPK_SEG_MAX];
   __shared__ int hist2[256];
-  __shared__ int red[NT_B / 64 + 1];
+  __shared__ int red[NT_R / 64 + 1];
   __shared__ int cut[2];
   __shared__ uint64_t pm[2];
   const int64_t t = blockIdx.x;
   const Tok tk = toks[t];
   const int n = tk.pos + 1;
-  if (n <= TOPK_ROW_MAX) return;
+  if (n <= seg_min_n) return;
   const int nseg_t = (n + TOPK_SEG - 1) / TOPK_SEG;
-  const int* gh = ws.hist + t * TOPK_BINS;
-  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = gh[i];
-  __syncthreads();
-  find_cut<NT_B>(hist, TOPK_BINS, top_k, red, cut);
-  const int bstar = cut[0];
-  const int need = top_k - cut[1];
   int* rec = ws.rec + t * TOPK_REC;
-  int* segc = ws.seg + t * ws.nseg;
-  const int32_t* row = scores + tk.cand_off;
+  int* segv = ws.seg + t * ws.nseg;
   const int ncand = rec[0];
-  uint64_t prefix = 0, mask = 0;
+  const int bstar = rec[1];
+  const int need = top_k - rec[2];
+  const uint32_t lo = (uint32_t)topk_bin_lo(bstar);
+  for (int g = threadIdx.x; g < nseg_t; g += NT_R) segc[g] = segv[g];  // elements above b*
+  uint64_t ck;
   if (ncand <= TOPK_CAND_CAP) {
     const uint64_t* cand = ws.cand + t * TOPK_CAND_CAP;
-    for (int i = threadIdx.x; i < ncand; i += NT_B) keys[i] = cand[i];
+    for (int i = threadIdx.x; i < ncand; i += NT_R) {
+      const uint64_t key = cand[i];
+      klo[i] = (uint32_t)key;
+      khi[i] = (uint32_t)(key >> 32);
+    }
     __syncthreads();
     if (threadIdx.x < 64) {
       uint64_t pf, mk;
-      wave_radix_cut([&](int i) { return keys[i]; }, ncand, need, hist2, &pf, &mk);
-      if (threadIdx.x == 0) {
-        pm[0] = pf;
-        pm[1] = mk;
-      }
+      wave_radix_cut([&](int i) { return ((uint64_t)khi[i] << 32) | klo[i]; }, ncand, need, hist2,
+                     &pf, &mk);
+      if (threadIdx.x == 0) pm[0] = cut_key(pf, lo);
+      (void)mk;
     }
     __syncthreads();
-    prefix = pm[0];
-    mask = pm[1];
-    for (int i = threadIdx.x; i < ncand; i += NT_B) {
-      const uint64_t key = keys[i];
-      if ((key & mask) >= prefix) atomicAdd(&segc[(int)(0xFFFFFFFFu - (uint32_t)key) / TOPK_SEG], 1);
+    ck = pm[0];
+    for (int i = threadIdx.x; i < ncand; i += NT_R) {
+      const uint64_t key = ((uint64_t)khi[i] << 32) | klo[i];
+      if (key >= ck) atomicAdd(&segc[(int)(0xFFFFFFFFu - klo[i]) / TOPK_SEG], 1);
     }
   } else {
     // more candidates than the buffer holds (heavy ties): cut straight from the score row
-    radix_cut<NT_B>(
+    const int32_t* row = scores + tk.cand_off;
+    radix_cut<NT_R>(
         n, need, [&](int i) { return sel_key(row[i], i); },
         [&](int i) { return score_bin((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
-    prefix = pm[0];
-    mask = pm[1];
-    for (int i = threadIdx.x; i < n; i += NT_B) {
-      const int v = row[i];
-      if (score_bin((uint32_t)v) == bstar && (sel_key(v, i) & mask) >= prefix)
+    ck = cut_key(pm[0], lo);
+    for (int i = threadIdx.x; i < n; i += NT_R) {
+      const uint32_t x = (uint32_t)row[i];
+      if (x >= lo && sel_key((int32_t)x, i) >= ck && score_bin(x) == bstar)
         atomicAdd(&segc[i / TOPK_SEG], 1);
     }
   }
   __syncthreads();
   // exclusive scan of the per-segment counts -> output offsets
   int carry = 0;
-  for (int c0 = 0; c0 < nseg_t; c0 += NT_B) {
+  for (int c0 = 0; c0 < nseg_t; c0 += NT_R) {
     const int c = c0 + threadIdx.x;
-    const int v = c < nseg_t ? atomicAdd(&segc[c], 0) : 0;
-    const int incl = block_incl_scan<NT_B>(v, red);
-    const int tot = red[NT_B / 64];
-    if (c < nseg_t) segc[c] = carry + incl - v;
+    const int v = c < nseg_t ? segc[c] : 0;
+    const int incl = block_incl_scan<NT_R>(v, red);
+    const int tot = red[NT_R / 64];
+    if (c < nseg_t) segv[c] = carry + incl - v;
     carry += tot;
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    rec[2] = bstar;
-    rec[4] = (int)(uint32_t)prefix;
-    rec[5] = (int)(uint32_t)(prefix >> 32);
-    rec[6] = (int)(uint32_t)mask;
-    rec[7] = (int)(uint32_t)(mask >> 32);
+    rec[0] = 0;  // the candidate counter starts the next call at zero
+    rec[4] = (int)(uint32_t)ck;
+    rec[5] = (int)(uint32_t)(ck >> 32);
   }
+  int* gh = ws.hist + t * TOPK_BINS;
+  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) gh[i] = 0;
 }
 
-// Pass 2: every segment writes its selected indices at their ranks (ascending index order).
-__global__ __launch_bounds__(NT_B) void topk_emit_kernel(const Tok* __restrict__ toks,
-                                                         const int32_t* __restrict__ scores,
-                                                         int top_k, TopkWs ws,
-                                                         int32_t* __restrict__ idx_out,
-                                                         int32_t* __restrict__ score_out) {
-  __shared__ int sc[TOPK_SEG];
+__global__ __launch_bounds__(NT_S) void topk_seg_emit_kernel(const Tok* __restrict__ toks,
+                                                             const int32_t* __restrict__ scores,
+                                                             int top_k, int seg_min_n, TopkWs ws,
+                                                             int32_t* __restrict__ idx_out,
+                                                             int32_t* __restrict__ score_out) {
+  __shared__ int wc[NT_S / 64];
   const int64_t t = blockIdx.y;
+  const int g = blockIdx.x;
   const Tok tk = toks[t];
   const int n = tk.pos + 1;
-  const int g = blockIdx.x;
   const int s0 = g * TOPK_SEG;
-  if (n <= TOPK_ROW_MAX || s0 >= n) return;
-  const int s1 = min(n, s0 + TOPK_SEG);
-  const int len = s1 - s0;
+  if (n <= seg_min_n || s0 >= n) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int len = min(n - s0, TOPK_SEG);
+  const int ib = wv * (64 * V_S) + lane;
+  const int rem = len - ib;
+  const bool full = len >= (wv + 1) * (64 * V_S);
+  uint32_t v[V_S];
+  lane_load<V_S>(v, scores + tk.cand_off + s0, len, ib, 0);
   const int* rec = ws.rec + t * TOPK_REC;
-  const int bstar = rec[2];
-  const uint64_t prefix = (uint64_t)(uint32_t)rec[4] | ((uint64_t)(uint32_t)rec[5] << 32);
-  const uint64_t mask = (uint64_t)(uint32_t)rec[6] | ((uint64_t)(uint32_t)rec[7] << 32);
+  const uint32_t tl = (uint32_t)rec[4], th = (uint32_t)rec[5];
   const int off = ws.seg[t * ws.nseg + g];
-  const int32_t* row = scores + tk.cand_off + s0;
-  {
-    constexpr int PER = TOPK_SEG / NT_B;
-    int vals[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * NT_B + threadIdx.x;
-      vals[j] = i < len ? row[i] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) sc[j * NT_B + threadIdx.x] = vals[j];
-  }
+  const int cnt = full ? pass_count<V_S, true>(v, s0 + ib, rem, th, tl)
+                       : pass_count<V_S, false>(v, s0 + ib, rem, th, tl);
+  if (lane == 0) wc[wv] = cnt;
   __syncthreads();
-  __shared__ int wcnt[NT_B / 64];
+  int pos = off;
+  for (int w = 0; w < wv; ++w) pos += wc[w];
+  pos = __builtin_amdgcn_readfirstlane(pos);
   int32_t* oi = idx_out + t * top_k;
   int32_t* os = score_out ? score_out + t * top_k : nullptr;
-  emit_in_order<NT_B>(
-      len, off,
-      [&](int i) {
-        const int bn = score_bin((uint32_t)sc[i]);
-        return bn > bstar || (bn == bstar && (sel_key(sc[i], s0 + i) & mask) >= prefix);
-      },
-      [&](int i, int pos) {
-        if (pos < top_k) {  // exactly top_k are selected per row; the guard only bounds writes
-          oi[pos] = s0 + i;
-          if (os) os[pos] = sc[i];
-        }
-      },
-      wcnt);
+  if (full)
+    pass_write<V_S, true>(v, s0 + ib, rem, th, tl, pos, top_k, oi, os);
+  else
+    pass_write<V_S, false>(v, s0 + ib, rem, th, tl, pos, top_k, oi, os);
 }
 
 }  // namespace
@@ -786,14 +834,6 @@ TopkWs topk_workspace(const smla_batch& b, void* ws) {
   return topk_ws(ws, b.total_q, topk_nseg(b));
 }
 
-hipError_t topk_prepare(const smla_batch& b, const TopkWs& w, hipStream_t s) {
-  if (b.max_kv <= TOPK_LDS_MAX) return hipSuccess;
-  // histogram (filled by the indexer) and per-row counters start at zero; they are adjacent
-  const int64_t n = (reinterpret_cast<const char*>(w.rec) - reinterpret_cast<const char*>(w.hist)) / 4 +
-                    (int64_t)TOPK_REC * b.total_q;
-  return launch_fill_i32(w.hist, n, 0, s);
-}
-
 hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
                        int32_t* score, const TopkWs& w, hipStream_t s) {
   TableView tv = table_view(b.table, b.batch, b.total_q);
@@ -811,18 +851,25 @@ hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.max_kv <= TOPK_LDS_MAX) return e;
-  hipLaunchKernelGGL(topk_row_kernel, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores, top_k, w,
-                     idx, score);
-  if ((e = hipGetLastError()) != hipSuccess || b.max_kv <= TOPK_ROW_MAX) return e;
+  // few query tokens: every long row goes through the segment kernels, which spread a row over
+  // many workgroups; otherwise one workgroup per row up to TOPK_ROW_MAX
+  const bool seg_all = b.total_q <= TOPK_SEG_ALL_MAX_Q;
+  const int seg_min_n = seg_all ? TOPK_LDS_MAX : TOPK_ROW_MAX;
+  if (!seg_all) {
+    hipLaunchKernelGGL(topk_row_kernel, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores, top_k, w,
+                       idx, score);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (b.max_kv <= seg_min_n) return e;
   const unsigned nseg = (unsigned)topk_nseg(b);
-  hipLaunchKernelGGL(topk_seg_count_kernel, dim3(nseg, b.total_q), dim3(NT_B), 0, s, tv.tok,
-                     scores, top_k, w);
+  hipLaunchKernelGGL(topk_seg_count_kernel, dim3(nseg, b.total_q), dim3(NT_S), 0, s, tv.tok,
+                     scores, top_k, seg_min_n, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(b.total_q), dim3(NT_B), 0, s, tv.tok, scores, top_k,
-                     w);
+  hipLaunchKernelGGL(topk_seg_resolve_kernel, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores,
+                     top_k, seg_min_n, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_emit_kernel, dim3(nseg, b.total_q), dim3(NT_B), 0, s, tv.tok, scores,
-                     top_k, w, idx, score);
+  hipLaunchKernelGGL(topk_seg_emit_kernel, dim3(nseg, b.total_q), dim3(NT_S), 0, s, tv.tok, scores,
+                     top_k, seg_min_n, w, idx, score);
   return hipGetLastError();
 }
 

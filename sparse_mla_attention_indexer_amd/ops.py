@@ -95,8 +95,9 @@ def indexer_scores(plan: BatchPlan, q_idx, k_idx, w, out=None):
 
 
 def topk_workspace(plan: BatchPlan, H_I: int, D_I: int, top_k: int) -> torch.Tensor:
+    # zero-filled once: the library returns its histogram and counters to zero after each call
     n = int(lib().smla_indexer_topk_workspace_bytes(plan.ref, H_I, D_I, top_k))
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=plan.device)
 
 
 def indexer_topk(plan: BatchPlan, q_idx, k_idx, w, top_k: int, with_scores=True, idx=None,

@@ -42,7 +42,15 @@ class Dev:
 
     def topk(self, top_k=None, with_scores=True):
         top_k = self.x.dims.top_k if top_k is None else top_k
-        idx, sc = ops.indexer_topk(self.plan, self.q_idx, self.k_idx, self.w, top_k, with_scores)
+        # one workspace per top_k, reused across calls: each call must leave it ready for the next
+        ws = self._ws.get(top_k) if hasattr(self, "_ws") else None
+        if ws is None:
+            d = self.x.dims
+            ws = ops.topk_workspace(self.plan, d.H_I, d.D_I, top_k)
+            self._ws = getattr(self, "_ws", {})
+            self._ws[top_k] = ws
+        idx, sc = ops.indexer_topk(self.plan, self.q_idx, self.k_idx, self.w, top_k, with_scores,
+                                   workspace=ws)
         torch.cuda.synchronize()
         return idx.cpu().numpy(), (sc.cpu().numpy() if sc is not None else None)
 

@@ -125,6 +125,34 @@ def test_tie_stress_long_rows(pattern, cached):
         assert (idx == np.arange(2048)[None, :]).all()
 
 
+@pytest.mark.parametrize("pattern", ["random", "zeros", "few_values"])
+def test_many_long_rows_one_workgroup_per_row(pattern):
+    # more query tokens than the segmented path takes, rows between the LDS and the register
+    # limits: one workgroup per row; sampled tokens against the oracle, properties everywhere
+    d = W.small_big_dims(n_q=200, cached=36000)
+    x = W.generate(d)
+    if pattern == "zeros":
+        x.k_idx[:] = 0
+    elif pattern == "few_values":
+        rng = np.random.default_rng(9)
+        x.k_idx[:] = 0
+        x.k_idx[:, 0] = rng.integers(0, 3, size=x.k_idx.shape[0])
+        x.q_idx[:] = 1
+    say(f"[case] many long rows {pattern}")
+    dev = Dev(x)
+    idx, sc = dev.topk()
+    tokens = np.array([0, 1, 57, 133, 198, 199])
+    ref_idx, ref_sc = oracle_topk(x, tokens)
+    assert_topk_equal(idx[tokens], sc[tokens], ref_idx, ref_sc, f"many rows {pattern}")
+    pos = dev.plan.positions
+    assert (idx >= 0).all() and (idx <= pos[:, None]).all()
+    assert (np.diff(idx, axis=1) > 0).all()
+    if pattern == "zeros":
+        assert (idx == np.arange(d.top_k)[None, :]).all()
+    idx2, sc2 = dev.topk()  # the workspace the first call left behind serves the second
+    assert np.array_equal(idx, idx2) and np.array_equal(sc, sc2)
+
+
 def test_tie_stress_short_rows():
     d = W.small_big_dims(n_q=40, cached=3000)
     x = W.generate(d)
