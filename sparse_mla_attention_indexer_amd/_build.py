@@ -27,6 +27,12 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
+# Per-source additions. sparse_mla.hip: MFMA accumulators in ordinary VGPRs (the attention kernel
+# rescales its output accumulators with vector ALU ops; with accumulator registers the compiler
+# copies all of them out and back on every tile).
+FILE_FLAGS = {
+    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
 
 
 def _run(cmd, verbose):
@@ -50,12 +56,22 @@ def hip_sources():
 
 
 def build_hip(verbose: bool = False, extra=()) -> str:
+    """Compiles every source to an object (with its per-file flags), then links the library."""
     srcs = hip_sources()
     if not srcs:
         raise RuntimeError("no HIP sources found")
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    objs = []
+    for src in srcs:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        _run([hipcc, *compile_flags, *FILE_FLAGS.get(os.path.basename(src), []), *extra,
+              f"-I{INCLUDE}", f"-I{CSRC}", "-c", "-o", obj, src], verbose)
+        objs.append(obj)
     tmp = HIP_LIB + ".tmp"
-    _run([hipcc, *HIP_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *srcs], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, HIP_LIB)
     return HIP_LIB
 

@@ -7,16 +7,21 @@
 // rows). Partial results over disjoint row sets merge by log-sum-exp (section "DCP").
 //
 // FP8 kernel (64 heads, 576/512 dims, 656-byte rows), one workgroup of 4 waves per (token,
-// split), 32-row tiles, double-buffered in LDS:
-//  1. all 256 threads gather the next tile's rows while the current one computes (each wave
-//     instruction reads 512 contiguous bytes of one row), then dequantise e4m3 * block scale to
-//     bf16 into a row-major K[row][576] tile (16-byte chunks XOR-swizzled by row);
-//  2. wave (g, h) holds Q of heads [32g, 32g+32) over dims [288h, 288h+288) and computes that
-//     half of S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (rows as M, heads as N, so each lane owns
-//     one head); the two waves of a head group add their halves through LDS;
-//  3. one running maximum per head; O is rescaled only when the maximum grows by more than 2^8
-//     (so P <= 256 and a bf16 P loses nothing);
-//  4. P stays in registers: its accumulator layout is reused as the B operand of
+// split), 32-row tiles:
+//  1. the rows of a tile are gathered straight into LDS by the load-to-LDS path (each wave
+//     instruction moves 64 16-byte pieces of rows; no registers are used), three tiles ahead of
+//     the one being computed, into a ring of raw tiles;
+//  2. while a tile is computed, the next one is dequantised from its raw copy into the other
+//     half of a double-buffered row-major K[row][576] tile of fp16 values (16-byte chunks
+//     XOR-swizzled by row): v_cvt_scalef32_pk_f16_fp8 applies the power-of-two part of the
+//     block scale exactly and one packed fp16 multiply applies the rest, one instruction per
+//     value; the bf16 rope dims are widened to fp16;
+//  3. wave (g, h) holds Q (converted to fp16) of heads [32g, 32g+32) over dims [288h, 288h+288)
+//     and computes that half of S^T = K Q^T on v_mfma_f32_32x32x16_f16 (rows as M, heads as N,
+//     so each lane owns one head); the two waves of a head group add their halves through LDS;
+//  4. one running maximum per head; O is rescaled only when the maximum grows by more than 2^8
+//     (so P <= 256 and an fp16 P keeps 11 significant bits);
+//  5. P stays in registers: its accumulator layout is reused as the B operand of
 //     O^T = V^T P^T (the contraction runs over rows in the order the accumulator holds them);
 //     V^T comes straight from the row-major tile through transposing LDS reads
 //     (ds_read_b64_tr_b16), so no second copy of the tile is stored. Wave (g, h) accumulates
@@ -28,6 +33,8 @@ namespace smla {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
@@ -39,14 +46,19 @@ constexpr int NT = 256;
 constexpr int TILE = 32;                   // rows per tile
 constexpr int KCH = MLA_DQK / 8;           // 72 16-byte chunks per K row
 constexpr int K_BYTES = TILE * MLA_DQK * 2;  // 36864 per buffer
+constexpr int ROW_CH = MLA_ROW_BYTES / 16;   // 41 16-byte chunks per stored row
+constexpr int RAW_CHUNKS = TILE * ROW_CH;    // 1312 per tile
+constexpr int RAW_INSTR = (RAW_CHUNKS + 63) / 64;  // 21 wave instructions per tile
+constexpr int RAW_SLOT = RAW_INSTR * 1024;   // 21504 bytes (the last instruction's tail is padding)
+constexpr int NRAW = 3;                    // raw tiles in flight
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LOG2 = 8.0f;
 
 struct __align__(16) MlaSmem {
-  unsigned char k[2][K_BYTES];  // K[row][chunk ^ swz(row)], two tiles
-  float sx[4][4][64][4];        // per wave: its half of S^T, [i/4][lane][i%4]
-  int idx[TOPK_MAX_K];          // the split's row indices (-1: skip)
-  float lsum[2][2][32];
+  unsigned char k[2][K_BYTES];       // K[row][chunk ^ swz(row)], two tiles
+  unsigned char raw[NRAW][RAW_SLOT];  // gathered rows as stored (656 bytes each, back to back)
+  float sx[4][4][64][4];              // per wave: its half of S^T, [i/4][lane][i%4]
+  int idx[TOPK_MAX_K];                // the split's row indices (-1: skip)
 };
 
 // Row swizzle of 16-byte chunks: a bijection on row & 7 that keeps the 8 consecutive rows of an
@@ -61,60 +73,146 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, y);
 }
 
-// Raw bytes of one tile for this thread: 8 rows x 8 value dims, one 16-byte piece of rope, and
-// the 8 rows' block scales.
-struct TileRegs {
-  v2u val[8];
-  v4u rope;
-  float scale[8];
-};
+// Barrier for LDS hand-offs inside the tile loop: waits for this wave's LDS operations only, so
+// the gathers in flight keep flying (a full __syncthreads would wait for them too). The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-__device__ __forceinline__ void tile_load(TileRegs& r, const int* sidx, int tr0,
-                                          const unsigned char* __restrict__ kv_req) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ix = sidx[tr0 + 8 * wave + i];
-    const unsigned char* rowp = kv_req + (int64_t)ix * MLA_ROW_BYTES;
-    r.val[i] = ix >= 0 ? *reinterpret_cast<const v2u*>(rowp + 8 * lane) : v2u{0u, 0u};
-    r.scale[i] = ix >= 0 ? *reinterpret_cast<const float*>(rowp + 512 + 4 * (lane >> 4)) : 0.f;
+// Waits until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Number of gather instructions a wave issues per tile (instructions w, w + 4, ... < 21).
+__device__ __forceinline__ int dma_per_tile(int wave) { return wave == 0 ? 6 : 5; }
+
+// Waits until this wave's gathers of all but the last `later` tiles it issued have landed
+// (`later` at most 2).
+__device__ __forceinline__ void wait_tiles_but(int later, int wave) {
+  if (wave == 0) {
+    if (later >= 2) wait_vmcnt<12>(); else if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<0>();
+  } else {
+    if (later >= 2) wait_vmcnt<10>(); else if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
   }
-  const int ix = sidx[tr0 + (tid >> 3)];
-  r.rope = ix >= 0 ? *reinterpret_cast<const v4u*>(kv_req + (int64_t)ix * MLA_ROW_BYTES + 528 + 16 * (tid & 7))
-                   : v4u{0u, 0u, 0u, 0u};
 }
 
-// LDS offsets a thread stores its part of a tile to: 8 value chunks (rows 8*wave + i, chunk =
-// lane) and one rope chunk; the same for every tile.
-struct StoreOffsets {
-  int val[8];
-  int rope;
+// One load-to-LDS instruction: lane l's 16 bytes at g land at lds + 16 l (lds wave-uniform).
+// Written as inline assembly so that the compiler does not track it: the tile loop waits for
+// these loads itself (wait_tiles_but), instead of the compiler draining every one of them before
+// each LDS write it cannot prove disjoint. M0 (the LDS base operand) is saved and restored.
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(a)
+      : "memory");
+}
+
+// Gathers one tile (rows sidx[0..TILE)) into a raw slot: chunk c of the tile is the 16 bytes at
+// offset 16 (c % 41) of row c / 41, placed at slot + 16 c. Wave w issues instructions w + 4j
+// (j < 5) and wave 0 also instruction 20, so every wave issues a fixed number (waits count
+// them); lanes past the tile's last chunk and rows without an index read the request's row 0,
+// and the dequantiser zeroes such rows. A lane's (row, piece) pairs are the same for every tile
+// and come precomputed in `gp`.
+struct GatherPlan {
+  int row[6];  // tile row of the lane's chunk per instruction (clamped), or -1 past the tile
+  int off[6];  // byte offset of the chunk inside its row
 };
 
-__device__ __forceinline__ StoreOffsets store_offsets() {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  StoreOffsets so;
+__device__ __forceinline__ GatherPlan gather_plan() {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  GatherPlan gp;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) so.val[i] = k_off(8 * wave + i, lane);
-  so.rope = k_off(tid >> 3, 64 + (tid & 7));
-  return so;
+  for (int j = 0; j < 6; ++j) {
+    const int qq = j < 5 ? wave + 4 * j : 20;
+    const int c = 64 * qq + lane;
+    gp.row[j] = c < RAW_CHUNKS ? c / ROW_CH : -1;
+    gp.off[j] = 16 * (c - ROW_CH * (c / ROW_CH));
+  }
+  return gp;
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& r, unsigned char* kb, const StoreOffsets& so) {
+__device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx,
+                                            const unsigned char* __restrict__ kv_req,
+                                            const GatherPlan& gp, bool wave0) {
+  const int wave = threadIdx.x >> 6;
+  int ix[6];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float s = r.scale[i];
-    unsigned pk[4];
+  for (int j = 0; j < 6; ++j) ix[j] = sidx[max(gp.row[j], 0)];  // all LDS reads first
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.val[i][h], false);
-      const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.val[i][h], true);
-      pk[2 * h] = pack_bf16(lo[0] * s, lo[1] * s);
-      pk[2 * h + 1] = pack_bf16(hi[0] * s, hi[1] * s);
+  for (int j = 0; j < 6; ++j) {
+    if (j == 5 && !wave0) break;
+    const int qq = j < 5 ? wave + 4 * j : 20;
+    const bool ok = (gp.row[j] >= 0) & (ix[j] >= 0);
+    const uint32_t r = ok ? (uint32_t)ix[j] : 0u, k = ok ? (uint32_t)gp.off[j] : 0u;
+    lds_load16(kv_req + ((uint64_t)r * MLA_ROW_BYTES + k), slot + 1024 * qq);
+  }
+}
+
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+  v2f x = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, v2h));
+}
+
+// Two bf16 (one dword) -> two fp16 (one dword), exact within the fp16 range.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned x) {
+  return pack_f16(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xFFFF0000u));
+}
+
+// Dequantises a raw tile into the fp16 K tile: 1024 value pieces (16 e4m3 codes of one row times
+// that row's block scale -> two 16-byte K chunks) and 256 rope pieces (8 bf16 -> 8 fp16); 5 per
+// thread. The scale s = 2^e * m (1 <= m < 2): the conversion instruction applies 2^e exactly and
+// a packed multiply applies fp16(m). Rows without an index become zeros.
+__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb,
+                                             const int* sidx) {
+  const int tid = threadIdx.x;
+  // the same answer in every wave; rows without an index only occur in a token's last tile
+  const bool all_valid = __ballot(sidx[tid & 31] >= 0) == ~0ull;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int task = NT * j + tid;
+    const int r = task >> 5, k = task & 31;
+    v4u raw = *reinterpret_cast<const v4u*>(slot + r * MLA_ROW_BYTES + 16 * k);
+    float sc = *reinterpret_cast<const float*>(slot + r * MLA_ROW_BYTES + 512 + 4 * (k >> 3));
+    if (!all_valid) {
+      const bool ok = sidx[r] >= 0;
+      raw = ok ? raw : v4u{0u, 0u, 0u, 0u};
+      sc = ok ? sc : 1.f;
     }
-    *reinterpret_cast<v4u*>(kb + so.val[i]) = v4u{pk[0], pk[1], pk[2], pk[3]};
+    const float m = __builtin_bit_cast(float, (__builtin_bit_cast(unsigned, sc) & 0x807FFFFFu) | 0x3F800000u);
+    const v2h mm = {(_Float16)m, (_Float16)m};
+    unsigned pk[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[h], sc, false) * mm;
+      const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[h], sc, true) * mm;
+      pk[2 * h] = __builtin_bit_cast(unsigned, lo);
+      pk[2 * h + 1] = __builtin_bit_cast(unsigned, hi);
+    }
+    *reinterpret_cast<v4u*>(kb + k_off(r, 2 * k)) = v4u{pk[0], pk[1], pk[2], pk[3]};
+    *reinterpret_cast<v4u*>(kb + k_off(r, 2 * k + 1)) = v4u{pk[4], pk[5], pk[6], pk[7]};
   }
-  *reinterpret_cast<v4u*>(kb + so.rope) = r.rope;
+  {
+    const int r = tid >> 3, k = tid & 7;
+    v4u x = *reinterpret_cast<const v4u*>(slot + r * MLA_ROW_BYTES + 528 + 16 * k);
+    if (!all_valid) x = sidx[r] >= 0 ? x : v4u{0u, 0u, 0u, 0u};
+    *reinterpret_cast<v4u*>(kb + k_off(r, 64 + k)) =
+        v4u{bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]), bf16x2_to_f16x2(x[3])};
+  }
 }
 
 // One (token, split): rows idx_row[r_begin, r_end) of the token's request.
@@ -139,31 +237,40 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const int col = lane & 31, half = lane >> 5;
   const int head = 32 * hg + col;
 
-  const Tok tk = toks[t];
-  const unsigned char* kv_req = kv + tk.row_start * MLA_ROW_BYTES;
   const int32_t* idx_row = idx + t * top_k;
   const int r_begin = split * rows_per_split;
   const int r_end = min(top_k, r_begin + rows_per_split);
   const int nrows = max(0, r_end - r_begin);
 
-  // the split's indices; rows past the token's position are never read
+  // the split's indices and this lane's Q fragments go out together; rows past the token's
+  // position are never read
   __shared__ int last_valid;
   if (tid == 0) last_valid = -1;
+  constexpr int PER = TOPK_MAX_K / NT;
+  int ixs[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = u * NT + tid;
+    ixs[u] = j < nrows ? idx_row[r_begin + j] : -1;
+  }
+  // Q^T fragments: head `head`, dims [288*kh + 16*ks + 8*half, +8), bf16 as loaded (widened to
+  // fp16 below, once the loads have landed)
+  v4u qraw[18];
+  {
+    const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 288 * kh + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qraw[ks] = *reinterpret_cast<const v4u*>(qh + 16 * ks);
+  }
+  const Tok tk = toks[t];
+  const unsigned char* kv_req = kv + tk.row_start * MLA_ROW_BYTES;
   __syncthreads();
   {
-    constexpr int PER = TOPK_MAX_K / NT;
-    int ixs[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {  // all loads in flight before any is used
-      const int j = u * NT + tid;
-      ixs[u] = j < nrows ? idx_row[r_begin + j] : -1;
-    }
     int lv = -1;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int j = u * NT + tid;
-      int ix = ixs[u] > tk.pos ? -1 : ixs[u];
-      if (j < TOPK_MAX_K) sm.idx[j] = ix;
+      const int ix = ixs[u] > tk.pos ? -1 : ixs[u];
+      sm.idx[j] = ix;
       if (ix >= 0) lv = j;
     }
     if (lv >= 0) atomicMax(&last_valid, lv);
@@ -171,13 +278,6 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   __syncthreads();
   const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
 
-  // Q^T fragments: head `head`, dims [288*kh + 16*ks + 8*half, +8)
-  v8bf qf[18];
-  {
-    const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 288 * kh + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const v8bf*>(qh + 16 * ks);
-  }
   v16f o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = v16f{};
@@ -203,39 +303,58 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 #pragma unroll
       for (int par = 0; par < 2; ++par)
         voff[ks][hi][par] = k_off(16 * ks + 8 * hi + vrow, (vdim >> 3) + 4 * par) + 2 * (vdim & 7);
-  const StoreOffsets so = store_offsets();
 
-  TileRegs R;
+  // the Q fragments are in registers before any gather goes out (the compiler does not count the
+  // gathers, so a later wait of its own for Q would drain them)
+  wait_vmcnt<0>();
+  v8h qf[18];
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks)
+    qf[ks] = __builtin_bit_cast(v8h, v4u{bf16x2_to_f16x2(qraw[ks][0]), bf16x2_to_f16x2(qraw[ks][1]),
+                                         bf16x2_to_f16x2(qraw[ks][2]), bf16x2_to_f16x2(qraw[ks][3])});
+  // Pipeline. Entering iteration `it`: K[it & 1] holds tile it, raw slot (it+1) % 3 holds tile
+  // it+1 (landed and visible), tile it+2 is in flight, slot it % 3 is free.
+  const GatherPlan gp = gather_plan();
+  const bool wave0 = __builtin_amdgcn_readfirstlane(wave) == 0;
+  for (int j = 0; j < NRAW && j < ntiles; ++j)
+    tile_gather(sm.raw[j], sm.idx + j * TILE, kv_req, gp, wave0);
   if (ntiles > 0) {
-    tile_load(R, sm.idx, 0, kv_req);
-    tile_store(R, sm.k[0], so);
-    if (ntiles > 1) tile_load(R, sm.idx, TILE, kv_req);
+    wait_tiles_but(min(ntiles, NRAW) - 1, wave);
+    lds_barrier();
+    tile_dequant(sm.raw[0], sm.k[0], sm.idx);
+    if (ntiles > 1) wait_tiles_but(min(ntiles, NRAW) - 2, wave);
+    lds_barrier();
   }
-  __syncthreads();
 
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
+    if (it + NRAW < ntiles)
+      tile_gather(sm.raw[it % NRAW], sm.idx + (it + NRAW) * TILE, kv_req, gp, wave0);
     const unsigned char* kb = sm.k[it & 1];
     // half of S^T over this wave's dims, as two independent accumulation chains
     v16f s = v16f{}, s2 = v16f{};
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
       const int nu = m < 4 ? 4 : 2;
-      v8bf a[4];
+      v8h a[4];
 #pragma unroll
-      for (int u = 0; u < nu; ++u) a[u] = *reinterpret_cast<const v8bf*>(kb + koff[u] + 128 * m);
+      for (int u = 0; u < nu; ++u) a[u] = *reinterpret_cast<const v8h*>(kb + koff[u] + 128 * m);
 #pragma unroll
       for (int u = 0; u < nu; u += 2) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], qf[4 * m + u], s, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u + 1], qf[4 * m + u + 1], s2, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u], qf[4 * m + u], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u + 1], qf[4 * m + u + 1], s2, 0, 0, 0);
       }
     }
+    // the next tile's bf16 copy, while the matrix cores work (unconditional, so that it shares a
+    // basic block with the MFMAs above; after the last tile it converts a stale slot into the
+    // idle buffer, which nothing reads)
+    tile_dequant(sm.raw[(it + 1) % NRAW], sm.k[(it + 1) & 1], sm.idx + min(it + 1, ntiles - 1) * TILE);
     s += s2;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4)
       *reinterpret_cast<float4*>(&sm.sx[wave][g4][lane][0]) =
           make_float4(s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const float4 o4 = *reinterpret_cast<const float4*>(&sm.sx[wave ^ 1][g4][lane][0]);
@@ -244,39 +363,46 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
       s[4 * g4 + 2] += o4.z;
       s[4 * g4 + 3] += o4.w;
     }
-    // lane holds head `head`, rows 8*(i/4) + 4*half + i%4 of the tile
+    // lane holds head `head`, rows 8*(i/4) + 4*half + i%4 of the tile; raw logits stay unscaled
+    // (c > 0 keeps their order) and c enters the exponent below
     const uint64_t valid = __ballot(sm.idx[it * TILE + col] >= 0);  // bit r: row r is valid
-    float tmax = -INFINITY;
+    if ((uint32_t)valid != 0xFFFFFFFFu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-      const float v = (valid >> row) & 1 ? s[i] * c : -INFINITY;
-      s[i] = v;
-      tmax = fmaxf(tmax, v);
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
+        if (!((valid >> row) & 1)) s[i] = -INFINITY;
+      }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    float tmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
     // both waves of a head group hold identical logits and take the same decision
     const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run + RESCALE_LOG2)) {
-      const float alpha = exp2f(m_run - m_new);
+    if (m_run == -INFINITY) {
+      m_run = m_new;  // first valid rows: O and l are still zero
+    } else if (__any(m_new > m_run + RESCALE_LOG2)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
-    // P in registers, packed as the B operand of the two 16-row k-steps
-    v8bf pb[2];
+    // P in registers, packed as the B operand of the two 16-row k-steps (no valid row so far:
+    // every logit is -inf and P must come out 0, not NaN)
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    v8h pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p8[j] = exp2f(s[8 * ks + j] - m_run);
+        p8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + j], c, -m_use));  // underflow to 0 is harmless
         l_run += p8[j];
       }
-      v4u pk = {pack_bf16(p8[0], p8[1]), pack_bf16(p8[2], p8[3]), pack_bf16(p8[4], p8[5]),
-                pack_bf16(p8[6], p8[7])};
-      pb[ks] = __builtin_bit_cast(v8bf, pk);
+      v4u pk = {pack_f16(p8[0], p8[1]), pack_f16(p8[2], p8[3]), pack_f16(p8[4], p8[5]),
+                pack_f16(p8[6], p8[7])};
+      pb[ks] = __builtin_bit_cast(v8h, pk);
     }
     // O^T[dims 256*kh + 32*mt + m][head] += V^T[dim][rows] P^T[rows][head]
 #pragma unroll
@@ -288,17 +414,17 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
             (__attribute__((address_space(3))) v4s*)(kb + voff[ks][0][par] + 128 * m));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4s*)(kb + voff[ks][1][par] + 128 * m));
-        const v8bf a = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], o[mt], 0, 0, 0);
+        const v8h a = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[ks], o[mt], 0, 0, 0);
       }
     }
-    // next tile: store the rows gathered during this one, start gathering the one after
-    if (it + 1 < ntiles) {
-      tile_store(R, sm.k[(it + 1) & 1], so);
-      if (it + 2 < ntiles) tile_load(R, sm.idx, (it + 2) * TILE, kv_req);
-    }
-    __syncthreads();
+    // tile it+2 must have landed before the next iteration dequantises it; only tile it+3 (issued
+    // at the top of this iteration) may still be in flight
+    if (it + 2 < ntiles) wait_tiles_but(it + 3 < ntiles ? 1 : 0, wave);
+    lds_barrier();
   }
+
+  wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS when it exits
 
   // denominator of each head: both lane halves, both waves of the head group hold the same
   l_run += __shfl_xor(l_run, 32);
