@@ -46,12 +46,14 @@ constexpr int IDX_D = 128;
 __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
                                              int step, const int8_t* __restrict__ q_idx,
                                              const int8_t* __restrict__ k_idx,
-                                             const int (&wl)[2][16], int32_t* __restrict__ out_row,
+                                             const uint32_t (&wl)[16], int32_t* __restrict__ out_row,
                                              int* lhist) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
   const int p = tk.pos;
+  const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
+  if (s_begin > last) return;
   // A fragments: head 32*mt + col, dims [64*half + 16*j, +16)
   v4i qa[2][4];
   const int8_t* qbase = q_idx + t * (IDX_H * IDX_D);
@@ -61,45 +63,68 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
 
+  // B fragments straight from memory: lane (col, half) reads 64 contiguous bytes of key `col`
   const int8_t* kbase = k_idx + tk.row_start * IDX_D + 64 * half;
-  const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
   auto load_keys = [&](int s, v4i (&kb)[4]) {
     const int kr = min(s + col, last);  // clamp: never read past the visible rows
     const v4i* kp = reinterpret_cast<const v4i*>(kbase + (int64_t)kr * IDX_D);
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kp[j];
   };
-  if (s_begin > last) return;
-  v4i kb[4];
-  load_keys(s_begin, kb);
-  for (int s = s_begin; s <= last; s += step) {
-    v4i kn[4];
-    load_keys(s + step, kn);  // next tile in flight while this one computes
+  // Scores go out through a buffer resource whose range ends at key `last`: the hardware drops
+  // the stores of keys past it and of the upper lane half, so every tile issues exactly one
+  // store and the compiler can count this wave's outstanding loads (a branch around the store
+  // would make it drain every prefetched key tile before each MFMA).
+  const __amdgpu_buffer_rsrc_t out_rs =
+      __builtin_amdgcn_make_buffer_rsrc(out_row, 0, (last + 1) * 4, 0x00020000);
+  // one 32-key tile: scores of the wave's query against keys s .. s+31
+  auto tile = [&](int s, const v4i (&kb)[4]) {
     v16i acc0 = {}, acc1 = {};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
     }
-    // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them
-    uint32_t sum = 0;
+    // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them.
+    // ReLU(dot) <= 2^21 and w < 2^10 (the weight contract), so 24-bit multiplies are exact and
+    // run at full rate (a 32-bit multiply is quarter rate); four independent partial sums keep
+    // the chain of dependent adds from setting the pace
+    uint32_t ps[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sum += (uint32_t)max(acc0[r], 0) * (uint32_t)wl[0][r];
-      sum += (uint32_t)max(acc1[r], 0) * (uint32_t)wl[1][r];
+      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
+      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
     }
+    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     sum += (uint32_t)__shfl_xor((int)sum, 32);
     const int key = s + col;
-    if (half == 0 && key <= last) {
-      out_row[key] = (int32_t)sum;
-      if (lhist) atomicAdd(&lhist[topk_bin(sum)], 1);
-    }
+    __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
+    if (lhist && half == 0 && key <= last) atomicAdd(&lhist[topk_bin(sum)], 1);
+  };
+  // NPF key tiles in flight per wave: enough bytes outstanding to cover HBM latency. The main
+  // loop runs whole groups of NPF tiles without exits, so the compiler's count of outstanding
+  // loads is the same on every pass (it only ever waits for the oldest tile); loads past the
+  // end read clamped rows and are never used.
+  constexpr int NPF = 4;
+  const int ntile = (last - s_begin) / step + 1;
+  v4i kb[NPF][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = kn[j];
+  for (int i = 0; i < NPF; ++i) load_keys(s_begin + i * step, kb[i]);
+  int s = s_begin;
+  int T = 0;
+  for (; T + NPF <= ntile; T += NPF, s += NPF * step) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      tile(s + i * step, kb[i]);
+      load_keys(s + (NPF + i) * step, kb[i]);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < NPF - 1; ++i)
+    if (T + i < ntile) tile(s + i * step, kb[i]);
 }
 
-__global__ __launch_bounds__(256) void indexer_mfma_kernel(const Item* __restrict__ items,
+__global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __restrict__ items,
                                                            const Tok* __restrict__ toks,
                                                            const int8_t* __restrict__ q_idx,
                                                            const int8_t* __restrict__ k_idx,
@@ -108,14 +133,19 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(const Item* __restric
                                                            int64_t stride, int* __restrict__ hist) {
   __shared__ int lhist[QT][TOPK_BINS];
   const Item it = items[blockIdx.x];
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar): everything derived from it (the query, its score row) stays in
+  // scalar registers, as buffer resources must
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  int wl[2][16];
+  // the weights of this lane's heads, two per register (heads 8*(r/4) + 4*half + r%4 in the low
+  // half, the same + 32 in the high half); w < 2^10 by the weight contract
+  uint32_t wl[16];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) wl[mt][r] = w[32 * mt + 8 * (r >> 2) + 4 * half + (r & 3)];
+  for (int r = 0; r < 16; ++r) {
+    const int h = 8 * (r >> 2) + 4 * half + (r & 3);
+    wl[r] = ((uint32_t)w[h] & 0xFFFFu) | ((uint32_t)w[32 + h] << 16);
+  }
 
 #pragma unroll 1
   for (int sgi = 0; sgi < 2; ++sgi) {
