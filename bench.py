@@ -288,9 +288,9 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp16",
         "dtypes": {"indexer": "int8 x int8 -> int32", "kv": "fp8 e4m3 + fp32 block scales",
-                   "attention": "bf16 MFMA, fp32 accumulate"},
+                   "attention": "fp16 MFMA on dequantised rows, fp32 accumulate and softmax"},
         "data": "synthetic",
         "config": {"workload": workload_name(d), "config_id": args.config, "batch": d.batch,
                    "query_tokens": d.total_q, "cached_tokens": d.cached, "heads": d.H,

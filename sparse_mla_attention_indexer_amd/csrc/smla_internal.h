@@ -87,7 +87,6 @@ constexpr int MLA_H = 64;
 constexpr int MLA_DQK = 576;
 constexpr int MLA_DV = 512;
 constexpr int MLA_ROW_BYTES = 656;
-constexpr int MLA_TILE = 64;
 
 inline __host__ __device__ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
