@@ -27,12 +27,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
 ]
-# Per-source additions. sparse_mla.hip: MFMA accumulators in ordinary VGPRs (the attention kernel
-# rescales its output accumulators with vector ALU ops; with accumulator registers the compiler
-# copies all of them out and back on every tile).
-FILE_FLAGS = {
-    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
-}
+# Per-source additions (none at present).
+FILE_FLAGS: dict = {}
 
 
 def _run(cmd, verbose):

@@ -6,34 +6,37 @@
 // "Why the numbers work": QK over 576 dims, PV over 512, BF16 queries and outputs, 656-byte FP8
 // rows). Partial results over disjoint row sets merge by log-sum-exp (section "DCP").
 //
-// FP8 kernel (64 heads, 576/512 dims, 656-byte rows), one workgroup of 4 waves per (token,
-// split), 32-row tiles:
-//  1. the rows of a tile are gathered straight into LDS by the load-to-LDS path (each wave
-//     instruction moves 64 16-byte pieces of rows; no registers are used), three tiles ahead of
-//     the one being computed, into a ring of raw tiles;
-//  2. while a tile is computed, the next one is dequantised from its raw copy into the other
-//     half of a double-buffered row-major K[row][576] tile of fp16 values (16-byte chunks
-//     XOR-swizzled by row): v_cvt_scalef32_pk_f16_fp8 applies the power-of-two part of the
-//     block scale exactly and one packed fp16 multiply applies the rest, one instruction per
-//     value; the bf16 rope dims are widened to fp16;
-//  3. wave (g, h) holds Q (converted to fp16) of heads [32g, 32g+32) over dims [288h, 288h+288)
-//     and computes that half of S^T = K Q^T on v_mfma_f32_32x32x16_f16 (rows as M, heads as N,
-//     so each lane owns one head); the two waves of a head group add their halves through LDS;
+// FP8 kernel (64 heads, 576/512 dims, 656-byte rows): one workgroup of 4 waves (one per SIMD,
+// 512 registers each) per (token, split), 32-row tiles. Every wave works on all stages, software
+// pipelined so that the matrix cores, the vector ALUs and the memory paths overlap:
+//  1. the rows of tile t+3 are moved from HBM straight into a ring of raw tiles in LDS by the
+//     load-to-LDS path (no registers involved), three tiles ahead of the one being computed;
+//  2. while tile t is multiplied, tile t+1 is dequantised from its raw copy into the other half
+//     of a double-buffered row-major K[row][576] fp16 tile: v_cvt_scalef32_pk_f16_fp8
+//     applies the power-of-two part of the block scale exactly and one packed fp16 multiply
+//     applies the rest; the bf16 rope dims are widened to fp16;
+//  3. wave (g, h) holds Q (fp16) of heads [32g, 32g+32) over dims [288h, 288h+288) and computes
+//     that half of S^T = K Q^T on v_mfma_f32_32x32x16_f16 (rows as M, heads as N, so each lane
+//     owns one head); the two waves of a head group add their halves through LDS;
 //  4. one running maximum per head; O is rescaled only when the maximum grows by more than 2^8
 //     (so P <= 256 and an fp16 P keeps 11 significant bits);
 //  5. P stays in registers: its accumulator layout is reused as the B operand of
 //     O^T = V^T P^T (the contraction runs over rows in the order the accumulator holds them);
 //     V^T comes straight from the row-major tile through transposing LDS reads
-//     (ds_read_b64_tr_b16), so no second copy of the tile is stored. Wave (g, h) accumulates
-//     O^T for dims [256h, 256h+256) of its 32 heads.
-// Decode splits a token's rows across workgroups and merges the partials by log-sum-exp.
+//     (ds_read_b64_tr_b16). Wave (g, h) accumulates O^T for dims [256h, 256h+256) of its 32
+//     heads.
+// The K tile's 16-byte chunks are XOR-swizzled by row so that the operand reads, the
+// transposing reads and the dequantiser's writes all spread over the 64 LDS banks. Rows without
+// an index (padding) read the request's first row and are masked out of the softmax, so the
+// latent cache must hold finite values.
+// Decode splits a token's rows across workgroups and merges the fp16 partials by log-sum-exp.
 #include "smla_internal.h"
 
 namespace smla {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -42,28 +45,40 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int NT = 256;
+constexpr int NT = 256;                    // 4 waves, one per SIMD
 constexpr int TILE = 32;                   // rows per tile
 constexpr int KCH = MLA_DQK / 8;           // 72 16-byte chunks per K row
 constexpr int K_BYTES = TILE * MLA_DQK * 2;  // 36864 per buffer
+constexpr int RB16 = 16 * KCH * 16;        // bytes between rows r and r + 16 (same swizzle)
 constexpr int ROW_CH = MLA_ROW_BYTES / 16;   // 41 16-byte chunks per stored row
 constexpr int RAW_CHUNKS = TILE * ROW_CH;    // 1312 per tile
 constexpr int RAW_INSTR = (RAW_CHUNKS + 63) / 64;  // 21 wave instructions per tile
 constexpr int RAW_SLOT = RAW_INSTR * 1024;   // 21504 bytes (the last instruction's tail is padding)
 constexpr int NRAW = 3;                    // raw tiles in flight
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float RESCALE_LOG2 = 8.0f;
+// Softmax reference (log2 units): P = 2^(logit - ref) with ref fixed for the whole split, so the
+// output accumulators are only ever touched by the matrix cores. The first tile with a valid
+// row sets ref = its maximum + REF_MARGIN; a later logit more than REF_HEADROOM above ref would
+// push an fp16 P towards its range limit, and then the split is recomputed with ref = the true
+// maximum, which the first pass has tracked.
+constexpr float REF_MARGIN = 4.0f;
+constexpr float REF_HEADROOM = 15.0f;
 
 struct __align__(16) MlaSmem {
-  unsigned char k[2][K_BYTES];       // K[row][chunk ^ swz(row)], two tiles
+  unsigned char k[2][K_BYTES];        // K[row][chunk ^ swz(row)], two tiles
   unsigned char raw[NRAW][RAW_SLOT];  // gathered rows as stored (656 bytes each, back to back)
   float sx[4][4][64][4];              // per wave: its half of S^T, [i/4][lane][i%4]
   int idx[TOPK_MAX_K];                // the split's row indices (-1: skip)
 };
+static_assert(sizeof(MlaSmem) <= 160 * 1024 - 16, "LDS budget");
 
-// Row swizzle of 16-byte chunks: a bijection on row & 7 that keeps the 8 consecutive rows of an
-// MFMA operand read and the 4-row pairs of a transposing read on distinct banks.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Row swizzle of 16-byte chunks (a bijection on the low three chunk bits, from row bits 0..3).
+// With 72 chunks per row, rows alternate between the two halves of the 64 banks; the swizzle
+// spreads (a) 32 rows at one chunk, (b) 4 aligned rows x 4 aligned chunks and (c) the
+// dequantiser's writes over all 16 bank groups, so every access is conflict free.
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 2) ^ row) & 1) | (((row >> 3) & 1) << 1);
+}
 __device__ __forceinline__ int k_off(int row, int chunk) { return (row * KCH + (chunk ^ swz(row))) * 16; }
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
@@ -73,9 +88,28 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, y);
 }
 
-// Barrier for LDS hand-offs inside the tile loop: waits for this wave's LDS operations only, so
-// the gathers in flight keep flying (a full __syncthreads would wait for them too). The empty asm
-// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+  v2f x = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, v2h));
+}
+
+// Two bf16 (one dword) -> two fp16 (one dword), exact within the fp16 range.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned x) {
+  return pack_f16(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ float swap_halves_max(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+  return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
+// Barrier for LDS hand-offs inside the tile loop: waits for this wave's LDS operations only,
+// so the gathers of later tiles keep flying (a full __syncthreads would wait for them too). The empty asm statements keep the compiler from
+// moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -91,11 +125,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-// Number of gather instructions a wave issues per tile (instructions w, w + 4, ... < 21).
-__device__ __forceinline__ int dma_per_tile(int wave) { return wave == 0 ? 6 : 5; }
-
-// Waits until this wave's gathers of all but the last `later` tiles it issued have landed
-// (`later` at most 2).
+// Gather instructions per tile: instruction q goes to wave q % 4, so wave 0 issues six and the
+// others five. Waits until this wave's gathers of all but the last `later` tiles it issued have
+// landed (`later` at most 2).
 __device__ __forceinline__ void wait_tiles_but(int later, int wave) {
   if (wave == 0) {
     if (later >= 2) wait_vmcnt<12>(); else if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<0>();
@@ -125,98 +157,78 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
 // Gathers one tile (rows sidx[0..TILE)) into a raw slot: chunk c of the tile is the 16 bytes at
 // offset 16 (c % 41) of row c / 41, placed at slot + 16 c. Wave w issues instructions w + 4j
 // (j < 5) and wave 0 also instruction 20, so every wave issues a fixed number (waits count
-// them); lanes past the tile's last chunk and rows without an index read the request's row 0,
-// and the dequantiser zeroes such rows. A lane's (row, piece) pairs are the same for every tile
-// and come precomputed in `gp`.
+// them). Lanes past the tile's last chunk and rows without an index read the request's first
+// row. A lane's chunk positions are the same for every tile: `base[j]` is the request's first
+// row plus the chunk's offset inside its row, `roff[j]` the byte offset of its row's index in
+// the tile's index list.
 struct GatherPlan {
-  int row[6];  // tile row of the lane's chunk per instruction (clamped), or -1 past the tile
-  int off[6];  // byte offset of the chunk inside its row
+  const unsigned char* base[6];
+  int roff[6];
 };
 
-__device__ __forceinline__ GatherPlan gather_plan() {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ GatherPlan gather_plan(int wave, const unsigned char* kv_req) {
+  const int lane = threadIdx.x & 63;
   GatherPlan gp;
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     const int qq = j < 5 ? wave + 4 * j : 20;
     const int c = 64 * qq + lane;
-    gp.row[j] = c < RAW_CHUNKS ? c / ROW_CH : -1;
-    gp.off[j] = 16 * (c - ROW_CH * (c / ROW_CH));
+    const int row = c < RAW_CHUNKS ? c / ROW_CH : 0;
+    gp.roff[j] = 4 * row;
+    gp.base[j] = kv_req + 16 * (c - ROW_CH * (c / ROW_CH));
   }
   return gp;
 }
 
 __device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx,
-                                            const unsigned char* __restrict__ kv_req,
-                                            const GatherPlan& gp, bool wave0) {
-  const int wave = threadIdx.x >> 6;
+                                            const GatherPlan& gp, int wave) {
   int ix[6];
 #pragma unroll
-  for (int j = 0; j < 6; ++j) ix[j] = sidx[max(gp.row[j], 0)];  // all LDS reads first
+  for (int j = 0; j < 6; ++j)  // all LDS reads first
+    ix[j] = *reinterpret_cast<const int*>(reinterpret_cast<const char*>(sidx) + gp.roff[j]);
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
-    if (j == 5 && !wave0) break;
+    if (j == 5 && wave != 0) break;  // wave-uniform
     const int qq = j < 5 ? wave + 4 * j : 20;
-    const bool ok = (gp.row[j] >= 0) & (ix[j] >= 0);
-    const uint32_t r = ok ? (uint32_t)ix[j] : 0u, k = ok ? (uint32_t)gp.off[j] : 0u;
-    lds_load16(kv_req + ((uint64_t)r * MLA_ROW_BYTES + k), slot + 1024 * qq);
+    lds_load16(gp.base[j] + (uint64_t)(uint32_t)max(ix[j], 0) * MLA_ROW_BYTES, slot + 1024 * qq);
   }
 }
 
-__device__ __forceinline__ unsigned pack_f16(float a, float b) {
-  v2f x = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, v2h));
-}
-
-// Two bf16 (one dword) -> two fp16 (one dword), exact within the fp16 range.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned x) {
-  return pack_f16(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xFFFF0000u));
-}
-
-// Dequantises a raw tile into the fp16 K tile: 1024 value pieces (16 e4m3 codes of one row times
-// that row's block scale -> two 16-byte K chunks) and 256 rope pieces (8 bf16 -> 8 fp16); 5 per
-// thread. The scale s = 2^e * m (1 <= m < 2): the conversion instruction applies 2^e exactly and
-// a packed multiply applies fp16(m). Rows without an index become zeros.
-__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb,
-                                             const int* sidx) {
-  const int tid = threadIdx.x;
-  // the same answer in every wave; rows without an index only occur in a token's last tile
-  const bool all_valid = __ballot(sidx[tid & 31] >= 0) == ~0ull;
+// Dequantises a raw tile into the fp16 K tile. Thread (r, m) = (tid / 8, tid % 8) takes 64 e4m3
+// codes of row r (dims 128 i + 16 m .. +16, i < 4) and 8 bf16 rope dims (512 + 8 m .. +8). The
+// scale s = 2^e * mant (1 <= mant < 2): the conversion applies 2^e exactly and a packed multiply
+// fp16(mant); the rope dims are widened. Rows without an index hold the request's first row,
+// which the softmax masks out.
+__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb, int r, int m) {
+  const unsigned char* row = slot + r * MLA_ROW_BYTES;
+  v4u code[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int task = NT * j + tid;
-    const int r = task >> 5, k = task & 31;
-    v4u raw = *reinterpret_cast<const v4u*>(slot + r * MLA_ROW_BYTES + 16 * k);
-    float sc = *reinterpret_cast<const float*>(slot + r * MLA_ROW_BYTES + 512 + 4 * (k >> 3));
-    if (!all_valid) {
-      const bool ok = sidx[r] >= 0;
-      raw = ok ? raw : v4u{0u, 0u, 0u, 0u};
-      sc = ok ? sc : 1.f;
-    }
-    const float m = __builtin_bit_cast(float, (__builtin_bit_cast(unsigned, sc) & 0x807FFFFFu) | 0x3F800000u);
-    const v2h mm = {(_Float16)m, (_Float16)m};
+  for (int i = 0; i < 4; ++i) code[i] = *reinterpret_cast<const v4u*>(row + 128 * i + 16 * m);
+  const v4u scale = *reinterpret_cast<const v4u*>(row + 512);
+  const v4u rope = *reinterpret_cast<const v4u*>(row + 528 + 16 * m);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the conversion reads only the exponent of its scale operand
+    const float sc = __builtin_bit_cast(float, scale[i] & 0x7F800000u);
+    const float mt = __builtin_bit_cast(float, (scale[i] & 0x807FFFFFu) | 0x3F800000u);
+    const v2h mm = {(_Float16)mt, (_Float16)mt};
     unsigned pk[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[h], sc, false) * mm;
-      const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[h], sc, true) * mm;
+      const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code[i][h], sc, false) * mm;
+      const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code[i][h], sc, true) * mm;
       pk[2 * h] = __builtin_bit_cast(unsigned, lo);
       pk[2 * h + 1] = __builtin_bit_cast(unsigned, hi);
     }
-    *reinterpret_cast<v4u*>(kb + k_off(r, 2 * k)) = v4u{pk[0], pk[1], pk[2], pk[3]};
-    *reinterpret_cast<v4u*>(kb + k_off(r, 2 * k + 1)) = v4u{pk[4], pk[5], pk[6], pk[7]};
+    *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m)) = v4u{pk[0], pk[1], pk[2], pk[3]};
+    *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m + 1)) = v4u{pk[4], pk[5], pk[6], pk[7]};
   }
-  {
-    const int r = tid >> 3, k = tid & 7;
-    v4u x = *reinterpret_cast<const v4u*>(slot + r * MLA_ROW_BYTES + 528 + 16 * k);
-    if (!all_valid) x = sidx[r] >= 0 ? x : v4u{0u, 0u, 0u, 0u};
-    *reinterpret_cast<v4u*>(kb + k_off(r, 64 + k)) =
-        v4u{bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]), bf16x2_to_f16x2(x[3])};
-  }
+  *reinterpret_cast<v4u*>(kb + k_off(r, 64 + m)) =
+      v4u{bf16x2_to_f16x2(rope[0]), bf16x2_to_f16x2(rope[1]), bf16x2_to_f16x2(rope[2]), bf16x2_to_f16x2(rope[3])};
 }
 
 // One (token, split): rows idx_row[r_begin, r_end) of the token's request.
-// Writes either the final bf16 output (+ lse) or an fp32 partial (+ lse) for the combine.
+// Writes either the final bf16 output (+ lse) or an fp16 partial (+ lse) for the combine.
 __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ toks,
                                                         const __bf16* __restrict__ q,
                                                         const unsigned char* __restrict__ kv,
@@ -224,7 +236,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
                                                         int top_k, int rows_per_split,
                                                         float sm_scale, __bf16* __restrict__ out,
                                                         float* __restrict__ lse_out,
-                                                        float* __restrict__ part_o,
+                                                        _Float16* __restrict__ part_o,
                                                         float* __restrict__ part_lse) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MlaSmem& sm = *reinterpret_cast<MlaSmem*>(smem_raw);
@@ -232,18 +244,14 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const int split = blockIdx.y;
   const int nsplit = gridDim.y;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int hg = wave >> 1, kh = wave & 1;
-  const int col = lane & 31, half = lane >> 5;
-  const int head = 32 * hg + col;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   const int32_t* idx_row = idx + t * top_k;
   const int r_begin = split * rows_per_split;
   const int r_end = min(top_k, r_begin + rows_per_split);
   const int nrows = max(0, r_end - r_begin);
 
-  // the split's indices and this lane's Q fragments go out together; rows past the token's
-  // position are never read
+  // the split's indices (rows past the token's position are never read) and the last valid one
   __shared__ int last_valid;
   if (tid == 0) last_valid = -1;
   constexpr int PER = TOPK_MAX_K / NT;
@@ -253,8 +261,11 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     const int j = u * NT + tid;
     ixs[u] = j < nrows ? idx_row[r_begin + j] : -1;
   }
-  // Q^T fragments: head `head`, dims [288*kh + 16*ks + 8*half, +8), bf16 as loaded (widened to
-  // fp16 below, once the loads have landed)
+  // this lane's Q^T fragments go out with the indices: head `head`, dims
+  // [288*kh + 16*ks + 8*half, +8), bf16 as loaded (widened to fp16 below)
+  const int hg = wave >> 1, kh = wave & 1;
+  const int col = lane & 31, half = lane >> 5;
+  const int head = 32 * hg + col;
   v4u qraw[18];
   {
     const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 288 * kh + 8 * half;
@@ -262,7 +273,6 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     for (int ks = 0; ks < 18; ++ks) qraw[ks] = *reinterpret_cast<const v4u*>(qh + 16 * ks);
   }
   const Tok tk = toks[t];
-  const unsigned char* kv_req = kv + tk.row_start * MLA_ROW_BYTES;
   __syncthreads();
   {
     int lv = -1;
@@ -278,78 +288,82 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   __syncthreads();
   const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
 
-  v16f o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = v16f{};
-  float m_run = -INFINITY;  // running max of this lane's head, log2 units
-  float l_run = 0.f;        // this lane's share of the softmax denominator
-  const float c = sm_scale * LOG2E;
-
-  // per-lane LDS offsets: S operand (K row `col`, chunk 36*kh + 2u + half (+ 8m)), and the
-  // transposing V reads (16-lane group g: dims +16*(g&1); 4 rows from 4*(g>>1) + lane%16 / 4)
-  int koff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = k_off(col, 36 * kh + 2 * u + half);
-  const int grp = lane >> 4, gl = lane & 15;
-  const int vrow = 4 * (grp >> 1) + (gl >> 2);          // + 16*ks (+8 for the second read)
-  const int vdim = 256 * kh + 16 * (grp & 1) + 4 * (gl & 3);  // + 32*mt
-  // The transposing V reads of (ks, second half, mt = 2m + par) sit at voff[ks][hi][par] + 128m:
-  // the chunk of dim vdim + 32mt is (vdim >> 3) + 4par + 8m and the swizzle leaves bit 3 up alone.
-  int voff[2][2][2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-      for (int par = 0; par < 2; ++par)
-        voff[ks][hi][par] = k_off(16 * ks + 8 * hi + vrow, (vdim >> 3) + 4 * par) + 2 * (vdim & 7);
-
-  // the Q fragments are in registers before any gather goes out (the compiler does not count the
-  // gathers, so a later wait of its own for Q would drain them)
-  wait_vmcnt<0>();
   v8h qf[18];
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks)
     qf[ks] = __builtin_bit_cast(v8h, v4u{bf16x2_to_f16x2(qraw[ks][0]), bf16x2_to_f16x2(qraw[ks][1]),
                                          bf16x2_to_f16x2(qraw[ks][2]), bf16x2_to_f16x2(qraw[ks][3])});
-  // Pipeline. Entering iteration `it`: K[it & 1] holds tile it, raw slot (it+1) % 3 holds tile
-  // it+1 (landed and visible), tile it+2 is in flight, slot it % 3 is free.
-  const GatherPlan gp = gather_plan();
-  const bool wave0 = __builtin_amdgcn_readfirstlane(wave) == 0;
-  for (int j = 0; j < NRAW && j < ntiles; ++j)
-    tile_gather(sm.raw[j], sm.idx + j * TILE, kv_req, gp, wave0);
-  if (ntiles > 0) {
-    wait_tiles_but(min(ntiles, NRAW) - 1, wave);
-    lds_barrier();
-    tile_dequant(sm.raw[0], sm.k[0], sm.idx);
-    if (ntiles > 1) wait_tiles_but(min(ntiles, NRAW) - 2, wave);
-    lds_barrier();
-  }
+  // per-lane LDS offsets: S operand (K row `col`, chunk 36*kh + 2u + half (+ 8m)), and the
+  // transposing V reads (16-lane group g: dims +16*(g&1); 4 rows from 4*(g>>1) + lane%16 / 4).
+  // The transposing V reads of (ks, second half, mt = 2m + par) sit at
+  // voff[hi][par] + RB16 * ks + 128 m: rows 16 apart share their swizzle, and the chunk of dim
+  // vdim + 32mt is (vdim >> 3) + 4par + 8m, whose bit 3 and up the swizzle leaves alone.
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = k_off(col, 36 * kh + 2 * u + half);
+  const int grp = lane >> 4, gl = lane & 15;
+  const int vrow = 4 * (grp >> 1) + (gl >> 2);
+  const int vdim = 256 * kh + 16 * (grp & 1) + 4 * (gl & 3);
+  int voff[2][2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      voff[hi][par] = k_off(8 * hi + vrow, (vdim >> 3) + 4 * par) + 2 * (vdim & 7);
+
+  // the Q fragments are in registers before any gather goes out (the compiler does not count the
+  // gathers, so a later wait of its own for Q would drain them)
+  wait_vmcnt<0>();
+  // dequantiser's share: tile row tid / 8, pieces m = tid % 8
+  const int pr = tid >> 3, pm = tid & 7;
+  const GatherPlan gp = gather_plan(wave, kv + tk.row_start * MLA_ROW_BYTES);
+  const float c = sm_scale * LOG2E;
+  float ref = -INFINITY;     // softmax reference of this lane's head (log2 units)
+  float seen = -INFINITY;    // largest scaled logit of this lane's head so far
+  __shared__ int redo;
+  v16f o[8];
+  float l_run;  // this lane's share of the softmax denominator
 
 #pragma unroll 1
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + NRAW < ntiles)
-      tile_gather(sm.raw[it % NRAW], sm.idx + (it + NRAW) * TILE, kv_req, gp, wave0);
-    const unsigned char* kb = sm.k[it & 1];
-    // half of S^T over this wave's dims, as two independent accumulation chains
-    v16f s = v16f{}, s2 = v16f{};
+  for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int m = 0; m < 5; ++m) {
-      const int nu = m < 4 ? 4 : 2;
+  for (int i = 0; i < 8; ++i) o[i] = v16f{};
+  l_run = 0.f;
+  bool over = false;  // a logit above ref + REF_HEADROOM
+  for (int j = 0; j < NRAW && j < ntiles; ++j) tile_gather(sm.raw[j], sm.idx + j * TILE, gp, wave);
+  if (ntiles > 0) {
+    wait_tiles_but(min(ntiles, NRAW) - 1, wave);
+    lds_barrier();  // every wave's part of tile 0 has landed
+    tile_dequant(sm.raw[0], sm.k[0], pr, pm);
+    if (ntiles > 1) wait_tiles_but(min(ntiles, NRAW) - 2, wave);
+  }
+  if (tid == 0) redo = 0;
+  lds_barrier();  // tile 0 is in K[0], tile 1 in raw slot 1
+
+  // Entering iteration `it`: K[it & 1] holds tile it, raw slot (it+1) % 3 holds tile it+1
+  // (landed and visible), tile it+2 is in flight, slot it % 3 is free.
+#pragma unroll 1
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + NRAW < ntiles) tile_gather(sm.raw[it % NRAW], sm.idx + (it + NRAW) * TILE, gp, wave);
+    const unsigned char* kb = sm.k[it & 1];
+    // half of S^T over this wave's dims (one accumulation chain: a dependent 32x32x16 MFMA
+    // issues at full rate)
+    v16f s = v16f{};
+    {
+      // operand reads four k-steps ahead of their MFMA
       v8h a[4];
 #pragma unroll
-      for (int u = 0; u < nu; ++u) a[u] = *reinterpret_cast<const v8h*>(kb + koff[u] + 128 * m);
+      for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const v8h*>(kb + koff[ks] );
 #pragma unroll
-      for (int u = 0; u < nu; u += 2) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u], qf[4 * m + u], s, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u + 1], qf[4 * m + u + 1], s2, 0, 0, 0);
+      for (int ks = 0; ks < 18; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 3], qf[ks], s, 0, 0, 0);
+        if (ks + 4 < 18)
+          a[ks & 3] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * ((ks + 4) >> 2));
       }
     }
-    // the next tile's bf16 copy, while the matrix cores work (unconditional, so that it shares a
-    // basic block with the MFMAs above; after the last tile it converts a stale slot into the
-    // idle buffer, which nothing reads)
-    tile_dequant(sm.raw[(it + 1) % NRAW], sm.k[(it + 1) & 1], sm.idx + min(it + 1, ntiles - 1) * TILE);
-    s += s2;
+    // the next tile's fp16 copy, while the matrix cores finish (unconditional: after the last
+    // tile it converts a stale slot into the idle buffer, which nothing reads)
+    tile_dequant(sm.raw[(it + 1) % NRAW], sm.k[(it + 1) & 1], pr, pm);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4)
       *reinterpret_cast<float4*>(&sm.sx[wave][g4][lane][0]) =
@@ -375,22 +389,15 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     }
     float tmax = s[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c;
-    // both waves of a head group hold identical logits and take the same decision
-    const float m_new = fmaxf(m_run, tmax);
-    if (m_run == -INFINITY) {
-      m_run = m_new;  // first valid rows: O and l are still zero
-    } else if (__any(m_new > m_run + RESCALE_LOG2)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
+    for (int i = 1; i < 16; ++i) tmax = __builtin_fmaxf(tmax, s[i]);
+    tmax = swap_halves_max(tmax) * c;
+    // both waves of a head group hold identical logits and take the same decisions
+    seen = __builtin_fmaxf(seen, tmax);
+    ref = ref == -INFINITY && tmax != -INFINITY ? tmax + REF_MARGIN : ref;
+    over |= tmax > ref + REF_HEADROOM;
     // P in registers, packed as the B operand of the two 16-row k-steps (no valid row so far:
     // every logit is -inf and P must come out 0, not NaN)
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float m_use = ref == -INFINITY ? 0.f : ref;
     v8h pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -409,11 +416,11 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const int par = mt & 1, m = mt >> 1;
+        const int par = mt & 1, mm = mt >> 1;
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(kb + voff[ks][0][par] + 128 * m));
+            (__attribute__((address_space(3))) v4s*)(kb + voff[0][par] + RB16 * ks + 128 * mm));
         const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(kb + voff[ks][1][par] + 128 * m));
+            (__attribute__((address_space(3))) v4s*)(kb + voff[1][par] + RB16 * ks + 128 * mm));
         const v8h a = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[ks], o[mt], 0, 0, 0);
       }
@@ -423,14 +430,19 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     if (it + 2 < ntiles) wait_tiles_but(it + 3 < ntiles ? 1 : 0, wave);
     lds_barrier();
   }
-
-  wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS when it exits
+  wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS
+  if (__any(over)) redo = 1;  // any wave: every wave redoes the split
+  __syncthreads();
+  if (!redo || pass == 1) break;
+  ref = seen;  // the second pass cannot exceed it
+  __syncthreads();
+  }
 
   // denominator of each head: both lane halves, both waves of the head group hold the same
-  l_run += __shfl_xor(l_run, 32);
+  l_run = swap_halves_sum(l_run);
   const bool empty = !(l_run > 0.f);
   const float inv = empty ? 0.f : 1.f / l_run;
-  const float lse = empty ? -INFINITY : (m_run + log2f(l_run)) * (1.0f / LOG2E);
+  const float lse = empty ? -INFINITY : (ref + log2f(l_run)) * (1.0f / LOG2E);
 
   if (part_o == nullptr) {
     __bf16* orow = out + (t * MLA_H + head) * MLA_DV;
@@ -445,49 +457,60 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
       }
     if (lse_out && kh == 0 && half == 0) lse_out[t * MLA_H + head] = lse;
   } else {
-    float* prow = part_o + ((t * nsplit + split) * MLA_H + head) * MLA_DV;
+    _Float16* prow = part_o + ((t * nsplit + split) * MLA_H + head) * MLA_DV;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int dim = 256 * kh + 32 * mt + 8 * g4 + 4 * half;
-        float4 v = make_float4(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv, o[mt][4 * g4 + 2] * inv,
-                               o[mt][4 * g4 + 3] * inv);
-        *reinterpret_cast<float4*>(prow + dim) = v;
+        v2u pk = {pack_f16(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv),
+                  pack_f16(o[mt][4 * g4 + 2] * inv, o[mt][4 * g4 + 3] * inv)};
+        *reinterpret_cast<v2u*>(prow + dim) = pk;
       }
     if (kh == 0 && half == 0) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
   }
 }
 
-// Merge split partials by log-sum-exp: one 128-thread block per (token, head), 4 dims/thread.
-__global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
+// Merge split partials by log-sum-exp: one 128-thread block per (token, head), 4 dims per
+// thread; every split's weight first, then all of the thread's partial loads at once.
+
+__global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           int nsplit, __bf16* __restrict__ out,
                                                           float* __restrict__ lse_out) {
   const int64_t th = blockIdx.x;  // t * H + h
   const int64_t t = th / MLA_H;
   const int h = (int)(th % MLA_H);
+  const float* pl = part_lse + t * nsplit * MLA_H + h;
+  const _Float16* po = part_o + (t * nsplit * MLA_H + h) * MLA_DV + 4 * threadIdx.x;
   float m = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) m = fmaxf(m, part_lse[(t * nsplit + j) * MLA_H + h]);
+  for (int j = 0; j < nsplit; ++j) m = fmaxf(m, pl[j * MLA_H]);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  const int d = 4 * threadIdx.x;
   if (m != -INFINITY) {
-    for (int j = 0; j < nsplit; ++j) {
-      const float lj = part_lse[(t * nsplit + j) * MLA_H + h];
-      if (lj == -INFINITY) continue;
-      const float wj = __expf(lj - m);
-      wsum += wj;
-      const float4 v = *reinterpret_cast<const float4*>(part_o + ((t * nsplit + j) * MLA_H + h) * MLA_DV + d);
-      acc[0] += wj * v.x;
-      acc[1] += wj * v.y;
-      acc[2] += wj * v.z;
-      acc[3] += wj * v.w;
+    for (int j0 = 0; j0 < nsplit; j0 += 8) {
+      v4h v[8];
+      float wj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, nsplit - 1);
+        v[u] = *reinterpret_cast<const v4h*>(po + (int64_t)j * MLA_H * MLA_DV);
+        const float lj = pl[j * MLA_H];
+        wj[u] = j0 + u < nsplit && lj != -INFINITY ? __expf(lj - m) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        wsum += wj[u];
+        acc[0] += wj[u] * (float)v[u][0];
+        acc[1] += wj[u] * (float)v[u][1];
+        acc[2] += wj[u] * (float)v[u][2];
+        acc[3] += wj[u] * (float)v[u][3];
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   v2u pk = {pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<v2u*>(out + th * MLA_DV + d) = pk;
+  *reinterpret_cast<v2u*>(out + th * MLA_DV + 4 * threadIdx.x) = pk;
   if (lse_out && threadIdx.x == 0) lse_out[th] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
@@ -579,7 +602,7 @@ size_t mla_workspace_bytes(const smla_batch& b, int32_t H, int32_t D_v, int32_t 
   const int s = mla_decode_splits(b, top_k);
   if (s <= 1) return 0;
   const size_t n = (size_t)b.total_q * s * H;
-  return align_up(n * D_v * sizeof(float), 256) + align_up(n * sizeof(float), 256);
+  return align_up(n * D_v * sizeof(_Float16), 256) + align_up(n * sizeof(float), 256);
 }
 
 hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, const int32_t* idx,
@@ -596,12 +619,12 @@ hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, co
     return true;
   }();
   (void)lds_set;
-  float* part_o = nullptr;
+  _Float16* part_o = nullptr;
   float* part_lse = nullptr;
   if (nsplit > 1) {
-    part_o = static_cast<float*>(ws);
+    part_o = static_cast<_Float16*>(ws);
     part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                        align_up((size_t)b.total_q * nsplit * MLA_H * MLA_DV * sizeof(float), 256));
+                                        align_up((size_t)b.total_q * nsplit * MLA_H * MLA_DV * sizeof(_Float16), 256));
   }
   mark_stage(STAGE_MLA, false, s);
   hipLaunchKernelGGL(mla_fp8_kernel, dim3(b.total_q, nsplit), dim3(NT), lds, s, tv.tok,
