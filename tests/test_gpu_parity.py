@@ -185,6 +185,32 @@ def test_mla_with_oracle_indices_unsorted_and_padded():
         assert_attn_close(out, ref, lse, ref_lse, f"oracle idx decode={decode}")
 
 
+def test_mla_growing_logits_recompute():
+    # The rope dims (a part of the key only, not of the value) of row s are scaled by
+    # 2^floor(12 s / rows): the logits of the later selected rows grow thousands of times larger
+    # than those of the first tile, far beyond what an fp16 P can span from the reference the
+    # first tile sets, so the kernel must notice and recompute the split with the true maximum
+    # (prefill: one split over all selected rows). Scaling by powers of two keeps the bf16 values
+    # exact; they stay inside the fp16 range (|x| < 5 * 2^12), and the values stay N(0, 1).
+    d = W.small_big_dims(n_q=4, cached=3000)
+    x = W.generate(d)
+    rows = x.kv.shape[0]
+    rope = x.kv[:, 528:656].copy().view(np.uint16).astype(np.uint32) << 16
+    grow = np.exp2(np.floor(12.0 * np.arange(rows) / rows)).astype(np.float32)
+    scaled = (rope.view(np.float32) * grow[:, None]).view(np.uint32) >> 16
+    x.kv[:, 528:656] = scaled.astype(np.uint16).view(np.uint8)
+    say("[case] growing logits")
+    dev = Dev(x)
+    tokens = np.arange(d.total_q)
+    idx, sc = dev.topk()
+    ref_idx, ref_sc = oracle_topk(x, tokens)
+    assert_topk_equal(idx, sc, ref_idx, ref_sc, "growing logits")
+    ref, ref_lse = oracle_mla(x, ref_idx, tokens)
+    for decode in (False, True):
+        out, lse = dev.mla(idx, decode=decode)
+        assert_attn_close(out, ref, lse, ref_lse, f"growing logits decode={decode}")
+
+
 # ---- full-size workloads, sampled tokens -------------------------------------------------
 
 def _sampled_full_config(cid, tokens, decode):
