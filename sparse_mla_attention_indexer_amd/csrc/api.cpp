@@ -89,12 +89,11 @@ int check_mla_args(const smla_batch* b, const void* q, const void* kv, int32_t f
 }
 
 // Indexer work plan: query tiles of up to QT tokens, tile i paired with tile n-1-i, each pair's
-// combined key range (front tile's keys, then back tile's) cut into KEY_CHUNK-key items.
-void plan_items(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
-                const std::vector<int32_t>& q_start, std::vector<smla::Item>* items) {
+// combined key range (front tile's keys, then back tile's) cut into C-key items.
+void plan_items_chunk(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                      const std::vector<int32_t>& q_start, int64_t C, std::vector<smla::Item>* items) {
   using smla::Item;
   using smla::Seg;
-  const int64_t C = smla::KEY_CHUNK;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t base = kv_len[b] - n_q[b];
     const int32_t nt = (n_q[b] + smla::QT - 1) / smla::QT;
@@ -125,6 +124,15 @@ void plan_items(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
         items->push_back(it);
       }
     }
+  }
+}
+
+void plan_items(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                const std::vector<int32_t>& q_start, std::vector<smla::Item>* items) {
+  plan_items_chunk(batch, n_q, kv_len, q_start, smla::KEY_CHUNK, items);
+  if ((int64_t)items->size() < smla::ITEMS_FILL) {
+    items->clear();
+    plan_items_chunk(batch, n_q, kv_len, q_start, smla::KEY_CHUNK_SMALL, items);
   }
 }
 
@@ -161,7 +169,7 @@ size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv) {
   if (batch < 1 || total_q < 1 || max_kv < 1) return 0;
   // every tile pair contributes at most ceil(E / C) <= E / C + 1 items, E <= 2 * max_kv
   const int64_t tiles = (int64_t)total_q / smla::QT + batch;
-  const int64_t items = tiles * (max_kv / smla::KEY_CHUNK + 2);
+  const int64_t items = tiles * (max_kv / smla::KEY_CHUNK_SMALL + 2);
   return table_layout(batch, total_q, items);
 }
 

@@ -36,9 +36,13 @@ struct alignas(32) Item {
 };
 
 // Indexer planning: query tiles of up to QT tokens; each front/back pair of tiles is cut into
-// chunks of KEY_CHUNK keys of combined work.
+// chunks of KEY_CHUNK keys of combined work, or of KEY_CHUNK_SMALL keys when that would give
+// fewer than ITEMS_FILL workgroups (decode batches: a few long rows), so that the chip gets
+// several workgroups per CU to balance.
 constexpr int QT = 4;
 constexpr int KEY_CHUNK = 4096;
+constexpr int KEY_CHUNK_SMALL = 2048;
+constexpr int ITEMS_FILL = 1024;
 
 // Top-k: rows with n <= TOPK_LDS_MAX candidates are selected by one workgroup in LDS; longer
 // rows by one workgroup each (up to TOPK_ROW_MAX) or by count / resolve / emit kernels over
