@@ -15,6 +15,8 @@
 // Work is planned on the host (smla_batch_build): query tiles of up to 4 tokens are paired
 // front with back (tile i with tile n-1-i), the pages' load-balanced chunk pairing applied to
 // causal query tiles on one GPU, and each pair's combined key range is cut into equal chunks.
+#include <type_traits>
+
 #include "smla_internal.h"
 
 namespace smla {
@@ -124,6 +126,156 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
     if (T + i < ntile) tile(s + i * step, kb[i]);
 }
 
+// ---- query tiles of 2..4 tokens: key tiles shared through LDS ---------------------------------
+// The tokens of one query tile see (almost) the same keys, so the workgroup loads each 32-key
+// tile once, straight into LDS (load-to-LDS, no registers), and every wave reads its B operands
+// from there. Key tiles go through a ring of three groups of four; the loads of group g+2 are
+// issued while group g is scored, and one barrier per group hands them over.
+constexpr int SG = 4;      // key tiles per group
+constexpr int SRING = 3;   // groups in the ring
+
+// Waits until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void idx_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Barrier that waits for this wave's LDS operations only (key loads of later groups keep flying).
+__device__ __forceinline__ void idx_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One load-to-LDS instruction (inline assembly, so that the compiler neither counts it nor
+// drains it before LDS writes): lane l's 16 bytes at g land at lds + 16 l. M0 is restored.
+__device__ __forceinline__ void idx_lds_load16(const void* g, void* lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(a)
+      : "memory");
+}
+
+// Segment of nq (2..4) tokens against keys [s0, s1). `ring`: SRING * SG tiles of 256 16-byte
+// slots; slot 32 * piece + key holds bytes [16 piece, 16 piece + 16) of the tile's key `key`,
+// so a wave's operand read (32 keys, one piece) is 512 consecutive bytes.
+__device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __restrict__ toks,
+                                                   const int8_t* __restrict__ q_idx,
+                                                   const int8_t* __restrict__ k_idx,
+                                                   const uint32_t (&wl)[16],
+                                                   int32_t* __restrict__ scores, int64_t stride,
+                                                   bool hist_on, int (*lhist)[TOPK_BINS],
+                                                   v4i (*ring)[256]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  // waves per token: 2 for two tokens (they take alternate key tiles), else 1
+  const int qpw = sg.nq == 2 ? 2 : 1;
+  const int qi = wave / qpw, par = wave % qpw;
+  const bool active = qi < sg.nq;
+  const int64_t t = sg.q0 + (active ? qi : 0);
+  const Tok tk = toks[t];
+  const Tok tl = toks[sg.q0 + sg.nq - 1];  // the tile's last token sees the most keys
+  const int kmax = min(sg.s1 - 1, tl.pos);   // last key any token of the tile may score
+  const int last = min(sg.s1 - 1, tk.pos);   // last key of this wave's token
+  const int ntile = (kmax - sg.s0) / 32 + 1;
+  const int ngroup = (ntile + SG - 1) / SG;
+
+  v4i qa[2][4];
+  const int8_t* qbase = q_idx + t * (IDX_H * IDX_D);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
+  idx_wait_vmcnt<0>();  // the fragments are in before any key load goes out
+
+  // key loads: wave w loads tile SG*g + w of group g; instruction d covers slots 64d .. 64d+63
+  const int8_t* kbase = k_idx + tk.row_start * IDX_D + 16 * (2 * 0 + half);
+  auto load_group = [&](int g) {
+    const int k = SG * g + wave;
+    const int key = min(sg.s0 + 32 * k + col, kmax);  // clamped: never past the visible rows
+    const int8_t* src = kbase + (int64_t)key * IDX_D;
+    v4i* dst = ring[(g % SRING) * SG + wave];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) idx_lds_load16(src + 32 * d, dst + 64 * d);
+  };
+  load_group(0);
+  if (ngroup > 1) load_group(1);
+
+  int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
+  const __amdgpu_buffer_rsrc_t out_rs =
+      __builtin_amdgcn_make_buffer_rsrc(out_row, 0, active ? (last + 1) * 4 : 0, 0x00020000);
+  int* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
+
+  auto epilogue = [&](const v16i& acc0, const v16i& acc1, int k) {
+    uint32_t ps[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
+      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
+    }
+    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    sum += (uint32_t)__shfl_xor((int)sum, 32);
+    const int key = sg.s0 + 32 * k + col;
+    __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
+    if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
+  };
+  auto products = [&](int g, int i, v16i& acc0, v16i& acc1) {
+    const v4i* kt = ring[(g % SRING) * SG + i];
+    v4i kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = kt[32 * (4 * half + j) + col];
+    acc0 = v16i{};
+    acc1 = v16i{};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+    }
+  };
+  auto group_tiles = [&](auto ntw, int g, int first, int stride) {
+    constexpr int NTW = decltype(ntw)::value;
+    v16i a0[2], a1[2];
+    products(g, first, a0[0], a1[0]);
+#pragma unroll
+    for (int u = 1; u < NTW; ++u) {
+      products(g, first + stride * u, a0[u & 1], a1[u & 1]);
+      epilogue(a0[(u - 1) & 1], a1[(u - 1) & 1], SG * g + first + stride * (u - 1));
+    }
+    epilogue(a0[(NTW - 1) & 1], a1[(NTW - 1) & 1], SG * g + first + stride * (NTW - 1));
+  };
+
+#pragma unroll 1
+  for (int g = 0; g < ngroup; ++g) {
+    // this wave's loads of group g have landed (only group g+1's may still fly), then everyone's
+    if (g + 1 < ngroup) idx_wait_vmcnt<4>(); else idx_wait_vmcnt<0>();
+    idx_lds_barrier();
+    if (active) {
+      // software pipelined over the wave's tiles of the group: the products of tile u+1 are
+      // issued before the ReLU/weight epilogue of tile u, so the matrix cores and the vector
+      // ALUs work at the same time (tiles past the segment compute on clamped keys; their
+      // stores fall outside the buffer range and are dropped)
+      if (qpw == 1) group_tiles(std::integral_constant<int, SG>{}, g, 0, 1);
+      else group_tiles(std::integral_constant<int, SG / 2>{}, g, par, 2);
+    }
+    // the slots of group g-1 are free (everyone passed the barrier above): group g+2 goes there
+    if (g + 2 < ngroup) load_group(g + 2);
+  }
+  idx_wait_vmcnt<0>();
+}
+
 __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __restrict__ items,
                                                            const Tok* __restrict__ toks,
                                                            const int8_t* __restrict__ q_idx,
@@ -132,6 +284,7 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
                                                            int32_t* __restrict__ scores,
                                                            int64_t stride, int* __restrict__ hist) {
   __shared__ int lhist[QT][TOPK_BINS];
+  __shared__ v4i ring[SRING * SG][256];
   const Item it = items[blockIdx.x];
   // wave-uniform (a scalar): everything derived from it (the query, its score row) stays in
   // scalar registers, as buffer resources must
@@ -158,10 +311,13 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
       for (int i = threadIdx.x; i < QT * TOPK_BINS; i += 256) (&lhist[0][0])[i] = 0;
       __syncthreads();
     }
-    // waves per query: 4 for a single query (they split the key tiles), 2 for two, else 1
-    const int qpw = sg.nq == 1 ? 4 : (sg.nq == 2 ? 2 : 1);
-    const int qi = wave / qpw;
-    if (qi < sg.nq) {
+    if (sg.nq >= 2) {
+      indexer_shared_seg(sg, toks, q_idx, k_idx, wl, scores, stride, hist_on, lhist, ring);
+      __syncthreads();  // the ring is reused by the next segment
+    } else if (wave < 4) {
+      // a single query: the 4 waves split its key tiles, loading keys straight into registers
+      const int qpw = 4;
+      const int qi = wave / qpw;
       const int phase = wave - qi * qpw;
       const int64_t t = sg.q0 + qi;
       const Tok tk = toks[t];
