@@ -43,103 +43,39 @@ namespace {
 constexpr int IDX_H = 64;
 constexpr int IDX_D = 128;
 
-// One wave: query token t against key tiles s = s_begin, s_begin + step, ... < s_end, s <= p.
-// `lhist` (LDS, optional) receives the histogram code of every score the wave writes.
-__device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
-                                             int step, const int8_t* __restrict__ q_idx,
-                                             const int8_t* __restrict__ k_idx,
-                                             const uint32_t (&wl)[16], int32_t* __restrict__ out_row,
-                                             int* lhist) {
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const int col = lane & 31;
-  const int p = tk.pos;
-  const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
-  if (s_begin > last) return;
-  // A fragments: head 32*mt + col, dims [64*half + 16*j, +16)
-  v4i qa[2][4];
-  const int8_t* qbase = q_idx + t * (IDX_H * IDX_D);
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
 
-  // B fragments straight from memory: lane (col, half) reads 64 contiguous bytes of key `col`
-  const int8_t* kbase = k_idx + tk.row_start * IDX_D + 64 * half;
-  auto load_keys = [&](int s, v4i (&kb)[4]) {
-    const int kr = min(s + col, last);  // clamp: never read past the visible rows
-    const v4i* kp = reinterpret_cast<const v4i*>(kbase + (int64_t)kr * IDX_D);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = kp[j];
-  };
-  // Scores go out through a buffer resource whose range ends at key `last`: the hardware drops
-  // the stores of keys past it and of the upper lane half, so every tile issues exactly one
-  // store and the compiler can count this wave's outstanding loads (a branch around the store
-  // would make it drain every prefetched key tile before each MFMA).
-  const __amdgpu_buffer_rsrc_t out_rs =
-      __builtin_amdgcn_make_buffer_rsrc(out_row, 0, (last + 1) * 4, 0x00020000);
-  // one 32-key tile: scores of the wave's query against keys s .. s+31
-  auto tile = [&](int s, const v4i (&kb)[4]) {
-    v16i acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
-    }
-    // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them.
-    // ReLU(dot) <= 2^21 and w < 2^10 (the weight contract), so 24-bit multiplies are exact and
-    // run at full rate (a 32-bit multiply is quarter rate); four independent partial sums keep
-    // the chain of dependent adds from setting the pace
-    uint32_t ps[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
-      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
-    }
-    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    sum += (uint32_t)__shfl_xor((int)sum, 32);
-    const int key = s + col;
-    __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
-    if (lhist && half == 0 && key <= last) atomicAdd(&lhist[topk_bin(sum)], 1);
-  };
-  // NPF key tiles in flight per wave: enough bytes outstanding to cover HBM latency. The main
-  // loop runs whole groups of NPF tiles without exits, so the compiler's count of outstanding
-  // loads is the same on every pass (it only ever waits for the oldest tile); loads past the
-  // end read clamped rows and are never used.
-  constexpr int NPF = 4;
-  const int ntile = (last - s_begin) / step + 1;
-  v4i kb[NPF][4];
-#pragma unroll
-  for (int i = 0; i < NPF; ++i) load_keys(s_begin + i * step, kb[i]);
-  int s = s_begin;
-  int T = 0;
-  for (; T + NPF <= ntile; T += NPF, s += NPF * step) {
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) {
-      tile(s + i * step, kb[i]);
-      load_keys(s + (NPF + i) * step, kb[i]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NPF - 1; ++i)
-    if (T + i < ntile) tile(s + i * step, kb[i]);
-}
-
-// ---- query tiles of 2..4 tokens: key tiles shared through LDS ---------------------------------
-// The tokens of one query tile see (almost) the same keys, so the workgroup loads each 32-key
-// tile once, straight into LDS (load-to-LDS, no registers), and every wave reads its B operands
-// from there. Key tiles go through a ring of three groups of four; the loads of group g+2 are
-// issued while group g is scored, and one barrier per group hands them over.
-constexpr int SG = 4;      // key tiles per group
-constexpr int SRING = 3;   // groups in the ring
-
-// Waits until at most N of this wave's vector-memory operations are outstanding.
+// Waits until at most N of this wave's vector-memory operations are outstanding (inline
+// assembly, so that it keeps its place among the hand-counted memory operations).
 template <int N>
 __device__ __forceinline__ void idx_wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits for all of this wave's loads, visibly to the compiler (it then knows that registers
+// loaded earlier are ready and adds no waits of its own after the hand-counted loads start).
+__device__ __forceinline__ void idx_wait_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   asm volatile("" ::: "memory");
+}
+
+// Raw buffer descriptor (stride 0) over `bytes` bytes at `base`: stores at offsets >= bytes are
+// dropped by the hardware, yet count as memory operations like any other.
+typedef int idx_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ idx_v4s idx_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  idx_v4s r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 4-byte buffer store as inline assembly: the compiler can neither merge, drop nor move it
+// across the other hand-counted operations.
+__device__ __forceinline__ void idx_store32(const idx_v4s& rs, uint32_t off, uint32_t v) {
+  asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(v), "v"(off), "s"(rs) : "memory");
 }
 
 // Barrier that waits for this wave's LDS operations only (key loads of later groups keep flying).
@@ -165,6 +101,123 @@ __device__ __forceinline__ void idx_lds_load16(const void* g, void* lds) {
       : "v"(g), "s"(a)
       : "memory");
 }
+
+// ---- single-token query tiles: each wave streams its own key tiles through LDS ----------------
+// One wave: query token t against key tiles s = s_begin, s_begin + step, ... < s_end, s <= p.
+// Key tiles reach LDS by the load-to-LDS path in whole 128-byte lines (eight lanes per key, one
+// 1 KB instruction per eight keys), KR tiles ahead in a ring of the wave's own; the slot of
+// piece P (16 bytes) of key c is 8 c + (P ^ ((c >> 1) & 7)), which keeps the B-operand reads
+// (32 keys, one piece) free of bank conflicts. The products of tile i+1 are issued before the
+// epilogue of tile i. `lh` (LDS, optional) receives the histogram code of every score.
+constexpr int KR = 4;  // key tiles per wave in flight or in use
+
+__device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
+                                             int step, const int8_t* __restrict__ q_idx,
+                                             const int8_t* __restrict__ k_idx,
+                                             const uint32_t (&wl)[16], int32_t* __restrict__ out_row,
+                                             int* lh, v4i (*ring)[256]) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int p = tk.pos;
+  const int last = s_end - 1 < p ? s_end - 1 : p;  // last key this wave may score
+  if (s_begin > last) return;
+  // A fragments: head 32*mt + col, dims [64*half + 16*j, +16)
+  v4i qa[2][4];
+  const int8_t* qbase = q_idx + t * (IDX_H * IDX_D);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
+  idx_wait_loads();  // the fragments are in before any key load goes out
+
+  // Scores go out through a buffer resource whose range ends at key `last`: the hardware drops
+  // the stores of keys past it, of the upper lane half and of the placeholder stores below, so
+  // every step issues exactly one store and the waits below can count this wave's memory
+  // operations exactly.
+  const idx_v4s out_rs = idx_rsrc(out_row, (last + 1) * 4);
+  const int8_t* kbase = k_idx + tk.row_start * IDX_D;
+  const int ntile = (last - s_begin) / step + 1;
+  const int dkey = lane >> 3, dpc = lane & 7;  // load lanes: key 8d + dkey, slot piece dpc
+  auto dma = [&](int i) {  // tile i (past the end: clamped keys, never scored)
+    const int s = s_begin + i * step;
+    v4i* dst = ring[i % KR];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int c = 8 * d + dkey;
+      const int key = min(s + c, last);
+      idx_lds_load16(kbase + (int64_t)key * IDX_D + 16 * (dpc ^ ((c >> 1) & 7)), dst + 64 * d);
+    }
+  };
+  auto placeholder_store = [&]() { idx_store32(out_rs, 0x7FFFFFF0u, 0u); };
+  auto products = [&](int i, v16i& acc0, v16i& acc1) {
+    const v4i* kt = ring[i % KR];
+    v4i kb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kb[j] = kt[8 * col + ((4 * half + j) ^ ((col >> 1) & 7))];
+    acc0 = v16i{};
+    acc1 = v16i{};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+    }
+  };
+  // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them.
+  // ReLU(dot) <= 2^21 and w < 2^10 (the weight contract), so 24-bit multiplies are exact and
+  // run at full rate (a 32-bit multiply is quarter rate); four independent partial sums keep
+  // the chain of dependent adds from setting the pace
+  auto epilogue = [&](const v16i& acc0, const v16i& acc1, int i) {
+    uint32_t ps[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
+      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
+    }
+    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    sum += (uint32_t)__shfl_xor((int)sum, 32);
+    const int key = s_begin + i * step + col;
+    idx_store32(out_rs, half ? 0x7FFFFFF0u : (uint32_t)key * 4u, sum);
+    if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
+  };
+
+  // Prologue: tiles 0 .. KR-2 with a placeholder store after each, as if earlier steps had run;
+  // then step i: load tile i+KR-1, wait for tile i+1 (after its loads: one store, then tile
+  // i+2's loads and a store, ..., tile i+KR-1's loads = 5 (KR-2) operations), products of tile
+  // i+1, epilogue of tile i.
+  static_assert(KR == 4, "wait counts below assume four tiles");
+  dma(0);
+  placeholder_store();
+  dma(1);
+  placeholder_store();
+  dma(2);
+  placeholder_store();
+  idx_wait_vmcnt<11>();  // tile 0: after it, a store, tile 1, a store, tile 2, a store
+  v16i a0[2], a1[2];
+  products(0, a0[0], a1[0]);
+#pragma unroll 1
+  for (int i = 0; i < ntile; i += 2) {
+    dma(i + 3);
+    idx_wait_vmcnt<10>();
+    if (i + 1 < ntile) products(i + 1, a0[1], a1[1]);
+    epilogue(a0[0], a1[0], i);
+    if (i + 1 >= ntile) break;
+    dma(i + 4);
+    idx_wait_vmcnt<10>();
+    if (i + 2 < ntile) products(i + 2, a0[0], a1[0]);
+    epilogue(a0[1], a1[1], i + 1);
+  }
+  idx_wait_vmcnt<0>();  // no key load may still be writing this wave's ring when it returns
+}
+
+// ---- query tiles of 2..4 tokens: key tiles shared through LDS ---------------------------------
+// The tokens of one query tile see (almost) the same keys, so the workgroup loads each 32-key
+// tile once, straight into LDS (load-to-LDS, no registers), and every wave reads its B operands
+// from there. Key tiles go through a ring of three groups of four; the loads of group g+2 are
+// issued while group g is scored, and one barrier per group hands them over.
+constexpr int SG = 4;      // key tiles per group
+constexpr int SRING = 3;   // groups in the ring
 
 // Segment of nq (2..4) tokens against keys [s0, s1). `ring`: SRING * SG tiles of 256 16-byte
 // slots; slot 32 * piece + key holds bytes [16 piece, 16 piece + 16) of the tile's key `key`,
@@ -199,7 +252,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
-  idx_wait_vmcnt<0>();  // the fragments are in before any key load goes out
+  idx_wait_loads();  // the fragments are in before any key load goes out
 
   // key loads: wave w loads tile SG*g + w of group g; instruction d covers slots 64d .. 64d+63
   const int8_t* kbase = k_idx + tk.row_start * IDX_D + 16 * (2 * 0 + half);
@@ -283,8 +336,13 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
                                                            const int32_t* __restrict__ w,
                                                            int32_t* __restrict__ scores,
                                                            int64_t stride, int* __restrict__ hist) {
-  __shared__ int lhist[QT][TOPK_BINS];
-  __shared__ v4i ring[SRING * SG][256];
+  // LDS, carved per segment: multi-token tiles take SRING * SG key tiles and QT histograms,
+  // single tokens 4 KR key tiles (KR per wave) and one histogram
+  constexpr int TILE_INTS = 256 * 4;
+  constexpr int MULTI_INTS = SRING * SG * TILE_INTS + QT * TOPK_BINS;
+  constexpr int SINGLE_INTS = 4 * KR * TILE_INTS + TOPK_BINS;
+  __shared__ __attribute__((aligned(16))) int smem[MULTI_INTS > SINGLE_INTS ? MULTI_INTS : SINGLE_INTS];
+  v4i (*const ring)[256] = reinterpret_cast<v4i (*)[256]>(smem);
   const Item it = items[blockIdx.x];
   // wave-uniform (a scalar): everything derived from it (the query, its score row) stays in
   // scalar registers, as buffer resources must
@@ -307,15 +365,16 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
     // rows longer than the LDS top-k path also get their score histogram (the last token of the
     // tile has the longest row)
     const bool hist_on = hist != nullptr && toks[sg.q0 + sg.nq - 1].pos + 1 > TOPK_LDS_MAX;
+    int (*const lhist)[TOPK_BINS] = reinterpret_cast<int (*)[TOPK_BINS]>(
+        smem + (sg.nq >= 2 ? SRING * SG : 4 * KR) * TILE_INTS);
     if (hist_on) {
-      for (int i = threadIdx.x; i < QT * TOPK_BINS; i += 256) (&lhist[0][0])[i] = 0;
+      for (int i = threadIdx.x; i < sg.nq * TOPK_BINS; i += 256) (&lhist[0][0])[i] = 0;
       __syncthreads();
     }
     if (sg.nq >= 2) {
       indexer_shared_seg(sg, toks, q_idx, k_idx, wl, scores, stride, hist_on, lhist, ring);
-      __syncthreads();  // the ring is reused by the next segment
-    } else if (wave < 4) {
-      // a single query: the 4 waves split its key tiles, loading keys straight into registers
+    } else {
+      // a single query: the 4 waves split its key tiles, each through its own part of the ring
       const int qpw = 4;
       const int qi = wave / qpw;
       const int phase = wave - qi * qpw;
@@ -323,16 +382,17 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
       const Tok tk = toks[t];
       int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
       int* lh = hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
-      indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row, lh);
+      indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row, lh,
+                   ring + KR * wave);
     }
+    __syncthreads();  // the ring (and the histogram) are reused by the next segment
     if (hist_on) {
-      __syncthreads();
       for (int q = 0; q < sg.nq; ++q) {
         const int64_t t = sg.q0 + q;
         if (toks[t].pos + 1 <= TOPK_LDS_MAX) continue;
         int* g = hist + t * TOPK_BINS;
         for (int i = threadIdx.x; i < TOPK_BINS; i += 256)
-          if (lhist[q][i]) atomicAdd(&g[i], lhist[q][i]);
+          if (lhist[q][i]) atomicAdd(&g[topk_hist_slot(i)], lhist[q][i]);
       }
       __syncthreads();
     }
@@ -367,7 +427,7 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restr
   }
   int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
   out_row[s] = (int32_t)score;
-  if (hist && tk.pos + 1 > TOPK_LDS_MAX) atomicAdd(&hist[t * TOPK_BINS + topk_bin(score)], 1);
+  if (hist && tk.pos + 1 > TOPK_LDS_MAX) atomicAdd(&hist[t * TOPK_BINS + topk_hist_slot(topk_bin(score))], 1);
 }
 
 }  // namespace

@@ -67,6 +67,11 @@ __device__ __forceinline__ int topk_bin(uint32_t s) {
   return 64 * (e - 5) + (int)((s >> (e - 6)) & 63u);
 }
 
+// Word of bin b in a row's histogram in device memory. A row's scores cluster in a few binades,
+// so its busy bins are neighbours, and every workgroup that scores part of the row adds to them;
+// many writers to one 128-byte line serialise, so bins less than 64 apart go to different lines.
+__device__ __forceinline__ int topk_hist_slot(int b) { return (b & 63) * 32 + (b >> 6); }
+
 // Smallest score whose code is b (the inverse of topk_bin on bin boundaries), as a 64-bit
 // value so that the bound past the last bin is representable.
 __device__ __forceinline__ uint64_t topk_bin_lo(int b) {
@@ -79,7 +84,8 @@ __device__ __forceinline__ uint64_t topk_bin_lo(int b) {
 // must be zero when a call starts: the kernels that consume them clear them again, so a
 // workspace zero-filled once stays ready for every later call.
 struct TopkWs {
-  int* hist;       // [total_q][TOPK_BINS] score histogram of each row (indexer fills it)
+  int* hist;       // [total_q][TOPK_BINS] score histogram of each row, bin b at word
+                   // topk_hist_slot(b) (the indexer fills it)
   int* rec;        // [total_q][TOPK_REC]
   int* seg;        // [total_q][nseg] per-segment counts above b*, then output offsets
   uint64_t* cand;  // [total_q][TOPK_CAND_CAP] keys of the b* candidates

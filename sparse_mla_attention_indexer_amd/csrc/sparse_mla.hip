@@ -180,12 +180,16 @@ __device__ __forceinline__ GatherPlan gather_plan(int wave, const unsigned char*
   return gp;
 }
 
-__device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx,
-                                            const GatherPlan& gp, int wave) {
-  int ix[6];
+// The row indices of a lane's chunks (LDS reads) and the loads that use them, separately so that
+// the reads can go out well before the loads.
+__device__ __forceinline__ void gather_rows(const int* sidx, const GatherPlan& gp, int (&ix)[6]) {
 #pragma unroll
-  for (int j = 0; j < 6; ++j)  // all LDS reads first
+  for (int j = 0; j < 6; ++j)
     ix[j] = *reinterpret_cast<const int*>(reinterpret_cast<const char*>(sidx) + gp.roff[j]);
+}
+
+__device__ __forceinline__ void gather_issue(unsigned char* slot, const int (&ix)[6],
+                                             const GatherPlan& gp, int wave) {
 #pragma unroll
   for (int j = 0; j < 6; ++j) {
     if (j == 5 && wave != 0) break;  // wave-uniform
@@ -194,20 +198,33 @@ __device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx
   }
 }
 
+__device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx,
+                                            const GatherPlan& gp, int wave) {
+  int ix[6];
+  gather_rows(sidx, gp, ix);
+  gather_issue(slot, ix, gp, wave);
+}
+
 // Dequantises a raw tile into the fp16 K tile. Thread (r, m) = (tid / 8, tid % 8) takes 64 e4m3
 // codes of row r (dims 128 i + 16 m .. +16, i < 4) and 8 bf16 rope dims (512 + 8 m .. +8). The
 // scale s = 2^e * mant (1 <= mant < 2): the conversion applies 2^e exactly and a packed multiply
 // fp16(mant); the rope dims are widened. Rows without an index hold the request's first row,
 // which the softmax masks out.
-__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb, int r, int m) {
-  const unsigned char* row = slot + r * MLA_ROW_BYTES;
+// The pieces are separate so that the tile loop can place them between the matrix instructions
+// of the previous tile: load() reads the thread's raw bytes, block(i) converts and stores dims
+// 128 i + 16 m .. +16, rope() the rope dims.
+struct Dequant {
   v4u code[4];
+  v4u scale;
+  v4u rope;
+  __device__ __forceinline__ void load(const unsigned char* slot, int r, int m) {
+    const unsigned char* row = slot + r * MLA_ROW_BYTES;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) code[i] = *reinterpret_cast<const v4u*>(row + 128 * i + 16 * m);
-  const v4u scale = *reinterpret_cast<const v4u*>(row + 512);
-  const v4u rope = *reinterpret_cast<const v4u*>(row + 528 + 16 * m);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) code[i] = *reinterpret_cast<const v4u*>(row + 128 * i + 16 * m);
+    scale = *reinterpret_cast<const v4u*>(row + 512);
+    rope = *reinterpret_cast<const v4u*>(row + 528 + 16 * m);
+  }
+  __device__ __forceinline__ void block(unsigned char* kb, int r, int m, int i) const {
     // the conversion reads only the exponent of its scale operand
     const float sc = __builtin_bit_cast(float, scale[i] & 0x7F800000u);
     const float mt = __builtin_bit_cast(float, (scale[i] & 0x807FFFFFu) | 0x3F800000u);
@@ -223,8 +240,18 @@ __device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned
     *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m)) = v4u{pk[0], pk[1], pk[2], pk[3]};
     *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m + 1)) = v4u{pk[4], pk[5], pk[6], pk[7]};
   }
-  *reinterpret_cast<v4u*>(kb + k_off(r, 64 + m)) =
-      v4u{bf16x2_to_f16x2(rope[0]), bf16x2_to_f16x2(rope[1]), bf16x2_to_f16x2(rope[2]), bf16x2_to_f16x2(rope[3])};
+  __device__ __forceinline__ void rope_store(unsigned char* kb, int r, int m) const {
+    *reinterpret_cast<v4u*>(kb + k_off(r, 64 + m)) =
+        v4u{bf16x2_to_f16x2(rope[0]), bf16x2_to_f16x2(rope[1]), bf16x2_to_f16x2(rope[2]), bf16x2_to_f16x2(rope[3])};
+  }
+};
+
+__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb, int r, int m) {
+  Dequant dq;
+  dq.load(slot, r, m);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dq.block(kb, r, m, i);
+  dq.rope_store(kb, r, m);
 }
 
 // One (token, split): rows idx_row[r_begin, r_end) of the token's request.
@@ -344,26 +371,37 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   // (landed and visible), tile it+2 is in flight, slot it % 3 is free.
 #pragma unroll 1
   for (int it = 0; it < ntiles; ++it) {
-    if (it + NRAW < ntiles) tile_gather(sm.raw[it % NRAW], sm.idx + (it + NRAW) * TILE, gp, wave);
     const unsigned char* kb = sm.k[it & 1];
     // half of S^T over this wave's dims (one accumulation chain: a dependent 32x32x16 MFMA
-    // issues at full rate)
+    // issues at full rate). The matrix instructions run on their own while the wave issues the
+    // work placed between them: the gather of tile it+3 and the fp16 copy of tile it+1 (the
+    // latter unconditional: after the last tile it converts a stale slot into the idle buffer,
+    // which nothing reads). Scheduling barriers keep the compiler from regrouping the pieces.
     v16f s = v16f{};
     {
-      // operand reads four k-steps ahead of their MFMA
-      v8h a[4];
+      unsigned char* kn = sm.k[(it + 1) & 1];
+      const bool gather = it + NRAW < ntiles;
+      int ix[6];
+      if (gather) gather_rows(sm.idx + (it + NRAW) * TILE, gp, ix);
+      Dequant dq;
+      // operand reads eight k-steps ahead of their MFMA (LDS latency under load exceeds the
+      // time of a few MFMAs)
+      v8h a[8];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const v8h*>(kb + koff[ks] );
+      for (int ks = 0; ks < 8; ++ks) a[ks] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * (ks >> 2));
+      dq.load(sm.raw[(it + 1) % NRAW], pr, pm);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 3], qf[ks], s, 0, 0, 0);
-        if (ks + 4 < 18)
-          a[ks & 3] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * ((ks + 4) >> 2));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 7], qf[ks], s, 0, 0, 0);
+        if (ks + 8 < 18)
+          a[ks & 7] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * ((ks + 8) >> 2));
+        if (ks == 1 && gather) gather_issue(sm.raw[it % NRAW], ix, gp, wave);
+        if (ks == 4 || ks == 7 || ks == 10 || ks == 13) dq.block(kn, pr, pm, (ks - 4) / 3);
+        if (ks == 15) dq.rope_store(kn, pr, pm);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the next tile's fp16 copy, while the matrix cores finish (unconditional: after the last
-    // tile it converts a stale slot into the idle buffer, which nothing reads)
-    tile_dequant(sm.raw[(it + 1) % NRAW], sm.k[(it + 1) & 1], pr, pm);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4)
       *reinterpret_cast<float4*>(&sm.sx[wave][g4][lane][0]) =
@@ -472,15 +510,19 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 }
 
 // Merge split partials by log-sum-exp: one 128-thread block per (token, head), 4 dims per
-// thread; every split's weight first, then all of the thread's partial loads at once.
+// thread; every split's weight first, then all of the thread's partial loads at once. Block b
+// takes token b % n_tok: workgroups are dealt to the XCDs round robin, so with n_tok a multiple
+// of 8 a token's merge runs on the XCD whose L2 holds the partials its splits just wrote (the
+// attention grid puts every split of token t on XCD t % 8 too).
 
 __global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
-                                                          int nsplit, __bf16* __restrict__ out,
+                                                          int nsplit, int n_tok,
+                                                          __bf16* __restrict__ out,
                                                           float* __restrict__ lse_out) {
-  const int64_t th = blockIdx.x;  // t * H + h
-  const int64_t t = th / MLA_H;
-  const int h = (int)(th % MLA_H);
+  const int64_t t = blockIdx.x % n_tok;
+  const int h = (int)(blockIdx.x / n_tok);
+  const int64_t th = t * MLA_H + h;
   const float* pl = part_lse + t * nsplit * MLA_H + h;
   const _Float16* po = part_o + (t * nsplit * MLA_H + h) * MLA_DV + 4 * threadIdx.x;
   float m = -INFINITY;
@@ -635,7 +677,7 @@ hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, co
   if (e != hipSuccess || nsplit == 1) return e;
   mark_stage(STAGE_COMBINE, false, s);
   hipLaunchKernelGGL(mla_combine_kernel, dim3(b.total_q * MLA_H), dim3(128), 0, s, part_o, part_lse,
-                     nsplit, static_cast<__bf16*>(out), lse);
+                     nsplit, b.total_q, static_cast<__bf16*>(out), lse);
   mark_stage(STAGE_COMBINE, true, s);
   return hipGetLastError();
 }

@@ -479,7 +479,7 @@ __device__ void hist_cut(const int* __restrict__ gh, int k, int* red, int* out) 
   static_assert(PER * NT == TOPK_BINS, "bins per thread");
   int h[PER];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) h[j] = gh[threadIdx.x * PER + j];
+  for (int j = 0; j < PER; ++j) h[j] = gh[topk_hist_slot(threadIdx.x * PER + j)];
   int local = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) local += h[j];
