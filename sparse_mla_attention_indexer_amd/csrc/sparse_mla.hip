@@ -482,30 +482,33 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const float inv = empty ? 0.f : 1.f / l_run;
   const float lse = empty ? -INFINITY : (ref + log2f(l_run)) * (1.0f / LOG2E);
 
-  if (part_o == nullptr) {
-    __bf16* orow = out + (t * MLA_H + head) * MLA_DV;
+  // The output goes out through LDS (the K buffers, idle once the tile loop is done) so that every
+  // global store writes whole lines: head h's 512 16-bit values sit at h * 1024 with 16-byte
+  // chunk c at 16 (c ^ (h & 63)), and a wave stores one head's row (1 KB) per instruction.
+  const bool split_out = part_o != nullptr;
+  unsigned char* stage = &sm.k[0][0];
+  static_assert(sizeof(sm.k) >= MLA_H * MLA_DV * 2, "output staging");
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dim = 256 * kh + 32 * mt + 8 * g4 + 4 * half;
-        v2u pk = {pack_bf16(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv),
-                  pack_bf16(o[mt][4 * g4 + 2] * inv, o[mt][4 * g4 + 3] * inv)};
-        *reinterpret_cast<v2u*>(orow + dim) = pk;
-      }
-    if (lse_out && kh == 0 && half == 0) lse_out[t * MLA_H + head] = lse;
-  } else {
-    _Float16* prow = part_o + ((t * nsplit + split) * MLA_H + head) * MLA_DV;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dim = 256 * kh + 32 * mt + 8 * g4 + 4 * half;
-        v2u pk = {pack_f16(o[mt][4 * g4] * inv, o[mt][4 * g4 + 1] * inv),
-                  pack_f16(o[mt][4 * g4 + 2] * inv, o[mt][4 * g4 + 3] * inv)};
-        *reinterpret_cast<v2u*>(prow + dim) = pk;
-      }
-    if (kh == 0 && half == 0) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float v0 = o[mt][4 * g4] * inv, v1 = o[mt][4 * g4 + 1] * inv;
+      const float v2 = o[mt][4 * g4 + 2] * inv, v3 = o[mt][4 * g4 + 3] * inv;
+      const v2u pk = split_out ? v2u{pack_f16(v0, v1), pack_f16(v2, v3)}
+                               : v2u{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+      const int chunk = 32 * kh + 4 * mt + g4;  // dims 256 kh + 32 mt + 8 g4 .. +8
+      *reinterpret_cast<v2u*>(stage + head * 1024 + 16 * (chunk ^ (head & 63)) + 8 * half) = pk;
+    }
+  __syncthreads();
+  unsigned char* dst = split_out ? reinterpret_cast<unsigned char*>(part_o + (t * nsplit + split) * MLA_H * MLA_DV)
+                                 : reinterpret_cast<unsigned char*>(out + t * MLA_H * MLA_DV);
+#pragma unroll 4
+  for (int hh = wave; hh < MLA_H; hh += NT / 64)
+    *reinterpret_cast<v4u*>(dst + hh * 1024 + 16 * lane) =
+        *reinterpret_cast<const v4u*>(stage + hh * 1024 + 16 * (lane ^ (hh & 63)));
+  if (kh == 0 && half == 0) {
+    if (split_out) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
+    else if (lse_out) lse_out[t * MLA_H + head] = lse;
   }
 }
 
