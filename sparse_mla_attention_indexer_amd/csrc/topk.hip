@@ -145,6 +145,13 @@ __device__ void wave_radix_cut(KeyAt key_at, int n, int need, int* h, uint64_t* 
     mask = shift + 8 >= 64 ? 0ull : ~((1ull << (shift + 8)) - 1);
     prefix = a & mask;  // common bits above the first differing digit
     for (; shift >= 0; shift -= 8) {
+      // a digit every key shares splits nothing (the high bits of the index half of the keys,
+      // for a start): take it from `a` without a pass
+      if ((((a ^ o) >> shift) & 255u) == 0) {
+        prefix |= a & (255ull << shift);
+        mask |= 255ull << shift;
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) h[4 * lane + j] = 0;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -719,18 +726,29 @@ __global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __res
   const int nseg_t = (n + TOPK_SEG - 1) / TOPK_SEG;
   int* rec = ws.rec + t * TOPK_REC;
   int* segv = ws.seg + t * ws.nseg;
+  // every candidate slot goes out together with the row record (slots past the count hold stale
+  // keys and are dropped below), so the count costs no round trip of its own
+  const uint64_t* cand = ws.cand + t * TOPK_CAND_CAP;
+  constexpr int CPT = TOPK_CAND_CAP / NT_R;
+  uint64_t kc[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) kc[u] = cand[u * NT_R + threadIdx.x];
+  const int sv0 = (int)threadIdx.x < nseg_t ? segv[threadIdx.x] : 0;  // elements above b*
   const int ncand = rec[0];
   const int bstar = rec[1];
   const int need = top_k - rec[2];
   const uint32_t lo = (uint32_t)topk_bin_lo(bstar);
-  for (int g = threadIdx.x; g < nseg_t; g += NT_R) segc[g] = segv[g];  // elements above b*
+  if ((int)threadIdx.x < nseg_t) segc[threadIdx.x] = sv0;
+  for (int g = threadIdx.x + NT_R; g < nseg_t; g += NT_R) segc[g] = segv[g];
   uint64_t ck;
   if (ncand <= TOPK_CAND_CAP) {
-    const uint64_t* cand = ws.cand + t * TOPK_CAND_CAP;
-    for (int i = threadIdx.x; i < ncand; i += NT_R) {
-      const uint64_t key = cand[i];
-      klo[i] = (uint32_t)key;
-      khi[i] = (uint32_t)(key >> 32);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int i = u * NT_R + threadIdx.x;
+      if (i < ncand) {
+        klo[i] = (uint32_t)kc[u];
+        khi[i] = (uint32_t)(kc[u] >> 32);
+      }
     }
     __syncthreads();
     if (threadIdx.x < 64) {
@@ -760,16 +778,29 @@ __global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __res
     }
   }
   __syncthreads();
-  // exclusive scan of the per-segment counts -> output offsets
-  int carry = 0;
-  for (int c0 = 0; c0 < nseg_t; c0 += NT_R) {
-    const int c = c0 + threadIdx.x;
-    const int v = c < nseg_t ? segc[c] : 0;
-    const int incl = block_incl_scan<NT_R>(v, red);
-    const int tot = red[NT_R / 64];
-    if (c < nseg_t) segv[c] = carry + incl - v;
-    carry += tot;
-    __syncthreads();
+  // exclusive scan of the per-segment counts -> output offsets (one wave when they fit)
+  if (nseg_t <= 64) {
+    if (threadIdx.x < 64) {
+      const int v = threadIdx.x < nseg_t ? segc[threadIdx.x] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if ((int)threadIdx.x >= d) incl += u;
+      }
+      if ((int)threadIdx.x < nseg_t) segv[threadIdx.x] = incl - v;
+    }
+  } else {
+    int carry = 0;
+    for (int c0 = 0; c0 < nseg_t; c0 += NT_R) {
+      const int c = c0 + threadIdx.x;
+      const int v = c < nseg_t ? segc[c] : 0;
+      const int incl = block_incl_scan<NT_R>(v, red);
+      const int tot = red[NT_R / 64];
+      if (c < nseg_t) segv[c] = carry + incl - v;
+      carry += tot;
+      __syncthreads();
+    }
   }
   if (threadIdx.x == 0) {
     rec[0] = 0;  // the candidate counter starts the next call at zero
