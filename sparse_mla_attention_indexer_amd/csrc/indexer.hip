@@ -59,6 +59,37 @@ __device__ __forceinline__ void idx_wait_loads() {
   asm volatile("" ::: "memory");
 }
 
+// The weights of a lane's heads (w < 2^10 by the weight contract): lo[r] for head
+// 8 (r / 4) + 4 half + r % 4, hi[r] for the same + 32. Kept unpacked so that the multiply-adds
+// need no sub-dword operand selection and fuse into v_mad_u32_u24.
+struct HeadW {
+  uint32_t lo[16], hi[16];
+};
+
+// a * b + c with 24-bit operands, one instruction (left to itself the compiler splits it into a
+// multiply and a three-input add, which costs more per product)
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// The score of the lane's key: sum over its 32 heads of ReLU(dot) * w, plus the other lane half's
+// (the other 32 heads). ReLU(dot) <= 2^21 and w < 2^10, so 24-bit multiplies are exact and run at
+// full rate; four independent partial sums keep the chain of dependent adds from setting the pace.
+__device__ __forceinline__ uint32_t relu_weighted_sum(const v16i& acc0, const v16i& acc1,
+                                                      const HeadW& w) {
+  uint32_t ps[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    ps[r & 3] = mad_u24((uint32_t)max(acc0[r], 0), w.lo[r], ps[r & 3]);
+    ps[r & 3] = mad_u24((uint32_t)max(acc1[r], 0), w.hi[r], ps[r & 3]);
+  }
+  const uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  const auto b = __builtin_amdgcn_permlane32_swap(sum, sum, false, false);  // no LDS round trip
+  return (uint32_t)b[0] + (uint32_t)b[1];
+}
+
 // Raw buffer descriptor (stride 0) over `bytes` bytes at `base`: stores at offsets >= bytes are
 // dropped by the hardware, yet count as memory operations like any other.
 typedef int idx_v4s __attribute__((ext_vector_type(4)));
@@ -114,7 +145,7 @@ constexpr int KR = 4;  // key tiles per wave in flight or in use
 __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
                                              int step, const int8_t* __restrict__ q_idx,
                                              const int8_t* __restrict__ k_idx,
-                                             const uint32_t (&wl)[16], int32_t* __restrict__ out_row,
+                                             const HeadW& wl, int32_t* __restrict__ out_row,
                                              int* lh, v4i (*ring)[256]) {
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -164,19 +195,9 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
       acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
     }
   };
-  // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4; ReLU * w summed over them.
-  // ReLU(dot) <= 2^21 and w < 2^10 (the weight contract), so 24-bit multiplies are exact and
-  // run at full rate (a 32-bit multiply is quarter rate); four independent partial sums keep
-  // the chain of dependent adds from setting the pace
+  // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4
   auto epilogue = [&](const v16i& acc0, const v16i& acc1, int i) {
-    uint32_t ps[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
-      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
-    }
-    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    sum += (uint32_t)__shfl_xor((int)sum, 32);
+    const uint32_t sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = s_begin + i * step + col;
     idx_store32(out_rs, half ? 0x7FFFFFF0u : (uint32_t)key * 4u, sum);
     if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
@@ -225,7 +246,7 @@ constexpr int SRING = 3;   // groups in the ring
 __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __restrict__ toks,
                                                    const int8_t* __restrict__ q_idx,
                                                    const int8_t* __restrict__ k_idx,
-                                                   const uint32_t (&wl)[16],
+                                                   const HeadW& wl,
                                                    int32_t* __restrict__ scores, int64_t stride,
                                                    bool hist_on, int (*lhist)[TOPK_BINS],
                                                    v4i (*ring)[256]) {
@@ -273,14 +294,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
   int* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
 
   auto epilogue = [&](const v16i& acc0, const v16i& acc1, int k) {
-    uint32_t ps[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ps[r & 3] += __umul24((uint32_t)max(acc0[r], 0), wl[r] & 0xFFFFu);
-      ps[r & 3] += __umul24((uint32_t)max(acc1[r], 0), wl[r] >> 16);
-    }
-    uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    sum += (uint32_t)__shfl_xor((int)sum, 32);
+    const uint32_t sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = sg.s0 + 32 * k + col;
     __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
     if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
@@ -349,13 +363,13 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  // the weights of this lane's heads, two per register (heads 8*(r/4) + 4*half + r%4 in the low
-  // half, the same + 32 in the high half); w < 2^10 by the weight contract
-  uint32_t wl[16];
+  // the weights of this lane's heads (w < 2^10 by the weight contract)
+  HeadW wl;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int h = 8 * (r >> 2) + 4 * half + (r & 3);
-    wl[r] = ((uint32_t)w[h] & 0xFFFFu) | ((uint32_t)w[32 + h] << 16);
+    wl.lo[r] = (uint32_t)w[h];
+    wl.hi[r] = (uint32_t)w[32 + h];
   }
 
 #pragma unroll 1
