@@ -232,23 +232,28 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
   idx_wait_vmcnt<0>();  // no key load may still be writing this wave's ring when it returns
 }
 
-// ---- query tiles of 2..4 tokens: key tiles shared through LDS ---------------------------------
+// ---- batches with query tiles of several tokens: key tiles shared through LDS -----------------
 // The tokens of one query tile see (almost) the same keys, so the workgroup loads each 32-key
 // tile once, straight into LDS (load-to-LDS, no registers), and every wave reads its B operands
-// from there. Key tiles go through a ring of three groups of four; the loads of group g+2 are
-// issued while group g is scored, and one barrier per group hands them over.
+// from there. Key tiles go through a ring of two groups of four: the loads of group g+1 are
+// issued right after the barrier that opens group g (every wave has then finished group g-1,
+// whose slots they take). The ring and histograms fit 48 KB, so three workgroups share a CU and
+// hide each other's latencies. The LDS histograms count in 16 bits, two bins per word (a
+// workgroup scores at most KEY_CHUNK keys per token and segment, so a count stays below 2^16).
 constexpr int SG = 4;      // key tiles per group
-constexpr int SRING = 3;   // groups in the ring
+constexpr int SRING = 2;   // groups in the ring
 
-// Segment of nq (2..4) tokens against keys [s0, s1). `ring`: SRING * SG tiles of 256 16-byte
-// slots; slot 32 * piece + key holds bytes [16 piece, 16 piece + 16) of the tile's key `key`,
-// so a wave's operand read (32 keys, one piece) is 512 consecutive bytes.
+// Segment of nq (1..4) tokens against keys [s0, s1) (one token: one wave works; such tiles only
+// end a request). `ring`: SRING * SG tiles of 256 16-byte slots; slot 32 * piece + key holds
+// bytes [16 piece, 16 piece + 16) of the tile's key `key`, so a wave's operand read (32 keys, one
+// piece) is 512 consecutive bytes.
 __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __restrict__ toks,
                                                    const int8_t* __restrict__ q_idx,
                                                    const int8_t* __restrict__ k_idx,
                                                    const HeadW& wl,
                                                    int32_t* __restrict__ scores, int64_t stride,
-                                                   bool hist_on, int (*lhist)[TOPK_BINS],
+                                                   bool hist_on,
+                                                   unsigned (*lhist)[TOPK_BINS / 2],
                                                    v4i (*ring)[256]) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -286,18 +291,20 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
     for (int d = 0; d < 4; ++d) idx_lds_load16(src + 32 * d, dst + 64 * d);
   };
   load_group(0);
-  if (ngroup > 1) load_group(1);
 
   int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
   const __amdgpu_buffer_rsrc_t out_rs =
       __builtin_amdgcn_make_buffer_rsrc(out_row, 0, active ? (last + 1) * 4 : 0, 0x00020000);
-  int* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
+  unsigned* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
 
   auto epilogue = [&](const v16i& acc0, const v16i& acc1, int k) {
     const uint32_t sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = sg.s0 + 32 * k + col;
     __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
-    if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
+    if (lh && half == 0 && key <= last) {
+      const int b = topk_bin(sum);
+      atomicAdd(&lh[b >> 1], 1u << (16 * (b & 1)));
+    }
   };
   auto products = [&](int g, int i, v16i& acc0, v16i& acc1) {
     const v4i* kt = ring[(g % SRING) * SG + i];
@@ -326,9 +333,11 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
 
 #pragma unroll 1
   for (int g = 0; g < ngroup; ++g) {
-    // this wave's loads of group g have landed (only group g+1's may still fly), then everyone's
-    if (g + 1 < ngroup) idx_wait_vmcnt<4>(); else idx_wait_vmcnt<0>();
+    // this wave's loads of group g have landed, then everyone's; group g+1 goes into the slots of
+    // group g-1, which every wave has finished
+    idx_wait_vmcnt<0>();
     idx_lds_barrier();
+    if (g + 1 < ngroup) load_group(g + 1);
     if (active) {
       // software pipelined over the wave's tiles of the group: the products of tile u+1 are
       // issued before the ReLU/weight epilogue of tile u, so the matrix cores and the vector
@@ -337,26 +346,25 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
       if (qpw == 1) group_tiles(std::integral_constant<int, SG>{}, g, 0, 1);
       else group_tiles(std::integral_constant<int, SG / 2>{}, g, par, 2);
     }
-    // the slots of group g-1 are free (everyone passed the barrier above): group g+2 goes there
-    if (g + 2 < ngroup) load_group(g + 2);
   }
   idx_wait_vmcnt<0>();
 }
 
-__global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __restrict__ items,
-                                                           const Tok* __restrict__ toks,
-                                                           const int8_t* __restrict__ q_idx,
-                                                           const int8_t* __restrict__ k_idx,
-                                                           const int32_t* __restrict__ w,
-                                                           int32_t* __restrict__ scores,
-                                                           int64_t stride, int* __restrict__ hist) {
-  // LDS, carved per segment: multi-token tiles take SRING * SG key tiles and QT histograms,
-  // single tokens 4 KR key tiles (KR per wave) and one histogram
+// One work item (up to two segments: a front and a back query tile) per workgroup. MULTI: the
+// batch has query tiles of several tokens (shared key tiles, three workgroups per CU); otherwise
+// every tile is one token (decode: each wave streams its own key tiles, two workgroups per CU).
+template <bool MULTI>
+__global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
+    const Item* __restrict__ items, const Tok* __restrict__ toks, const int8_t* __restrict__ q_idx,
+    const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w, int32_t* __restrict__ scores,
+    int64_t stride, int* __restrict__ hist) {
+  // LDS: the key ring, then the histograms (QT packed ones, or one of int counters)
   constexpr int TILE_INTS = 256 * 4;
-  constexpr int MULTI_INTS = SRING * SG * TILE_INTS + QT * TOPK_BINS;
-  constexpr int SINGLE_INTS = 4 * KR * TILE_INTS + TOPK_BINS;
-  __shared__ __attribute__((aligned(16))) int smem[MULTI_INTS > SINGLE_INTS ? MULTI_INTS : SINGLE_INTS];
+  constexpr int RING_TILES = MULTI ? SRING * SG : 4 * KR;
+  constexpr int LDS_INTS = RING_TILES * TILE_INTS + (MULTI ? QT * TOPK_BINS / 2 : TOPK_BINS);
+  __shared__ __attribute__((aligned(16))) int smem[LDS_INTS];
   v4i (*const ring)[256] = reinterpret_cast<v4i (*)[256]>(smem);
+  int* const lhist_base = smem + RING_TILES * TILE_INTS;
   const Item it = items[blockIdx.x];
   // wave-uniform (a scalar): everything derived from it (the query, its score row) stays in
   // scalar registers, as buffer resources must
@@ -379,34 +387,39 @@ __global__ __launch_bounds__(256, 2) void indexer_mfma_kernel(const Item* __rest
     // rows longer than the LDS top-k path also get their score histogram (the last token of the
     // tile has the longest row)
     const bool hist_on = hist != nullptr && toks[sg.q0 + sg.nq - 1].pos + 1 > TOPK_LDS_MAX;
-    int (*const lhist)[TOPK_BINS] = reinterpret_cast<int (*)[TOPK_BINS]>(
-        smem + (sg.nq >= 2 ? SRING * SG : 4 * KR) * TILE_INTS);
+    constexpr int HIST_WORDS = MULTI ? TOPK_BINS / 2 : TOPK_BINS;  // per token
     if (hist_on) {
-      for (int i = threadIdx.x; i < sg.nq * TOPK_BINS; i += 256) (&lhist[0][0])[i] = 0;
+      for (int i = threadIdx.x; i < sg.nq * HIST_WORDS; i += 256) lhist_base[i] = 0;
       __syncthreads();
     }
-    if (sg.nq >= 2) {
-      indexer_shared_seg(sg, toks, q_idx, k_idx, wl, scores, stride, hist_on, lhist, ring);
+    if constexpr (MULTI) {
+      indexer_shared_seg(sg, toks, q_idx, k_idx, wl, scores, stride, hist_on,
+                         reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring);
     } else {
-      // a single query: the 4 waves split its key tiles, each through its own part of the ring
-      const int qpw = 4;
-      const int qi = wave / qpw;
-      const int phase = wave - qi * qpw;
-      const int64_t t = sg.q0 + qi;
+      // one token: the 4 waves split its key tiles, each through its own part of the ring
+      const int64_t t = sg.q0;
       const Tok tk = toks[t];
       int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
-      int* lh = hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
-      indexer_wave(tk, t, sg.s0 + 32 * phase, sg.s1, 32 * qpw, q_idx, k_idx, wl, out_row, lh,
+      int* lh = hist_on ? lhist_base : nullptr;
+      indexer_wave(tk, t, sg.s0 + 32 * wave, sg.s1, 128, q_idx, k_idx, wl, out_row, lh,
                    ring + KR * wave);
     }
-    __syncthreads();  // the ring (and the histogram) are reused by the next segment
+    __syncthreads();  // the ring (and the histograms) are reused by the next segment
     if (hist_on) {
       for (int q = 0; q < sg.nq; ++q) {
         const int64_t t = sg.q0 + q;
         if (toks[t].pos + 1 <= TOPK_LDS_MAX) continue;
         int* g = hist + t * TOPK_BINS;
-        for (int i = threadIdx.x; i < TOPK_BINS; i += 256)
-          if (lhist[q][i]) atomicAdd(&g[topk_hist_slot(i)], lhist[q][i]);
+        const int* lq = lhist_base + q * HIST_WORDS;
+        for (int i = threadIdx.x; i < HIST_WORDS; i += 256) {
+          const unsigned c = (unsigned)lq[i];
+          if (MULTI) {
+            if (c & 0xFFFFu) atomicAdd(&g[topk_hist_slot(2 * i)], (int)(c & 0xFFFFu));
+            if (c >> 16) atomicAdd(&g[topk_hist_slot(2 * i + 1)], (int)(c >> 16));
+          } else if (c) {
+            atomicAdd(&g[topk_hist_slot(i)], (int)c);
+          }
+        }
       }
       __syncthreads();
     }
@@ -452,8 +465,12 @@ hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const i
   if (b.n_items <= 0) return hipSuccess;
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const int64_t stride = compact ? 0 : b.max_kv;
-  hipLaunchKernelGGL(indexer_mfma_kernel, dim3(b.n_items), dim3(256), 0, s, tv.item, tv.tok,
-                     q_idx, k_idx, w, scores, stride, hist);
+  if (b.max_q <= 1)
+    hipLaunchKernelGGL(indexer_mfma_kernel<false>, dim3(b.n_items), dim3(256), 0, s, tv.item,
+                       tv.tok, q_idx, k_idx, w, scores, stride, hist);
+  else
+    hipLaunchKernelGGL(indexer_mfma_kernel<true>, dim3(b.n_items), dim3(256), 0, s, tv.item,
+                       tv.tok, q_idx, k_idx, w, scores, stride, hist);
   return hipGetLastError();
 }
 
