@@ -46,6 +46,9 @@ def lib():
         L.smla_oracle_bf16.argtypes = [ctypes.c_uint16]
         L.smla_oracle_bf16.restype = ctypes.c_double
         L.smla_oracle_dequant_row.argtypes = [P, i32, i32, P]
+        L.smla_oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.smla_oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.smla_oracle_fp8_row_encode.argtypes = [P, P]
         L.smla_oracle_indexer_scores.argtypes = [P, P, P, i32, i32, i64, P]
         L.smla_oracle_topk.argtypes = [P, i64, i32, P, P]
         L.smla_oracle_attend.argtypes = [P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_double,
@@ -77,6 +80,20 @@ def e4m3(code: int) -> float:
 
 def bf16(bits: int) -> float:
     return lib().smla_oracle_bf16(bits)
+
+
+def e4m3_encode(v: float) -> int:
+    """OCP E4M3 code of v, round to nearest-even, saturating at 448."""
+    return int(lib().smla_oracle_e4m3_encode(float(v)))
+
+
+def fp8_row_encode(latent: np.ndarray) -> np.ndarray:
+    """One token's 576 bf16 bit patterns (uint16) -> its 656-byte FP8 row (uint8)."""
+    lat = np.ascontiguousarray(latent, dtype=np.uint16)
+    assert lat.shape == (576,)
+    row = np.zeros(656, np.uint8)
+    lib().smla_oracle_fp8_row_encode(_p(lat), _p(row))
+    return row
 
 
 def dequant_row(row: np.ndarray, fmt: int, D_qk: int) -> np.ndarray:

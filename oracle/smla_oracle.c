@@ -43,6 +43,41 @@ double smla_oracle_bf16(uint16_t bits) {
   return (double)f;
 }
 
+/* Round to nearest-even on the E4M3 grid: exponents -6..8 carry 3 fraction bits, below 2^-6
+ * the grid is the multiples of 2^-9; rint() rounds half to even in the default mode. */
+uint8_t smla_oracle_e4m3_encode(double v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E; /* the largest finite magnitude (S.1111.110) */
+  if (a < 0.015625) return sign | (uint8_t)rint(a * 512.0); /* 0..8; 8 is the code of 2^-6 */
+  int e;
+  const double f = frexp(a, &e); /* a = f * 2^e, 0.5 <= f < 1 */
+  int E = e - 1;                  /* a = (2f) * 2^E, 1 <= 2f < 2 */
+  double m = rint((2.0 * f - 1.0) * 8.0);
+  if (m == 8.0) {
+    m = 0.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && m == 7.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((E + 7) << 3) | (int)m);
+}
+
+int smla_oracle_fp8_row_encode(const uint16_t* latent, uint8_t* row) {
+  for (int b = 0; b < 4; ++b) {
+    double amax = 0.0;
+    for (int d = 128 * b; d < 128 * (b + 1); ++d) amax = fmax(amax, fabs(smla_oracle_bf16(latent[d])));
+    const float scale = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+    for (int d = 128 * b; d < 128 * (b + 1); ++d)
+      row[d] = smla_oracle_e4m3_encode(smla_oracle_bf16(latent[d]) / (double)scale);
+    memcpy(row + 512 + 4 * b, &scale, 4);
+  }
+  for (int d = 0; d < 64; ++d) {
+    row[528 + 2 * d] = (uint8_t)(latent[512 + d] & 0xFF);
+    row[529 + 2 * d] = (uint8_t)(latent[512 + d] >> 8);
+  }
+  return 0;
+}
+
 int smla_oracle_dequant_row(const uint8_t* row, int32_t fmt, int32_t D_qk, double* out) {
   if (!row || !out) return -1;
   if (fmt == 0) {

@@ -19,6 +19,14 @@
  *    in fp64 over the dequantised rows.
  *  - Row dequantisation: bf16 rows decode exactly; 656-byte rows decode
  *      v[d] = e4m3(code[d]) * scale[d / 128] for d < 512 and v[d] = bf16(rope[d - 512]) otherwise.
+ *  - Row encoding (appending a token to the cache), the inverse: a token's 576 bf16 latent values
+ *    become its 656-byte row (the pages size the FP8 latent row at 656 bytes, in FlashMLA's
+ *    fp8_ds_mla format: "Why the numbers work"; their per-token cache budget counts the same 656
+ *    bytes per layer). For each 128-dim block b of the 512 value dims,
+ *      scale_b = binary32(amax_b / 448)   (1 when the block is all zero)
+ *      code_d  = E4M3(v_d / scale_b)      quotient in binary64, rounded to nearest-even,
+ *                                         saturating at 448 (OCP E4M3FN has no infinity)
+ *    then the four scales (little-endian binary32) and the 64 rope dims as stored.
  */
 #ifndef SMLA_ORACLE_H
 #define SMLA_ORACLE_H
@@ -33,6 +41,12 @@ extern "C" {
 double smla_oracle_e4m3(uint8_t code);
 /* bfloat16 bit pattern -> value. */
 double smla_oracle_bf16(uint16_t bits);
+/* Value -> OCP E4M3 ("FN") code, round to nearest-even on 3 mantissa bits (subnormals are
+ * multiples of 2^-9), |v| >= 448 saturating to +-448; the sign of a zero is kept. */
+uint8_t smla_oracle_e4m3_encode(double v);
+/* One token's latent row (576 bf16 bit patterns: 512 value dims, then 64 rope dims) -> its
+ * 656-byte FP8 row (layout above). */
+int smla_oracle_fp8_row_encode(const uint16_t* latent, uint8_t* row);
 /* Dequantise one latent row of `fmt` (0 bf16, 1 fp8-656) into D_qk doubles. */
 int smla_oracle_dequant_row(const uint8_t* row, int32_t fmt, int32_t D_qk, double* out);
 

@@ -63,6 +63,80 @@ def test_fp8_row_layout_hand_built():
     assert np.array_equal(v, exp)
 
 
+def test_e4m3_encode_matches_torch_cast_below_the_saturation_midpoint():
+    # torch's float32 -> float8_e4m3fn cast rounds to nearest-even; it agrees with the encoder for
+    # |v| < 464 (above, torch gives NaN where the cache format saturates). Random values over every
+    # binade, plus every midpoint between neighbouring codes (the ties), plus the codes themselves.
+    rng = np.random.default_rng(7)
+    vals = [rng.uniform(-1, 1, 4000) * 2.0 ** rng.integers(-12, 9, 4000)]
+    grid = np.array([oracle.e4m3(c) for c in range(0x7F)])  # 0 .. 448 ascending
+    vals += [grid, (grid[1:] + grid[:-1]) / 2.0, -(grid[1:] + grid[:-1]) / 2.0]
+    v = np.concatenate(vals).astype(np.float32)
+    v = v[np.abs(v) < 464]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(x)) for x in v], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3(c)) == c, hex(c)
+    # ties go to the even mantissa: 1 + 1/16 -> 1.0, 1 + 3/16 -> 1.25; subnormal ties likewise
+    assert oracle.e4m3_encode(1.0625) == 0x38 and oracle.e4m3_encode(1.1875) == 0x3A
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00 and oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02
+    assert oracle.e4m3_encode(15 * 2.0 ** -10) == 0x08  # rounds up into the smallest normal
+    # saturation at the largest finite magnitude, keeping the sign
+    for v, c in ((448.0, 0x7E), (463.9, 0x7E), (470.0, 0x7E), (1e9, 0x7E), (-500.0, 0xFE)):
+        assert oracle.e4m3_encode(v) == c, v
+    assert oracle.e4m3_encode(-0.0) == 0x80 and oracle.e4m3_encode(0.0) == 0x00
+
+
+def test_fp8_row_encode_hand_built():
+    # block 0 all zero (scale 1, codes 0); block 1 amax 448 (scale exactly 1: every value an
+    # e4m3 point codes exactly); block 2 amax 896 (scale 2); block 3 a single -3.0 (scale 3/448,
+    # its code -448); rope dims copied as stored
+    lat = np.zeros(576, np.float64)
+    lat[128], lat[129], lat[200] = 448.0, -1.5, 0.875
+    lat[256], lat[300] = 896.0, 3.0
+    lat[400] = -3.0
+    lat[512], lat[575] = 1.0, -2.5
+    bits = bf16_bits(lat)
+    row = oracle.fp8_row_encode(bits)
+    scales = row[512:528].view(np.float32)
+    assert scales[0] == 1.0 and scales[1] == 1.0 and scales[2] == 2.0
+    assert scales[3] == np.float32(3.0 / 448.0)
+    assert not row[0:128].any()
+    assert row[128] == 0x7E and row[129] == 0xBC and row[200] == 0x36
+    assert row[256] == 0x7E and row[300] == 0x3C  # 896 / 2 = 448; 3 / 2 = 1.5 = 1.100b x 2^0
+    assert row[400] == 0xFE and not np.delete(row[384:512], 16).any()
+    assert np.array_equal(row[528:656].view(np.uint16), bits[512:576])
+
+
+def test_fp8_row_encode_then_decode_within_half_a_step():
+    # encode N(0,1) rows (plus a tiny and a huge block), decode with the oracle's dequantiser:
+    # every value comes back within half an e4m3 step of its binade times the block scale
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        lat = rng.standard_normal(576)
+        if trial % 4 == 1:
+            lat[128:256] *= 1e-30
+        if trial % 4 == 2:
+            lat[256:384] *= 1e30
+        bits = bf16_bits(lat)
+        x = bf16_vals(bits)
+        row = oracle.fp8_row_encode(bits)
+        back = oracle.dequant_row(row, W.KV_FP8_656, 576)
+        scales = row[512:528].view(np.float32).astype(np.float64)
+        for b in range(4):
+            xs, ys, s = x[128 * b:128 * (b + 1)], back[128 * b:128 * (b + 1)], scales[b]
+            q = np.abs(xs) / s
+            step = np.where(q < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(q, 2.0 ** -6))) - 3))
+            assert np.all(np.abs(ys - xs) <= 0.5 * step * s * (1 + 1e-12)), (trial, b)
+        assert np.array_equal(back[512:], x[512:])
+
+
 def test_fp8_rows_within_e4m3_rounding_of_generated_latents():
     d = W.small_big_dims(n_q=4, cached=60)
     x = W.generate(d, parts=("kv",))
