@@ -39,6 +39,7 @@ DECODE_CONFIGS = (1, 4)
 WORKLOAD_TAGS = {0: "tiny_1x512", 1: "decode_32x65536", 2: "chunk_2048after65536",
                  3: "prefill_32768", 4: "decode_4x4after1048576"}
 STAGES = ("indexer", "topk", "mla", "combine")
+APPEND_BYTES_PER_ROW = 1152 + 656 + 128 + 128 + 8
 
 
 def workload_name(d):
@@ -118,6 +119,41 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def append_measurement(dev, steps):
+    """The cache-append step (smla_kv_append) beside the headline: the decode step's new rows and
+    a bulk append of 65,536 rows (HBM-bound: 2,072 algorithmic bytes per row = 1,152 B bf16 latent
+    in + 656 B FP8 row out + 128 B key in + 128 B key out + 8 B row index), timed with torch
+    events on the current stream the library launches on. Not part of the headline metric."""
+    import torch
+
+    from sparse_mla_attention_indexer_amd import ops
+
+    out = {}
+    R = 1 << 17
+    kv = torch.zeros((R, 656), dtype=torch.uint8, device=dev)
+    k_idx = torch.zeros((R, 128), dtype=torch.int8, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for label, n in (("decode_step", 32), ("bulk", 1 << 16)):
+        lat = torch.randn((n, 576), generator=g).to(torch.bfloat16).to(dev)
+        k_new = torch.randint(-128, 128, (n, 128), generator=g, dtype=torch.int8).to(dev)
+        rows = torch.randperm(R, generator=g)[:n].to(torch.int64).to(dev)
+        for _ in range(3):
+            ops.kv_append(lat, rows, kv, k_new, k_idx)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            ops.kv_append(lat, rows, kv, k_new, k_idx)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        gbs = n * APPEND_BYTES_PER_ROW / (us * 1e-6) / 1e9
+        out[label] = {"rows": n, "us": round(us, 2), "achieved": round(gbs, 1), "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["bytes_per_row"] = APPEND_BYTES_PER_ROW
+    return out
 
 
 def algorithmic(d, positions):
@@ -299,6 +335,8 @@ def main():
         "roofline": roof,
         "mla_roofline": mla_roof,
     }
+    if d.kv_format == W.KV_FP8_656:
+        result["append"] = append_measurement(dev, args.steps)
     if not args.no_cpu_baseline:
         sample = np.arange(d.total_q) if d.total_q <= 32 else np.linspace(0, d.total_q - 1, 32).astype(np.int64)
         print(f"[bench] oracle on {sample.size} tokens", file=sys.stderr, flush=True)

@@ -147,6 +147,26 @@ int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, i
                            size_t ws_bytes, void* stream);
 
 /*
+ * New tokens into the caches (the step before scoring and attention in each decode or prefill
+ * chunk): token i's latent row becomes row rows[i] of the FP8_656 latent cache, and its indexer
+ * key row rows[i] of the key cache. The pages size the latent row at 656 bytes (FlashMLA's
+ * fp8_ds_mla format; "Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why the numbers
+ * work") and count those 656 bytes per token and layer in their cache budget.
+ * latent (device) [n, 576] bf16: 512 value dims, then 64 rope dims.
+ * rows (device) [n] int64: destination rows (distinct; the caller keeps them inside the caches).
+ * kv (device) [R, 656] bytes: row r receives 512 E4M3 codes, 4 fp32 block scales (little-endian,
+ *   value dims 128b..128b+127) and the 64 rope dims as given. Block scale = fp32(amax_b / 448)
+ *   (1 for an all-zero block); code = E4M3(value / scale) with the quotient in fp64, rounded to
+ *   nearest-even, saturated at 448. Values must be finite.
+ * k_new (device, optional) [n, D_I] int8 and k_idx (device) [R, D_I] int8: key i is copied to row
+ *   rows[i] of k_idx; D_I a multiple of 16, at most 1024.
+ * n = 0 is a no-op. Alignment: latent, kv, k_new, k_idx 16 bytes; rows 8 bytes. Asynchronous on
+ * `stream`; the caller owns every buffer.
+ */
+int smla_kv_append(int64_t n, const void* latent, const int8_t* k_new, int32_t D_I,
+                   const int64_t* rows, void* kv, int8_t* k_idx, void* stream);
+
+/*
  * Optional per-stage timing for benchmarks and profilers: while set, the GPU entry points record
  * begin[s] before and end[s] after the launches of stage s on the call's stream, for
  * s = 0 indexer scores, 1 top-k select, 2 sparse MLA, 3 split-KV combine (decode only).

@@ -341,6 +341,26 @@ int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, i
                     ws_bytes, stream, 1);
 }
 
+int smla_kv_append(int64_t n, const void* latent, const int8_t* k_new, int32_t D_I,
+                   const int64_t* rows, void* kv, int8_t* k_idx, void* stream) {
+  g_err.clear();
+  if (n < 0 || n > (int64_t(1) << 33)) return fail(SMLA_E_INVALID, "n=%lld outside [0, 2^33]", (long long)n);
+  if (n == 0) return SMLA_OK;
+  if (!latent || !rows || !kv) return fail(SMLA_E_INVALID, "latent, rows and kv must be non-NULL");
+  if (!aligned(latent, 16) || !aligned(kv, 16) || !aligned(rows, 8))
+    return fail(SMLA_E_INVALID, "latent and kv must be 16-byte aligned, rows 8-byte aligned");
+  if (k_new) {
+    if (!k_idx) return fail(SMLA_E_INVALID, "k_idx must be non-NULL when k_new is given");
+    if (D_I < 16 || D_I > 1024 || D_I % 16)
+      return fail(SMLA_E_UNSUPPORTED, "D_I=%d: indexer keys must be a multiple of 16 bytes, at most 1024", D_I);
+    if (!aligned(k_new, 16) || !aligned(k_idx, 16))
+      return fail(SMLA_E_INVALID, "k_new and k_idx must be 16-byte aligned");
+  }
+  hipError_t e = smla::launch_kv_append(n, latent, rows, kv, k_new, D_I, k_idx,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "kv append launch");
+}
+
 const char* smla_status_str(int status) {
   switch (status) {
     case SMLA_OK: return "SMLA_OK";

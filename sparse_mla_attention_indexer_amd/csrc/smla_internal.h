@@ -143,6 +143,8 @@ int mla_decode_splits(const smla_batch& b, int32_t top_k);
 hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, const int32_t* idx,
                           int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
                           int decode, hipStream_t s);
+hipError_t launch_kv_append(int64_t n, const void* latent, const int64_t* rows, void* kv,
+                            const int8_t* k_new, int32_t D_I, int8_t* k_idx, hipStream_t s);
 hipError_t launch_mla_generic(const smla_batch& b, const void* q, const void* kv, int32_t H,
                               int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
                               float sm_scale, void* out, float* lse, hipStream_t s);

@@ -170,3 +170,26 @@ def sparse_mla(plan: BatchPlan, q, kv, kv_format: int, D_v: int, idx, sm_scale: 
                                      lse.data_ptr() if lse is not None else None,
                                      workspace.data_ptr(), workspace.numel(), _stream(d)))
     return out, lse
+
+
+def kv_append(latent, rows, kv, k_new=None, k_idx=None):
+    """New tokens into the caches: latent [n, 576] bf16 -> FP8 rows kv[rows] ([R, 656] uint8),
+    and (optionally) indexer keys k_new [n, D_I] int8 -> k_idx[rows]. See smla_kv_append."""
+    d = kv.device
+    n = latent.shape[0] if latent.dim() == 2 else -1
+    _req(latent, "latent", torch.bfloat16, (n, 576), d)
+    _req(rows, "rows", torch.int64, (n,), d)
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != 656 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous uint8 [R, 656] tensor")
+    D_I = 0
+    if k_new is not None:
+        if k_idx is None:
+            raise ValueError("k_idx is required with k_new")
+        D_I = k_new.shape[1] if k_new.dim() == 2 else -1
+        _req(k_new, "k_new", torch.int8, (n, D_I), d)
+        if k_idx.dtype != torch.int8 or k_idx.dim() != 2 or k_idx.shape[1] != D_I or not k_idx.is_contiguous():
+            raise ValueError("k_idx must be a contiguous int8 [R, D_I] tensor")
+    check("smla_kv_append",
+          lib().smla_kv_append(n, latent.data_ptr(), k_new.data_ptr() if k_new is not None else None,
+                               D_I, rows.data_ptr(), kv.data_ptr(),
+                               k_idx.data_ptr() if k_idx is not None else None, _stream(d)))

@@ -128,6 +128,19 @@ def test_mla_validation(L):
     del args
 
 
+def test_kv_append_validation(L):
+    assert L.smla_kv_append(0, None, None, 0, None, None, None, None) == _lib.SMLA_OK  # no-op
+    assert L.smla_kv_append(-1, FAKE, None, 0, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_kv_append(4, None, None, 0, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_kv_append(4, FAKE + 8, None, 0, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert "aligned" in _lib.last_error()
+    assert L.smla_kv_append(4, FAKE, FAKE, 128, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert "k_idx" in _lib.last_error()
+    for bad in (8, 24, 2048):
+        rc = L.smla_kv_append(4, FAKE, FAKE, bad, FAKE, FAKE, FAKE, None)
+        assert rc == _lib.SMLA_E_UNSUPPORTED, bad
+
+
 def test_status_strings(L):
     assert _lib.status_str(0) == "SMLA_OK"
     assert _lib.status_str(-3) == "SMLA_E_WORKSPACE"

@@ -239,6 +239,48 @@ def _sampled_full_config(cid, tokens, decode):
     assert (valid.sum(1) == np.minimum(pos + 1, d.top_k)).all()
 
 
+def test_kv_append_rows_bit_exact_against_oracle_encoder():
+    # 301 new tokens (ragged against the 4 rows of a workgroup) into prefilled caches: N(0,1)
+    # rows plus blocks that are all zero, tiny, huge, all negative, and one whose quotients fall
+    # exactly on E4M3 ties; every written row must equal the oracle's encoding byte for byte, and
+    # every other row must be untouched
+    import torch
+
+    import oracle
+    from sparse_mla_attention_indexer_amd import ops
+
+    say("[case] kv append 301 rows")
+    rng = np.random.default_rng(2024)
+    n, R, D_I = 301, 1000, 128
+    lat = rng.standard_normal((n, 576))
+    lat[0] = 0.0
+    lat[1, 128:256] = 0.0
+    lat[2, 256:384] *= 1e-30
+    lat[3, 0:128] *= 1e30
+    lat[4, 384:512] = -np.abs(lat[4, 384:512])
+    lat[5, 0:128] = 0.0
+    lat[5, 0], lat[5, 1], lat[5, 2], lat[5, 3] = 448.0, 1.0625, 1.1875, 3 * 2.0 ** -10  # scale 1
+    lat_t = torch.from_numpy(lat.astype(np.float32)).to(torch.bfloat16)
+    bits = lat_t.view(torch.int16).numpy().view(np.uint16)
+    rows = rng.permutation(R)[:n].astype(np.int64)
+    k_new = rng.integers(-128, 128, (n, D_I), dtype=np.int8)
+    dev = torch.device("cuda:0")
+    kv = torch.full((R, 656), 0xA5, dtype=torch.uint8, device=dev)
+    k_idx = torch.full((R, D_I), 0x5A, dtype=torch.int8, device=dev)
+    ops.kv_append(lat_t.to(dev), torch.from_numpy(rows).to(dev), kv, torch.from_numpy(k_new).to(dev), k_idx)
+    ops.kv_append(lat_t[:0].to(dev), torch.empty(0, dtype=torch.int64, device=dev), kv)  # no-op
+    got_kv, got_k = kv.cpu().numpy(), k_idx.cpu().numpy()
+    for i in range(n):
+        ref = oracle.fp8_row_encode(bits[i])
+        assert np.array_equal(got_kv[rows[i]], ref), (i, np.nonzero(got_kv[rows[i]] != ref)[0][:8])
+        assert np.array_equal(got_k[rows[i]], k_new[i]), i
+    rest = np.setdiff1d(np.arange(R), rows)
+    assert (got_kv[rest] == 0xA5).all() and (got_k[rest] == 0x5A).all()
+    # the special rows decode as expected too
+    assert not got_kv[rows[0], :512].any()
+    assert (got_kv[rows[5], :4] == np.array([0x7E, 0x38, 0x3A, 0x02], np.uint8)).all()
+
+
 def test_config1_decode_full_size():
     _sampled_full_config(1, range(32), decode=True)
 
