@@ -513,10 +513,11 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 }
 
 // Merge split partials by log-sum-exp: one 128-thread block per (token, head), 4 dims per
-// thread; every split's weight first, then all of the thread's partial loads at once. Block b
-// takes token b % n_tok: workgroups are dealt to the XCDs round robin, so with n_tok a multiple
-// of 8 a token's merge runs on the XCD whose L2 holds the partials its splits just wrote (the
-// attention grid puts every split of token t on XCD t % 8 too).
+// thread. The first eight splits' partials go out together with their lse values, so a merge of
+// up to eight splits costs one memory round trip. Block b takes token b % n_tok: workgroups are
+// dealt to the XCDs round robin, so with n_tok a multiple of 8 a token's merge runs on the XCD
+// whose L2 holds the partials its splits just wrote (the attention grid puts every split of
+// token t on XCD t % 8 too).
 
 __global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
@@ -528,28 +529,34 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __rest
   const int64_t th = t * MLA_H + h;
   const float* pl = part_lse + t * nsplit * MLA_H + h;
   const _Float16* po = part_o + (t * nsplit * MLA_H + h) * MLA_DV + 4 * threadIdx.x;
+  v4h v[8];
+  float lj[8];
+  auto load8 = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, nsplit - 1);
+      v[u] = *reinterpret_cast<const v4h*>(po + (int64_t)j * MLA_H * MLA_DV);
+      lj[u] = j0 + u < nsplit ? pl[j * MLA_H] : -INFINITY;
+    }
+  };
+  load8(0);
   float m = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) m = fmaxf(m, pl[j * MLA_H]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m = fmaxf(m, lj[u]);
+  for (int j = 8; j < nsplit; ++j) m = fmaxf(m, pl[j * MLA_H]);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (m != -INFINITY) {
     for (int j0 = 0; j0 < nsplit; j0 += 8) {
-      v4h v[8];
-      float wj[8];
+      if (j0 > 0) load8(j0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = min(j0 + u, nsplit - 1);
-        v[u] = *reinterpret_cast<const v4h*>(po + (int64_t)j * MLA_H * MLA_DV);
-        const float lj = pl[j * MLA_H];
-        wj[u] = j0 + u < nsplit && lj != -INFINITY ? __expf(lj - m) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        wsum += wj[u];
-        acc[0] += wj[u] * (float)v[u][0];
-        acc[1] += wj[u] * (float)v[u][1];
-        acc[2] += wj[u] * (float)v[u][2];
-        acc[3] += wj[u] * (float)v[u][3];
+        const float wj = lj[u] != -INFINITY ? __expf(lj[u] - m) : 0.f;
+        wsum += wj;
+        acc[0] += wj * (float)v[u][0];
+        acc[1] += wj * (float)v[u][1];
+        acc[2] += wj * (float)v[u][2];
+        acc[3] += wj * (float)v[u][3];
       }
     }
   }
