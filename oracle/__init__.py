@@ -50,6 +50,7 @@ def lib():
         L.smla_oracle_e4m3_encode.restype = ctypes.c_uint8
         L.smla_oracle_fp8_row_encode.argtypes = [P, P]
         L.smla_oracle_indexer_scores.argtypes = [P, P, P, i32, i32, i64, P]
+        L.smla_oracle_indexer_scores_fp8.argtypes = [P, P, P, P, i32, i32, i64, P, P]
         L.smla_oracle_topk.argtypes = [P, i64, i32, P, P]
         L.smla_oracle_attend.argtypes = [P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_double,
                                          P, P]
@@ -116,6 +117,25 @@ def indexer_scores(q_tok, keys, w) -> np.ndarray:
     if rc != 0:
         raise OverflowError("indexer score outside [0, 2^31)")
     return out
+
+
+def indexer_scores_fp8(q_tok, keys, k_scale, w):
+    """FP8-key scores of one query token: q_tok [H_I, D_I] and keys [n, D_I] E4M3 codes (uint8),
+    k_scale [n] and w [H_I] float32. Returns (score, magnitude), both float64 [n]."""
+    q_tok = _c(q_tok, np.uint8)
+    keys = _c(keys, np.uint8)
+    k_scale = _c(k_scale, np.float32)
+    w = _c(w, np.float32)
+    H_I, D_I = q_tok.shape
+    n = keys.shape[0]
+    assert keys.shape == (n, D_I) and k_scale.shape == (n,) and w.shape == (H_I,)
+    out = np.empty(n, np.float64)
+    mag = np.empty(n, np.float64)
+    rc = lib().smla_oracle_indexer_scores_fp8(_p(q_tok), _p(keys), _p(k_scale), _p(w), H_I, D_I,
+                                              n, _p(out), _p(mag))
+    if rc != 0:
+        raise ValueError("indexer_scores_fp8: NaN code, or a negative or non-finite weight or scale")
+    return out, mag
 
 
 def topk(scores, top_k: int):

@@ -117,6 +117,40 @@ int smla_oracle_indexer_scores(const int8_t* q_tok, const int8_t* keys, const in
   return bad ? -1 : 0;
 }
 
+int smla_oracle_indexer_scores_fp8(const uint8_t* q_tok, const uint8_t* keys, const float* k_scale,
+                                   const float* w, int32_t H_I, int32_t D_I, int64_t n,
+                                   double* out, double* abs_out) {
+  /* every E4M3 value is a multiple of 2^-9 below 2^9, so each product is a multiple of 2^-18
+   * below 2^18 and a sum of D_I <= 2^16 of them needs at most 52 bits: exact in binary64 */
+  if (D_I < 1 || D_I > 65536 || H_I < 1) return -1;
+  for (int32_t h = 0; h < H_I; ++h)
+    if (!(w[h] >= 0.0f) || !isfinite(w[h])) return -1;
+  for (int64_t i = 0; i < (int64_t)H_I * D_I; ++i)
+    if (isnan(smla_oracle_e4m3(q_tok[i]))) return -1;
+  for (int64_t s = 0; s < n; ++s) {
+    const uint8_t* k = keys + s * D_I;
+    const double scale = (double)k_scale[s];
+    if (!(scale >= 0.0) || !isfinite(scale)) return -1;
+    double acc = 0.0, mag = 0.0;
+    for (int32_t h = 0; h < H_I; ++h) {
+      const uint8_t* qh = q_tok + (int64_t)h * D_I;
+      double dot = 0.0, dabs = 0.0;
+      for (int32_t d = 0; d < D_I; ++d) {
+        const double kv = smla_oracle_e4m3(k[d]);
+        if (isnan(kv)) return -1;
+        const double prod = smla_oracle_e4m3(qh[d]) * kv;
+        dot += prod;
+        dabs += fabs(prod);
+      }
+      acc += (double)w[h] * (dot > 0.0 ? dot : 0.0);
+      mag += (double)w[h] * dabs;
+    }
+    out[s] = scale * acc;
+    if (abs_out) abs_out[s] = scale * mag;
+  }
+  return 0;
+}
+
 typedef struct {
   int64_t score;
   int64_t s;

@@ -55,6 +55,19 @@ int smla_oracle_dequant_row(const uint8_t* row, int32_t fmt, int32_t D_qk, doubl
 int smla_oracle_indexer_scores(const int8_t* q_tok, const int8_t* keys, const int32_t* w,
                                int32_t H_I, int32_t D_I, int64_t n, int64_t* out);
 
+/* FP8 indexer keys (the pages' deployed key: 128 E4M3 values and one binary32 scale per token,
+ * 132 bytes; "Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why the numbers work").
+ * Scores of one query token (q_tok [H_I, D_I] E4M3 codes) against keys [n, D_I] (E4M3 codes)
+ * with per-key scales k_scale [n] and per-head weights w [H_I] (binary32, >= 0):
+ *   score(s) = k_scale[s] * sum_h w[h] * max(0, sum_d e4m3(q[h,d]) * e4m3(k[s,d]))
+ * in binary64, where every dot product is exact. out [n]; abs_out [n] (optional) receives
+ * k_scale[s] * sum_h w[h] * sum_d |e4m3(q[h,d]) * e4m3(k[s,d])|, the magnitude against which a
+ * differently ordered or narrower accumulation is judged. Returns -1 on a NaN code or on a
+ * weight or scale that is negative or not finite. */
+int smla_oracle_indexer_scores_fp8(const uint8_t* q_tok, const uint8_t* keys, const float* k_scale,
+                                   const float* w, int32_t H_I, int32_t D_I, int64_t n,
+                                   double* out, double* abs_out);
+
 /* Exact top-k of scores[0..n) by (score desc, index asc). idx/score [top_k], in that order;
  * slots past min(n, top_k) hold idx -1 and score -1. */
 int smla_oracle_topk(const int64_t* scores, int64_t n, int32_t top_k, int32_t* idx,

@@ -235,6 +235,73 @@ def test_indexer_and_topk_hand_worked_example():
         assert list(zip(idx.tolist(), sc.tolist())) == pairs
 
 
+# ---- indexer with FP8 keys (128 E4M3 values + a binary32 scale per token) -------------------
+
+def _to_e4m3(values):
+    """E4M3 codes of values that the format holds exactly, by torch's cast (independent of the
+    oracle's own encoder)."""
+    return torch.from_numpy(np.asarray(values, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_fp8_indexer_integer_codes_equal_the_int8_indexer():
+    # integers in [-8, 7] are exact E4M3 values; with unit key scales and integer weights the FP8
+    # score is the int8 score (a separately pinned function) exactly
+    rng = np.random.default_rng(21)
+    q, k, w = _rand_indexer(rng, 64, 128, 400)
+    ref = oracle.indexer_scores(q, k, w)
+    got, mag = oracle.indexer_scores_fp8(_to_e4m3(q), _to_e4m3(k), np.ones(400, np.float32),
+                                         w.astype(np.float32))
+    assert np.array_equal(got, ref.astype(np.float64))
+    ref_mag = np.abs(k.astype(np.int64)[:, None, :] * q.astype(np.int64)[None]).sum(-1) @ w.astype(np.int64)
+    assert np.array_equal(mag, ref_mag.astype(np.float64))
+
+
+def test_fp8_indexer_hand_built():
+    # head 0: dot = 1.5*0.5 - 2*0.25 + 0*3 + 0.5*2 = 1.25, weight 2; head 1: dot = -5.75, weight 5;
+    # key scale 0.75: score = 0.75 * 2 * 1.25 = 1.875, magnitude = 0.75 * (2 * 2.25 + 5 * 5.75)
+    q = _to_e4m3([[1.5, -2.0, 0.0, 0.5], [-1.0, -1.0, -1.0, -1.0]])
+    k = _to_e4m3([[0.5, 0.25, 3.0, 2.0]])
+    got, mag = oracle.indexer_scores_fp8(q, k, np.array([0.75], np.float32), np.array([2.0, 5.0], np.float32))
+    assert got.tolist() == [1.875]
+    assert mag.tolist() == [24.9375]
+
+
+def test_fp8_indexer_random_codes_match_float64_matmul():
+    # every code but NaN, subnormals and +-448 included; numpy's float64 matmul over torch's
+    # decoding (each dot product is exact in binary64, so only the head sum may round)
+    rng = np.random.default_rng(5)
+    H, D, n = 16, 128, 64
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q = rng.choice(codes, size=(H, D))
+    k = rng.choice(codes, size=(n, D))
+    scale = rng.uniform(0.01, 4.0, n).astype(np.float32)
+    w = rng.uniform(0.0, 2.0, H).astype(np.float32)
+    dots = _e4m3_values(k) @ _e4m3_values(q).T  # [n, H]
+    ref = scale.astype(np.float64) * (np.maximum(dots, 0.0) @ w.astype(np.float64))
+    got, mag = oracle.indexer_scores_fp8(q, k, scale, w)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=0)
+    assert (mag >= np.abs(got)).all()
+
+
+def test_fp8_indexer_rejects_nan_codes_and_bad_weights():
+    q = _to_e4m3(np.ones((2, 4)))
+    k = _to_e4m3(np.ones((3, 4)))
+    ok_s, ok_w = np.ones(3, np.float32), np.ones(2, np.float32)
+    oracle.indexer_scores_fp8(q, k, ok_s, ok_w)
+    bad_k = k.copy()
+    bad_k[1, 2] = 0x7F
+    with pytest.raises(ValueError):
+        oracle.indexer_scores_fp8(q, bad_k, ok_s, ok_w)
+    with pytest.raises(ValueError):
+        oracle.indexer_scores_fp8(q, k, ok_s, np.array([1.0, -1.0], np.float32))
+    with pytest.raises(ValueError):
+        oracle.indexer_scores_fp8(q, k, np.array([1.0, np.inf, 1.0], np.float32), ok_w)
+
+
 # ---- top-k -------------------------------------------------------------------------------
 
 def test_topk_short_prefix_takes_everything():
