@@ -117,6 +117,37 @@ int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int
                              int32_t* idx, int32_t* score, void* ws, size_t ws_bytes,
                              void* stream);
 
+/*
+ * Indexer scores over FP8 keys, full matrix (parity and debugging; O(total_q * max_kv) memory).
+ * The pages' deployed indexer key is 128 E4M3 values plus one fp32 scale per token, 132 bytes
+ * ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why the numbers work"):
+ *   score(t, s) = k_scale[s] * sum_h w[t,h] * ReLU(sum_d q[t,h,d] * k[s,d])
+ * q (device) [total_q, H_I, D_I] OCP E4M3 codes, 16-byte aligned; k (device) [total_rows, D_I]
+ * E4M3 codes, 16-byte aligned; k_scale (device) [total_rows] fp32 >= 0; w (device)
+ * [total_q, H_I] fp32 >= 0, per query token (a query's own scale folds into it).
+ * The products are exact; each head's dot product is summed by the FP8 matrix cores, whose
+ * sums are not IEEE-rounded fp32 (errors of order 2^-18 of the sum of |products| occur); the
+ * head sum and the scale are fp32. scores (device, 16-byte aligned) [total_q, max_kv] fp32:
+ * score(t, s) for s <= p, -1.0f for p < s < max_kv. Scores are >= +0 for valid inputs; NaN
+ * codes (0x7F, 0xFF) or negative or non-finite w or k_scale give unspecified scores, never a
+ * fault. Supported (H_I, D_I): (64, 128) only (SMLA_E_UNSUPPORTED otherwise).
+ */
+int smla_indexer_scores_fp8(const smla_batch* b, const uint8_t* q, const uint8_t* k,
+                            const float* k_scale, const float* w, int32_t H_I, int32_t D_I,
+                            float* scores, void* stream);
+
+/*
+ * FP8-key scores followed by the exact per-query top-k of those fp32 scores (larger score first,
+ * ties to the lower index), with the contract of smla_indexer_scores_topk otherwise: idx
+ * [total_q, top_k] ascending with -1 padding; score (optional) [total_q, top_k] fp32, -1.0f on
+ * padding. ws: smla_indexer_topk_workspace_bytes(b, 64, 128, top_k) bytes, zero-filled before
+ * its first use; one workspace serves both key formats (calls must not overlap).
+ */
+int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const uint8_t* k,
+                                 const float* k_scale, const float* w, int32_t H_I, int32_t D_I,
+                                 int32_t top_k, int32_t* idx, float* score, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* Workspace for the sparse-MLA entry points (decode needs split partials; prefill none). */
 size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v,
                                        int32_t top_k, int32_t decode);

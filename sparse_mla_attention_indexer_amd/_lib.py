@@ -27,6 +27,8 @@ EXPORTS = (
     "smla_indexer_scores",
     "smla_indexer_topk_workspace_bytes",
     "smla_indexer_scores_topk",
+    "smla_indexer_scores_fp8",
+    "smla_indexer_scores_topk_fp8",
     "smla_sparse_mla_workspace_bytes",
     "smla_sparse_mla_prefill",
     "smla_sparse_mla_decode",
@@ -78,6 +80,8 @@ def lib():
         L.smla_indexer_topk_workspace_bytes.argtypes = [BP, i32, i32, i32]
         L.smla_indexer_topk_workspace_bytes.restype = sz
         L.smla_indexer_scores_topk.argtypes = [BP, P, P, P, i32, i32, i32, P, P, P, sz, P]
+        L.smla_indexer_scores_fp8.argtypes = [BP, P, P, P, P, i32, i32, P, P]
+        L.smla_indexer_scores_topk_fp8.argtypes = [BP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
         L.smla_sparse_mla_workspace_bytes.argtypes = [BP, i32, i32, i32, i32]
         L.smla_sparse_mla_workspace_bytes.restype = sz
         for fn in ("smla_sparse_mla_prefill", "smla_sparse_mla_decode"):

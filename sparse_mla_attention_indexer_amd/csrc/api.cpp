@@ -294,6 +294,63 @@ int smla_indexer_scores_topk(const smla_batch* b, const int8_t* q_idx, const int
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k launch");
 }
 
+static int check_indexer_fp8_args(const smla_batch* b, const uint8_t* q, const uint8_t* k,
+                                  const float* k_scale, const float* w, int32_t H_I, int32_t D_I) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!q || !k || !k_scale || !w) return fail(SMLA_E_INVALID, "q, k, k_scale and w must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(k_scale, 4) || !aligned(w, 4))
+    return fail(SMLA_E_INVALID, "q and k must be 16-byte aligned, k_scale and w 4-byte aligned");
+  if (H_I != 64 || D_I != 128)
+    return fail(SMLA_E_UNSUPPORTED, "FP8 indexer shape H_I=%d D_I=%d unsupported (64x128 only)", H_I, D_I);
+  return SMLA_OK;
+}
+
+int smla_indexer_scores_fp8(const smla_batch* b, const uint8_t* q, const uint8_t* k,
+                            const float* k_scale, const float* w, int32_t H_I, int32_t D_I,
+                            float* scores, void* stream) {
+  g_err.clear();
+  int rc = check_indexer_fp8_args(b, q, k, k_scale, w, H_I, D_I);
+  if (rc) return rc;
+  if (!scores || !aligned(scores, 16)) return fail(SMLA_E_INVALID, "scores must be non-NULL, 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* out = reinterpret_cast<int32_t*>(scores);
+  hipError_t e = smla::launch_fill_i32(out, (int64_t)b->total_q * b->max_kv, (int32_t)0xBF800000u, s);
+  if (e == hipSuccess) e = smla::launch_indexer_fp8(*b, q, k, k_scale, w, out, 0, nullptr, s);
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "indexer launch");
+}
+
+int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const uint8_t* k,
+                                 const float* k_scale, const float* w, int32_t H_I, int32_t D_I,
+                                 int32_t top_k, int32_t* idx, float* score, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_indexer_fp8_args(b, q, k, k_scale, w, H_I, D_I);
+  if (rc) return rc;
+  if (top_k < 1 || top_k > smla::TOPK_MAX_K)
+    return fail(SMLA_E_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, smla::TOPK_MAX_K);
+  if (b->max_kv > (int64_t)smla::TOPK_SEG * smla::TOPK_SEG_MAX)
+    return fail(SMLA_E_UNSUPPORTED, "kv_len %lld above the top-k limit %lld", (long long)b->max_kv,
+                (long long)smla::TOPK_SEG * smla::TOPK_SEG_MAX);
+  if (!idx || !aligned(idx, 4) || (score && !aligned(score, 4)))
+    return fail(SMLA_E_INVALID, "idx must be non-NULL; idx and score 4-byte aligned");
+  const size_t need = smla_indexer_topk_workspace_bytes(b, H_I, D_I, top_k);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return fail(SMLA_E_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* scores = static_cast<int32_t*>(ws);
+  void* tws = static_cast<char*>(ws) + smla::align_up(sizeof(int32_t) * (size_t)b->total_cand, 256);
+  const smla::TopkWs tw = smla::topk_workspace(*b, tws);
+  smla::mark_stage(smla::STAGE_INDEXER, false, s);
+  hipError_t e = smla::launch_indexer_fp8(*b, q, k, k_scale, w, scores, 1, tw.hist, s);
+  smla::mark_stage(smla::STAGE_INDEXER, true, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  smla::mark_stage(smla::STAGE_TOPK, false, s);
+  e = smla::launch_topk(*b, scores, top_k, idx, reinterpret_cast<int32_t*>(score), tw, s, true);
+  smla::mark_stage(smla::STAGE_TOPK, true, s);
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k launch");
+}
+
 size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v, int32_t top_k,
                                        int32_t decode) {
   if (!b || b->total_q < 1 || top_k < 1) return 0;

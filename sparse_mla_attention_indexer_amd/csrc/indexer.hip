@@ -12,6 +12,12 @@
 // half h covers dims [64h, 64h+64)), and the query fragments use the same permutation. The
 // ReLU * w head reduction runs in the accumulator registers, then across the two lane halves.
 //
+// FP8 keys (the pages' deployed key: 128 E4M3 values and one fp32 scale per token, 132 bytes;
+// section "Why the numbers work") take the same kernels with v_mfma_f32_32x32x64_f8f6f4 (two
+// 64-dim k-steps instead of four 32-dim ones, the same bytes per lane), fp32 accumulators, fp32
+// per-token head weights and the key's scale applied to the head sum (a positive factor passes
+// through the ReLU). The scales of a key tile ride with its keys into LDS.
+//
 // Work is planned on the host (smla_batch_build): query tiles of up to 4 tokens are paired
 // front with back (tile i with tile n-1-i), the pages' load-balanced chunk pairing applied to
 // causal query tiles on one GPU, and each pair's combined key range is cut into equal chunks.
@@ -22,7 +28,9 @@
 namespace smla {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,6 +98,55 @@ __device__ __forceinline__ uint32_t relu_weighted_sum(const v16i& acc0, const v1
   return (uint32_t)b[0] + (uint32_t)b[1];
 }
 
+// FP8 keys: fp32 weights of a lane's heads (same head order as HeadW), per query token.
+struct HeadWF {
+  float lo[16], hi[16];
+};
+
+__device__ __forceinline__ HeadWF load_head_wf(const float* w_tok) {
+  const int half = (threadIdx.x & 63) >> 5;
+  HeadWF wl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 8 * (r >> 2) + 4 * half + (r & 3);
+    wl.lo[r] = w_tok[h];
+    wl.hi[r] = w_tok[32 + h];
+  }
+  return wl;
+}
+
+// ReLU of an fp32 value as one integer max on its bits: every negative value (-0 included) has
+// the sign bit set and becomes +0. (A float max would first quiet the operand: two instructions.)
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// FP8 keys: the lane's key score before its scale, sum over the 64 heads of ReLU(dot) * w in fp32
+// (four partial sums from +0, so the result is never -0).
+__device__ __forceinline__ float relu_weighted_sum_f(const v16f& acc0, const v16f& acc1,
+                                                     const HeadWF& w) {
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    ps[r & 3] = __builtin_fmaf(relu_bits(acc0[r]), w.lo[r], ps[r & 3]);
+    ps[r & 3] = __builtin_fmaf(relu_bits(acc1[r]), w.hi[r], ps[r & 3]);
+  }
+  const float sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, sum),
+                                                  __builtin_bit_cast(unsigned, sum), false, false);
+  return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
+// One E4M3 x E4M3 step over 64 dims: lane half h supplies the same 32 bytes (dims) of its head
+// and of its key, so the contraction pairs equal dims whatever the instruction's k order.
+__device__ __forceinline__ v16f mfma_f8(const v4i& a0, const v4i& a1, const v4i& b0, const v4i& b1,
+                                        const v16f& c) {
+  const v8i a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8i b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  // format 0 (E4M3) for both operands; no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Raw buffer descriptor (stride 0) over `bytes` bytes at `base`: stores at offsets >= bytes are
 // dropped by the hardware, yet count as memory operations like any other.
 typedef int idx_v4s __attribute__((ext_vector_type(4)));
@@ -133,6 +190,21 @@ __device__ __forceinline__ void idx_lds_load16(const void* g, void* lds) {
       : "memory");
 }
 
+// As idx_lds_load16 with 4 bytes per lane (lane l's dword lands at lds + 4 l).
+__device__ __forceinline__ void idx_lds_load4(const void* g, void* lds) {
+  const unsigned a = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(a)
+      : "memory");
+}
+
 // ---- single-token query tiles: each wave streams its own key tiles through LDS ----------------
 // One wave: query token t against key tiles s = s_begin, s_begin + step, ... < s_end, s <= p.
 // Key tiles reach LDS by the load-to-LDS path in whole 128-byte lines (eight lanes per key, one
@@ -140,13 +212,18 @@ __device__ __forceinline__ void idx_lds_load16(const void* g, void* lds) {
 // piece P (16 bytes) of key c is 8 c + (P ^ ((c >> 1) & 7)), which keeps the B-operand reads
 // (32 keys, one piece) free of bank conflicts. The products of tile i+1 are issued before the
 // epilogue of tile i. `lh` (LDS, optional) receives the histogram code of every score.
+// F8: a fifth load per tile brings the tile's 32 key scales into `scl` (one slot per ring tile).
 constexpr int KR = 4;  // key tiles per wave in flight or in use
 
+template <bool F8>
 __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_begin, int s_end,
                                              int step, const int8_t* __restrict__ q_idx,
                                              const int8_t* __restrict__ k_idx,
-                                             const HeadW& wl, int32_t* __restrict__ out_row,
-                                             int* lh, v4i (*ring)[256]) {
+                                             const float* __restrict__ k_scale,
+                                             const HeadW& wl, const float* __restrict__ w_f,
+                                             int32_t* __restrict__ out_row,
+                                             int* lh, v4i (*ring)[256], float (*scl)[64]) {
+  using Acc = std::conditional_t<F8, v16f, v16i>;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -161,6 +238,8 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
+  HeadWF wf;
+  if constexpr (F8) wf = load_head_wf(w_f + t * IDX_H);
   idx_wait_loads();  // the fragments are in before any key load goes out
 
   // Scores go out through a buffer resource whose range ends at key `last`: the hardware drops
@@ -169,6 +248,7 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
   // operations exactly.
   const idx_v4s out_rs = idx_rsrc(out_row, (last + 1) * 4);
   const int8_t* kbase = k_idx + tk.row_start * IDX_D;
+  const float* sbase = F8 ? k_scale + tk.row_start : nullptr;
   const int ntile = (last - s_begin) / step + 1;
   const int dkey = lane >> 3, dpc = lane & 7;  // load lanes: key 8d + dkey, slot piece dpc
   auto dma = [&](int i) {  // tile i (past the end: clamped keys, never scored)
@@ -180,52 +260,66 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
       const int key = min(s + c, last);
       idx_lds_load16(kbase + (int64_t)key * IDX_D + 16 * (dpc ^ ((c >> 1) & 7)), dst + 64 * d);
     }
+    if constexpr (F8) idx_lds_load4(sbase + min(s + (lane & 31), last), scl[i % KR]);
   };
   auto placeholder_store = [&]() { idx_store32(out_rs, 0x7FFFFFF0u, 0u); };
-  auto products = [&](int i, v16i& acc0, v16i& acc1) {
+  auto products = [&](int i, Acc& acc0, Acc& acc1) {
     const v4i* kt = ring[i % KR];
     v4i kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kt[8 * col + ((4 * half + j) ^ ((col >> 1) & 7))];
-    acc0 = v16i{};
-    acc1 = v16i{};
+    acc0 = Acc{};
+    acc1 = Acc{};
+    if constexpr (F8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+      for (int j = 0; j < 4; j += 2) {
+        acc0 = mfma_f8(qa[0][j], qa[0][j + 1], kb[j], kb[j + 1], acc0);
+        acc1 = mfma_f8(qa[1][j], qa[1][j + 1], kb[j], kb[j + 1], acc1);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+      }
     }
   };
   // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4
-  auto epilogue = [&](const v16i& acc0, const v16i& acc1, int i) {
-    const uint32_t sum = relu_weighted_sum(acc0, acc1, wl);
+  auto epilogue = [&](const Acc& acc0, const Acc& acc1, int i) {
+    uint32_t sum;
+    if constexpr (F8)
+      sum = __builtin_bit_cast(uint32_t, relu_weighted_sum_f(acc0, acc1, wf) * scl[i % KR][col]);
+    else
+      sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = s_begin + i * step + col;
     idx_store32(out_rs, half ? 0x7FFFFFF0u : (uint32_t)key * 4u, sum);
-    if (lh && half == 0 && key <= last) atomicAdd(&lh[topk_bin(sum)], 1);
+    if (lh && half == 0 && key <= last) atomicAdd(&lh[F8 ? topk_fbin(sum) : topk_bin(sum)], 1);
   };
 
   // Prologue: tiles 0 .. KR-2 with a placeholder store after each, as if earlier steps had run;
   // then step i: load tile i+KR-1, wait for tile i+1 (after its loads: one store, then tile
-  // i+2's loads and a store, ..., tile i+KR-1's loads = 5 (KR-2) operations), products of tile
-  // i+1, epilogue of tile i.
+  // i+2's loads and a store, ..., tile i+KR-1's loads = 5 (KR-2) operations; 6 (KR-2) with the
+  // scale loads), products of tile i+1, epilogue of tile i.
   static_assert(KR == 4, "wait counts below assume four tiles");
+  constexpr int OPS = F8 ? 6 : 5;  // memory operations per tile and step
   dma(0);
   placeholder_store();
   dma(1);
   placeholder_store();
   dma(2);
   placeholder_store();
-  idx_wait_vmcnt<11>();  // tile 0: after it, a store, tile 1, a store, tile 2, a store
-  v16i a0[2], a1[2];
+  idx_wait_vmcnt<2 * OPS + 1>();  // tile 0: after it, a store, tile 1, a store, tile 2, a store
+  Acc a0[2], a1[2];
   products(0, a0[0], a1[0]);
 #pragma unroll 1
   for (int i = 0; i < ntile; i += 2) {
     dma(i + 3);
-    idx_wait_vmcnt<10>();
+    idx_wait_vmcnt<2 * OPS>();
     if (i + 1 < ntile) products(i + 1, a0[1], a1[1]);
     epilogue(a0[0], a1[0], i);
     if (i + 1 >= ntile) break;
     dma(i + 4);
-    idx_wait_vmcnt<10>();
+    idx_wait_vmcnt<2 * OPS>();
     if (i + 2 < ntile) products(i + 2, a0[0], a1[0]);
     epilogue(a0[1], a1[1], i + 1);
   }
@@ -247,14 +341,18 @@ constexpr int SRING = 2;   // groups in the ring
 // end a request). `ring`: SRING * SG tiles of 256 16-byte slots; slot 32 * piece + key holds
 // bytes [16 piece, 16 piece + 16) of the tile's key `key`, so a wave's operand read (32 keys, one
 // piece) is 512 consecutive bytes.
+// F8: each wave's key load also brings its tile's 32 key scales into `scl`.
+template <bool F8>
 __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __restrict__ toks,
                                                    const int8_t* __restrict__ q_idx,
                                                    const int8_t* __restrict__ k_idx,
-                                                   const HeadW& wl,
+                                                   const float* __restrict__ k_scale,
+                                                   const HeadW& wl, const float* __restrict__ w_f,
                                                    int32_t* __restrict__ scores, int64_t stride,
                                                    bool hist_on,
                                                    unsigned (*lhist)[TOPK_BINS / 2],
-                                                   v4i (*ring)[256]) {
+                                                   v4i (*ring)[256], float (*scl)[64]) {
+  using Acc = std::conditional_t<F8, v16f, v16i>;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -278,10 +376,13 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
+  HeadWF wf;
+  if constexpr (F8) wf = load_head_wf(w_f + t * IDX_H);
   idx_wait_loads();  // the fragments are in before any key load goes out
 
   // key loads: wave w loads tile SG*g + w of group g; instruction d covers slots 64d .. 64d+63
   const int8_t* kbase = k_idx + tk.row_start * IDX_D + 16 * (2 * 0 + half);
+  const float* sbase = F8 ? k_scale + tk.row_start : nullptr;
   auto load_group = [&](int g) {
     const int k = SG * g + wave;
     const int key = min(sg.s0 + 32 * k + col, kmax);  // clamped: never past the visible rows
@@ -289,6 +390,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
     v4i* dst = ring[(g % SRING) * SG + wave];
 #pragma unroll
     for (int d = 0; d < 4; ++d) idx_lds_load16(src + 32 * d, dst + 64 * d);
+    if constexpr (F8) idx_lds_load4(sbase + key, scl[(g % SRING) * SG + wave]);
   };
   load_group(0);
 
@@ -297,31 +399,44 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
       __builtin_amdgcn_make_buffer_rsrc(out_row, 0, active ? (last + 1) * 4 : 0, 0x00020000);
   unsigned* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
 
-  auto epilogue = [&](const v16i& acc0, const v16i& acc1, int k) {
-    const uint32_t sum = relu_weighted_sum(acc0, acc1, wl);
+  auto epilogue = [&](const Acc& acc0, const Acc& acc1, int k) {
+    uint32_t sum;
+    if constexpr (F8)
+      sum = __builtin_bit_cast(uint32_t, relu_weighted_sum_f(acc0, acc1, wf) *
+                                             scl[((k / SG) % SRING) * SG + k % SG][col]);
+    else
+      sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = sg.s0 + 32 * k + col;
     __builtin_amdgcn_raw_buffer_store_b32(sum, out_rs, half ? 0x7FFFFFF0 : key * 4, 0, 0);
     if (lh && half == 0 && key <= last) {
-      const int b = topk_bin(sum);
+      const int b = F8 ? topk_fbin(sum) : topk_bin(sum);
       atomicAdd(&lh[b >> 1], 1u << (16 * (b & 1)));
     }
   };
-  auto products = [&](int g, int i, v16i& acc0, v16i& acc1) {
+  auto products = [&](int g, int i, Acc& acc0, Acc& acc1) {
     const v4i* kt = ring[(g % SRING) * SG + i];
     v4i kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kt[32 * (4 * half + j) + col];
-    acc0 = v16i{};
-    acc1 = v16i{};
+    acc0 = Acc{};
+    acc1 = Acc{};
+    if constexpr (F8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+      for (int j = 0; j < 4; j += 2) {
+        acc0 = mfma_f8(qa[0][j], qa[0][j + 1], kb[j], kb[j + 1], acc0);
+        acc1 = mfma_f8(qa[1][j], qa[1][j + 1], kb[j], kb[j + 1], acc1);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[0][j], kb[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[1][j], kb[j], acc1, 0, 0, 0);
+      }
     }
   };
   auto group_tiles = [&](auto ntw, int g, int first, int stride) {
     constexpr int NTW = decltype(ntw)::value;
-    v16i a0[2], a1[2];
+    Acc a0[2], a1[2];
     products(g, first, a0[0], a1[0]);
 #pragma unroll
     for (int u = 1; u < NTW; ++u) {
@@ -353,31 +468,41 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
 // One work item (up to two segments: a front and a back query tile) per workgroup. MULTI: the
 // batch has query tiles of several tokens (shared key tiles, three workgroups per CU); otherwise
 // every tile is one token (decode: each wave streams its own key tiles, two workgroups per CU).
-template <bool MULTI>
+// F8: FP8 keys (q and k as E4M3 codes, k_scale per key, fp32 weights per query token, scores as
+// fp32 bit patterns); otherwise int8 keys and int32 weights shared by every token.
+template <bool MULTI, bool F8>
 __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
     const Item* __restrict__ items, const Tok* __restrict__ toks, const int8_t* __restrict__ q_idx,
-    const int8_t* __restrict__ k_idx, const int32_t* __restrict__ w, int32_t* __restrict__ scores,
-    int64_t stride, int* __restrict__ hist) {
-  // LDS: the key ring, then the histograms (QT packed ones, or one of int counters)
+    const int8_t* __restrict__ k_idx, const float* __restrict__ k_scale, const void* __restrict__ w,
+    int32_t* __restrict__ scores, int64_t stride, int* __restrict__ hist) {
+  // LDS: the key ring, then the histograms (QT packed ones, or one of int counters), then (F8)
+  // one slot of 64 key scales per ring tile
   constexpr int TILE_INTS = 256 * 4;
   constexpr int RING_TILES = MULTI ? SRING * SG : 4 * KR;
-  constexpr int LDS_INTS = RING_TILES * TILE_INTS + (MULTI ? QT * TOPK_BINS / 2 : TOPK_BINS);
+  constexpr int HIST_INTS = MULTI ? QT * TOPK_BINS / 2 : TOPK_BINS;
+  constexpr int LDS_INTS = RING_TILES * TILE_INTS + HIST_INTS + (F8 ? RING_TILES * 64 : 0);
   __shared__ __attribute__((aligned(16))) int smem[LDS_INTS];
   v4i (*const ring)[256] = reinterpret_cast<v4i (*)[256]>(smem);
   int* const lhist_base = smem + RING_TILES * TILE_INTS;
+  float (*const scl)[64] = reinterpret_cast<float (*)[64]>(lhist_base + HIST_INTS);
+  const float* const w_f = static_cast<const float*>(w);
   const Item it = items[blockIdx.x];
   // wave-uniform (a scalar): everything derived from it (the query, its score row) stays in
   // scalar registers, as buffer resources must
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  // the weights of this lane's heads (w < 2^10 by the weight contract)
+  // the weights of this lane's heads (w < 2^10 by the weight contract; F8: per token, loaded
+  // with the token's query)
   HeadW wl;
+  if constexpr (!F8) {
+    const int32_t* w_i = static_cast<const int32_t*>(w);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int h = 8 * (r >> 2) + 4 * half + (r & 3);
-    wl.lo[r] = (uint32_t)w[h];
-    wl.hi[r] = (uint32_t)w[32 + h];
+    for (int r = 0; r < 16; ++r) {
+      const int h = 8 * (r >> 2) + 4 * half + (r & 3);
+      wl.lo[r] = (uint32_t)w_i[h];
+      wl.hi[r] = (uint32_t)w_i[32 + h];
+    }
   }
 
 #pragma unroll 1
@@ -393,16 +518,17 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
       __syncthreads();
     }
     if constexpr (MULTI) {
-      indexer_shared_seg(sg, toks, q_idx, k_idx, wl, scores, stride, hist_on,
-                         reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring);
+      indexer_shared_seg<F8>(sg, toks, q_idx, k_idx, k_scale, wl, w_f, scores, stride, hist_on,
+                             reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring,
+                             scl);
     } else {
       // one token: the 4 waves split its key tiles, each through its own part of the ring
       const int64_t t = sg.q0;
       const Tok tk = toks[t];
       int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
       int* lh = hist_on ? lhist_base : nullptr;
-      indexer_wave(tk, t, sg.s0 + 32 * wave, sg.s1, 128, q_idx, k_idx, wl, out_row, lh,
-                   ring + KR * wave);
+      indexer_wave<F8>(tk, t, sg.s0 + 32 * wave, sg.s1, 128, q_idx, k_idx, k_scale, wl, w_f,
+                       out_row, lh, ring + KR * wave, scl + KR * wave);
     }
     __syncthreads();  // the ring (and the histograms) are reused by the next segment
     if (hist_on) {
@@ -466,11 +592,28 @@ hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const i
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const int64_t stride = compact ? 0 : b.max_kv;
   if (b.max_q <= 1)
-    hipLaunchKernelGGL(indexer_mfma_kernel<false>, dim3(b.n_items), dim3(256), 0, s, tv.item,
-                       tv.tok, q_idx, k_idx, w, scores, stride, hist);
+    hipLaunchKernelGGL((indexer_mfma_kernel<false, false>), dim3(b.n_items), dim3(256), 0, s,
+                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist);
   else
-    hipLaunchKernelGGL(indexer_mfma_kernel<true>, dim3(b.n_items), dim3(256), 0, s, tv.item,
-                       tv.tok, q_idx, k_idx, w, scores, stride, hist);
+    hipLaunchKernelGGL((indexer_mfma_kernel<true, false>), dim3(b.n_items), dim3(256), 0, s,
+                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_fp8(const smla_batch& b, const uint8_t* q, const uint8_t* k,
+                              const float* k_scale, const float* w, int32_t* scores, int compact,
+                              int* hist, hipStream_t s) {
+  if (b.n_items <= 0) return hipSuccess;
+  TableView tv = table_view(b.table, b.batch, b.total_q);
+  const int64_t stride = compact ? 0 : b.max_kv;
+  const int8_t* qi = reinterpret_cast<const int8_t*>(q);
+  const int8_t* ki = reinterpret_cast<const int8_t*>(k);
+  if (b.max_q <= 1)
+    hipLaunchKernelGGL((indexer_mfma_kernel<false, true>), dim3(b.n_items), dim3(256), 0, s,
+                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist);
+  else
+    hipLaunchKernelGGL((indexer_mfma_kernel<true, true>), dim3(b.n_items), dim3(256), 0, s,
+                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist);
   return hipGetLastError();
 }
 

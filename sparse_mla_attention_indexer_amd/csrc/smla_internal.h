@@ -67,6 +67,21 @@ __device__ __forceinline__ int topk_bin(uint32_t s) {
   return 64 * (e - 5) + (int)((s >> (e - 6)) & 63u);
 }
 
+// Monotone 11-bit code of a non-negative fp32 score given as its bit pattern (FP8 keys): 64 bins
+// per binade over [2^-16, 2^16); smaller scores share bin 0, larger ones bin 2047. Any monotone
+// code selects exactly; a range that puts a row's scores into few bins only costs speed.
+constexpr uint32_t TOPK_FBIN_BASE = 0x37800000u;  // 2^-16
+__device__ __forceinline__ int topk_fbin(uint32_t s) {
+  if (s < TOPK_FBIN_BASE) return 0;
+  const uint32_t b = (s - TOPK_FBIN_BASE) >> 17;
+  return b > 2047u ? 2047 : (int)b;
+}
+__device__ __forceinline__ uint64_t topk_fbin_lo(int b) {
+  if (b <= 0) return 0;
+  if (b >= TOPK_BINS) return 1ull << 32;
+  return TOPK_FBIN_BASE + ((uint64_t)b << 17);
+}
+
 // Word of bin b in a row's histogram in device memory. A row's scores cluster in a few binades,
 // so its busy bins are neighbours, and every workgroup that scores part of the row adds to them;
 // many writers to one 128-byte line serialise, so bins less than 64 apart go to different lines.
@@ -129,14 +144,22 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
                                const int32_t* w, int32_t* scores, int compact, int* hist,
                                hipStream_t s);
+// FP8 keys: q (E4M3 codes) [total_q, 64, 128], k (E4M3 codes) [total_rows, 128], k_scale
+// [total_rows] fp32, w [total_q, 64] fp32; scores are fp32 bit patterns.
+hipError_t launch_indexer_fp8(const smla_batch& b, const uint8_t* q, const uint8_t* k,
+                              const float* k_scale, const float* w, int32_t* scores, int compact,
+                              int* hist, hipStream_t s);
 hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, const int8_t* k_idx,
                                   const int32_t* w, int32_t H_I, int32_t D_I, int32_t* scores,
                                   int compact, int* hist, hipStream_t s);
 
 size_t topk_workspace_bytes(const smla_batch& b, int32_t top_k);
 TopkWs topk_workspace(const smla_batch& b, void* ws);
+// fscores: the scores are bit patterns of non-negative fp32 values (FP8 keys); padding scores
+// are then -1.0f instead of -1.
 hipError_t launch_topk(const smla_batch& b, const int32_t* scores_compact, int32_t top_k,
-                       int32_t* idx, int32_t* score, const TopkWs& w, hipStream_t s);
+                       int32_t* idx, int32_t* score, const TopkWs& w, hipStream_t s,
+                       bool fscores = false);
 
 size_t mla_workspace_bytes(const smla_batch& b, int32_t H, int32_t D_v, int32_t top_k, int decode);
 int mla_decode_splits(const smla_batch& b, int32_t top_k);

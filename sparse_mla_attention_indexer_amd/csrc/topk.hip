@@ -22,7 +22,12 @@ namespace smla {
 
 namespace {
 
-__device__ __forceinline__ int score_bin(uint32_t s) { return topk_bin(s); }
+// Histogram code of a score: integer scores (int8 keys) or the bit patterns of non-negative fp32
+// scores (FP8 keys); both codes are monotone in the 32-bit pattern.
+template <bool FB>
+__device__ __forceinline__ int score_bin(uint32_t s) { return FB ? topk_fbin(s) : topk_bin(s); }
+template <bool FB>
+__device__ __forceinline__ uint64_t bin_lo(int b) { return FB ? topk_fbin_lo(b) : topk_bin_lo(b); }
 
 __device__ __forceinline__ uint64_t sel_key(int32_t score, int64_t s) {
   return ((uint64_t)(uint32_t)score << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
@@ -234,10 +239,12 @@ __device__ void emit_in_order(int len, int base, Sel sel, Emit emit, int* wcnt) 
 // ---- path A: rows of n <= TOPK_LDS_MAX, one 1024-thread workgroup per row ----------------
 constexpr int NT_A = 1024;
 
+template <bool FB>
 __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ toks,
                                                         const int32_t* __restrict__ scores,
                                                         int top_k, int32_t* __restrict__ idx_out,
-                                                        int32_t* __restrict__ score_out) {
+                                                        int32_t* __restrict__ score_out,
+                                                        int32_t pad_score) {
   extern __shared__ int smem[];
   int* sc = smem;                 // [TOPK_LDS_MAX]
   int* hist = sc + TOPK_LDS_MAX;  // [TOPK_BINS]
@@ -256,7 +263,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
   if (n <= top_k) {
     for (int j = threadIdx.x; j < top_k; j += NT_A) {
       oi[j] = j < n ? j : -1;
-      if (os) os[j] = j < n ? row[j] : -1;
+      if (os) os[j] = j < n ? row[j] : pad_score;
     }
     return;
   }
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
       const int i = j * NT_A + threadIdx.x;
       if (i < n) {
         sc[i] = vals[j];
-        atomicAdd(&hist[score_bin((uint32_t)vals[j])], 1);
+        atomicAdd(&hist[score_bin<FB>((uint32_t)vals[j])], 1);
       }
     }
   }
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
       const int lane = threadIdx.x & 63;
       for (int i0 = 0; i0 < n; i0 += NT_A) {
         const int i = i0 + threadIdx.x;
-        const bool f = i < n && score_bin((uint32_t)sc[i]) == bstar;
+        const bool f = i < n && score_bin<FB>((uint32_t)sc[i]) == bstar;
         const uint64_t m = __ballot(f);
         if (m) {
           int base = 0;
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
     } else {
       radix_cut<NT_A>(
           n, need, [&](int i) { return sel_key(sc[i], i); },
-          [&](int i) { return score_bin((uint32_t)sc[i]) == bstar; }, hist2, red, cut, pm);
+          [&](int i) { return score_bin<FB>((uint32_t)sc[i]) == bstar; }, hist2, red, cut, pm);
     }
     prefix = pm[0];
     mask = pm[1];
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
   emit_in_order<NT_A>(
       n, 0,
       [&](int i) {
-        const int bn = score_bin((uint32_t)sc[i]);
+        const int bn = score_bin<FB>((uint32_t)sc[i]);
         return bn > bstar || (bn == bstar && (sel_key(sc[i], i) & mask) >= prefix);
       },
       [&](int i, int pos) {
@@ -474,8 +481,9 @@ __device__ __forceinline__ uint64_t cut_key(uint64_t prefix, uint32_t lo) {
   return max(prefix, (uint64_t)lo << 32);
 }
 
+template <bool FB>
 __device__ __forceinline__ uint32_t bin_hm1(int b) {  // top score of bin b
-  return (uint32_t)min(topk_bin_lo(b + 1) - 1, (uint64_t)0xFFFFFFFFu);
+  return (uint32_t)min(bin_lo<FB>(b + 1) - 1, (uint64_t)0xFFFFFFFFu);
 }
 
 // b* and the count above it from a row's global histogram, 2048 / NT bins per thread in
@@ -522,6 +530,7 @@ constexpr int NT_R = 1024;
 constexpr int NW_R = NT_R / 64;
 constexpr int V_R = TOPK_ROW_MAX / NT_R;  // scores per lane
 
+template <bool FB>
 __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ toks,
                                                         const int32_t* __restrict__ scores,
                                                         int top_k, TopkWs ws,
@@ -557,8 +566,8 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
     hist_cut<NT_R>(gh, top_k, red, cut);  // while the row is in flight
     bstar = cut[0];
     need = top_k - cut[1];
-    lo = (uint32_t)topk_bin_lo(bstar);
-    const uint32_t hm1 = bin_hm1(bstar);
+    lo = (uint32_t)bin_lo<FB>(bstar);
+    const uint32_t hm1 = bin_hm1<FB>(bstar);
     const int above = full ? pass_gather<V_R, true>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP)
                            : pass_gather<V_R, false>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP);
     if (lane == 0) wsel[wv] = above;
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
   // more candidates than LDS holds (heavy ties): cut and emit straight from the score row
   radix_cut<NT_R>(
       n, need, [&](int i) { return sel_key(row[i], i); },
-      [&](int i) { return score_bin((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
+      [&](int i) { return score_bin<FB>((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
   const uint64_t ck = cut_key(pm[0], lo);
   const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
   const int c0 = wv * (64 * V_R);
@@ -660,6 +669,7 @@ constexpr int NT_S = 256;
 constexpr int V_S = TOPK_SEG / NT_S;  // 16 per lane: wave w owns [1024 w, 1024 (w + 1))
 static_assert(V_S == 16, "one buffer resource per segment");
 
+template <bool FB>
 __global__ __launch_bounds__(NT_S) void topk_seg_count_kernel(const Tok* __restrict__ toks,
                                                               const int32_t* __restrict__ scores,
                                                               int top_k, int seg_min_n,
@@ -685,7 +695,7 @@ __global__ __launch_bounds__(NT_S) void topk_seg_count_kernel(const Tok* __restr
   if (threadIdx.x == 0) nk = 0;
   hist_cut<NT_S>(ws.hist + t * TOPK_BINS, top_k, red, cut);
   const int bstar = cut[0];
-  const uint32_t lo = (uint32_t)topk_bin_lo(bstar), hm1 = bin_hm1(bstar);
+  const uint32_t lo = (uint32_t)bin_lo<FB>(bstar), hm1 = bin_hm1<FB>(bstar);
   const int above = full ? pass_gather<V_S, true>(v, s0 + ib, rem, lo, hm1, klo, khi, &nk, TOPK_SEG)
                          : pass_gather<V_S, false>(v, s0 + ib, rem, lo, hm1, klo, khi, &nk, TOPK_SEG);
   if (lane == 0) wab[wv] = above;
@@ -709,6 +719,7 @@ __global__ __launch_bounds__(NT_S) void topk_seg_count_kernel(const Tok* __restr
     cand[base + i] = ((uint64_t)khi[i] << 32) | klo[i];
 }
 
+template <bool FB>
 __global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __restrict__ toks,
                                                                 const int32_t* __restrict__ scores,
                                                                 int top_k, int seg_min_n,
@@ -737,7 +748,7 @@ __global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __res
   const int ncand = rec[0];
   const int bstar = rec[1];
   const int need = top_k - rec[2];
-  const uint32_t lo = (uint32_t)topk_bin_lo(bstar);
+  const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
   if ((int)threadIdx.x < nseg_t) segc[threadIdx.x] = sv0;
   for (int g = threadIdx.x + NT_R; g < nseg_t; g += NT_R) segc[g] = segv[g];
   uint64_t ck;
@@ -769,11 +780,11 @@ __global__ __launch_bounds__(NT_R) void topk_seg_resolve_kernel(const Tok* __res
     const int32_t* row = scores + tk.cand_off;
     radix_cut<NT_R>(
         n, need, [&](int i) { return sel_key(row[i], i); },
-        [&](int i) { return score_bin((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
+        [&](int i) { return score_bin<FB>((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
     ck = cut_key(pm[0], lo);
     for (int i = threadIdx.x; i < n; i += NT_R) {
       const uint32_t x = (uint32_t)row[i];
-      if (x >= lo && sel_key((int32_t)x, i) >= ck && score_bin(x) == bstar)
+      if (x >= lo && sel_key((int32_t)x, i) >= ck && score_bin<FB>(x) == bstar)
         atomicAdd(&segc[i / TOPK_SEG], 1);
     }
   }
@@ -865,20 +876,24 @@ TopkWs topk_workspace(const smla_batch& b, void* ws) {
   return topk_ws(ws, b.total_q, topk_nseg(b));
 }
 
-hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
-                       int32_t* score, const TopkWs& w, hipStream_t s) {
+namespace {
+
+template <bool FB>
+hipError_t launch_topk_t(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
+                         int32_t* score, const TopkWs& w, hipStream_t s) {
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const size_t lds_a = sizeof(int) * (TOPK_LDS_MAX + TOPK_BINS);
   static const bool lds_set = [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_lds_kernel),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_lds_kernel<FB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
     return true;
   }();
   (void)lds_set;
+  const int32_t pad = FB ? (int32_t)0xBF800000u : -1;  // -1.0f or -1
   hipError_t e = hipSuccess;
   if (b.min_cand <= TOPK_LDS_MAX) {
-    hipLaunchKernelGGL(topk_lds_kernel, dim3(b.total_q), dim3(NT_A), lds_a, s, tv.tok, scores,
-                       top_k, idx, score);
+    hipLaunchKernelGGL(topk_lds_kernel<FB>, dim3(b.total_q), dim3(NT_A), lds_a, s, tv.tok, scores,
+                       top_k, idx, score, pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.max_kv <= TOPK_LDS_MAX) return e;
@@ -887,21 +902,29 @@ hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k
   const bool seg_all = b.total_q <= TOPK_SEG_ALL_MAX_Q;
   const int seg_min_n = seg_all ? TOPK_LDS_MAX : TOPK_ROW_MAX;
   if (!seg_all) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores, top_k, w,
-                       idx, score);
+    hipLaunchKernelGGL(topk_row_kernel<FB>, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores, top_k,
+                       w, idx, score);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.max_kv <= seg_min_n) return e;
   const unsigned nseg = (unsigned)topk_nseg(b);
-  hipLaunchKernelGGL(topk_seg_count_kernel, dim3(nseg, b.total_q), dim3(NT_S), 0, s, tv.tok,
+  hipLaunchKernelGGL(topk_seg_count_kernel<FB>, dim3(nseg, b.total_q), dim3(NT_S), 0, s, tv.tok,
                      scores, top_k, seg_min_n, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_seg_resolve_kernel, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores,
+  hipLaunchKernelGGL(topk_seg_resolve_kernel<FB>, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores,
                      top_k, seg_min_n, w);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(topk_seg_emit_kernel, dim3(nseg, b.total_q), dim3(NT_S), 0, s, tv.tok, scores,
                      top_k, seg_min_n, w, idx, score);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
+                       int32_t* score, const TopkWs& w, hipStream_t s, bool fscores) {
+  return fscores ? launch_topk_t<true>(b, scores, top_k, idx, score, w, s)
+                 : launch_topk_t<false>(b, scores, top_k, idx, score, w, s);
 }
 
 }  // namespace smla

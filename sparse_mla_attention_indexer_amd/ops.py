@@ -124,6 +124,60 @@ def indexer_topk(plan: BatchPlan, q_idx, k_idx, w, top_k: int, with_scores=True,
     return idx, score
 
 
+def _check_indexer_fp8(plan: BatchPlan, q, k, k_scale, w):
+    d = plan.device
+    if q.dim() != 3:
+        raise ValueError("q must be [total_q, H_I, D_I] E4M3 codes (uint8)")
+    H_I, D_I = int(q.shape[1]), int(q.shape[2])
+    _req(q, "q", torch.uint8, (plan.total_q, H_I, D_I), d)
+    if k.dim() != 2 or k.shape[0] < plan.total_rows:
+        raise ValueError(f"k must be [>= {plan.total_rows}, D_I] E4M3 codes (uint8)")
+    _req(k, "k", torch.uint8, (k.shape[0], D_I), d)
+    _req(k_scale, "k_scale", torch.float32, (k.shape[0],), d)
+    _req(w, "w", torch.float32, (plan.total_q, H_I), d)
+    return H_I, D_I
+
+
+def indexer_scores_fp8(plan: BatchPlan, q, k, k_scale, w, out=None):
+    """FP8 keys: full score matrix [total_q, max_kv] fp32 (-1.0 where s > p)."""
+    H_I, D_I = _check_indexer_fp8(plan, q, k, k_scale, w)
+    if out is None:
+        out = torch.empty((plan.total_q, plan.max_kv), dtype=torch.float32, device=plan.device)
+    _req(out, "out", torch.float32, (plan.total_q, plan.max_kv), plan.device)
+    with torch.cuda.device(plan.device):
+        check("smla_indexer_scores_fp8",
+              lib().smla_indexer_scores_fp8(plan.ref, q.data_ptr(), k.data_ptr(), k_scale.data_ptr(),
+                                            w.data_ptr(), H_I, D_I, out.data_ptr(),
+                                            _stream(plan.device)))
+    return out
+
+
+def indexer_topk_fp8(plan: BatchPlan, q, k, k_scale, w, top_k: int, with_scores=True, idx=None,
+                     score=None, workspace=None):
+    """FP8 keys: exact top-k per query token of the fp32 scores; idx [total_q, top_k] ascending,
+    -1 padded; optional scores fp32 (-1.0 on padding)."""
+    H_I, D_I = _check_indexer_fp8(plan, q, k, k_scale, w)
+    shape = (plan.total_q, top_k)
+    if idx is None:
+        idx = torch.empty(shape, dtype=torch.int32, device=plan.device)
+    _req(idx, "idx", torch.int32, shape, plan.device)
+    if with_scores and score is None:
+        score = torch.empty(shape, dtype=torch.float32, device=plan.device)
+    if score is not None:
+        _req(score, "score", torch.float32, shape, plan.device)
+    if workspace is None:
+        workspace = topk_workspace(plan, H_I, D_I, top_k)
+    with torch.cuda.device(plan.device):
+        check("smla_indexer_scores_topk_fp8",
+              lib().smla_indexer_scores_topk_fp8(plan.ref, q.data_ptr(), k.data_ptr(),
+                                                 k_scale.data_ptr(), w.data_ptr(), H_I, D_I, top_k,
+                                                 idx.data_ptr(),
+                                                 score.data_ptr() if score is not None else None,
+                                                 workspace.data_ptr(), workspace.numel(),
+                                                 _stream(plan.device)))
+    return idx, score
+
+
 def mla_workspace(plan: BatchPlan, H: int, D_v: int, top_k: int, decode: bool) -> torch.Tensor:
     n = int(lib().smla_sparse_mla_workspace_bytes(plan.ref, H, D_v, top_k, int(decode)))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)

@@ -145,6 +145,39 @@ def generate(d: Dims, seed: int | None = None, nthreads: int = 0, *, parts=("q",
     return Inputs(d, seed, q, kv, q_idx, k_idx, w, n_q, kv_len)
 
 
+@dataclass
+class Fp8IndexerInputs:
+    q: np.ndarray        # uint8 E4M3 codes [total_q, H_I, D_I]
+    k: np.ndarray        # uint8 E4M3 codes [total_rows, D_I]
+    k_scale: np.ndarray  # float32 [total_rows]
+    w: np.ndarray        # float32 [total_q, H_I]
+
+
+def _e4m3_codes(rng, shape, e_lo=5, e_hi=10):
+    """Random E4M3 bit patterns from two random bytes per code: sign and the 3 mantissa bits from
+    the first, the 4-bit exponent field (on [e_lo, e_hi], near uniform) from the second, whose top
+    4 of 256 values make the code zero (1 in 64). Never a NaN code."""
+    n = int(np.prod(shape))
+    r = np.frombuffer(rng.bytes(2 * n), np.uint8).reshape(2, n)
+    a, b = r[0], r[1]
+    codes = (a & np.uint8(0x87)) | ((np.uint8(e_lo) + b % np.uint8(e_hi - e_lo + 1)) << np.uint8(3))
+    codes[b >= 252] = 0
+    return codes.reshape(shape)
+
+
+def fp8_indexer_inputs(d: Dims, seed: int | None = None) -> Fp8IndexerInputs:
+    """Inputs for the FP8-key indexer at the shapes of `d` (H_I x D_I per query token): E4M3 codes
+    with exponent fields 5..10 (magnitudes 1/4 .. 7.5, one code in 64 zero), key scales uniform
+    on [1/64, 1/8), per-token head weights uniform on [1/4, 1)."""
+    seed = int(d.seed if seed is None else seed) ^ 0xF8F8F8F8
+    rng = np.random.default_rng(seed)
+    q = _e4m3_codes(rng, (d.total_q, d.H_I, d.D_I))
+    k = _e4m3_codes(rng, (d.total_rows, d.D_I))
+    k_scale = rng.uniform(1 / 64, 1 / 8, d.total_rows).astype(np.float32)
+    w = rng.uniform(0.25, 1.0, (d.total_q, d.H_I)).astype(np.float32)
+    return Fp8IndexerInputs(q, k, k_scale, w)
+
+
 def latent_f64(d: Dims, seed: int, row0: int, nrows: int) -> np.ndarray:
     out = np.empty((nrows, d.D_qk), np.float64)
     rc = lib().smla_workload_latent_f64(ctypes.byref(d), seed, row0, nrows, _ptr(out))

@@ -105,6 +105,31 @@ def test_topk_validation(L):
     assert rc == _lib.SMLA_E_INVALID
 
 
+def test_fp8_indexer_validation(L):
+    b = _fake_batch()
+    rc = L.smla_indexer_scores_fp8(None, FAKE, FAKE, FAKE, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID
+    rc = L.smla_indexer_scores_fp8(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 16, 32, FAKE, None)
+    assert rc == _lib.SMLA_E_UNSUPPORTED  # no generic FP8 kernel
+    rc = L.smla_indexer_scores_fp8(ctypes.byref(b), FAKE, FAKE, None, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID      # the key scales are required
+    rc = L.smla_indexer_scores_fp8(ctypes.byref(b), FAKE, FAKE + 8, FAKE, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID
+    rc = L.smla_indexer_scores_fp8(ctypes.byref(b), FAKE, FAKE, FAKE + 2, FAKE, 64, 128, FAKE, None)
+    assert rc == _lib.SMLA_E_INVALID
+    need = L.smla_indexer_topk_workspace_bytes(ctypes.byref(b), 64, 128, 2048)
+    for k in (0, 2049):
+        rc = L.smla_indexer_scores_topk_fp8(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 64, 128, k,
+                                            FAKE, None, FAKE, need, None)
+        assert rc == _lib.SMLA_E_UNSUPPORTED
+    rc = L.smla_indexer_scores_topk_fp8(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 64, 128, 2048,
+                                        FAKE, None, FAKE, need - 1, None)
+    assert rc == _lib.SMLA_E_WORKSPACE
+    rc = L.smla_indexer_scores_topk_fp8(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, 64, 128, 2048,
+                                        None, None, FAKE, need, None)
+    assert rc == _lib.SMLA_E_INVALID
+
+
 def test_mla_validation(L):
     b = _fake_batch()
     args = dict(H=64, D_qk=576, D_v=512)

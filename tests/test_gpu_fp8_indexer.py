@@ -1,0 +1,191 @@
+"""GPU parity of the FP8-key indexer (128 E4M3 values and an fp32 scale per key) and its top-k.
+
+The FP8 matrix cores sum a head's 128 exact products in a narrower accumulator than IEEE fp32,
+so scores are compared with the oracle within a bound derived from that (below), while the
+selection is compared exactly: the top-k the library returns must be the oracle's top-k of the
+library's own fp32 scores (the decision taken on the same values, in the same precision). With
+integer-valued codes every partial sum is a small integer, which any accumulator holds exactly:
+then the FP8 path must reproduce the int8 path bit for bit, scores and indices.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indexer_amd import ops
+from sparse_mla_attention_indexer_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import say, sort_by_index  # noqa: E402
+
+# |gpu - oracle| <= SCORE_RTOL * (k_scale * sum_h w_h * sum_d |q_hd k_d|): the matrix cores keep
+# about 18 bits of a dot product relative to its largest terms (2^-18 of the sum of |products|
+# was the largest error seen on one instruction), the fp32 head sum and scale add ~2^-17. The
+# bound leaves a factor of ~30 over that; a dropped term, a wrong scale, weight or head is off
+# by far more.
+SCORE_RTOL = 2.0 ** -12
+
+
+def _e4m3(values):
+    """E4M3 codes of exactly representable values (torch's cast, independent of the library)."""
+    return torch.from_numpy(np.asarray(values, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+class Fp8Dev:
+    def __init__(self, n_q, kv_len, q, k, k_scale, w, device="cuda:0"):
+        self.device = torch.device(device)
+        self.plan = ops.BatchPlan(np.asarray(n_q, np.int32), np.asarray(kv_len, np.int64), self.device)
+        self.q = torch.from_numpy(np.ascontiguousarray(q)).to(self.device)
+        self.k = torch.from_numpy(np.ascontiguousarray(k)).to(self.device)
+        self.k_scale = torch.from_numpy(np.ascontiguousarray(k_scale, np.float32)).to(self.device)
+        self.w = torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(self.device)
+        self.ws = {}
+
+    def scores(self):
+        s = ops.indexer_scores_fp8(self.plan, self.q, self.k, self.k_scale, self.w)
+        torch.cuda.synchronize()
+        return s.cpu().numpy()
+
+    def topk(self, top_k):
+        if top_k not in self.ws:
+            self.ws[top_k] = ops.topk_workspace(self.plan, 64, 128, top_k)
+        idx, sc = ops.indexer_topk_fp8(self.plan, self.q, self.k, self.k_scale, self.w, top_k,
+                                       workspace=self.ws[top_k])
+        torch.cuda.synchronize()
+        return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _token_rows(n_q, kv_len):
+    """(token, first row of its request, position) for every query token of a batch."""
+    out, row0, t = [], 0, 0
+    for nq, kl in zip(n_q, kv_len):
+        for j in range(nq):
+            out.append((t, row0, int(kl) - int(nq) + j))
+            t += 1
+        row0 += int(kl)
+    return out
+
+
+def _check_topk_on_own_scores(idx, sc, full, toks, top_k, label):
+    """idx/sc [total_q, top_k] from the top-k entry point against the oracle's top-k of the
+    library's own full-matrix scores (fp32 bit patterns order like the values: all >= +0)."""
+    for t, _, p in toks:
+        row = full[t, : p + 1]
+        assert (row >= 0).all() and not np.signbit(row).any(), f"{label}: negative score in row {t}"
+        ref_i, _ = oracle.topk(row.view(np.int32).astype(np.int64), top_k)
+        ref_s = np.where(ref_i >= 0, row[np.maximum(ref_i, 0)], np.float32(-1.0)).astype(np.float32)
+        ri, rs = sort_by_index(ref_i[None], ref_s[None])
+        assert np.array_equal(idx[t], ri[0]), f"{label}: row {t} selection differs"
+        assert np.array_equal(sc[t].view(np.int32), rs[0].view(np.int32)), f"{label}: row {t} scores differ"
+        assert (full[t, p + 1:] == -1.0).all()
+
+
+def _check_scores_against_oracle(full, x, toks, label, tokens=None, key_step=1):
+    worst_ratio = 0.0
+    for t, row0, p in toks:
+        if tokens is not None and t not in tokens:
+            continue
+        keys = np.arange(0, p + 1, key_step)
+        ref, mag = oracle.indexer_scores_fp8(x.q[t], x.k[row0 + keys], x.k_scale[row0 + keys], x.w[t])
+        got = full[t, keys].astype(np.float64)
+        err = np.abs(got - ref)
+        bound = SCORE_RTOL * mag + 1e-30
+        worst = int(np.argmax(err / bound))
+        assert (err <= bound).all(), (f"{label}: token {t} key {keys[worst]}: got {got[worst]!r} "
+                                      f"ref {ref[worst]!r} bound {bound[worst]!r}")
+        worst_ratio = max(worst_ratio, float(np.max(err / (mag + 1e-30))))
+    say(f"  {label}: largest |score - oracle| / magnitude = {worst_ratio:.3e} (bound {SCORE_RTOL:.3e})")
+
+
+@pytest.mark.parametrize("shape", ["decode", "multi"])
+def test_fp8_integer_codes_reproduce_int8_path(shape):
+    # decode: one token per request (the single-token kernel, segmented and LDS top-k paths);
+    # multi: several tokens per request (the shared-tile kernel, all three top-k paths)
+    if shape == "decode":
+        n_q = np.array([1, 1, 1, 1], np.int32)
+        kv_len = np.array([300000, 2049, 40000, 50], np.int64)
+    else:
+        n_q = np.array([1, 4, 2, 3, 1], np.int32)
+        kv_len = np.array([3000, 50, 2049, 40000, 2048], np.int64)
+    d = W.small_big_dims(batch=1, n_q=int(n_q.sum()), cached=int(kv_len.sum() - n_q.sum()))
+    x = W.generate(d, parts=("q_idx", "k_idx", "w"))
+    say(f"[case] fp8 integer codes vs int8 path ({shape})", n_q.tolist(), kv_len.tolist())
+    dv = torch.device("cuda:0")
+    plan = ops.BatchPlan(n_q, kv_len, dv)
+    q_i, k_i, w_i = (torch.from_numpy(a).to(dv) for a in (x.q_idx, x.k_idx, x.w))
+    ref_scores = ops.indexer_scores(plan, q_i, k_i, w_i).cpu().numpy()
+    ri, rs = ops.indexer_topk(plan, q_i, k_i, w_i, 2048, workspace=ops.topk_workspace(plan, 64, 128, 2048))
+    ref_idx, ref_sc = ri.cpu().numpy(), rs.cpu().numpy()
+    total_q = int(n_q.sum())
+    w_tok = np.broadcast_to(x.w.astype(np.float32), (total_q, 64))
+    dev = Fp8Dev(n_q, kv_len, _e4m3(x.q_idx), _e4m3(x.k_idx), np.ones(d.total_rows, np.float32), w_tok)
+    full = dev.scores()
+    valid = ref_scores >= 0
+    assert np.array_equal(full[valid], ref_scores[valid].astype(np.float32))
+    assert (full[~valid] == -1.0).all()
+    idx, sc = dev.topk(2048)
+    assert np.array_equal(idx, ref_idx)
+    pad = ref_idx < 0
+    assert np.array_equal(sc[~pad], ref_sc[~pad].astype(np.float32)) and (sc[pad] == -1.0).all()
+
+
+@pytest.mark.parametrize("shape", ["decode", "multi"])
+def test_fp8_random_codes_against_oracle(shape):
+    if shape == "decode":
+        n_q = np.array([1, 1, 1], np.int32)
+        kv_len = np.array([40000, 3000, 2049], np.int64)
+    else:
+        n_q = np.array([3, 4, 2], np.int32)
+        kv_len = np.array([3000, 40000, 700], np.int64)
+    d = W.small_big_dims(batch=1, n_q=int(n_q.sum()), cached=int(kv_len.sum() - n_q.sum()))
+    x = W.fp8_indexer_inputs(d, seed=0x5EED3000 + len(shape))
+    say(f"[case] fp8 random codes vs oracle ({shape})", n_q.tolist(), kv_len.tolist())
+    dev = Fp8Dev(n_q, kv_len, x.q, x.k, x.k_scale, x.w)
+    full = dev.scores()
+    toks = _token_rows(n_q, kv_len)
+    _check_scores_against_oracle(full, x, toks, shape)
+    for top_k in (2048, 100):
+        idx, sc = dev.topk(top_k)
+        _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"{shape} k={top_k}")
+    idx2, sc2 = dev.topk(2048)
+    assert np.array_equal(idx2, dev.topk(2048)[0]), "FP8 top-k not deterministic"
+
+
+def test_fp8_zero_keys_and_scales_outside_the_histogram_range():
+    # rows of all-zero keys and zero scales (massive ties at +0), scores above 2^16 and below
+    # 2^-16 (the histogram's end bins): the selection stays exact on the library's own scores
+    n_q = np.array([1, 1, 1], np.int32)
+    kv_len = np.array([40000, 70000, 5000], np.int64)
+    d = W.small_big_dims(batch=1, n_q=3, cached=int(kv_len.sum() - 3))
+    x = W.fp8_indexer_inputs(d, seed=0x5EED3100)
+    r0 = 0
+    x.k[r0: r0 + 30000] = 0                           # request 0: 30,000 zero keys, then random
+    x.k_scale[r0 + 35000: r0 + 40000] = 0.0           # and zero scales at the end
+    r1 = int(kv_len[0])
+    x.k_scale[r1: r1 + 35000] *= np.float32(2.0 ** 12)   # request 1: scores above 2^16 ...
+    x.k_scale[r1 + 35000: r1 + 70000] *= np.float32(2.0 ** -30)  # ... and below 2^-16
+    say("[case] fp8 zero keys, zero / huge / tiny scales")
+    dev = Fp8Dev(n_q, kv_len, x.q, x.k, x.k_scale, x.w)
+    full = dev.scores()
+    toks = _token_rows(n_q, kv_len)
+    _check_scores_against_oracle(full, x, toks, "edge", key_step=7)
+    for top_k in (2048, 1):
+        idx, sc = dev.topk(top_k)
+        _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"edge k={top_k}")
+
+
+def test_fp8_decode_batch_full_size():
+    # the decode batch's shape (32 requests x 1 token after 65,536 cached): every row's selection
+    # on the library's own scores; scores of sampled tokens against the oracle
+    d = W.config_dims(1)
+    x = W.fp8_indexer_inputs(d)
+    n_q = np.full(d.batch, d.n_q, np.int32)
+    kv_len = np.full(d.batch, d.max_kv, np.int64)
+    say("[case] fp8 decode batch full size")
+    dev = Fp8Dev(n_q, kv_len, x.q, x.k, x.k_scale, x.w)
+    full = dev.scores()
+    idx, sc = dev.topk(d.top_k)
+    toks = _token_rows(n_q, kv_len)
+    _check_topk_on_own_scores(idx, sc, full, toks, d.top_k, "fp8 decode full")
+    _check_scores_against_oracle(full, x, toks, "fp8 decode full", tokens={0, 13, 31})
