@@ -40,6 +40,7 @@ WORKLOAD_TAGS = {0: "tiny_1x512", 1: "decode_32x65536", 2: "chunk_2048after65536
                  3: "prefill_32768", 4: "decode_4x4after1048576"}
 STAGES = ("indexer", "topk", "mla", "combine")
 APPEND_BYTES_PER_ROW = 1152 + 656 + 128 + 128 + 8
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 
 
 def workload_name(d):
@@ -156,6 +157,89 @@ def append_measurement(dev, steps):
     return out
 
 
+def stage_times(step, steps):
+    """Average per-stage kernel time (ms) over `steps` calls of step(), from HIP events the library
+    records on its own launch stream around each stage."""
+    from sparse_mla_attention_indexer_amd import _lib
+
+    hip = HipEvents()
+    L = _lib.lib()
+    ev = [[(hip.create(), hip.create()) for _ in STAGES] for _ in range(steps)]
+    import torch
+
+    torch.cuda.synchronize()
+    for k in range(steps):
+        begin = (ctypes.c_void_p * len(STAGES))(*[e[0] for e in ev[k]])
+        end = (ctypes.c_void_p * len(STAGES))(*[e[1] for e in ev[k]])
+        _lib.check("smla_set_stage_events", L.smla_set_stage_events(begin, end, len(STAGES)))
+        step()
+    torch.cuda.synchronize()
+    L.smla_set_stage_events(None, None, 0)
+    return ev, hip
+
+
+def fp8_indexer_measurement(dev, d, plan, steps, warmup, attend):
+    """The whole step with FP8 indexer keys (128 E4M3 values + an fp32 scale per key, 132 B) in
+    place of the workload's int8 keys: FP8 indexer, top-k and the same sparse MLA (`attend(idx)`),
+    so that the caches see what they see in the headline step (an indexer timed alone finds part
+    of its keys still in the 256 MB last-level cache). Beside the headline, not part of it.
+    Algorithmic bytes of the indexer: every visible key once (132 B) plus each token's E4M3 query
+    (8,192 B) and fp32 weights (256 B); HBM-bound below the FP8 ridge of 5.0 PFLOP/s / 8 TB/s =
+    625 FLOP/B, else against the FP8 peak."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_indexer_amd import ops
+    from sparse_mla_attention_indexer_amd import workload as W
+
+    x8 = W.fp8_indexer_inputs(d)
+    q8 = torch.from_numpy(x8.q).to(dev)
+    k8 = torch.from_numpy(x8.k).to(dev)
+    ks = torch.from_numpy(x8.k_scale).to(dev)
+    w8 = torch.from_numpy(x8.w).to(dev)
+    del x8
+    idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
+    ws = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
+
+    def step():
+        ops.indexer_topk_fp8(plan, q8, k8, ks, w8, d.top_k, with_scores=False, idx=idx, workspace=ws)
+        attend(idx)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev, hip = stage_times(step, steps)
+    ms = {}
+    for s, name in enumerate(STAGES[:2]):
+        ms[name] = sum(hip.elapsed_ms(*ev[k][s]) for k in range(steps)) / steps
+    for row in ev:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
+    pairs = float(np.sum(plan.positions + 1))
+    nbytes = d.total_rows * (d.D_I + 4) + d.total_q * d.H_I * (d.D_I + 4)
+    flops = 2.0 * d.H_I * d.D_I * pairs
+    sec = ms["indexer"] * 1e-3
+    if flops / nbytes < FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = nbytes / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = flops / sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s (fp8)", "frac": round(ach / FP8_PEAK_TFLOPS, 4)}
+    roof["kernel_ms"] = round(ms["indexer"], 4)
+    return {"key": "128 x e4m3 + fp32 scale (132 B)", "value": round(d.total_q / (step_ms * 1e-3), 1),
+            "unit": "query-tokens/s", "ms_per_step": round(step_ms, 4),
+            "stages_ms": {k: round(v, 4) for k, v in ms.items()},
+            "roofline": roof, "algorithmic_bytes": nbytes, "flops": flops}
+
+
 def algorithmic(d, positions):
     """Algorithmic work of one step (unique bytes; FLOPs/ops), per stage."""
     import numpy as np
@@ -270,17 +354,7 @@ def main():
     # per-stage kernel time: K more steps with HIP events the library records on its own launch
     # stream around each stage (event markers cost a few microseconds each, so they stay out of
     # the headline region)
-    hip = HipEvents()
-    L = _lib.lib()
-    ev = [[(hip.create(), hip.create()) for _ in STAGES] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        begin = (ctypes.c_void_p * len(STAGES))(*[e[0] for e in ev[k]])
-        end = (ctypes.c_void_p * len(STAGES))(*[e[1] for e in ev[k]])
-        _lib.check("smla_set_stage_events", L.smla_set_stage_events(begin, end, len(STAGES)))
-        step()
-    torch.cuda.synchronize()
-    L.smla_set_stage_events(None, None, 0)
+    ev, hip = stage_times(step, args.steps)
 
     stage_ms = {}
     for s, name in enumerate(STAGES):
@@ -337,6 +411,12 @@ def main():
     }
     if d.kv_format == W.KV_FP8_656:
         result["append"] = append_measurement(dev, args.steps)
+    if d.H_I == 64 and d.D_I == 128:
+        print("[bench] FP8-key indexer", file=sys.stderr, flush=True)
+        result["indexer_fp8"] = fp8_indexer_measurement(
+            dev, d, plan, args.steps, args.warmup,
+            lambda sel: ops.sparse_mla(plan, q, kv, d.kv_format, d.D_v, sel, d.sm_scale, decode=decode,
+                                       out=out, lse=lse, workspace=ws_mla))
     if not args.no_cpu_baseline:
         sample = np.arange(d.total_q) if d.total_q <= 32 else np.linspace(0, d.total_q - 1, 32).astype(np.int64)
         print(f"[bench] oracle on {sample.size} tokens", file=sys.stderr, flush=True)

@@ -268,6 +268,9 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
     v4i kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kt[8 * col + ((4 * half + j) ^ ((col >> 1) & 7))];
+    // all four operand reads go out before the first matrix instruction (left alone, the compiler
+    // may hold one back and stall the matrix sequence on its own LDS round trip)
+    __builtin_amdgcn_sched_barrier(0);
     acc0 = Acc{};
     acc1 = Acc{};
     if constexpr (F8) {
@@ -418,6 +421,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
     v4i kb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) kb[j] = kt[32 * (4 * half + j) + col];
+    __builtin_amdgcn_sched_barrier(0);  // all four operand reads before the first product
     acc0 = Acc{};
     acc1 = Acc{};
     if constexpr (F8) {
