@@ -5,8 +5,8 @@
 // Row layout (the pages size the FP8 latent row at 656 bytes, FlashMLA's fp8_ds_mla format:
 // "Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why the numbers work"): the 512 value
 // dims as OCP E4M3 codes, four little-endian fp32 scales (one per 128 value dims), the 64 rope dims
-// as bf16. Block scale = fp32(amax / 448), 1 for an all-zero block; a value's code is the quotient
-// value / scale, formed in fp64, rounded to nearest-even on the E4M3 grid and saturated at 448.
+// as bf16. Block scale = fp32(amax / 448), 1 for an all-zero block; a value's code is the exact
+// quotient value / scale rounded to nearest-even on the E4M3 grid and saturated at 448.
 #include "smla_internal.h"
 
 namespace smla {
@@ -37,6 +37,35 @@ __device__ __forceinline__ uint32_t e4m3_rne(double x) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
+// E4M3 code of v / s (s > 0) given r = RN(1 / s): the fp32 estimate x = |v| r is within 2^-22
+// (relative) of the quotient, so rounding x gives the quotient's code unless x lies within a few
+// of its last 20 bits of a rounding midpoint; there (rarely, and at every exact tie) the
+// decision is taken again from the binary64 quotient. Above 448 the code saturates.
+__device__ __forceinline__ uint32_t e4m3_code(float v, float r, double ds) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  const float x = a * r;
+  uint32_t code;
+  bool near;
+  if (!(x < 448.f)) {
+    code = 0x7Eu;
+    near = false;
+  } else if (x < 0.015625f) {  // below 2^-6: multiples of 2^-9
+    const float t = x * 512.f;
+    near = fabsf(t - floorf(t) - 0.5f) < 1.0f / 65536.f;
+    code = (uint32_t)rintf(t);
+  } else {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t rest = b & 0xFFFFFu;  // the 20 mantissa bits below the code's 3
+    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+    near = rest - (0x80000u - 16u) < 32u;
+    if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) ++code;
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  if (near) code = e4m3_rne((double)a / ds);
+  return sign | code;
+}
+
 // One wave per token: lane l converts value dims [8 l, 8 l + 8), block l / 16; lanes 0..7 move
 // the rope dims, and the first D_I / 16 lanes the indexer key.
 __global__ __launch_bounds__(256) void kv_append_kernel(int64_t n, const uint16_t* __restrict__ latent,
@@ -65,11 +94,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int64_t n, const uint16_
   for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));  // the lane's block
   const float scale = amax > 0.f ? (float)((double)amax / 448.0) : 1.0f;
   const double ds = (double)scale;
+  const float rcp = 1.0f / scale;  // correctly rounded
   uint32_t lo = 0u, hi = 0u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_rne((double)v[i] / ds) << (8 * i);
-    hi |= e4m3_rne((double)v[4 + i] / ds) << (8 * i);
+    lo |= e4m3_code(v[i], rcp, ds) << (8 * i);
+    hi |= e4m3_code(v[4 + i], rcp, ds) << (8 * i);
   }
   *reinterpret_cast<v2u*>(dst + 8 * lane) = v2u{lo, hi};
   if ((lane & 15) == 0) *reinterpret_cast<float*>(dst + 512 + 4 * (lane >> 4)) = scale;
