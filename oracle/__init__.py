@@ -52,6 +52,8 @@ def lib():
         L.smla_oracle_indexer_scores.argtypes = [P, P, P, i32, i32, i64, P]
         L.smla_oracle_indexer_scores_fp8.argtypes = [P, P, P, P, i32, i32, i64, P, P]
         L.smla_oracle_topk.argtypes = [P, i64, i32, P, P]
+        L.smla_oracle_topk_merge.argtypes = [P, P, i32, i32, i32, P, P]
+        L.smla_oracle_lse_merge.argtypes = [i32, i32, i32, P, P, P, P]
         L.smla_oracle_attend.argtypes = [P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_double,
                                          P, P]
         L.smla_oracle_indexer_topk_batch.argtypes = [i32, P, P, P, P, P, i32, i32, i32, P, i64, P,
@@ -146,6 +148,34 @@ def topk(scores, top_k: int):
     if lib().smla_oracle_topk(_p(scores), scores.size, top_k, _p(idx), _p(sc)) != 0:
         raise ValueError("topk failed")
     return idx, sc
+
+
+def topk_merge(idx_lists, score_lists, top_k: int):
+    """DCP top-k merge of one query token: per-shard lists [n_lists, k_in] (local indices, shard
+    l holds tokens l, l + n_lists, ...) -> the top_k of their union by (score desc, global index
+    asc), -1 padding."""
+    idx_lists = _c(idx_lists, np.int32)
+    score_lists = _c(score_lists, np.int32)
+    n_lists, k_in = idx_lists.shape
+    idx = np.empty(top_k, np.int32)
+    sc = np.empty(top_k, np.int32)
+    if lib().smla_oracle_topk_merge(_p(idx_lists), _p(score_lists), n_lists, k_in, top_k, _p(idx),
+                                    _p(sc)) != 0:
+        raise ValueError("topk_merge failed")
+    return idx, sc
+
+
+def lse_merge(outs, lses):
+    """LSE merge of partial attention results over disjoint row sets: outs [n, H, D_v],
+    lses [n, H] -> (out [H, D_v], lse [H])."""
+    outs = _c(outs, np.float64)
+    lses = _c(lses, np.float64)
+    n, H, D_v = outs.shape
+    out = np.empty((H, D_v), np.float64)
+    lse = np.empty(H, np.float64)
+    if lib().smla_oracle_lse_merge(n, H, D_v, _p(outs), _p(lses), _p(out), _p(lse)) != 0:
+        raise ValueError("lse_merge failed")
+    return out, lse
 
 
 def attend(q_tok, rows, fmt, D_v, idx, sm_scale):

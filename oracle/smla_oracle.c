@@ -187,6 +187,55 @@ int smla_oracle_topk(const int64_t* scores, int64_t n, int32_t top_k, int32_t* i
   return 0;
 }
 
+int smla_oracle_topk_merge(const int32_t* idx_lists, const int32_t* score_lists, int32_t n_lists,
+                           int32_t k_in, int32_t top_k, int32_t* idx, int32_t* score) {
+  if (n_lists < 1 || k_in < 1 || top_k < 1) return -1;
+  cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)n_lists * (size_t)k_in);
+  if (!c) return -1;
+  int64_t n = 0;
+  for (int32_t l = 0; l < n_lists; ++l)
+    for (int32_t j = 0; j < k_in; ++j) {
+      const int32_t local = idx_lists[(int64_t)l * k_in + j];
+      if (local < 0) continue;
+      c[n].score = score_lists[(int64_t)l * k_in + j];
+      c[n].s = (int64_t)local * n_lists + l;  /* shard l holds tokens l, l + n_lists, ... */
+      ++n;
+    }
+  qsort(c, (size_t)n, sizeof(cand_t), cmp_cand);
+  for (int32_t j = 0; j < top_k; ++j) {
+    idx[j] = j < n ? (int32_t)c[j].s : -1;
+    if (score) score[j] = j < n ? (int32_t)c[j].score : -1;
+  }
+  free(c);
+  return 0;
+}
+
+int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double* outs,
+                          const double* lses, double* out, double* lse) {
+  if (n_parts < 1 || H < 1 || D_v < 1) return -1;
+  for (int32_t h = 0; h < H; ++h) {
+    double m = -INFINITY;
+    for (int32_t i = 0; i < n_parts; ++i) m = fmax(m, lses[(int64_t)i * H + h]);
+    double z = 0.0;
+    for (int32_t d = 0; d < D_v; ++d) out[(int64_t)h * D_v + d] = 0.0;
+    if (m == -INFINITY) {  /* no part saw a row */
+      lse[h] = -INFINITY;
+      continue;
+    }
+    for (int32_t i = 0; i < n_parts; ++i) {
+      const double li = lses[(int64_t)i * H + h];
+      if (li == -INFINITY) continue;
+      const double wi = exp(li - m);
+      z += wi;
+      for (int32_t d = 0; d < D_v; ++d)
+        out[(int64_t)h * D_v + d] += wi * outs[((int64_t)i * H + h) * D_v + d];
+    }
+    for (int32_t d = 0; d < D_v; ++d) out[(int64_t)h * D_v + d] /= z;
+    lse[h] = m + log(z);
+  }
+  return 0;
+}
+
 int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,
                        int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
                        double sm_scale, double* out, double* lse) {

@@ -73,6 +73,21 @@ int smla_oracle_indexer_scores_fp8(const uint8_t* q_tok, const uint8_t* keys, co
 int smla_oracle_topk(const int64_t* scores, int64_t n, int32_t top_k, int32_t* idx,
                      int32_t* score);
 
+/* DCP merges (the pages shard the KV cache round-robin, every n-th token to one GPU, and merge
+ * what the shards compute: "Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "DCP").
+ * Top-k merge of one query token: n_lists per-shard lists (idx_lists/score_lists
+ * [n_lists][k_in], local indices, -1 padding), shard l holding the tokens l, l + n_lists, ...:
+ * the top_k of the union by (score desc, global index asc), global = local * n_lists + l. The
+ * result is in that order, -1 padded (as smla_oracle_topk). */
+int smla_oracle_topk_merge(const int32_t* idx_lists, const int32_t* score_lists, int32_t n_lists,
+                           int32_t k_in, int32_t top_k, int32_t* idx, int32_t* score);
+/* LSE merge of n_parts partial attention results over disjoint row sets: outs [n][H][D_v],
+ * lses [n][H] (natural log; -inf for a part with no row). m = max lse; w_i = exp(lse_i - m);
+ * out = sum w_i out_i / sum w_i; lse = m + log sum w_i (-inf and a zero output when no part saw
+ * a row). */
+int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double* outs,
+                          const double* lses, double* out, double* lse);
+
 /* Attention of one query token q_tok [H, D_qk] (bf16 bits) over rows[idx[i]] (row_bytes each),
  * skipping idx < 0; out [H, D_v], lse [H] (either may be NULL). Returns -1 if no row is valid. */
 int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,

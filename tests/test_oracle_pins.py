@@ -482,3 +482,67 @@ def test_attention_permutation_invariant_and_lse_merge():
     lm = np.logaddexp(la, lb)
     om = np.exp(la - lm)[:, None] * oa + np.exp(lb - lm)[:, None] * ob
     assert np.allclose(om, o1, atol=1e-13) and np.allclose(lm, l1, atol=1e-13)
+
+
+# ---- DCP merges (shard l holds tokens l, l + n, ...) -----------------------------------------
+
+@pytest.mark.parametrize("values", [1 << 20, 3, 1])
+def test_topk_merge_of_shard_topks_is_the_unsharded_topk(values):
+    # every member of the global top-k is in its own shard's top-k, so merging the shards' lists
+    # loses nothing: the merge equals the unsharded top-k (a separately pinned function), ties to
+    # the lower global index included (values=1: every score equal; 3: heavy ties)
+    rng = np.random.default_rng(values)
+    n_sh, k = 8, 64
+    for n in (5000, 700, 40, 8 * k):
+        row = rng.integers(0, values, size=n).astype(np.int64)
+        ref_i, ref_s = oracle.topk(row, k)
+        lists_i = np.full((n_sh, k), -1, np.int32)
+        lists_s = np.full((n_sh, k), -1, np.int32)
+        for sh in range(n_sh):
+            lists_i[sh], lists_s[sh] = oracle.topk(row[sh::n_sh], k)
+        got_i, got_s = oracle.topk_merge(lists_i, lists_s, k)
+        assert np.array_equal(got_i, ref_i) and np.array_equal(got_s, ref_s), n
+
+
+def test_topk_merge_hand_built():
+    # shard 0 holds tokens 0, 2, 4 (scores 5, 9, 9), shard 1 tokens 1, 3 (scores 9, 2); top 3 by
+    # (score desc, global index asc): 1 (9), 2 (9), 4 (9)
+    lists_i = np.array([[0, 1, 2], [0, 1, -1]], np.int32)
+    lists_s = np.array([[5, 9, 9], [9, 2, -1]], np.int32)
+    idx, sc = oracle.topk_merge(lists_i, lists_s, 3)
+    assert idx.tolist() == [1, 2, 4] and sc.tolist() == [9, 9, 9]
+    idx, sc = oracle.topk_merge(lists_i, lists_s, 6)
+    assert idx.tolist() == [1, 2, 4, 0, 3, -1] and sc.tolist() == [9, 9, 9, 5, 2, -1]
+
+
+def test_lse_merge_of_shard_attention_is_the_unsharded_attention():
+    # attention over each shard's rows, merged, equals attention over all rows (the separately
+    # pinned attend); a shard without rows (lse -inf) drops out
+    rng = np.random.default_rng(12)
+    vals = rng.standard_normal((64, 20))
+    rows = _rows_bf16(vals)
+    q = bf16_bits(rng.standard_normal((5, 20)))
+    sel = rng.permutation(64)[:40].astype(np.int32)
+    ref_o, ref_l = oracle.attend(q, rows, W.KV_BF16, 16, sel, 0.3)
+    n_sh = 4
+    outs, lses = [], []
+    for sh in range(n_sh + 1):
+        part = sel[sel % n_sh == sh] if sh < n_sh else np.array([], np.int32)
+        if part.size:
+            o, l = oracle.attend(q, rows, W.KV_BF16, 16, part, 0.3)
+        else:
+            o, l = np.zeros((5, 16)), np.full(5, -np.inf)
+        outs.append(o)
+        lses.append(l)
+    got_o, got_l = oracle.lse_merge(np.array(outs), np.array(lses))
+    assert np.allclose(got_o, ref_o, atol=1e-13) and np.allclose(got_l, ref_l, atol=1e-13)
+
+
+def test_lse_merge_closed_form():
+    # two parts with lse log 1 and log 3: weights 1/4 and 3/4; merged lse log 4
+    outs = np.array([[[1.0, 0.0]], [[0.0, 2.0]]])
+    lses = np.log(np.array([[1.0], [3.0]]))
+    out, lse = oracle.lse_merge(outs, lses)
+    assert np.allclose(out, [[0.25, 1.5]], atol=1e-15) and np.allclose(lse, [np.log(4.0)], atol=1e-15)
+    out, lse = oracle.lse_merge(outs[:1] * 0, np.full((1, 1), -np.inf))
+    assert lse[0] == -np.inf and (out == 0).all()
