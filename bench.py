@@ -240,6 +240,94 @@ def fp8_indexer_measurement(dev, d, plan, steps, warmup, attend):
             "roofline": roof, "algorithmic_bytes": nbytes, "flops": flops}
 
 
+def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
+    """The single-GPU DCP simulation on the decode batch: the KV cache of every request cut round
+    robin into n_sh shards (shard l holds tokens l, l + n_sh, ...), each shard's indexer + top-k and
+    sparse MLA at its real shape, and the exact merges (top-k merge, local indices, LSE merge).
+    Reports one shard's step, the merges, and their sum: what one GPU of a DCP group would spend
+    on compute per step (the all-gathers between GPUs are not modelled)."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_indexer_amd import ops
+
+    q = torch.from_numpy(x.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    q_idx = torch.from_numpy(x.q_idx).to(dev)
+    w = torch.from_numpy(x.w).to(dev)
+    row0 = np.concatenate([[0], np.cumsum(x.kv_len)[:-1]])
+    shards = []
+    for sh in range(n_sh):
+        lens, rows = [], []
+        for b, kl in enumerate(x.kv_len):
+            g = np.arange(sh, int(kl), n_sh)
+            lens.append(g.size)
+            rows.append(row0[b] + g)
+        rows = np.concatenate(rows)
+        plan = ops.BatchPlan(np.ones(d.batch, np.int32), np.array(lens, np.int64), dev)
+        kv = torch.from_numpy(np.ascontiguousarray(x.kv[rows])).to(dev)
+        k_idx = torch.from_numpy(np.ascontiguousarray(x.k_idx[rows])).to(dev)
+        ws_t = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
+        ws_m = ops.mla_workspace(plan, d.H, d.D_v, d.top_k, True)
+        shards.append((plan, kv, k_idx, ws_t, ws_m))
+    lists_i = torch.empty((n_sh, d.total_q, d.top_k), dtype=torch.int32, device=dev)
+    lists_s = torch.empty_like(lists_i)
+    local = torch.empty_like(lists_i)
+    outs = torch.empty((n_sh, d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=dev)
+    lses = torch.empty((n_sh, d.total_q, d.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
+    sc = torch.empty_like(idx)
+    out = torch.empty((d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((d.total_q, d.H), dtype=torch.float32, device=dev)
+
+    def shard_select(sh):
+        plan, _, k_idx, ws_t, _ = shards[sh]
+        ops.indexer_topk(plan, q_idx, k_idx, w, d.top_k, idx=lists_i[sh], score=lists_s[sh], workspace=ws_t)
+
+    def shard_attend(sh):
+        plan, kv, _, _, ws_m = shards[sh]
+        ops.sparse_mla(plan, q, kv, d.kv_format, d.D_v, local[sh], d.sm_scale, decode=True,
+                       out=outs[sh], lse=lses[sh], workspace=ws_m)
+
+    def merge_select():
+        ops.topk_merge(lists_i, lists_s, d.top_k, idx=idx, score=sc)
+        for sh in range(n_sh):
+            ops.dcp_local_indices(idx, n_sh, sh, out=local[sh])
+
+    def merge_attend():
+        ops.lse_merge(outs, lses, out=out, lse=lse)
+
+    def whole():
+        for sh in range(n_sh):
+            shard_select(sh)
+        merge_select()
+        for sh in range(n_sh):
+            shard_attend(sh)
+        merge_attend()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    whole()  # every buffer holds a real selection before the parts are timed alone
+    shard_ms = timed(lambda: (shard_select(0), shard_attend(0)))
+    merge_ms = timed(lambda: (merge_select(), merge_attend()))
+    whole_ms = timed(whole)
+    return {"shards": n_sh, "shard_rows_per_request": int(np.ceil(int(x.kv_len[0]) / n_sh)),
+            "shard_step_ms": round(shard_ms, 4), "merge_ms": round(merge_ms, 4),
+            "per_gpu_compute_ms": round(shard_ms + merge_ms, 4),
+            "one_gpu_all_shards_ms": round(whole_ms, 4),
+            "note": "one shard's indexer + top-k + sparse MLA at its real shape, plus the merges; "
+                    "the cross-GPU all-gathers are not modelled"}
+
+
 def algorithmic(d, positions):
     """Algorithmic work of one step (unique bytes; FLOPs/ops), per stage."""
     import numpy as np
@@ -411,6 +499,9 @@ def main():
     }
     if d.kv_format == W.KV_FP8_656:
         result["append"] = append_measurement(dev, args.steps)
+    if decode and (x.n_q == 1).all() and d.kv_format == W.KV_FP8_656:
+        print("[bench] DCP simulation", file=sys.stderr, flush=True)
+        result["dcp_sim"] = dcp_measurement(dev, x, d, args.steps, args.warmup)
     if d.H_I == 64 and d.D_I == 128:
         print("[bench] FP8-key indexer", file=sys.stderr, flush=True)
         result["indexer_fp8"] = fp8_indexer_measurement(

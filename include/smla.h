@@ -148,6 +148,46 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
                                  int32_t top_k, int32_t* idx, float* score, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/*
+ * Decode context parallelism on one GPU (the pages shard the KV cache round robin, every n-th
+ * token to one GPU, and merge what the shards compute: "Serving GLM-5.3 ... PCP, DCP, Hybrid
+ * HiSparse", section "DCP"). Shard l of n holds the tokens l, l + n, l + 2n, ... of every request,
+ * so its local row j is global row j n + l. Each shard runs smla_indexer_scores_topk and a
+ * sparse-MLA entry point on its own rows; these three calls merge the results.
+ *
+ * smla_topk_merge: the exact global top-k of each query token from the shards' lists. idx_lists
+ * and score_lists (device) hold n_lists stacked [total_q, k_in] arrays, list l at element offset
+ * l * list_stride (list_stride >= total_q * k_in): local indices (-1 padding) and their scores
+ * (non-negative int32, or the bit patterns of non-negative fp32 scores). idx (device)
+ * [total_q, top_k]: the top_k global indices by (score desc, index asc), in ascending index
+ * order, -1 padded; score (device, optional) [total_q, top_k] likewise, -1 on padding. The merge
+ * is exact because a member of the global top-k is in its own shard's top-k. 1 <= n_lists,
+ * 1 <= k_in, n_lists * k_in <= 16,384, 1 <= top_k <= 2,048; global indices must stay below 2^31.
+ */
+int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
+                    const int32_t* score_lists, int64_t list_stride, int32_t top_k, int32_t* idx,
+                    int32_t* score, void* stream);
+
+/*
+ * smla_dcp_local_indices: shard `shard`'s part of a global selection. idx (device)
+ * [total_q, top_k] global indices (-1 padding); local_idx (device) [total_q, top_k]: the entries
+ * g with g mod n_shards == shard, as g div n_shards, in their order, then -1. 1 <= n_shards,
+ * 0 <= shard < n_shards, 1 <= top_k <= 2,048.
+ */
+int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
+                           int32_t shard, int32_t* local_idx, void* stream);
+
+/*
+ * smla_lse_merge: partial attention results over disjoint row sets merged by log-sum-exp.
+ * outs (device) [n_parts, total_q, H, D_v] bf16; lses (device) [n_parts, total_q, H] fp32,
+ * natural log, -inf for a part that saw no row. out (device) [total_q, H, D_v] bf16:
+ * sum_i w_i out_i / sum_i w_i with w_i = exp(lse_i - max lse); lse (device, optional)
+ * [total_q, H]: max + log sum w_i (-inf and a zero output where no part saw a row).
+ * 1 <= n_parts <= 64, 1 <= H, 1 <= D_v <= 4,096; bf16 arrays 2-byte aligned, fp32 4-byte.
+ */
+int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, const void* outs,
+                   const float* lses, void* out, float* lse, void* stream);
+
 /* Workspace for the sparse-MLA entry points (decode needs split partials; prefill none). */
 size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v,
                                        int32_t top_k, int32_t decode);

@@ -29,6 +29,9 @@ EXPORTS = (
     "smla_indexer_scores_topk",
     "smla_indexer_scores_fp8",
     "smla_indexer_scores_topk_fp8",
+    "smla_topk_merge",
+    "smla_dcp_local_indices",
+    "smla_lse_merge",
     "smla_sparse_mla_workspace_bytes",
     "smla_sparse_mla_prefill",
     "smla_sparse_mla_decode",
@@ -82,6 +85,9 @@ def lib():
         L.smla_indexer_scores_topk.argtypes = [BP, P, P, P, i32, i32, i32, P, P, P, sz, P]
         L.smla_indexer_scores_fp8.argtypes = [BP, P, P, P, P, i32, i32, P, P]
         L.smla_indexer_scores_topk_fp8.argtypes = [BP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
+        L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, P, P, P]
+        L.smla_dcp_local_indices.argtypes = [i32, i32, P, i32, i32, P, P]
+        L.smla_lse_merge.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         L.smla_sparse_mla_workspace_bytes.argtypes = [BP, i32, i32, i32, i32]
         L.smla_sparse_mla_workspace_bytes.restype = sz
         for fn in ("smla_sparse_mla_prefill", "smla_sparse_mla_decode"):

@@ -351,6 +351,52 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k launch");
 }
 
+int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
+                    const int32_t* score_lists, int64_t list_stride, int32_t top_k, int32_t* idx,
+                    int32_t* score, void* stream) {
+  g_err.clear();
+  if (total_q < 1 || n_lists < 1 || k_in < 1 || top_k < 1)
+    return fail(SMLA_E_INVALID, "total_q, n_lists, k_in and top_k must be >= 1");
+  if ((int64_t)n_lists * k_in > smla::MERGE_MAX_CAND || top_k > smla::TOPK_MAX_K)
+    return fail(SMLA_E_UNSUPPORTED, "n_lists * k_in = %lld above %d or top_k = %d above %d",
+                (long long)n_lists * k_in, smla::MERGE_MAX_CAND, top_k, smla::TOPK_MAX_K);
+  if (list_stride < (int64_t)total_q * k_in)
+    return fail(SMLA_E_INVALID, "list_stride %lld below total_q * k_in", (long long)list_stride);
+  if (!idx_lists || !score_lists || !idx || !aligned(idx_lists, 4) || !aligned(score_lists, 4) ||
+      !aligned(idx, 4) || (score && !aligned(score, 4)))
+    return fail(SMLA_E_INVALID, "idx_lists, score_lists and idx must be non-NULL, all 4-byte aligned");
+  hipError_t e = smla::launch_topk_merge(total_q, n_lists, k_in, idx_lists, score_lists, list_stride,
+                                         top_k, idx, score, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k merge launch");
+}
+
+int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
+                           int32_t shard, int32_t* local_idx, void* stream) {
+  g_err.clear();
+  if (total_q < 1 || top_k < 1 || top_k > smla::TOPK_MAX_K || n_shards < 1 || shard < 0 ||
+      shard >= n_shards)
+    return fail(SMLA_E_INVALID, "need total_q >= 1, 1 <= top_k <= %d, 0 <= shard < n_shards",
+                smla::TOPK_MAX_K);
+  if (!idx || !local_idx || !aligned(idx, 4) || !aligned(local_idx, 4))
+    return fail(SMLA_E_INVALID, "idx and local_idx must be non-NULL, 4-byte aligned");
+  hipError_t e = smla::launch_local_indices(total_q, top_k, idx, n_shards, shard, local_idx,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "local indices launch");
+}
+
+int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, const void* outs,
+                   const float* lses, void* out, float* lse, void* stream) {
+  g_err.clear();
+  if (total_q < 1 || H < 1 || D_v < 1 || D_v > 4096 || n_parts < 1 || n_parts > 64)
+    return fail(SMLA_E_INVALID, "need total_q, H >= 1, 1 <= D_v <= 4096, 1 <= n_parts <= 64");
+  if (!outs || !lses || !out || !aligned(outs, 2) || !aligned(lses, 4) || !aligned(out, 2) ||
+      (lse && !aligned(lse, 4)))
+    return fail(SMLA_E_INVALID, "outs, lses and out must be non-NULL and aligned");
+  hipError_t e = smla::launch_lse_merge(total_q, H, D_v, n_parts, outs, lses, out, lse,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "lse merge launch");
+}
+
 size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v, int32_t top_k,
                                        int32_t decode) {
   if (!b || b->total_q < 1 || top_k < 1) return 0;

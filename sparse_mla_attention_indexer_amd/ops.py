@@ -178,6 +178,69 @@ def indexer_topk_fp8(plan: BatchPlan, q, k, k_scale, w, top_k: int, with_scores=
     return idx, score
 
 
+def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None):
+    """DCP top-k merge: idx_lists / score_lists [n_lists, total_q, k_in] int32 (shard l holds the
+    tokens l, l + n_lists, ...; local indices, -1 padding) -> the exact global top_k per token,
+    idx [total_q, top_k] ascending (-1 padded) and its scores."""
+    if idx_lists.dim() != 3 or score_lists.shape != idx_lists.shape:
+        raise ValueError("idx_lists and score_lists must both be [n_lists, total_q, k_in]")
+    n_lists, total_q, k_in = (int(v) for v in idx_lists.shape)
+    d = idx_lists.device
+    _req(idx_lists, "idx_lists", torch.int32, (n_lists, total_q, k_in), d)
+    _req(score_lists, "score_lists", torch.int32, (n_lists, total_q, k_in), d)
+    if idx is None:
+        idx = torch.empty((total_q, top_k), dtype=torch.int32, device=d)
+    if score is None:
+        score = torch.empty((total_q, top_k), dtype=torch.int32, device=d)
+    _req(idx, "idx", torch.int32, (total_q, top_k), d)
+    _req(score, "score", torch.int32, (total_q, top_k), d)
+    with torch.cuda.device(d):
+        check("smla_topk_merge",
+              lib().smla_topk_merge(total_q, n_lists, k_in, idx_lists.data_ptr(), score_lists.data_ptr(),
+                                    total_q * k_in, top_k, idx.data_ptr(), score.data_ptr(), _stream(d)))
+    return idx, score
+
+
+def dcp_local_indices(idx, n_shards: int, shard: int, out=None):
+    """Shard `shard`'s part of a global selection idx [total_q, top_k] (global indices): its
+    entries g with g % n_shards == shard as g // n_shards, in order, then -1."""
+    if idx.dim() != 2:
+        raise ValueError("idx must be [total_q, top_k]")
+    total_q, top_k = (int(v) for v in idx.shape)
+    _req(idx, "idx", torch.int32, (total_q, top_k), idx.device)
+    if out is None:
+        out = torch.empty_like(idx)
+    _req(out, "out", torch.int32, (total_q, top_k), idx.device)
+    with torch.cuda.device(idx.device):
+        check("smla_dcp_local_indices",
+              lib().smla_dcp_local_indices(total_q, top_k, idx.data_ptr(), n_shards, shard,
+                                           out.data_ptr(), _stream(idx.device)))
+    return out
+
+
+def lse_merge(outs, lses, out=None, lse=None):
+    """Partial attention results over disjoint row sets merged by log-sum-exp: outs
+    [n_parts, total_q, H, D_v] bf16, lses [n_parts, total_q, H] fp32 -> out [total_q, H, D_v]
+    bf16, lse [total_q, H] fp32."""
+    if outs.dim() != 4:
+        raise ValueError("outs must be [n_parts, total_q, H, D_v]")
+    n, total_q, H, D_v = (int(v) for v in outs.shape)
+    d = outs.device
+    _req(outs, "outs", torch.bfloat16, (n, total_q, H, D_v), d)
+    _req(lses, "lses", torch.float32, (n, total_q, H), d)
+    if out is None:
+        out = torch.empty((total_q, H, D_v), dtype=torch.bfloat16, device=d)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=d)
+    _req(out, "out", torch.bfloat16, (total_q, H, D_v), d)
+    _req(lse, "lse", torch.float32, (total_q, H), d)
+    with torch.cuda.device(d):
+        check("smla_lse_merge",
+              lib().smla_lse_merge(total_q, H, D_v, n, outs.data_ptr(), lses.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr(), _stream(d)))
+    return out, lse
+
+
 def mla_workspace(plan: BatchPlan, H: int, D_v: int, top_k: int, decode: bool) -> torch.Tensor:
     n = int(lib().smla_sparse_mla_workspace_bytes(plan.ref, H, D_v, top_k, int(decode)))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)

@@ -1,0 +1,153 @@
+"""GPU parity of the single-GPU DCP simulation: the KV cache of every request cut round robin into
+8 shards (shard l holds tokens l, l + 8, ...), the indexer, top-k and sparse MLA run on each
+shard's own rows, and the library's merges rebuild the unsharded answers.
+
+The merged top-k must equal the unsharded top-k bit for bit (and the oracle's merge of the same
+lists); the LSE-merged attention must match the fp64 oracle's unsharded attention within the
+attention tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indexer_amd import ops
+from sparse_mla_attention_indexer_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import Dev, assert_attn_close, oracle_mla, say  # noqa: E402
+
+N_SH = 8
+
+
+class Shards:
+    """Shard s of a decode batch (one query token per request): rows g = s, s + 8, ... of each
+    request up to the token's position, uploaded as a batch of its own."""
+
+    def __init__(self, x, dev: Dev):
+        d = x.dims
+        assert (x.n_q == 1).all()
+        self.dev = dev
+        self.parts = []
+        row0 = np.concatenate([[0], np.cumsum(x.kv_len)[:-1]])
+        for s in range(N_SH):
+            lens, rows = [], []
+            for b, kl in enumerate(x.kv_len):
+                p = int(kl) - 1
+                g = np.arange(s, p + 1, N_SH)
+                lens.append(g.size)
+                rows.append(row0[b] + g)
+            rows = np.concatenate(rows)
+            plan = ops.BatchPlan(np.ones(d.batch, np.int32), np.array(lens, np.int64), dev.device)
+            kv = torch.from_numpy(np.ascontiguousarray(x.kv[rows])).to(dev.device)
+            k_idx = torch.from_numpy(np.ascontiguousarray(x.k_idx[rows])).to(dev.device)
+            self.parts.append((plan, kv, k_idx))
+
+    def topk_lists(self, top_k):
+        d = self.dev.x.dims
+        idx = torch.empty((N_SH, d.total_q, top_k), dtype=torch.int32, device=self.dev.device)
+        sc = torch.empty_like(idx)
+        for s, (plan, _, k_idx) in enumerate(self.parts):
+            ops.indexer_topk(plan, self.dev.q_idx, k_idx, self.dev.w, top_k, idx=idx[s], score=sc[s],
+                             workspace=ops.topk_workspace(plan, 64, 128, top_k))
+        return idx, sc
+
+    def attention(self, merged_idx):
+        d = self.dev.x.dims
+        outs = torch.empty((N_SH, d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=self.dev.device)
+        lses = torch.empty((N_SH, d.total_q, d.H), dtype=torch.float32, device=self.dev.device)
+        for s, (plan, kv, _) in enumerate(self.parts):
+            local = ops.dcp_local_indices(merged_idx, N_SH, s)
+            ops.sparse_mla(plan, self.dev.q, kv, d.kv_format, d.D_v, local, d.sm_scale, decode=True,
+                           out=outs[s], lse=lses[s])
+        return ops.lse_merge(outs, lses)
+
+
+def _run(x, label, sample):
+    d = x.dims
+    dev = Dev(x)
+    say(f"[case] dcp x{N_SH} {label}: B={d.batch} kv_len={int(x.kv_len[0])}")
+    ref_idx, ref_sc = dev.topk()
+    sh = Shards(x, dev)
+    lists_i, lists_s = sh.topk_lists(d.top_k)
+    idx, sc = ops.topk_merge(lists_i, lists_s, d.top_k)
+    torch.cuda.synchronize()
+    idx_np, sc_np = idx.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(idx_np, ref_idx), "merged selection differs from the unsharded one"
+    assert np.array_equal(sc_np, ref_sc)
+    li, ls = lists_i.cpu().numpy(), lists_s.cpu().numpy()
+    for t in sample:
+        oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], d.top_k)
+        o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
+        assert np.array_equal(idx_np[t], oi[o]) and np.array_equal(sc_np[t], os_[o]), t
+    out, lse = sh.attention(idx)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mla(x, ref_idx[sample], sample)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[sample]
+    assert_attn_close(got, ref_o, lse.cpu().numpy()[sample], ref_l, f"dcp {label}")
+    # the unsharded decode path on the same selection agrees too
+    full_out, _ = dev.mla(ref_idx, decode=True)
+    ok, rep = W.check_attn(full_out[sample], ref_o)
+    assert ok
+
+
+def test_dcp_small_decode_batch():
+    x = W.generate(W.small_big_dims(batch=4, n_q=1, cached=20000))
+    _run(x, "4 x 1 after 20000", np.arange(4))
+
+
+def test_dcp_decode_batch_full_size():
+    x = W.generate(W.config_dims(1))
+    _run(x, "decode batch", np.array([0, 17, 31]))
+
+
+@pytest.mark.parametrize("values", [3, 1 << 30])
+def test_topk_merge_against_oracle(values):
+    # random per-shard lists (ascending local indices, scores with heavy ties or none), k below,
+    # at and above the union's size
+    rng = np.random.default_rng(values & 0xFFFF)
+    total_q, k_in = 5, 2048
+    li = np.full((N_SH, total_q, k_in), -1, np.int32)
+    ls = np.full((N_SH, total_q, k_in), -1, np.int32)
+    for s in range(N_SH):
+        for t in range(total_q):
+            n = [2048, 1500, 7, 0, 2048][t]
+            li[s, t, :n] = np.sort(rng.choice(100000, size=n, replace=False))
+            ls[s, t, :n] = rng.integers(0, values, size=n)
+    dv = torch.device("cuda:0")
+    for top_k in (2048, 1, 100):
+        idx, sc = ops.topk_merge(torch.from_numpy(li).to(dv), torch.from_numpy(ls).to(dv), top_k)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for t in range(total_q):
+            oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], top_k)
+            o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
+            assert np.array_equal(idx[t], oi[o]) and np.array_equal(sc[t], os_[o]), (top_k, t)
+
+
+def test_local_indices_and_lse_merge_small():
+    dv = torch.device("cuda:0")
+    rng = np.random.default_rng(3)
+    g = np.full((3, 300), -1, np.int32)
+    for t, n in enumerate((300, 123, 0)):
+        g[t, :n] = np.sort(rng.choice(5000, size=n, replace=False))
+    gt = torch.from_numpy(g).to(dv)
+    for s in (0, 3, 7):
+        got = ops.dcp_local_indices(gt, N_SH, s).cpu().numpy()
+        for t in range(3):
+            sel = g[t][(g[t] >= 0) & (g[t] % N_SH == s)] // N_SH
+            ref = np.concatenate([sel, np.full(300 - sel.size, -1)]).astype(np.int32)
+            assert np.array_equal(got[t], ref)
+    # LSE merge against the oracle's merge of the same bf16 partials (one part empty)
+    n, tq, H, D = 5, 3, 4, 40
+    outs = rng.standard_normal((n, tq, H, D)).astype(np.float32)
+    lses = rng.uniform(-3, 3, (n, tq, H)).astype(np.float32)
+    lses[2] = -np.inf
+    ob = torch.from_numpy(outs).to(torch.bfloat16)
+    out, lse = ops.lse_merge(ob.to(dv), torch.from_numpy(lses).to(dv))
+    outs64 = ob.double().numpy()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for t in range(tq):
+        ro, rl = oracle.lse_merge(outs64[:, t], lses[:, t].astype(np.float64))
+        assert np.abs(out[t] - ro).max() <= 1e-2 and np.abs(lse[t] - rl).max() <= 1e-5
