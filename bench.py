@@ -290,8 +290,7 @@ def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
 
     def merge_select():
         ops.topk_merge(lists_i, lists_s, d.top_k, idx=idx, score=sc)
-        for sh in range(n_sh):
-            ops.dcp_local_indices(idx, n_sh, sh, out=local[sh])
+        ops.dcp_local_indices(idx, n_sh, out=local)
 
     def merge_attend():
         ops.lse_merge(outs, lses, out=out, lse=lse)

@@ -158,24 +158,26 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
  * smla_topk_merge: the exact global top-k of each query token from the shards' lists. idx_lists
  * and score_lists (device) hold n_lists stacked [total_q, k_in] arrays, list l at element offset
  * l * list_stride (list_stride >= total_q * k_in): local indices (-1 padding) and their scores
- * (non-negative int32, or the bit patterns of non-negative fp32 scores). idx (device)
+ * (non-negative int32 with float_scores = 0; the bit patterns of non-negative fp32 scores, as
+ * smla_indexer_scores_topk_fp8 returns them, with float_scores = 1). idx (device)
  * [total_q, top_k]: the top_k global indices by (score desc, index asc), in ascending index
- * order, -1 padded; score (device, optional) [total_q, top_k] likewise, -1 on padding. The merge
+ * order, -1 padded; score (device, optional) [total_q, top_k] likewise, -1 (-1.0f) on padding. The merge
  * is exact because a member of the global top-k is in its own shard's top-k. 1 <= n_lists,
  * 1 <= k_in, n_lists * k_in <= 16,384, 1 <= top_k <= 2,048; global indices must stay below 2^31.
  */
 int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
-                    const int32_t* score_lists, int64_t list_stride, int32_t top_k, int32_t* idx,
-                    int32_t* score, void* stream);
+                    const int32_t* score_lists, int64_t list_stride, int32_t float_scores,
+                    int32_t top_k, int32_t* idx, int32_t* score, void* stream);
 
 /*
- * smla_dcp_local_indices: shard `shard`'s part of a global selection. idx (device)
- * [total_q, top_k] global indices (-1 padding); local_idx (device) [total_q, top_k]: the entries
- * g with g mod n_shards == shard, as g div n_shards, in their order, then -1. 1 <= n_shards,
- * 0 <= shard < n_shards, 1 <= top_k <= 2,048.
+ * smla_dcp_local_indices: every shard's part of a global selection. idx (device)
+ * [total_q, top_k] global indices (-1 padding); local_idx (device) [n_shards, total_q, top_k]:
+ * for shard s, the entries g with g mod n_shards == s, as g div n_shards, in their order, then -1
+ * (the order the sparse-MLA entry points read them in, padding last). 1 <= n_shards <= 65,535,
+ * 1 <= top_k <= 2,048.
  */
 int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
-                           int32_t shard, int32_t* local_idx, void* stream);
+                           int32_t* local_idx, void* stream);
 
 /*
  * smla_lse_merge: partial attention results over disjoint row sets merged by log-sum-exp.

@@ -85,8 +85,8 @@ def lib():
         L.smla_indexer_scores_topk.argtypes = [BP, P, P, P, i32, i32, i32, P, P, P, sz, P]
         L.smla_indexer_scores_fp8.argtypes = [BP, P, P, P, P, i32, i32, P, P]
         L.smla_indexer_scores_topk_fp8.argtypes = [BP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
-        L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, P, P, P]
-        L.smla_dcp_local_indices.argtypes = [i32, i32, P, i32, i32, P, P]
+        L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, i32, P, P, P]
+        L.smla_dcp_local_indices.argtypes = [i32, i32, P, i32, P, P]
         L.smla_lse_merge.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         L.smla_sparse_mla_workspace_bytes.argtypes = [BP, i32, i32, i32, i32]
         L.smla_sparse_mla_workspace_bytes.restype = sz

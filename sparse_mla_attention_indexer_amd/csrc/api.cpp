@@ -352,8 +352,8 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
 }
 
 int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
-                    const int32_t* score_lists, int64_t list_stride, int32_t top_k, int32_t* idx,
-                    int32_t* score, void* stream) {
+                    const int32_t* score_lists, int64_t list_stride, int32_t float_scores,
+                    int32_t top_k, int32_t* idx, int32_t* score, void* stream) {
   g_err.clear();
   if (total_q < 1 || n_lists < 1 || k_in < 1 || top_k < 1)
     return fail(SMLA_E_INVALID, "total_q, n_lists, k_in and top_k must be >= 1");
@@ -365,21 +365,22 @@ int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_
   if (!idx_lists || !score_lists || !idx || !aligned(idx_lists, 4) || !aligned(score_lists, 4) ||
       !aligned(idx, 4) || (score && !aligned(score, 4)))
     return fail(SMLA_E_INVALID, "idx_lists, score_lists and idx must be non-NULL, all 4-byte aligned");
+  if (float_scores != 0 && float_scores != 1) return fail(SMLA_E_INVALID, "float_scores must be 0 or 1");
   hipError_t e = smla::launch_topk_merge(total_q, n_lists, k_in, idx_lists, score_lists, list_stride,
-                                         top_k, idx, score, static_cast<hipStream_t>(stream));
+                                         top_k, idx, score, float_scores != 0,
+                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k merge launch");
 }
 
 int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
-                           int32_t shard, int32_t* local_idx, void* stream) {
+                           int32_t* local_idx, void* stream) {
   g_err.clear();
-  if (total_q < 1 || top_k < 1 || top_k > smla::TOPK_MAX_K || n_shards < 1 || shard < 0 ||
-      shard >= n_shards)
-    return fail(SMLA_E_INVALID, "need total_q >= 1, 1 <= top_k <= %d, 0 <= shard < n_shards",
+  if (total_q < 1 || top_k < 1 || top_k > smla::TOPK_MAX_K || n_shards < 1 || n_shards > 65535)
+    return fail(SMLA_E_INVALID, "need total_q >= 1, 1 <= top_k <= %d, 1 <= n_shards <= 65535",
                 smla::TOPK_MAX_K);
   if (!idx || !local_idx || !aligned(idx, 4) || !aligned(local_idx, 4))
     return fail(SMLA_E_INVALID, "idx and local_idx must be non-NULL, 4-byte aligned");
-  hipError_t e = smla::launch_local_indices(total_q, top_k, idx, n_shards, shard, local_idx,
+  hipError_t e = smla::launch_local_indices(total_q, top_k, idx, n_shards, local_idx,
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "local indices launch");
 }

@@ -8,11 +8,8 @@
 // a member of the global top-k has fewer than k rows above it anywhere, so it is in its own
 // shard's top-k too.
 //
-//  - topk_merge_kernel: one workgroup per query token; the union of the shards' lists as unique
-//    64-bit keys (score << 32 | ~global index) in LDS, an MSD radix select over 8-bit digits for
-//    the k-th largest key, then the selected (global index, score) pairs sorted by index
-//    (bitonic, in LDS).
-//  - local_indices_kernel: a shard's part of a global selection, as ascending local indices,
+//  - the top-k merge lives with the other selection kernels (topk.hip: topk_merge_kernel);
+//  - local_indices_kernel: each shard's part of a global selection, as ascending local indices,
 //    compacted to the front (the attention kernel skips trailing padding tiles).
 //  - lse_merge_kernel: per (token, head), weights exp(lse_i - max) over the parts, bf16 in and out.
 #include "smla_internal.h"
@@ -22,110 +19,16 @@ namespace smla {
 namespace {
 
 
-constexpr int NT_M = 256;
-
-__global__ __launch_bounds__(NT_M) void topk_merge_kernel(int n_lists, int k_in,
-                                                          const int32_t* __restrict__ idx_lists,
-                                                          const int32_t* __restrict__ score_lists,
-                                                          int64_t list_stride, int top_k,
-                                                          int32_t* __restrict__ idx_out,
-                                                          int32_t* __restrict__ score_out) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);                      // [MERGE_MAX_CAND]
-  uint64_t* sel = keys + MERGE_MAX_CAND;  // [TOPK_MAX_K] (global index << 32 | score), pow2
-  __shared__ int hist[256];
-  __shared__ int nkeys, nsel, digit, need_s;
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid == 0) nkeys = 0, nsel = 0;
-  __syncthreads();
-
-  // the union: every valid entry of every list, as (score, global index) keys
-  const int ncand = n_lists * k_in;
-  for (int c = tid; c < ncand; c += NT_M) {
-    const int l = c / k_in, j = c - l * k_in;
-    const int64_t off = l * list_stride + t * k_in + j;
-    const int32_t local = idx_lists[off];
-    if (local >= 0) {
-      const uint32_t g = (uint32_t)local * (uint32_t)n_lists + (uint32_t)l;
-      const int slot = atomicAdd(&nkeys, 1);
-      keys[slot] = ((uint64_t)(uint32_t)score_lists[off] << 32) | (uint64_t)(0xFFFFFFFFu - g);
-    }
-  }
-  __syncthreads();
-  const int n = nkeys;
-
-  // the cut: the min(top_k, n)-th largest key, digit by digit from the top
-  uint64_t prefix = 0, mask = 0;
-  const int take = min(top_k, n);
-  if (take < n) {
-    int need = take;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += NT_M)
-        if ((keys[i] & mask) == prefix) atomicAdd(&hist[(keys[i] >> shift) & 255], 1);
-      __syncthreads();
-      if (tid == 0) {
-        int above = 0, d = 255;
-        for (; d > 0; --d) {
-          if (above + hist[d] >= need) break;
-          above += hist[d];
-        }
-        digit = d;
-        need_s = need - above;
-      }
-      __syncthreads();
-      prefix |= (uint64_t)digit << shift;
-      mask |= (uint64_t)255 << shift;
-      need = need_s;
-      __syncthreads();
-    }
-  }
-  // selected: every key at or above the cut (keys are unique: exactly `take` of them)
-  for (int i = tid; i < n; i += NT_M) {
-    if (take == n || keys[i] >= prefix) {
-      const int slot = atomicAdd(&nsel, 1);
-      if (slot < TOPK_MAX_K)  // duplicate indices in the lists (invalid input) cannot overrun
-        sel[slot] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)keys[i]) << 32) | (keys[i] >> 32);
-    }
-  }
-  __syncthreads();
-  // ascending global index: bitonic sort of the selected pairs, padded with all-ones
-  int m = 1;
-  while (m < take) m <<= 1;
-  for (int i = take + tid; i < m; i += NT_M) sel[i] = ~0ull;
-  __syncthreads();
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < m / 2; i += NT_M) {
-        const int lo = 2 * i - (i & (stride - 1));  // first element of the i-th pair
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = sel[lo], b = sel[hi];
-        if ((a > b) == up) {
-          sel[lo] = b;
-          sel[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  int32_t* oi = idx_out + t * top_k;
-  int32_t* os = score_out ? score_out + t * top_k : nullptr;
-  for (int j = tid; j < top_k; j += NT_M) {
-    oi[j] = j < take ? (int32_t)(sel[j] >> 32) : -1;
-    if (os) os[j] = j < take ? (int32_t)(uint32_t)sel[j] : -1;
-  }
-}
-
-// Shard `shard` of n_shards: the entries g of a global selection with g mod n == shard, as
-// g div n, in order, then -1. One 256-thread workgroup per token; each thread a contiguous chunk.
-__global__ __launch_bounds__(256) void local_indices_kernel(int top_k, const int32_t* __restrict__ idx,
-                                                            int n_shards, int shard,
+// Every shard's part of a global selection: shard s (blockIdx.y) gets the entries g with
+// g mod n == s, as g div n, in order, then -1. One 256-thread workgroup per (token, shard); each
+// thread takes a contiguous chunk.
+__global__ __launch_bounds__(256) void local_indices_kernel(int total_q, int top_k,
+                                                            const int32_t* __restrict__ idx,
+                                                            int n_shards,
                                                             int32_t* __restrict__ local_idx) {
   __shared__ int pre[257];
   const int64_t t = blockIdx.x;
+  const int shard = blockIdx.y;
   const int tid = threadIdx.x;
   const int chunk = (top_k + 255) / 256;
   const int j0 = min(tid * chunk, top_k), j1 = min(j0 + chunk, top_k);
@@ -138,7 +41,7 @@ __global__ __launch_bounds__(256) void local_indices_kernel(int top_k, const int
   if (tid == 0)
     for (int i = 1; i <= 256; ++i) pre[i] += pre[i - 1];
   __syncthreads();
-  int32_t* out = local_idx + t * top_k;
+  int32_t* out = local_idx + ((int64_t)shard * total_q + t) * top_k;
   int pos = pre[tid];
   for (int j = j0; j < j1; ++j) {
     const int32_t g = row[j];
@@ -183,29 +86,10 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(int total_q, int H, int D
 
 }  // namespace
 
-size_t topk_merge_lds_bytes() {
-  return sizeof(uint64_t) * (MERGE_MAX_CAND + TOPK_MAX_K);
-}
-
-hipError_t launch_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
-                             const int32_t* score_lists, int64_t list_stride, int32_t top_k,
-                             int32_t* idx, int32_t* score, hipStream_t s) {
-  const size_t lds = topk_merge_lds_bytes();
-  static const bool lds_set = [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    return true;
-  }();
-  (void)lds_set;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)total_q), dim3(NT_M), lds, s, n_lists, k_in,
-                     idx_lists, score_lists, list_stride, top_k, idx, score);
-  return hipGetLastError();
-}
-
 hipError_t launch_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
-                                int32_t shard, int32_t* local_idx, hipStream_t s) {
-  hipLaunchKernelGGL(local_indices_kernel, dim3((unsigned)total_q), dim3(256), 0, s, top_k, idx,
-                     n_shards, shard, local_idx);
+                                int32_t* local_idx, hipStream_t s) {
+  hipLaunchKernelGGL(local_indices_kernel, dim3((unsigned)total_q, (unsigned)n_shards), dim3(256), 0, s,
+                     total_q, top_k, idx, n_shards, local_idx);
   return hipGetLastError();
 }
 

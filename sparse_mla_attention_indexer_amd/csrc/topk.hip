@@ -350,6 +350,146 @@ __global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ 
       wcnt);
 }
 
+// ---- DCP top-k merge: the union of per-shard lists, one 1024-thread workgroup per token ----
+// Shard l of n_lists holds the tokens l, l + n_lists, ...; list entry (local j, score) is global
+// index j n_lists + l. The union's keys sit in LDS; the cut is found as for a row (histogram of
+// score codes, then an exact radix select inside the cut bin), and the selected (index, score)
+// pairs are sorted by index (bitonic) before they are written.
+template <bool FB>
+__global__ __launch_bounds__(NT_A) void topk_merge_kernel(int n_lists, int k_in,
+                                                          const int32_t* __restrict__ idx_lists,
+                                                          const int32_t* __restrict__ score_lists,
+                                                          int64_t list_stride, int top_k,
+                                                          int32_t* __restrict__ idx_out,
+                                                          int32_t* __restrict__ score_out) {
+  extern __shared__ __align__(16) unsigned char smem_m[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem_m);  // [MERGE_MAX_CAND], 0: no entry
+  int* hist = reinterpret_cast<int*>(keys + MERGE_MAX_CAND);  // [TOPK_BINS]
+  uint64_t* work = reinterpret_cast<uint64_t*>(hist + TOPK_BINS);  // [TOPK_MAX_K]: b* keys, then the selection
+  __shared__ int hist2[256];
+  __shared__ int red[NT_A / 64 + 1];
+  __shared__ int cut[2];
+  __shared__ uint64_t pm[2];
+  __shared__ int nvalid, nk, nsel;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) nvalid = 0, nk = 0, nsel = 0;
+  for (int i = tid; i < TOPK_BINS; i += NT_A) hist[i] = 0;
+  __syncthreads();
+  const int ncand = n_lists * k_in;
+  int mine = 0;
+  for (int c = tid; c < ncand; c += NT_A) {
+    const int l = c / k_in;
+    const int64_t off = l * list_stride + t * k_in + (c - l * k_in);
+    const int32_t local = idx_lists[off];
+    uint64_t key = 0;  // valid keys have ~index >= 2^31, so 0 is below all of them
+    if (local >= 0) {
+      const uint32_t sc = (uint32_t)score_lists[off];
+      key = sel_key((int32_t)sc, (int64_t)local * n_lists + l);
+      atomicAdd(&hist[score_bin<FB>(sc)], 1);
+      ++mine;
+    }
+    keys[c] = key;
+  }
+  if (mine) atomicAdd(&nvalid, mine);
+  __syncthreads();
+  const int n = nvalid;
+  const int take = min(top_k, n);
+  int bstar = -1;  // every valid key selected
+  uint64_t prefix = 0, mask = 0;
+  if (take < n) {
+    find_cut<NT_A>(hist, TOPK_BINS, take, red, cut);
+    bstar = cut[0];
+    const int need = take - cut[1];
+    if (hist[bstar] != need) {
+      const int nb = hist[bstar];
+      if (nb <= TOPK_MAX_K) {
+        const int lane = tid & 63;
+        for (int i0 = 0; i0 < ncand; i0 += NT_A) {
+          const int i = i0 + tid;
+          const bool f = i < ncand && keys[i] != 0 && score_bin<FB>((uint32_t)(keys[i] >> 32)) == bstar;
+          const uint64_t m = __ballot(f);
+          if (m) {
+            int base = 0;
+            const int leader = __builtin_ctzll(m);
+            if (lane == leader) base = atomicAdd(&nk, __popcll(m));
+            base = __shfl(base, leader);
+            if (f) work[base + __popcll(m & ((1ull << lane) - 1))] = keys[i];
+          }
+        }
+        __syncthreads();
+        if (tid < 64) {
+          uint64_t pf, mk;
+          wave_radix_cut([&](int i) { return work[i]; }, nb, need, hist2, &pf, &mk);
+          if (tid == 0) {
+            pm[0] = pf;
+            pm[1] = mk;
+          }
+        }
+        __syncthreads();
+      } else {
+        radix_cut<NT_A>(
+            ncand, need, [&](int i) { return keys[i]; },
+            [&](int i) { return keys[i] != 0 && score_bin<FB>((uint32_t)(keys[i] >> 32)) == bstar; },
+            hist2, red, cut, pm);
+      }
+      prefix = pm[0];
+      mask = pm[1];
+    }
+  }
+  __syncthreads();  // `work` is reused for the selection
+  {
+    const int lane = tid & 63;
+    for (int c0 = 0; c0 < ncand; c0 += NT_A) {  // one counter update per wave and pass
+      const int c = c0 + tid;
+      const uint64_t key = c < ncand ? keys[c] : 0;
+      bool f = key != 0;
+      if (f && bstar >= 0) {
+        const int b = score_bin<FB>((uint32_t)(key >> 32));
+        f = b > bstar || (b == bstar && (key & mask) >= prefix);
+      }
+      const uint64_t m = __ballot(f);
+      if (m) {
+        int base = 0;
+        const int leader = __builtin_ctzll(m);
+        if (lane == leader) base = atomicAdd(&nsel, __popcll(m));
+        base = __shfl(base, leader);
+        const int slot = base + __popcll(m & ((1ull << lane) - 1));
+        if (f && slot < TOPK_MAX_K)  // exactly `take` for valid input; duplicates cannot overrun
+          work[slot] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)key) << 32) | (key >> 32);
+      }
+    }
+  }
+  __syncthreads();
+  // ascending global index: bitonic sort of the selected (index, score) pairs
+  int m = 1;
+  while (m < take) m <<= 1;
+  for (int i = take + tid; i < m; i += NT_A) work[i] = ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= m; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < m / 2; i += NT_A) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t a = work[lo], b = work[hi];
+        if ((a > b) == up) {
+          work[lo] = b;
+          work[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* oi = idx_out + t * top_k;
+  int32_t* os = score_out ? score_out + t * top_k : nullptr;
+  const int32_t pad = FB ? (int32_t)0xBF800000u : -1;
+  for (int j = tid; j < top_k; j += NT_A) {
+    oi[j] = j < take ? (int32_t)(work[j] >> 32) : -1;
+    if (os) os[j] = j < take ? (int32_t)(uint32_t)work[j] : pad;
+  }
+}
+
 // ---- rows of n > TOPK_LDS_MAX: workspace layout ------------------------------------------
 __host__ __device__ inline TopkWs topk_ws(void* base, int64_t total_q, int64_t nseg) {
   char* p = static_cast<char*>(base);
@@ -920,6 +1060,31 @@ hipError_t launch_topk_t(const smla_batch& b, const int32_t* scores, int32_t top
 }
 
 }  // namespace
+
+size_t topk_merge_lds_bytes() {
+  return sizeof(uint64_t) * (MERGE_MAX_CAND + TOPK_MAX_K) + sizeof(int) * TOPK_BINS;
+}
+
+hipError_t launch_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
+                             const int32_t* score_lists, int64_t list_stride, int32_t top_k,
+                             int32_t* idx, int32_t* score, bool fscores, hipStream_t s) {
+  const size_t lds = topk_merge_lds_bytes();
+  static const bool lds_set = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    return true;
+  }();
+  (void)lds_set;
+  if (fscores)
+    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3((unsigned)total_q), dim3(NT_A), lds, s, n_lists,
+                       k_in, idx_lists, score_lists, list_stride, top_k, idx, score);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<false>, dim3((unsigned)total_q), dim3(NT_A), lds, s, n_lists,
+                       k_in, idx_lists, score_lists, list_stride, top_k, idx, score);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
                        int32_t* score, const TopkWs& w, hipStream_t s, bool fscores) {

@@ -178,10 +178,11 @@ def indexer_topk_fp8(plan: BatchPlan, q, k, k_scale, w, top_k: int, with_scores=
     return idx, score
 
 
-def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None):
+def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None, float_scores=False):
     """DCP top-k merge: idx_lists / score_lists [n_lists, total_q, k_in] int32 (shard l holds the
-    tokens l, l + n_lists, ...; local indices, -1 padding) -> the exact global top_k per token,
-    idx [total_q, top_k] ascending (-1 padded) and its scores."""
+    tokens l, l + n_lists, ...; local indices, -1 padding; scores as int32, or fp32 bit patterns
+    with float_scores) -> the exact global top_k per token, idx [total_q, top_k] ascending (-1
+    padded) and its scores (int32 bit patterns)."""
     if idx_lists.dim() != 3 or score_lists.shape != idx_lists.shape:
         raise ValueError("idx_lists and score_lists must both be [n_lists, total_q, k_in]")
     n_lists, total_q, k_in = (int(v) for v in idx_lists.shape)
@@ -197,24 +198,26 @@ def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None):
     with torch.cuda.device(d):
         check("smla_topk_merge",
               lib().smla_topk_merge(total_q, n_lists, k_in, idx_lists.data_ptr(), score_lists.data_ptr(),
-                                    total_q * k_in, top_k, idx.data_ptr(), score.data_ptr(), _stream(d)))
+                                    total_q * k_in, int(bool(float_scores)), top_k, idx.data_ptr(),
+                                    score.data_ptr(), _stream(d)))
     return idx, score
 
 
-def dcp_local_indices(idx, n_shards: int, shard: int, out=None):
-    """Shard `shard`'s part of a global selection idx [total_q, top_k] (global indices): its
-    entries g with g % n_shards == shard as g // n_shards, in order, then -1."""
+def dcp_local_indices(idx, n_shards: int, out=None):
+    """Every shard's part of a global selection idx [total_q, top_k] (global indices): out
+    [n_shards, total_q, top_k], for shard s the entries g with g % n_shards == s as
+    g // n_shards, in order, then -1."""
     if idx.dim() != 2:
         raise ValueError("idx must be [total_q, top_k]")
     total_q, top_k = (int(v) for v in idx.shape)
     _req(idx, "idx", torch.int32, (total_q, top_k), idx.device)
     if out is None:
-        out = torch.empty_like(idx)
-    _req(out, "out", torch.int32, (total_q, top_k), idx.device)
+        out = torch.empty((n_shards, total_q, top_k), dtype=torch.int32, device=idx.device)
+    _req(out, "out", torch.int32, (n_shards, total_q, top_k), idx.device)
     with torch.cuda.device(idx.device):
         check("smla_dcp_local_indices",
-              lib().smla_dcp_local_indices(total_q, top_k, idx.data_ptr(), n_shards, shard,
-                                           out.data_ptr(), _stream(idx.device)))
+              lib().smla_dcp_local_indices(total_q, top_k, idx.data_ptr(), n_shards, out.data_ptr(),
+                                           _stream(idx.device)))
     return out
 
 

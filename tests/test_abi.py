@@ -130,6 +130,29 @@ def test_fp8_indexer_validation(L):
     assert rc == _lib.SMLA_E_INVALID
 
 
+def test_dcp_merge_validation(L):
+    # top-k merge: sizes, union cap, list stride, flag, pointers
+    ok = dict(total_q=4, n_lists=8, k_in=2048, stride=4 * 2048, flt=0, top_k=2048)
+
+    def merge(**kw):
+        a = {**ok, **kw}
+        return L.smla_topk_merge(a["total_q"], a["n_lists"], a["k_in"], FAKE, FAKE, a["stride"],
+                                 a["flt"], a["top_k"], FAKE, None, None)
+
+    assert merge(n_lists=0) == _lib.SMLA_E_INVALID
+    assert merge(n_lists=9) == _lib.SMLA_E_UNSUPPORTED   # 9 x 2048 candidates > 16,384
+    assert merge(top_k=2049) == _lib.SMLA_E_UNSUPPORTED
+    assert merge(stride=100) == _lib.SMLA_E_INVALID
+    assert merge(flt=2) == _lib.SMLA_E_INVALID
+    assert L.smla_topk_merge(4, 8, 2048, None, FAKE, 4 * 2048, 0, 2048, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_dcp_local_indices(4, 2049, FAKE, 8, FAKE, None) == _lib.SMLA_E_INVALID
+    assert L.smla_dcp_local_indices(4, 2048, FAKE, 0, FAKE, None) == _lib.SMLA_E_INVALID
+    assert L.smla_dcp_local_indices(4, 2048, None, 8, FAKE, None) == _lib.SMLA_E_INVALID
+    assert L.smla_lse_merge(4, 64, 512, 0, FAKE, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_lse_merge(4, 64, 5000, 8, FAKE, FAKE, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_lse_merge(4, 64, 512, 8, FAKE, FAKE + 2, FAKE, None, None) == _lib.SMLA_E_INVALID
+
+
 def test_mla_validation(L):
     b = _fake_batch()
     args = dict(H=64, D_qk=576, D_v=512)

@@ -57,9 +57,9 @@ class Shards:
         d = self.dev.x.dims
         outs = torch.empty((N_SH, d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=self.dev.device)
         lses = torch.empty((N_SH, d.total_q, d.H), dtype=torch.float32, device=self.dev.device)
+        local = ops.dcp_local_indices(merged_idx, N_SH)
         for s, (plan, kv, _) in enumerate(self.parts):
-            local = ops.dcp_local_indices(merged_idx, N_SH, s)
-            ops.sparse_mla(plan, self.dev.q, kv, d.kv_format, d.D_v, local, d.sm_scale, decode=True,
+            ops.sparse_mla(plan, self.dev.q, kv, d.kv_format, d.D_v, local[s], d.sm_scale, decode=True,
                            out=outs[s], lse=lses[s])
         return ops.lse_merge(outs, lses)
 
@@ -102,11 +102,12 @@ def test_dcp_decode_batch_full_size():
     _run(x, "decode batch", np.array([0, 17, 31]))
 
 
-@pytest.mark.parametrize("values", [3, 1 << 30])
+@pytest.mark.parametrize("values", [3, 1 << 30, "fp32"])
 def test_topk_merge_against_oracle(values):
-    # random per-shard lists (ascending local indices, scores with heavy ties or none), k below,
-    # at and above the union's size
-    rng = np.random.default_rng(values & 0xFFFF)
+    # random per-shard lists (ascending local indices, scores with heavy ties or none, or fp32
+    # bit patterns), k below, at and above the union's size
+    fp = values == "fp32"
+    rng = np.random.default_rng(7 if fp else values & 0xFFFF)
     total_q, k_in = 5, 2048
     li = np.full((N_SH, total_q, k_in), -1, np.int32)
     ls = np.full((N_SH, total_q, k_in), -1, np.int32)
@@ -114,15 +115,21 @@ def test_topk_merge_against_oracle(values):
         for t in range(total_q):
             n = [2048, 1500, 7, 0, 2048][t]
             li[s, t, :n] = np.sort(rng.choice(100000, size=n, replace=False))
-            ls[s, t, :n] = rng.integers(0, values, size=n)
+            if fp:
+                ls[s, t, :n] = rng.gamma(2.0, 30.0, size=n).astype(np.float32).view(np.int32)
+            else:
+                ls[s, t, :n] = rng.integers(0, values, size=n)
     dv = torch.device("cuda:0")
+    pad = np.float32(-1.0).view(np.int32) if fp else -1
     for top_k in (2048, 1, 100):
-        idx, sc = ops.topk_merge(torch.from_numpy(li).to(dv), torch.from_numpy(ls).to(dv), top_k)
+        idx, sc = ops.topk_merge(torch.from_numpy(li).to(dv), torch.from_numpy(ls).to(dv), top_k,
+                                 float_scores=fp)
         idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
         for t in range(total_q):
             oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], top_k)
             o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
-            assert np.array_equal(idx[t], oi[o]) and np.array_equal(sc[t], os_[o]), (top_k, t)
+            ref_s = np.where(oi[o] < 0, pad, os_[o])
+            assert np.array_equal(idx[t], oi[o]) and np.array_equal(sc[t], ref_s), (top_k, t)
 
 
 def test_local_indices_and_lse_merge_small():
@@ -132,8 +139,9 @@ def test_local_indices_and_lse_merge_small():
     for t, n in enumerate((300, 123, 0)):
         g[t, :n] = np.sort(rng.choice(5000, size=n, replace=False))
     gt = torch.from_numpy(g).to(dv)
-    for s in (0, 3, 7):
-        got = ops.dcp_local_indices(gt, N_SH, s).cpu().numpy()
+    allsh = ops.dcp_local_indices(gt, N_SH).cpu().numpy()
+    for s in range(N_SH):
+        got = allsh[s]
         for t in range(3):
             sel = g[t][(g[t] >= 0) & (g[t] % N_SH == s)] // N_SH
             ref = np.concatenate([sel, np.full(300 - sel.size, -1)]).astype(np.int32)
