@@ -56,12 +56,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (bf)f);
 }
 
-// One 64-thread block per (token, head); thread x covers dims x, x + 64, ...
-__global__ __launch_bounds__(64) void lse_merge_kernel(int total_q, int H, int D_v, int n_parts,
-                                                       const uint16_t* __restrict__ outs,
-                                                       const float* __restrict__ lses,
-                                                       uint16_t* __restrict__ out,
-                                                       float* __restrict__ lse_out) {
+// One 128-thread block per (token, head); thread x covers dims 4x .. 4x + 3, then 512 further on.
+// All parts' lse values and the first eight parts' outputs go out together.
+__global__ __launch_bounds__(128) void lse_merge_kernel(int total_q, int H, int D_v, int n_parts,
+                                                        const uint16_t* __restrict__ outs,
+                                                        const float* __restrict__ lses,
+                                                        uint16_t* __restrict__ out,
+                                                        float* __restrict__ lse_out) {
   const int64_t th = blockIdx.x;  // token * H + head
   const int64_t plane_o = (int64_t)total_q * H * D_v, plane_l = (int64_t)total_q * H;
   float m = -INFINITY;
@@ -72,14 +73,25 @@ __global__ __launch_bounds__(64) void lse_merge_kernel(int total_q, int H, int D
     z += li == -INFINITY ? 0.f : __expf(li - m);
   }
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  for (int d = threadIdx.x; d < D_v; d += 64) {
-    float acc = 0.f;
+  const bool vec = (D_v & 3) == 0 && ((uintptr_t)outs & 7) == 0;  // 8-byte loads
+  for (int d0 = 4 * threadIdx.x; d0 < D_v; d0 += 512) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < n_parts; ++i) {
       const float li = lses[i * plane_l + th];
       if (li == -INFINITY) continue;
-      acc += __expf(li - m) * bf16_to_f32(outs[i * plane_o + th * D_v + d]);
+      const float wi = __expf(li - m);
+      const uint16_t* src = outs + i * plane_o + th * D_v + d0;
+      if (vec) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        acc[0] += wi * __uint_as_float(v.x << 16);
+        acc[1] += wi * __uint_as_float(v.x & 0xFFFF0000u);
+        acc[2] += wi * __uint_as_float(v.y << 16);
+        acc[3] += wi * __uint_as_float(v.y & 0xFFFF0000u);
+      } else {
+        for (int e = 0; e < 4 && d0 + e < D_v; ++e) acc[e] += wi * bf16_to_f32(src[e]);
+      }
     }
-    out[th * D_v + d] = f32_to_bf16(acc * inv);
+    for (int e = 0; e < 4 && d0 + e < D_v; ++e) out[th * D_v + d0 + e] = f32_to_bf16(acc[e] * inv);
   }
   if (lse_out && threadIdx.x == 0) lse_out[th] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
@@ -96,7 +108,7 @@ hipError_t launch_local_indices(int32_t total_q, int32_t top_k, const int32_t* i
 hipError_t launch_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts,
                             const void* outs, const float* lses, void* out, float* lse,
                             hipStream_t s) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((int64_t)total_q * H)), dim3(64), 0, s,
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((int64_t)total_q * H)), dim3(128), 0, s,
                      total_q, H, D_v, n_parts, static_cast<const uint16_t*>(outs), lses,
                      static_cast<uint16_t*>(out), lse);
   return hipGetLastError();

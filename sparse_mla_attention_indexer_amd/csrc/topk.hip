@@ -378,18 +378,30 @@ __global__ __launch_bounds__(NT_A) void topk_merge_kernel(int n_lists, int k_in,
   __syncthreads();
   const int ncand = n_lists * k_in;
   int mine = 0;
-  for (int c = tid; c < ncand; c += NT_A) {
-    const int l = c / k_in;
-    const int64_t off = l * list_stride + t * k_in + (c - l * k_in);
-    const int32_t local = idx_lists[off];
-    uint64_t key = 0;  // valid keys have ~index >= 2^31, so 0 is below all of them
-    if (local >= 0) {
-      const uint32_t sc = (uint32_t)score_lists[off];
-      key = sel_key((int32_t)sc, (int64_t)local * n_lists + l);
-      atomicAdd(&hist[score_bin<FB>(sc)], 1);
-      ++mine;
+  {
+    // every load of the thread's candidates in flight before any is used
+    constexpr int PER = MERGE_MAX_CAND / NT_A;
+    int32_t lv[PER], sv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = u * NT_A + tid;
+      const int l = c / k_in;
+      const int64_t off = l * list_stride + t * k_in + (c - l * k_in);
+      lv[u] = c < ncand ? idx_lists[off] : -1;
+      sv[u] = c < ncand ? score_lists[off] : 0;
     }
-    keys[c] = key;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = u * NT_A + tid;
+      if (c >= ncand) break;
+      uint64_t key = 0;  // valid keys have ~index >= 2^31, so 0 is below all of them
+      if (lv[u] >= 0) {
+        key = sel_key(sv[u], (int64_t)lv[u] * n_lists + c / k_in);
+        atomicAdd(&hist[score_bin<FB>((uint32_t)sv[u])], 1);
+        ++mine;
+      }
+      keys[c] = key;
+    }
   }
   if (mine) atomicAdd(&nvalid, mine);
   __syncthreads();
