@@ -254,13 +254,14 @@ __device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned
   dq.rope_store(kb, r, m);
 }
 
-// One (token, split): rows idx_row[r_begin, r_end) of the token's request.
+// One (token, split): the split's share of the tiles of the token's index list, up to its last
+// valid entry.
 // Writes either the final bf16 output (+ lse) or an fp16 partial (+ lse) for the combine.
 __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ toks,
                                                         const __bf16* __restrict__ q,
                                                         const unsigned char* __restrict__ kv,
                                                         const int32_t* __restrict__ idx,
-                                                        int top_k, int rows_per_split,
+                                                        int top_k,
                                                         float sm_scale, __bf16* __restrict__ out,
                                                         float* __restrict__ lse_out,
                                                         _Float16* __restrict__ part_o,
@@ -274,20 +275,23 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
   const int32_t* idx_row = idx + t * top_k;
-  const int r_begin = split * rows_per_split;
-  const int r_end = min(top_k, r_begin + rows_per_split);
-  const int nrows = max(0, r_end - r_begin);
 
-  // the split's indices (rows past the token's position are never read) and the last valid one
-  __shared__ int last_valid;
-  if (tid == 0) last_valid = -1;
+  // The split's indices. First guess, right for a list whose last entry is valid: the splits share
+  // all of the list's tiles. The last entry is loaded with them to check.
+  __shared__ int last_all, last_valid;
+  if (tid == 0) last_all = -1, last_valid = -1;
   constexpr int PER = TOPK_MAX_K / NT;
+  const int tiles_k = (top_k + TILE - 1) / TILE;
+  int per_split = (tiles_k + nsplit - 1) / nsplit;
+  int r_begin = min(split * per_split, tiles_k) * TILE;
+  int r_end = min(top_k, (split + 1) * per_split * TILE);
   int ixs[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int j = u * NT + tid;
-    ixs[u] = j < nrows ? idx_row[r_begin + j] : -1;
+    ixs[u] = r_begin + j < r_end ? idx_row[r_begin + j] : -1;
   }
+  const int32_t last_entry = idx_row[top_k - 1];
   // this lane's Q^T fragments go out with the indices: head `head`, dims
   // [288*kh + 16*ks + 8*half, +8), bf16 as loaded (widened to fp16 below)
   const int hg = wave >> 1, kh = wave & 1;
@@ -303,12 +307,40 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   __syncthreads();
   {
     int lv = -1;
+    if (last_entry >= 0 && last_entry <= tk.pos) {  // uniform
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int j = u * NT + tid;
-      const int ix = ixs[u] > tk.pos ? -1 : ixs[u];
-      sm.idx[j] = ix;
-      if (ix >= 0) lv = j;
+      for (int u = 0; u < PER; ++u) {
+        const int j = u * NT + tid;
+        const int ix = ixs[u] > tk.pos ? -1 : ixs[u];
+        sm.idx[j] = ix;
+        if (ix >= 0) lv = j;
+      }
+    } else {
+      // Padding at the end (a short context, a shard's part of a selection): the splits share
+      // the tiles up to the last valid entry instead, so the valid rows spread over all of them.
+      int la = -1;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int j = u * NT + tid;
+        ixs[u] = j < top_k ? idx_row[j] : -1;
+        if (ixs[u] > tk.pos) ixs[u] = -1;
+        if (ixs[u] >= 0) la = j;
+      }
+      if (la >= 0) atomicMax(&last_all, la);
+      __syncthreads();
+      const int tiles_all = (last_all + TILE) / TILE;
+      per_split = (tiles_all + nsplit - 1) / nsplit;
+      r_begin = min(split * per_split, tiles_all) * TILE;
+      r_end = max(r_begin, min((split + 1) * per_split * TILE, last_all + 1));
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int j = u * NT + tid;
+        if (j >= r_begin && j < r_end) {  // entry j goes to slot j - r_begin
+          sm.idx[j - r_begin] = ixs[u];
+          if (ixs[u] >= 0) lv = j - r_begin;
+        }
+        if (j >= r_end - r_begin) sm.idx[j] = -1;  // the slots no entry lands in
+      }
     }
     if (lv >= 0) atomicMax(&last_valid, lv);
   }
@@ -662,8 +694,6 @@ hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, co
                           int decode, hipStream_t s) {
   TableView tv = table_view(b.table, b.batch, b.total_q);
   const int nsplit = decode ? mla_decode_splits(b, top_k) : 1;
-  const int tiles = (top_k + TILE - 1) / TILE;
-  const int rows_per_split = ((tiles + nsplit - 1) / nsplit) * TILE;
   const size_t lds = sizeof(MlaSmem);
   static const bool lds_set = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&mla_fp8_kernel),
@@ -681,7 +711,7 @@ hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, co
   mark_stage(STAGE_MLA, false, s);
   hipLaunchKernelGGL(mla_fp8_kernel, dim3(b.total_q, nsplit), dim3(NT), lds, s, tv.tok,
                      static_cast<const __bf16*>(q), static_cast<const unsigned char*>(kv), idx, top_k,
-                     rows_per_split, sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse);
+                     sm_scale, static_cast<__bf16*>(out), lse, part_o, part_lse);
   mark_stage(STAGE_MLA, true, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
