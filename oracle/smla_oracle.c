@@ -236,6 +236,75 @@ int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double*
   return 0;
 }
 
+static int cmp_i64(const void* a, const void* b) {
+  const int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+  return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t resident_from,
+                            int32_t H, int32_t* hot_tok, int32_t* hot_age, int32_t step,
+                            int64_t hot_base, int32_t* idx_out, int32_t* copy_src, int32_t* n_copy) {
+  /* the distinct offloaded selections of the request, ascending */
+  int64_t* u = (int64_t*)malloc(sizeof(int64_t) * ((size_t)n_q * top_k + 1));
+  int32_t* slot_of = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n_q * top_k + 1));
+  unsigned char* used = (unsigned char*)calloc((size_t)H + 1, 1);
+  if (!u || !slot_of || !used) { free(u); free(slot_of); free(used); return -1; }
+  int64_t n = 0;
+  for (int64_t i = 0; i < (int64_t)n_q * top_k; ++i)
+    if (idx[i] >= 0 && idx[i] < resident_from) u[n++] = idx[i];
+  qsort(u, (size_t)n, sizeof(int64_t), cmp_i64);
+  int64_t m = 0;
+  for (int64_t i = 0; i < n; ++i)
+    if (m == 0 || u[m - 1] != u[i]) u[m++] = u[i];
+  /* hits: a slot already holding the token is used again (its age becomes this step) */
+  int64_t hits = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    slot_of[i] = -1;
+    for (int32_t j = 0; j < H; ++j)
+      if (hot_tok[j] == u[i]) {
+        slot_of[i] = j;
+        used[j] = 1;
+        hot_age[j] = step;
+        ++hits;
+        break;
+      }
+  }
+  if (m - hits > (int64_t)H - hits) { free(u); free(slot_of); free(used); return -2; }
+  /* misses, ascending, take the least recently used free slots: (age, slot) ascending */
+  int32_t nc = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    if (slot_of[i] >= 0) continue;
+    int32_t best = -1;
+    for (int32_t j = 0; j < H; ++j) {
+      if (used[j]) continue;
+      if (best < 0 || hot_age[j] < hot_age[best]) best = j;  /* ties: the lower slot */
+    }
+    used[best] = 1;
+    slot_of[i] = best;
+    hot_tok[best] = (int32_t)u[i];
+    hot_age[best] = step;
+    if (copy_src) copy_src[2 * nc] = (int32_t)u[i], copy_src[2 * nc + 1] = best;
+    ++nc;
+  }
+  if (n_copy) *n_copy = nc;
+  /* every selection: resident rows in place, offloaded ones at their slot */
+  for (int64_t i = 0; i < (int64_t)n_q * top_k; ++i) {
+    const int32_t s = idx[i];
+    if (s < 0) { idx_out[i] = -1; continue; }
+    if (s >= resident_from) { idx_out[i] = s; continue; }
+    int64_t lo = 0, hi = m - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (u[mid] < s) lo = mid + 1; else hi = mid;
+    }
+    idx_out[i] = (int32_t)(hot_base + slot_of[lo]);
+  }
+  free(u);
+  free(slot_of);
+  free(used);
+  return 0;
+}
+
 int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,
                        int32_t H, int32_t D_qk, int32_t D_v, const int32_t* idx, int32_t top_k,
                        double sm_scale, double* out, double* lse) {

@@ -88,6 +88,23 @@ int smla_oracle_topk_merge(const int32_t* idx_lists, const int32_t* score_lists,
 int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double* outs,
                           const double* lses, double* out, double* lse);
 
+/* Hot-buffer resolve of one request (the pages' hybrid offload keeps the rows the indexer
+ * selects in a GPU hot buffer with LRU replacement; a miss copies one row from pinned host
+ * memory into an LRU slot: "vLLM GLM 5.3 ... Hybrid HiSparse", technical implementation).
+ * idx [n_q, top_k]: the request's selections (local rows, -1 padding). Rows >= resident_from are
+ * resident and read in place; the others must sit in the hot buffer of H slots, hot_tok[H]
+ * (token or -1) and hot_age[H] (step of last use, -1 never), updated in place:
+ *  - U = the distinct offloaded selections, ascending;
+ *  - a token of U already in a slot is a hit: that slot's age becomes `step`;
+ *  - the misses, ascending, take the slots not hit in this call in (age, slot) ascending order
+ *    (least recently used first, ties to the lower slot); each gets the token and age `step`,
+ *    and its row is to be copied from host memory (copy_src: pairs (token, slot), n_copy of them);
+ *  - idx_out: -1 stays -1, a resident row stays, an offloaded row becomes hot_base + its slot.
+ * Returns -2 when the misses do not fit (more distinct offloaded rows than H). */
+int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t resident_from,
+                            int32_t H, int32_t* hot_tok, int32_t* hot_age, int32_t step,
+                            int64_t hot_base, int32_t* idx_out, int32_t* copy_src, int32_t* n_copy);
+
 /* Attention of one query token q_tok [H, D_qk] (bf16 bits) over rows[idx[i]] (row_bytes each),
  * skipping idx < 0; out [H, D_v], lse [H] (either may be NULL). Returns -1 if no row is valid. */
 int smla_oracle_attend(const uint16_t* q_tok, const uint8_t* rows, int32_t fmt, int32_t row_bytes,

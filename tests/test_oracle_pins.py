@@ -546,3 +546,90 @@ def test_lse_merge_closed_form():
     assert np.allclose(out, [[0.25, 1.5]], atol=1e-15) and np.allclose(lse, [np.log(4.0)], atol=1e-15)
     out, lse = oracle.lse_merge(outs[:1] * 0, np.full((1, 1), -np.inf))
     assert lse[0] == -np.inf and (out == 0).all()
+
+
+# ---- hot-buffer resolve (hybrid offload: resident rows in place, offloaded rows through an LRU
+# hot buffer; "vLLM GLM 5.3 ... Hybrid HiSparse", technical implementation) -----------------
+
+def test_hot_resolve_worked_example():
+    # worked by hand from the rule: distinct offloaded selections ascending; hits keep their slot;
+    # misses take the slots not hit in (last use, slot) order; the output names hot_base + slot
+    tok = np.full(4, -1, np.int32)
+    age = np.full(4, -1, np.int32)
+    # step 0: U = [3, 7], both miss, empty slots 0 and 1 in slot order
+    out, cp = oracle.hot_resolve(np.array([[7, 3, 150, -1]]), 100, tok, age, 0, 500)
+    assert out.tolist() == [[501, 500, 150, -1]] and cp == [(3, 0), (7, 1)]
+    assert tok.tolist() == [3, 7, -1, -1] and age.tolist() == [0, 0, -1, -1]
+    # step 1 (two tokens share the buffer): U = [3, 5, 9]; 3 hits slot 0; 5 and 9 take the
+    # never-used slots 2 and 3 before slot 1 (used at step 0)
+    out, cp = oracle.hot_resolve(np.array([[9, 3, 120], [3, 5, -1]]), 100, tok, age, 1, 500)
+    assert out.tolist() == [[503, 500, 120], [500, 502, -1]] and cp == [(5, 2), (9, 3)]
+    assert tok.tolist() == [3, 7, 5, 9] and age.tolist() == [1, 0, 1, 1]
+    # step 2: U = [2, 5, 7, 11]; 5 and 7 hit; slots 0 and 3 (both last used at step 1) go to 2, 11
+    out, cp = oracle.hot_resolve(np.array([[2, 5, 11, 7]]), 100, tok, age, 2, 500)
+    assert out.tolist() == [[500, 502, 503, 501]] and cp == [(2, 0), (11, 3)]
+    assert tok.tolist() == [2, 7, 5, 11] and age.tolist() == [2, 2, 2, 2]
+    # five distinct offloaded rows do not fit four slots
+    with pytest.raises(ValueError):
+        oracle.hot_resolve(np.array([[20, 21, 22, 23, 24]]), 100, tok, age, 3, 500)
+    # a fully resident request passes through untouched
+    out, cp = oracle.hot_resolve(np.array([[2, 5, -1]]), 0, tok, age, 3, 500)
+    assert out.tolist() == [[2, 5, -1]] and cp == [] and tok.tolist() == [2, 7, 5, 11]
+
+
+def test_hot_resolve_one_row_per_step_is_textbook_lru():
+    # with one offloaded selection per step every last-use step differs, and the rule is the
+    # textbook least-recently-used cache: free slots first (lowest first), else the slot of the
+    # entry used longest ago
+    from collections import OrderedDict
+    rng = np.random.default_rng(11)
+    H = 5
+    tok = np.full(H, -1, np.int32)
+    age = np.full(H, -1, np.int32)
+    lru, free = OrderedDict(), list(range(H))
+    for step in range(400):
+        u = int(rng.integers(0, 12))
+        if u in lru:
+            lru.move_to_end(u)
+            want_copy = []
+        else:
+            slot = free.pop(0) if free else lru.popitem(last=False)[1]
+            lru[u] = slot
+            want_copy = [(u, slot)]
+        out, cp = oracle.hot_resolve(np.array([[u, 40 + u, -1]]), 30, tok, age, step, 0)
+        assert cp == want_copy, step
+        assert out.tolist() == [[lru[u], 40 + u, -1]], step
+        assert sorted(t for t in tok.tolist() if t >= 0) == sorted(lru), step
+
+
+def test_hot_resolve_invariants_over_random_steps():
+    # several tokens per request with shared and repeated selections, resident rows and padding:
+    # after each step the state must be consistent and the evictions least-recently-used
+    rng = np.random.default_rng(12)
+    H, rf, base = 48, 200, 1000
+    tok = np.full(H, -1, np.int32)
+    age = np.full(H, -1, np.int32)
+    for step in range(60):
+        n_q, k = int(rng.integers(1, 4)), 16
+        centre = int(rng.integers(0, rf))
+        idx = (centre + rng.integers(-25, 25, size=(n_q, k))) % (rf + 40)
+        idx[rng.random((n_q, k)) < 0.1] = -1
+        t0, a0 = tok.copy(), age.copy()
+        u = np.unique(idx[(idx >= 0) & (idx < rf)])
+        if u.size > H:
+            continue
+        out, cp = oracle.hot_resolve(idx, rf, tok, age, step, base)
+        assert len(set(t for t in tok.tolist() if t >= 0)) == (tok >= 0).sum()
+        off = (idx >= 0) & (idx < rf)
+        assert np.array_equal(out[~off], np.where(idx[~off] < 0, -1, idx[~off]))
+        assert np.array_equal(tok[out[off] - base], idx[off])
+        misses = [int(v) for v in u if v not in set(t0.tolist())]
+        assert [c[0] for c in cp] == misses                  # ascending misses, each copied once
+        used = np.unique(out[off] - base)
+        assert (age[used] == step).all() and np.array_equal(np.delete(age, used), np.delete(a0, used))
+        evicted = [c[1] for c in cp]
+        hit = set(used.tolist()) - set(evicted)
+        kept = [j for j in range(H) if j not in hit and j not in evicted]
+        for e in evicted:                                    # (last use, slot) order
+            assert all((a0[e], e) < (a0[j], j) for j in kept), (step, e)
+        assert all(tok[j] == t0[j] for j in hit) and all(tok[j] == t0[j] for j in kept)
