@@ -190,6 +190,41 @@ int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, i
 int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, const void* outs,
                    const float* lses, void* out, float* lse, void* stream);
 
+/*
+ * Hot-buffer resolve of a step's top-k under hybrid offload ("vLLM GLM 5.3 ... Hybrid
+ * HiSparse", technical implementation: with mixed residency a request's older rows are in host
+ * memory and only its tail is resident; the rows the indexer selects from the offloaded part are
+ * served from a per-request GPU hot buffer of n_slots rows (the pages default to 2 x top_k),
+ * managed least-recently-used; a miss copies one row from pinned host memory into an LRU slot).
+ *
+ * idx (device) [total_q, top_k]: the step's selections (local rows, -1 padding). Per request b
+ * (device arrays of `batch` entries): resident_from[b] = first resident local row (rows below
+ * it are offloaded; 0 = fully resident, nothing to do); hot_base[b] = local row of hot slot 0,
+ * with 0 <= hot_base and hot_base + n_slots <= resident_from (the hot buffer sits in the
+ * request's released rows); host_row0[b] = host row of the request's local row 0.
+ * hot_tok / hot_age (device) [batch, n_slots]: the slots' token (-1 empty) and step of last use
+ * (-1 never), initialised by the caller to -1 and updated in place; step >= 0 is this call's.
+ * host_rows (host, pinned: hipHostMalloc or a pinned torch tensor) [host_n_rows, row_bytes] is
+ * read by the kernel directly; kv (device) rows of row_bytes (a multiple of 16), laid out as in
+ * the batch; a miss of token u goes to kv row R_b + hot_base[b] + slot.
+ *
+ * Rule within one call (the pages fix none; this is the reading taken): the distinct offloaded
+ * selections of the request's tokens, ascending; a selection whose token a slot holds is a hit
+ * and that slot is used again; the misses, ascending, take the slots not hit in this call in
+ * (last use, slot) order. Every used slot gets last use = step.
+ * idx_out (device) [total_q, top_k], not aliasing idx: -1 for padding, resident rows as they
+ * are, offloaded rows as hot_base[b] + slot — ready for the sparse-MLA entry points.
+ * n_copied (device) [batch]: rows copied for request b, or (nothing changed, idx_out -1) -1 when
+ * the distinct offloaded selections outnumber n_slots, -2 when resident_from / hot_base are
+ * out of bounds, -3 when host rows [host_row0, host_row0 + resident_from) leave host_rows.
+ * Limits: max n_q * top_k <= 8192, n_slots <= 8192. Calls for one request must be ordered.
+ */
+int smla_hot_resolve(const smla_batch* b, const int32_t* idx, int32_t top_k,
+                     const int32_t* resident_from, const int32_t* hot_base, int32_t n_slots,
+                     int32_t* hot_tok, int32_t* hot_age, int32_t step, const void* host_rows,
+                     int64_t host_n_rows, const int64_t* host_row0, int32_t row_bytes, void* kv,
+                     int32_t* idx_out, int32_t* n_copied, void* stream);
+
 /* Workspace for the sparse-MLA entry points (decode needs split partials; prefill none). */
 size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D_v,
                                        int32_t top_k, int32_t decode);

@@ -256,6 +256,9 @@ int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int6
   int64_t m = 0;
   for (int64_t i = 0; i < n; ++i)
     if (m == 0 || u[m - 1] != u[i]) u[m++] = u[i];
+  /* the misses fit the slots not hit exactly when the distinct rows fit all slots; a request
+   * that does not fit is rejected before anything changes */
+  if (m > H) { free(u); free(slot_of); free(used); return -2; }
   /* hits: a slot already holding the token is used again (its age becomes this step) */
   int64_t hits = 0;
   for (int64_t i = 0; i < m; ++i) {
@@ -269,7 +272,6 @@ int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int6
         break;
       }
   }
-  if (m - hits > (int64_t)H - hits) { free(u); free(slot_of); free(used); return -2; }
   /* misses, ascending, take the least recently used free slots: (age, slot) ascending */
   int32_t nc = 0;
   for (int64_t i = 0; i < m; ++i) {

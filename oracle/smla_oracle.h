@@ -100,7 +100,7 @@ int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double*
  *    (least recently used first, ties to the lower slot); each gets the token and age `step`,
  *    and its row is to be copied from host memory (copy_src: pairs (token, slot), n_copy of them);
  *  - idx_out: -1 stays -1, a resident row stays, an offloaded row becomes hot_base + its slot.
- * Returns -2 when the misses do not fit (more distinct offloaded rows than H). */
+ * Returns -2, with nothing changed, when the distinct offloaded rows outnumber the H slots. */
 int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t resident_from,
                             int32_t H, int32_t* hot_tok, int32_t* hot_age, int32_t step,
                             int64_t hot_base, int32_t* idx_out, int32_t* copy_src, int32_t* n_copy);

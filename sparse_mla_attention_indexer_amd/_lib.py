@@ -32,6 +32,7 @@ EXPORTS = (
     "smla_topk_merge",
     "smla_dcp_local_indices",
     "smla_lse_merge",
+    "smla_hot_resolve",
     "smla_sparse_mla_workspace_bytes",
     "smla_sparse_mla_prefill",
     "smla_sparse_mla_decode",
@@ -88,6 +89,7 @@ def lib():
         L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, i32, P, P, P]
         L.smla_dcp_local_indices.argtypes = [i32, i32, P, i32, P, P]
         L.smla_lse_merge.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+        L.smla_hot_resolve.argtypes = [BP, P, i32, P, P, i32, P, P, i32, P, i64, P, i32, P, P, P, P]
         L.smla_sparse_mla_workspace_bytes.argtypes = [BP, i32, i32, i32, i32]
         L.smla_sparse_mla_workspace_bytes.restype = sz
         for fn in ("smla_sparse_mla_prefill", "smla_sparse_mla_decode"):

@@ -385,6 +385,44 @@ int smla_dcp_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, i
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "local indices launch");
 }
 
+int smla_hot_resolve(const smla_batch* b, const int32_t* idx, int32_t top_k,
+                     const int32_t* resident_from, const int32_t* hot_base, int32_t n_slots,
+                     int32_t* hot_tok, int32_t* hot_age, int32_t step, const void* host_rows,
+                     int64_t host_n_rows, const int64_t* host_row0, int32_t row_bytes, void* kv,
+                     int32_t* idx_out, int32_t* n_copied, void* stream) {
+  g_err.clear();
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (top_k < 1 || (int64_t)b->max_q * top_k > smla::HOT_MAX_SEL)
+    return fail(SMLA_E_UNSUPPORTED, "need top_k >= 1 and max n_q * top_k <= %d", smla::HOT_MAX_SEL);
+  if (n_slots < 1 || n_slots > smla::HOT_MAX_SLOTS)
+    return fail(SMLA_E_UNSUPPORTED, "n_slots=%d outside [1, %d]", n_slots, smla::HOT_MAX_SLOTS);
+  if (step < 0) return fail(SMLA_E_INVALID, "step must be >= 0 (-1 marks a slot never used)");
+  if (row_bytes < 16 || row_bytes > 65536 || row_bytes % 16 != 0)
+    return fail(SMLA_E_INVALID, "row_bytes=%d must be a multiple of 16 in [16, 65536]", row_bytes);
+  if (host_n_rows < 0) return fail(SMLA_E_INVALID, "host_n_rows must be >= 0");
+  if (!idx || !resident_from || !hot_base || !hot_tok || !hot_age || !host_rows || !host_row0 ||
+      !kv || !idx_out || !n_copied)
+    return fail(SMLA_E_INVALID, "null pointer");
+  if (!aligned(idx, 4) || !aligned(resident_from, 4) || !aligned(hot_base, 4) ||
+      !aligned(hot_tok, 4) || !aligned(hot_age, 4) || !aligned(host_row0, 8) ||
+      !aligned(idx_out, 4) || !aligned(n_copied, 4) || !aligned(host_rows, 16) || !aligned(kv, 16))
+    return fail(SMLA_E_INVALID, "misaligned pointer (host_rows and kv: 16 bytes)");
+  if (idx_out == idx) return fail(SMLA_E_INVALID, "idx_out must not alias idx");
+  // the kernel reads host rows directly: they must be pinned, device-mapped host memory
+  hipPointerAttribute_t attr{};
+  hipError_t e = hipPointerGetAttributes(&attr, host_rows);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost || !attr.devicePointer) {
+    (void)hipGetLastError();
+    return fail(SMLA_E_INVALID, "host_rows must be pinned host memory (hipHostMalloc)");
+  }
+  const void* dev_rows = attr.devicePointer;
+  e = smla::launch_hot_resolve(b->table, b->batch, idx, top_k, resident_from, hot_base, n_slots,
+                               hot_tok, hot_age, step, dev_rows, host_n_rows, host_row0, row_bytes,
+                               kv, idx_out, n_copied, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : hip_fail(e, "hot resolve launch");
+}
+
 int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, const void* outs,
                    const float* lses, void* out, float* lse, void* stream) {
   g_err.clear();

@@ -244,6 +244,53 @@ def lse_merge(outs, lses, out=None, lse=None):
     return out, lse
 
 
+def hot_resolve(plan: BatchPlan, idx, resident_from, hot_base, hot_tok, hot_age, step: int,
+                host_rows, host_row0, kv, idx_out=None, n_copied=None):
+    """Resolve a step's selections idx [total_q, top_k] against each request's hot buffer:
+    offloaded rows (local row < resident_from[b]) are served from hot slots (hot_tok / hot_age
+    [batch, n_slots] int32, updated in place), misses copied from host_rows (a pinned CPU tensor
+    [n, row_bytes] uint8, request b's local row u at host row host_row0[b] + u) into kv rows
+    R_b + hot_base[b] + slot. Returns (idx_out [total_q, top_k], n_copied [batch]); a negative
+    n_copied[b] means request b was rejected (see the C header)."""
+    d = plan.device
+    if idx.dim() != 2:
+        raise ValueError("idx must be [total_q, top_k]")
+    top_k = int(idx.shape[1])
+    _req(idx, "idx", torch.int32, (plan.total_q, top_k), d)
+    for name, t in (("resident_from", resident_from), ("hot_base", hot_base)):
+        _req(t, name, torch.int32, (plan.batch,), d)
+    _req(host_row0, "host_row0", torch.int64, (plan.batch,), d)
+    if hot_tok.dim() != 2:
+        raise ValueError("hot_tok must be [batch, n_slots]")
+    n_slots = int(hot_tok.shape[1])
+    _req(hot_tok, "hot_tok", torch.int32, (plan.batch, n_slots), d)
+    _req(hot_age, "hot_age", torch.int32, (plan.batch, n_slots), d)
+    if host_rows.device.type != "cpu" or not host_rows.is_pinned() or host_rows.dim() != 2:
+        raise ValueError("host_rows must be a pinned 2-D CPU tensor")
+    if host_rows.dtype != torch.uint8 or not host_rows.is_contiguous():
+        raise ValueError("host_rows must be contiguous uint8")
+    row_bytes = int(host_rows.shape[1])
+    if kv.dim() != 2 or kv.device != d or not kv.is_contiguous() or kv.shape[0] < plan.total_rows:
+        raise ValueError(f"kv must be a contiguous [>= {plan.total_rows}, row] tensor on {d}")
+    if int(kv.shape[1]) * kv.element_size() != row_bytes:
+        raise ValueError("kv rows and host rows differ in size")
+    if idx_out is None:
+        idx_out = torch.empty_like(idx)
+    if n_copied is None:
+        n_copied = torch.empty(plan.batch, dtype=torch.int32, device=d)
+    _req(idx_out, "idx_out", torch.int32, (plan.total_q, top_k), d)
+    _req(n_copied, "n_copied", torch.int32, (plan.batch,), d)
+    with torch.cuda.device(d):
+        check("smla_hot_resolve",
+              lib().smla_hot_resolve(plan.ref, idx.data_ptr(), top_k, resident_from.data_ptr(),
+                                     hot_base.data_ptr(), n_slots, hot_tok.data_ptr(),
+                                     hot_age.data_ptr(), int(step), host_rows.data_ptr(),
+                                     int(host_rows.shape[0]), host_row0.data_ptr(), row_bytes,
+                                     kv.data_ptr(), idx_out.data_ptr(), n_copied.data_ptr(),
+                                     _stream(d)))
+    return idx_out, n_copied
+
+
 def mla_workspace(plan: BatchPlan, H: int, D_v: int, top_k: int, decode: bool) -> torch.Tensor:
     n = int(lib().smla_sparse_mla_workspace_bytes(plan.ref, H, D_v, top_k, int(decode)))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=plan.device)

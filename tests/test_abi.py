@@ -153,6 +153,30 @@ def test_dcp_merge_validation(L):
     assert L.smla_lse_merge(4, 64, 512, 8, FAKE, FAKE + 2, FAKE, None, None) == _lib.SMLA_E_INVALID
 
 
+def test_hot_resolve_validation(L):
+    # sizes, step, row size, pointers and aliasing are refused on the host; a host pointer
+    # that is not pinned HIP memory is refused too (here: no runtime at all), never launched
+    b = _fake_batch()
+    ok = dict(top_k=2048, n_slots=4096, step=0, row_bytes=656, host=FAKE, idx=FAKE, out=FAKE + 256)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.smla_hot_resolve(ctypes.byref(b), a["idx"], a["top_k"], FAKE, FAKE, a["n_slots"],
+                                  FAKE, FAKE, a["step"], a["host"], 1 << 20, FAKE, a["row_bytes"],
+                                  FAKE, a["out"], FAKE, None)
+
+    assert call(top_k=0) == _lib.SMLA_E_UNSUPPORTED
+    assert call(top_k=8193) == _lib.SMLA_E_UNSUPPORTED      # n_q * top_k above 8192
+    assert call(n_slots=0) == _lib.SMLA_E_UNSUPPORTED
+    assert call(n_slots=8193) == _lib.SMLA_E_UNSUPPORTED
+    assert call(step=-1) == _lib.SMLA_E_INVALID
+    assert call(row_bytes=650) == _lib.SMLA_E_INVALID
+    assert call(host=None) == _lib.SMLA_E_INVALID
+    assert call(host=FAKE + 8) == _lib.SMLA_E_INVALID        # 16-byte alignment
+    assert call(out=FAKE) == _lib.SMLA_E_INVALID             # idx_out aliases idx
+    assert call() == _lib.SMLA_E_INVALID                     # not pinned host memory
+
+
 def test_mla_validation(L):
     b = _fake_batch()
     args = dict(H=64, D_qk=576, D_v=512)

@@ -1,0 +1,173 @@
+"""GPU parity of the hot-buffer resolve (hybrid offload: a request's older rows in pinned host
+memory, the selected ones served from a GPU hot buffer managed least-recently-used).
+
+Over several steps with drifting selections (hits and misses), the library's rewritten
+selections, the slot table (token and last use), the copy counts and the hot rows themselves
+must equal the oracle's bit for bit; attention over the rewritten selections, with every
+offloaded device row overwritten, must match the oracle's attention over the original
+selections and the whole cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mla_attention_indexer_amd import ops
+from sparse_mla_attention_indexer_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import Dev, assert_attn_close, oracle_mla, say  # noqa: E402
+
+POISON = 0xEE
+
+
+class Offload:
+    """A batch whose rows below resident_from[b] are only in pinned host memory (the device
+    copies are overwritten with POISON), with a hot buffer of n_slots rows at hot_base[b]."""
+
+    def __init__(self, n_q, kv_len, rows, resident_from, hot_base, n_slots, device="cuda:0"):
+        self.dv = torch.device(device)
+        self.plan = ops.BatchPlan(n_q, kv_len, self.dv)
+        self.n_q, self.kv_len = np.asarray(n_q), np.asarray(kv_len, np.int64)
+        self.row0 = np.concatenate([[0], np.cumsum(self.kv_len)[:-1]]).astype(np.int64)
+        self.rows = rows
+        self.host = torch.from_numpy(rows).pin_memory()
+        dev_rows = rows.copy()
+        for b, rf in enumerate(resident_from):
+            dev_rows[self.row0[b]: self.row0[b] + rf] = POISON
+        self.kv = torch.from_numpy(dev_rows).to(self.dv)
+        self.rf = np.asarray(resident_from, np.int32)
+        self.hb = np.asarray(hot_base, np.int32)
+        B = len(n_q)
+        self.t_rf = torch.from_numpy(self.rf).to(self.dv)
+        self.t_hb = torch.from_numpy(self.hb).to(self.dv)
+        self.t_h0 = torch.from_numpy(self.row0).to(self.dv)
+        self.tok = torch.full((B, n_slots), -1, dtype=torch.int32, device=self.dv)
+        self.age = torch.full((B, n_slots), -1, dtype=torch.int32, device=self.dv)
+        self.o_tok = np.full((B, n_slots), -1, np.int32)
+        self.o_age = np.full((B, n_slots), -1, np.int32)
+
+    def step(self, idx_np, step):
+        idx = torch.from_numpy(np.ascontiguousarray(idx_np, np.int32)).to(self.dv)
+        out, nc = ops.hot_resolve(self.plan, idx, self.t_rf, self.t_hb, self.tok, self.age, step,
+                                  self.host, self.t_h0, self.kv)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), nc.cpu().numpy()
+
+    def check_against_oracle(self, idx_np, step, label):
+        got, nc = self.step(idx_np, step)
+        q0 = 0
+        for b, nq in enumerate(self.n_q):
+            sel = idx_np[q0: q0 + nq]
+            try:
+                ref, cp = oracle.hot_resolve(sel, int(self.rf[b]), self.o_tok[b], self.o_age[b], step,
+                                             int(self.hb[b]))
+                want_nc = len(cp)
+            except ValueError:
+                ref, want_nc = np.full_like(sel, -1), -1
+            assert np.array_equal(got[q0: q0 + nq], ref), f"{label}: request {b} selections differ"
+            assert nc[b] == want_nc, f"{label}: request {b} copied {nc[b]}, oracle {want_nc}"
+            q0 += nq
+        assert np.array_equal(self.tok.cpu().numpy(), self.o_tok), f"{label}: slot tokens differ"
+        assert np.array_equal(self.age.cpu().numpy(), self.o_age), f"{label}: slot ages differ"
+        kv = self.kv.cpu().numpy()
+        for b in range(len(self.n_q)):
+            for s in np.nonzero(self.o_tok[b] >= 0)[0]:
+                r = self.row0[b] + self.hb[b] + s
+                assert np.array_equal(kv[r], self.rows[self.row0[b] + self.o_tok[b, s]]), (label, b, s)
+        return nc
+
+
+def _drifting_selection(rng, n_q, kv_len, rf, top_k, centre, spread):
+    """Per token: top_k distinct rows, most of them near `centre` in the offloaded range, some
+    resident, ascending, the tail padded with -1."""
+    out = []
+    for nq, kl, r in zip(n_q, kv_len, rf):
+        for _ in range(nq):
+            n_valid = int(rng.integers(top_k // 2, top_k + 1))
+            lo = max(0, centre - spread)
+            pool = np.arange(lo, min(kl, max(r, 1) if r > 0 else kl, centre + spread))
+            n_off = min(pool.size, int(n_valid * 0.8)) if r > 0 else 0
+            a = rng.choice(pool, size=n_off, replace=False) if n_off else np.zeros(0, np.int64)
+            res = rng.choice(np.arange(r, kl), size=min(n_valid - n_off, kl - r), replace=False)
+            v = np.sort(np.concatenate([a, res]))
+            row = np.full(top_k, -1, np.int32)
+            row[: v.size] = v
+            out.append(row)
+    return np.stack(out)
+
+
+def test_hot_resolve_steps_against_oracle():
+    rng = np.random.default_rng(0x407)
+    n_q = np.array([1, 3, 2, 1], np.int32)
+    kv_len = np.array([6000, 9000, 5000, 3000], np.int64)
+    rf = [4000, 6000, 0, 3000]     # request 2 fully resident; request 3 fully offloaded
+    hb = [0, 100, 0, 2000]
+    n_slots, top_k = 512, 256
+    rows = rng.integers(0, 256, size=(int(kv_len.sum()), 656), dtype=np.uint8)
+    off = Offload(n_q, kv_len, rows, rf, hb, n_slots)
+    say("[case] hot resolve: 4 requests, 8 steps, 512 slots, top_k 256")
+    total = 0
+    for step in range(8):
+        centre = 600 + 180 * step
+        idx = _drifting_selection(rng, n_q, kv_len, rf, top_k, centre, 260)
+        if step == 5:  # a decode token's list out of order: the sorting path
+            rng.shuffle(idx[0])
+        last = off.check_against_oracle(idx, step, f"step {step}")
+        total += int(last[last > 0].sum())
+    assert total > 0
+    # the same selection again: all hits, nothing copied
+    nc = off.check_against_oracle(idx, 8, "repeat")
+    assert (nc[(np.array(rf) > 0) & (last >= 0)] == 0).all()
+
+
+def test_hot_resolve_rejections():
+    rng = np.random.default_rng(0x408)
+    n_q = np.array([1, 1, 1, 1], np.int32)
+    kv_len = np.array([3000, 3000, 3000, 3000], np.int64)
+    rows = rng.integers(0, 256, size=(12000, 656), dtype=np.uint8)
+    # request 1: hot buffer overlaps resident rows; request 2: host rows outside the pool
+    off = Offload(n_q, kv_len, rows, [2000, 2000, 2000, 2000], [0, 1800, 0, 0], 256)
+    off.t_h0[2] = 11000
+    idx = np.full((4, 300), -1, np.int32)
+    idx[0, :200] = np.arange(200) * 3               # fits
+    idx[1, :10] = np.arange(10)
+    idx[2, :10] = np.arange(10)
+    idx[3, :300] = np.arange(300)                   # 300 distinct offloaded rows > 256 slots
+    got, nc = off.step(idx, 0)
+    assert nc.tolist() == [200, -2, -3, -1]
+    assert (got[1:] == -1).all()
+    t = off.tok.cpu().numpy()
+    assert (t[1:] == -1).all() and (off.age.cpu().numpy()[1:] == -1).all()
+    ref, _ = oracle.hot_resolve(idx[:1], 2000, off.o_tok[0], off.o_age[0], 0, 0)
+    assert np.array_equal(got[:1], ref)
+    # pageable host memory is refused before anything runs
+    with pytest.raises(ValueError):
+        ops.hot_resolve(off.plan, torch.from_numpy(idx).to(off.dv), off.t_rf, off.t_hb, off.tok,
+                        off.age, 1, torch.from_numpy(rows), off.t_h0, off.kv)
+
+
+def test_hot_resolve_then_attention_decode():
+    # a decode batch whose older rows are offloaded: top-k, resolve into a hot buffer of twice
+    # top-k rows, attention over the resolved rows with every offloaded device row overwritten
+    x = W.generate(W.small_big_dims(batch=4, n_q=1, cached=20000))
+    d = x.dims
+    dev = Dev(x)
+    say(f"[case] hot resolve + attention: B={d.batch} kv_len={int(x.kv_len[0])}")
+    ref_idx, _ = dev.topk()
+    rf = (x.kv_len - 4096).astype(np.int32)
+    n_slots = 2 * d.top_k
+    off = Offload(x.n_q, x.kv_len, x.kv, rf, np.zeros(d.batch, np.int32), n_slots)
+    nc = off.check_against_oracle(ref_idx, 0, "decode cold step")
+    assert (nc > 0).all()
+    got_idx, nc = off.step(ref_idx, 1)  # the same selection again: all hits
+    assert (nc == 0).all()
+    idx_t = torch.from_numpy(got_idx).to(off.dv)
+    out, lse = ops.sparse_mla(off.plan, dev.q, off.kv, d.kv_format, d.D_v, idx_t, d.sm_scale,
+                              decode=True)
+    torch.cuda.synchronize()
+    sample = np.arange(d.batch)
+    ref_o, ref_l = oracle_mla(x, ref_idx[sample], sample)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[sample]
+    assert_attn_close(got, ref_o, lse.cpu().numpy()[sample], ref_l, "hot-resolved attention")

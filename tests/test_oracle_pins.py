@@ -570,8 +570,9 @@ def test_hot_resolve_worked_example():
     assert out.tolist() == [[500, 502, 503, 501]] and cp == [(2, 0), (11, 3)]
     assert tok.tolist() == [2, 7, 5, 11] and age.tolist() == [2, 2, 2, 2]
     # five distinct offloaded rows do not fit four slots
-    with pytest.raises(ValueError):
-        oracle.hot_resolve(np.array([[20, 21, 22, 23, 24]]), 100, tok, age, 3, 500)
+    with pytest.raises(ValueError):  # (5 and 7 would hit: the rejection must not touch them)
+        oracle.hot_resolve(np.array([[5, 7, 20, 21, 22]]), 100, tok, age, 3, 500)
+    assert tok.tolist() == [2, 7, 5, 11] and age.tolist() == [2, 2, 2, 2]
     # a fully resident request passes through untouched
     out, cp = oracle.hot_resolve(np.array([[2, 5, -1]]), 0, tok, age, 3, 500)
     assert out.tolist() == [[2, 5, -1]] and cp == [] and tok.tolist() == [2, 7, 5, 11]
