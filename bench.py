@@ -327,6 +327,90 @@ def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
                     "the cross-GPU all-gathers are not modelled"}
 
 
+def hot_resolve_measurement(dev, x, d, plan, q, select, attend, steps, warmup, resident=16384):
+    """Hybrid offload on the decode batch: each request keeps its last `resident` rows on the GPU,
+    the older ones only in pinned host memory, and a hot buffer of 2 x top_k slots in its released
+    rows. Times the resolve cold (every offloaded selection a miss, copied from host memory) and
+    warm (the same selection again: all hits), and the whole warm step (top-k, resolve, sparse
+    MLA over the resolved rows)."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_indexer_amd import ops
+    from sparse_mla_attention_indexer_amd import workload as W
+
+    B = d.batch
+    rf = np.maximum(x.kv_len - resident, 0).astype(np.int32)
+    n_slots = 2 * d.top_k
+    if (rf < n_slots).any() or d.kv_format != W.KV_FP8_656:
+        return None
+    row0 = np.concatenate([[0], np.cumsum(x.kv_len)[:-1]]).astype(np.int64)
+    host = torch.from_numpy(x.kv).pin_memory()
+    kv = torch.from_numpy(x.kv).to(dev)
+    for b in range(B):  # the device copies of offloaded rows are gone
+        kv[int(row0[b]): int(row0[b]) + int(rf[b])].fill_(0xEE)
+    t_rf = torch.from_numpy(rf).to(dev)
+    t_hb = torch.zeros(B, dtype=torch.int32, device=dev)
+    t_h0 = torch.from_numpy(row0).to(dev)
+    tok = torch.full((B, n_slots), -1, dtype=torch.int32, device=dev)
+    age = torch.full_like(tok, -1)
+    idx = select()
+    out_idx = torch.empty_like(idx)
+    nc = torch.empty(B, dtype=torch.int32, device=dev)
+    state = {"step": 0}
+
+    def resolve():
+        ops.hot_resolve(plan, idx, t_rf, t_hb, tok, age, state["step"], host, t_h0, kv,
+                        idx_out=out_idx, n_copied=nc)
+        state["step"] += 1
+
+    def events(n, before, fn):
+        tot = 0.0
+        for _ in range(n):
+            before()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / n
+
+    def reset():
+        tok.fill_(-1)
+        age.fill_(-1)
+
+    for _ in range(warmup):
+        reset()
+        resolve()
+    cold_ms = events(steps, reset, resolve)
+    copied = int(nc.sum().item())
+    warm_ms = events(steps, lambda: None, resolve)
+    assert int(nc.sum().item()) == 0
+
+    def whole():
+        select()
+        resolve()
+        attend(out_idx, kv)
+
+    for _ in range(warmup):
+        whole()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        whole()
+    b.record()
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / steps
+    return {"resident_rows_per_request": resident, "slots_per_request": n_slots,
+            "cold_resolve_ms": round(cold_ms, 4), "cold_rows_copied": copied,
+            "cold_host_read_GBps": round(copied * 656 / (cold_ms * 1e-3) / 1e9, 2),
+            "warm_resolve_ms": round(warm_ms, 4), "warm_step_ms": round(step_ms, 4),
+            "note": "rows below kv_len - resident only in pinned host memory; cold = every "
+                    "offloaded selection a miss, warm = the same selection again"}
+
+
 def algorithmic(d, positions):
     """Algorithmic work of one step (unique bytes; FLOPs/ops), per stage."""
     import numpy as np
@@ -501,6 +585,21 @@ def main():
     if decode and (x.n_q == 1).all() and d.kv_format == W.KV_FP8_656:
         print("[bench] DCP simulation", file=sys.stderr, flush=True)
         result["dcp_sim"] = dcp_measurement(dev, x, d, args.steps, args.warmup)
+    if decode and (x.n_q == 1).all() and d.kv_format == W.KV_FP8_656:
+        print("[bench] hybrid offload resolve", file=sys.stderr, flush=True)
+
+        def select():
+            ops.indexer_topk(plan, q_idx, k_idx, w, d.top_k, with_scores=False, idx=idx,
+                             workspace=ws_topk)
+            return idx
+
+        hot = hot_resolve_measurement(
+            dev, x, d, plan, q, select,
+            lambda sel, kv_h: ops.sparse_mla(plan, q, kv_h, d.kv_format, d.D_v, sel, d.sm_scale,
+                                             decode=True, out=out, lse=lse, workspace=ws_mla),
+            args.steps, args.warmup)
+        if hot is not None:
+            result["hot_resolve"] = hot
     if d.H_I == 64 and d.D_I == 128:
         print("[bench] FP8-key indexer", file=sys.stderr, flush=True)
         result["indexer_fp8"] = fp8_indexer_measurement(

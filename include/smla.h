@@ -217,7 +217,7 @@ int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, con
  * n_copied (device) [batch]: rows copied for request b, or (nothing changed, idx_out -1) -1 when
  * the distinct offloaded selections outnumber n_slots, -2 when resident_from / hot_base are
  * out of bounds, -3 when host rows [host_row0, host_row0 + resident_from) leave host_rows.
- * Limits: max n_q * top_k <= 8192, n_slots <= 8192. Calls for one request must be ordered.
+ * Limits: max n_q * top_k <= 8192, n_slots <= 4096. Calls for one request must be ordered.
  */
 int smla_hot_resolve(const smla_batch* b, const int32_t* idx, int32_t top_k,
                      const int32_t* resident_from, const int32_t* hot_base, int32_t n_slots,

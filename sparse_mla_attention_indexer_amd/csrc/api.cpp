@@ -11,6 +11,7 @@
 
 #include "smla.h"
 #include "smla_internal.h"
+#include "hot_resolve.h"
 
 namespace {
 

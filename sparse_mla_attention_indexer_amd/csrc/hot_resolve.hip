@@ -16,14 +16,14 @@
 // One 1024-thread workgroup per request, everything in LDS:
 //   1. the offloaded selections (others as +inf), sorted unless already ascending (a decode
 //      token's top-k is), and marked at first occurrences;
-//   2. the slot table as (token << 32 | slot), sorted; each distinct selection binary-searched;
+//   2. the slot table in an LDS hash table (token -> slot); each distinct selection looked up;
 //   3. if there are misses: the slots not hit as (last use, slot), sorted — miss number r takes
 //      the r-th; the miss rows are copied host -> hot slot by whole waves, 16 bytes a lane;
 //   4. every selection rewritten: -1 stays, a resident row stays, an offloaded row becomes
 //      hot_base + its slot.
 // Nothing in the request changes when its distinct offloaded selections outnumber the slots or
 // its hot buffer / host rows fall outside their bounds (status < 0, selections set to -1).
-#include "smla_internal.h"
+#include "hot_resolve.h"
 
 namespace smla {
 
@@ -87,7 +87,7 @@ __device__ int block_exclusive_scan(int v, int* part, int* total) {
 struct HrLds {
   int sel[HOT_MAX_SEL];    // offloaded selections (else INT_MAX), sorted
   int res[HOT_MAX_SEL];    // slot of the distinct selection at a first occurrence
-  uint64_t key[HOT_MAX_SLOTS];  // slot table, then victims, then (token, slot) of the misses
+  uint64_t key[2 * HOT_MAX_SLOTS];  // slot hash table, then victims, then the misses' (token, slot)
   int part[HR_THREADS / 64 + 1];
 };
 
@@ -145,15 +145,29 @@ __global__ __launch_bounds__(HR_THREADS) void hot_resolve_kernel(
     return;
   }
 
-  // 2. slot table sorted by token; hits found by binary search. Each thread owns the
-  // contiguous chunk [c0, c1) of the sorted selections, so miss ranks follow token order.
+  // 2. hits: the slot table goes into an LDS hash table of 2 x PH entries (token << 32 | slot,
+  // open addressing, at most half full), probed once per distinct selection. Each thread owns
+  // the contiguous chunk [c0, c1) of the sorted selections, so miss ranks follow token order.
   const int PH = next_pow2(n_slots);
-  for (int j = threadIdx.x; j < PH; j += HR_THREADS) {
-    const int t = j < n_slots ? tok[j] : -1;
-    L.key[j] = t >= 0 ? ((uint64_t)(uint32_t)t << 32) | (uint32_t)j : HR_NONE;
+  const int TB = 2 * PH, tb_shift = 32 - __builtin_ctz((unsigned)TB);
+  auto home = [&](uint32_t t) { return (int)((t * 2654435761u) >> tb_shift) & (TB - 1); };
+  for (int j = threadIdx.x; j < TB; j += HR_THREADS) L.key[j] = HR_NONE;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n_slots; j += HR_THREADS) {
+    const int t = tok[j];
+    if (t < 0) continue;
+    const uint64_t e = ((uint64_t)(uint32_t)t << 32) | (uint32_t)j;
+    for (int h = home((uint32_t)t), probe = 0; probe < TB; h = (h + 1) & (TB - 1), ++probe) {
+      const uint64_t old = atomicCAS(reinterpret_cast<unsigned long long*>(&L.key[h]),
+                                     (unsigned long long)HR_NONE, (unsigned long long)e);
+      if (old == HR_NONE) break;
+      if ((old >> 32) == (uint64_t)(uint32_t)t) {  // the token twice: the lower slot wins
+        atomicMin(reinterpret_cast<unsigned long long*>(&L.key[h]), (unsigned long long)e);
+        break;
+      }
+    }
   }
   __syncthreads();
-  bitonic_sort_lds(L.key, PH);
   const int chunk = (P + HR_THREADS - 1) / HR_THREADS;
   const int c0 = min((int)threadIdx.x * chunk, P), c1 = min(c0 + chunk, P);
   auto first = [&](int i) { return L.sel[i] != INT_MAX && (i == 0 || L.sel[i - 1] != L.sel[i]); };
@@ -161,15 +175,17 @@ __global__ __launch_bounds__(HR_THREADS) void hot_resolve_kernel(
   for (int i = c0; i < c1; ++i) {
     if (!first(i)) continue;
     const uint32_t v = (uint32_t)L.sel[i];
-    int lo = 0, hi = PH;  // first entry with token >= v (empty entries sort last)
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((L.key[mid] >> 32) < v) lo = mid + 1;
-      else hi = mid;
+    int slot = -1;
+    for (int h = home(v), probe = 0; probe < TB; h = (h + 1) & (TB - 1), ++probe) {
+      const uint64_t e = L.key[h];
+      if (e == HR_NONE) break;
+      if ((uint32_t)(e >> 32) == v) {
+        slot = (int)(uint32_t)e;
+        break;
+      }
     }
-    const bool hit = lo < PH && L.key[lo] != HR_NONE && (uint32_t)(L.key[lo] >> 32) == v;
-    L.res[i] = hit ? (int)(uint32_t)L.key[lo] : -1;
-    my_miss += !hit;
+    L.res[i] = slot;
+    my_miss += slot < 0;
   }
   int n_miss;
   const int rank0 = block_exclusive_scan(my_miss, L.part, &n_miss);  // also: searches done

@@ -136,10 +136,6 @@ enum Stage { STAGE_INDEXER = 0, STAGE_TOPK = 1, STAGE_MLA = 2, STAGE_COMBINE = 3
 // Record the begin (end = false) or end event of stage s on stream st, if one is set.
 void mark_stage(int s, bool end, hipStream_t st);
 
-// Hot-buffer resolve limits: selections per request (n_q * top_k) and slots per request.
-constexpr int HOT_MAX_SEL = 8192;
-constexpr int HOT_MAX_SLOTS = 8192;
-
 // ---- kernel launchers (defined in the .hip files) -----------------------------------------
 // Each returns hipSuccess or the launch error; arguments were validated by the caller.
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
@@ -180,13 +176,6 @@ hipError_t launch_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, con
                              int32_t* idx, int32_t* score, bool fscores, hipStream_t s);
 hipError_t launch_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
                                 int32_t* local_idx, hipStream_t s);
-size_t hot_resolve_lds_bytes();
-hipError_t launch_hot_resolve(const void* table, int32_t batch, const int32_t* idx, int32_t top_k,
-                              const int32_t* resident_from, const int32_t* hot_base,
-                              int32_t n_slots, int32_t* hot_tok, int32_t* hot_age, int32_t step,
-                              const void* host_rows, int64_t host_n_rows, const int64_t* host_row0,
-                              int32_t row_bytes, void* kv, int32_t* idx_out, int32_t* n_copied,
-                              hipStream_t s);
 hipError_t launch_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts,
                             const void* outs, const float* lses, void* out, float* lse,
                             hipStream_t s);

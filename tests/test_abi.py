@@ -168,7 +168,7 @@ def test_hot_resolve_validation(L):
     assert call(top_k=0) == _lib.SMLA_E_UNSUPPORTED
     assert call(top_k=8193) == _lib.SMLA_E_UNSUPPORTED      # n_q * top_k above 8192
     assert call(n_slots=0) == _lib.SMLA_E_UNSUPPORTED
-    assert call(n_slots=8193) == _lib.SMLA_E_UNSUPPORTED
+    assert call(n_slots=4097) == _lib.SMLA_E_UNSUPPORTED
     assert call(step=-1) == _lib.SMLA_E_INVALID
     assert call(row_bytes=650) == _lib.SMLA_E_INVALID
     assert call(host=None) == _lib.SMLA_E_INVALID
