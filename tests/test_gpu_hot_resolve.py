@@ -171,3 +171,26 @@ def test_hot_resolve_then_attention_decode():
     ref_o, ref_l = oracle_mla(x, ref_idx[sample], sample)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)[sample]
     assert_attn_close(got, ref_o, lse.cpu().numpy()[sample], ref_l, "hot-resolved attention")
+
+
+def test_hot_resolve_maximum_sizes():
+    # the limits: 4 tokens x top-k 2,048 = 8,192 selections per request (the sorting path at its
+    # largest) and 4,096 slots; later steps move the selection window so the buffer fills and
+    # least-recently-used slots are evicted
+    rng = np.random.default_rng(0x409)
+    n_q = np.array([4, 4], np.int32)
+    kv_len = np.array([200000, 120000], np.int64)
+    rf = [150000, 100000]
+    rows = rng.integers(0, 256, size=(int(kv_len.sum()), 656), dtype=np.uint8)
+    off = Offload(n_q, kv_len, rows, rf, [0, 5000], 4096)
+    say("[case] hot resolve maximum sizes: 2 x 4 tokens x 2048, 4096 slots")
+    for step, lo in enumerate((0, 2000, 4000, 4000)):
+        idx = np.full((8, 2048), -1, np.int32)
+        for t in range(8):
+            b = t // 4
+            o = np.sort(rng.choice(np.arange(lo, lo + 3000) + (0 if b == 0 else 6000), 1500, replace=False))
+            r = np.sort(rng.choice(np.arange(rf[b], int(kv_len[b])), 548, replace=False))
+            idx[t] = np.concatenate([o, r])
+        nc = off.check_against_oracle(idx, step, f"max step {step}")
+        assert (nc >= 0).all()
+        say(f"  step {step}: rows copied {nc.tolist()}")
