@@ -203,7 +203,8 @@ int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, con
  * with 0 <= hot_base and hot_base + n_slots <= resident_from (the hot buffer sits in the
  * request's released rows); host_row0[b] = host row of the request's local row 0.
  * hot_tok / hot_age (device) [batch, n_slots]: the slots' token (-1 empty) and step of last use
- * (-1 never), initialised by the caller to -1 and updated in place; step >= 0 is this call's.
+ * (-1 never), initialised by the caller to -1 and updated in place; step >= 0 is this call's
+ * and must grow from call to call for the least-recently-used order to hold.
  * host_rows (host, pinned: hipHostMalloc or a pinned torch tensor) [host_n_rows, row_bytes] is
  * read by the kernel directly; kv (device) rows of row_bytes (a multiple of 16), laid out as in
  * the batch; a miss of token u goes to kv row R_b + hot_base[b] + slot.
