@@ -194,3 +194,38 @@ def test_hot_resolve_maximum_sizes():
         nc = off.check_against_oracle(idx, step, f"max step {step}")
         assert (nc >= 0).all()
         say(f"  step {step}: rows copied {nc.tolist()}")
+
+
+def test_hot_resolve_long_rows_and_prefill_attention():
+    # two tokens per request sharing the buffer: the prefill entry point attends over the
+    # resolved rows; the same selections over 1,152-byte rows (a bf16 576-dim row: 72 x 16 bytes,
+    # so a lane copies more than one piece of a row) match the oracle too
+    x = W.generate(W.small_big_dims(batch=3, n_q=2, cached=6000, top_k=512, seed=0x5EED4100))
+    d = x.dims
+    dev = Dev(x)
+    say(f"[case] hot resolve + prefill attention: B={d.batch} n_q=2 kv_len={int(x.kv_len[0])}")
+    ref_idx, _ = dev.topk()
+    rf = (x.kv_len - 1500).astype(np.int32)
+    off = Offload(x.n_q, x.kv_len, x.kv, rf, np.zeros(d.batch, np.int32), 2 * d.top_k)
+    nc = off.check_against_oracle(ref_idx, 0, "two tokens, step 0")
+    assert (nc > 0).all()
+    got_idx, nc = off.step(ref_idx, 1)
+    assert (nc == 0).all()
+    idx_t = torch.from_numpy(got_idx).to(off.dv)
+    out, lse = ops.sparse_mla(off.plan, dev.q, off.kv, d.kv_format, d.D_v, idx_t, d.sm_scale,
+                              decode=False)
+    torch.cuda.synchronize()
+    sample = np.arange(d.total_q)
+    ref_o, ref_l = oracle_mla(x, ref_idx[sample], sample)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[sample]
+    assert_attn_close(got, ref_o, lse.cpu().numpy()[sample], ref_l, "hot-resolved prefill")
+    rng = np.random.default_rng(0x40A)
+    long_rows = rng.integers(0, 256, size=(d.total_rows, 1152), dtype=np.uint8)
+    off2 = Offload(x.n_q, x.kv_len, long_rows, rf, np.full(d.batch, 7, np.int32), 2 * d.top_k)
+    off2.check_against_oracle(ref_idx, 0, "1152-byte rows, step 0")
+    shifted = np.where(ref_idx >= 0, np.maximum(ref_idx - 900, 0), -1).astype(np.int32)
+    for t in range(shifted.shape[0]):  # keep each token's list distinct and ascending
+        v = np.unique(shifted[t][shifted[t] >= 0])
+        shifted[t] = -1
+        shifted[t, : v.size] = v
+    off2.check_against_oracle(shifted, 1, "1152-byte rows, step 1")
