@@ -26,28 +26,34 @@ __global__ __launch_bounds__(256) void local_indices_kernel(int total_q, int top
                                                             const int32_t* __restrict__ idx,
                                                             int n_shards,
                                                             int32_t* __restrict__ local_idx) {
-  __shared__ int pre[257];
+  __shared__ int wsum[4];
   const int64_t t = blockIdx.x;
   const int shard = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = (top_k + 255) / 256;
   const int j0 = min(tid * chunk, top_k), j1 = min(j0 + chunk, top_k);
   const int32_t* row = idx + t * top_k;
   int cnt = 0;
   for (int j = j0; j < j1; ++j) cnt += row[j] >= 0 && row[j] % n_shards == shard;
-  pre[tid + 1] = cnt;
-  if (tid == 0) pre[0] = 0;
+  // exclusive prefix of the counts: a shuffle scan in each wave, then the four wave totals
+  int x = cnt;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
   __syncthreads();
-  if (tid == 0)
-    for (int i = 1; i <= 256; ++i) pre[i] += pre[i - 1];
-  __syncthreads();
+  int pos = x - cnt, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    pos += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
   int32_t* out = local_idx + ((int64_t)shard * total_q + t) * top_k;
-  int pos = pre[tid];
   for (int j = j0; j < j1; ++j) {
     const int32_t g = row[j];
     if (g >= 0 && g % n_shards == shard) out[pos++] = g / n_shards;
   }
-  for (int j = pre[256] + tid; j < top_k; j += 256) out[j] = -1;
+  for (int j = total + tid; j < top_k; j += 256) out[j] = -1;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
