@@ -238,11 +238,17 @@ size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D
  * out (device) [total_q, H, D_v] bf16; lse (device, optional) [total_q, H] fp32 natural-log
  * log-sum-exp of the scaled logits (-inf and zero output for a token with no valid index).
  * logit_i = sm_scale * q_h . v_i over D_qk dims; output = softmax-weighted sum of v_i[0:D_v].
- * Supported: FP8_656 with (H, D_qk, D_v) = (64, 576, 512) on fp16 MFMA with fp32 accumulation;
- * BF16 rows with H <= 16, D_qk <= 256, D_v <= D_qk on a generic fp32 kernel. top_k <= 2048.
- * FP8_656 precision: q and the dequantised row values (code x block scale, and the bf16 rope
- * dims) are converted to fp16, so they must lie inside the fp16 range (|x| < 65504); values
- * below 2^-14 keep fewer significant bits. Nothing checks this on the device.
+ * Supported: FP8_656 with (H, D_qk, D_v) = (64, 576, 512) on the matrix cores; BF16 rows with
+ * H <= 16, D_qk <= 256, D_v <= D_qk on a generic fp32 kernel. top_k <= 2048.
+ * FP8_656 arithmetic: the logits multiply q (bf16 as given) by the E4M3 codes and bf16 rope dims,
+ * both exact in bf16, with fp32 accumulation; each 128-dim block's fp32 scale is applied to its
+ * part of the logit in fp32, so any finite scale and the whole bf16 range of q are supported.
+ * Softmax in fp32. The output products use P' = P * scale relative to a power of two chosen per
+ * split, in fp16 (11 significant bits) while every row's scale stays within [2^-10, 2^3] of it,
+ * otherwise in bf16 (the split is recomputed); fp32 accumulation; bf16 outputs. Intermediate sums
+ * are fp32: finite results need |q . v| and |v| well inside the fp32 range (|v| < 2^90).
+ * Entries that are -1 (or above p) never reach the output, whatever their placeholder row holds
+ * (NaN codes or scales included).
  * _prefill runs one workgroup per query token; _decode also splits each token's rows across
  * workgroups and merges the partials by log-sum-exp (for few query tokens).
  */

@@ -6,86 +6,115 @@
 // "Why the numbers work": QK over 576 dims, PV over 512, BF16 queries and outputs, 656-byte FP8
 // rows). Partial results over disjoint row sets merge by log-sum-exp (section "DCP").
 //
-// FP8 kernel (64 heads, 576/512 dims, 656-byte rows): one workgroup of 4 waves (one per SIMD,
-// 512 registers each) per (token, split), 32-row tiles. Every wave works on all stages, software
-// pipelined so that the matrix cores, the vector ALUs and the memory paths overlap:
-//  1. the rows of tile t+3 are moved from HBM straight into a ring of raw tiles in LDS by the
-//     load-to-LDS path (no registers involved), three tiles ahead of the one being computed;
-//  2. while tile t is multiplied, tile t+1 is dequantised from its raw copy into the other half
-//     of a double-buffered row-major K[row][576] fp16 tile: v_cvt_scalef32_pk_f16_fp8
-//     applies the power-of-two part of the block scale exactly and one packed fp16 multiply
-//     applies the rest; the bf16 rope dims are widened to fp16;
-//  3. wave (g, h) holds Q (fp16) of heads [32g, 32g+32) over dims [288h, 288h+288) and computes
-//     that half of S^T = K Q^T on v_mfma_f32_32x32x16_f16 (rows as M, heads as N, so each lane
-//     owns one head); the two waves of a head group add their halves through LDS;
-//  4. one running maximum per head; O is rescaled only when the maximum grows by more than 2^8
-//     (so P <= 256 and an fp16 P keeps 11 significant bits);
-//  5. P stays in registers: its accumulator layout is reused as the B operand of
-//     O^T = V^T P^T (the contraction runs over rows in the order the accumulator holds them);
-//     V^T comes straight from the row-major tile through transposing LDS reads
-//     (ds_read_b64_tr_b16). Wave (g, h) accumulates O^T for dims [256h, 256h+256) of its 32
-//     heads.
-// The K tile's 16-byte chunks are XOR-swizzled by row so that the operand reads, the
-// transposing reads and the dequantiser's writes all spread over the 64 LDS banks. Rows without
-// an index (padding) read the request's first row and are masked out of the softmax, so the
-// latent cache must hold finite values.
-// Decode splits a token's rows across workgroups and merges the fp16 partials by log-sum-exp.
+// FP8 kernel (64 heads, 576/512 dims, 656-byte rows): one workgroup of 8 waves (two per SIMD)
+// per (token, split), over 32-row tiles. Wave w owns FP8 block b = w & 3 (value dims
+// 128b..128b+127) and half h = w >> 2:
+//  - gather: the rows of a tile move from HBM straight into LDS by the load-to-LDS path, two
+//    tiles ahead, as stored (row r at 656 r): each load instruction covers 1 KB of consecutive
+//    row bytes, and since a row is an odd number (41) of 16-byte chunks, one chunk of 16
+//    consecutive rows falls on 16 distinct bank groups, so every operand read below is free of
+//    bank conflicts;
+//  - QK: the wave multiplies rows 16h..16h+15 of the tile by all 64 heads over block b's 128 E4M3
+//    codes, converted exactly to bf16 without their scale (v_cvt_scalef32_pk_bf16_fp8 with scale
+//    1), on v_mfma_f32_16x16x32_bf16 with rows as M and heads as N (four head tiles share each
+//    converted fragment). The block's fp32 scale then multiplies the code part of each row's
+//    partial logit, and a 16-deep k-step (v_mfma_f32_16x16x16_bf16) adds 16 of the 64 bf16 rope
+//    dims: partial_b = s_b[row] * (q_b . code_b) + q_rope_b . rope_b;
+//  - reduce: after a barrier, wave (b, h) sums the four block partials of head tile b, rows of
+//    half h, and forms P = 2^(logit * c - ref) in fp32; for each block b' it writes
+//    P'_b' = P * u_b'[row] in fp16, where u_b = s_b / 2^E_b is the scale relative to a power of
+//    two fixed per split (the first tile's largest scale of the block), zero for rows without an
+//    index;
+//  - PV: wave (b, h) accumulates O^T for dims 128b + 64h .. +64 of all 64 heads over the 32 rows
+//    on v_mfma_f32_16x16x32_f16: V^T comes from the raw codes through transposing 8-bit LDS reads
+//    (ds_read_b64_tr_b8) and the exact conversion to fp16, P'_b^T from LDS, so
+//    O_b = 2^E_b sum_r P_r u_b[r] code_r / sum_r P_r.
+// The K and V operands are therefore exact (an E4M3 code is a bf16 and an fp16 value, and q is
+// bf16 as given) and the scales are applied in fp32. P' keeps fp16's 11 significant bits while
+// every row's u stays within [2^-10, 2^3] (or is 0); one wave checks that for each tile, and a
+// split whose rows fall outside is recomputed with P' = P * s in bf16 (full range, 8 bits).
+// Rows without an index (padding) are masked: their logits become -inf, their P' is zero and
+// their V codes are zeroed before the products, so a padding row's bytes (which may be NaN)
+// never reach an output.
+// The reduction of tile t and the products of tile t-1 share one phase between barriers, so the
+// matrix cores and the vector ALUs overlap across the two waves of each SIMD.
+// Decode splits a token's rows across workgroups and merges bf16 partials by log-sum-exp.
+#include <type_traits>
+
 #include "smla_internal.h"
 
 namespace smla {
 
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int NT = 256;                    // 4 waves, one per SIMD
-constexpr int TILE = 32;                   // rows per tile
-constexpr int KCH = MLA_DQK / 8;           // 72 16-byte chunks per K row
-constexpr int K_BYTES = TILE * MLA_DQK * 2;  // 36864 per buffer
-constexpr int RB16 = 16 * KCH * 16;        // bytes between rows r and r + 16 (same swizzle)
-constexpr int ROW_CH = MLA_ROW_BYTES / 16;   // 41 16-byte chunks per stored row
-constexpr int RAW_CHUNKS = TILE * ROW_CH;    // 1312 per tile
-constexpr int RAW_INSTR = (RAW_CHUNKS + 63) / 64;  // 21 wave instructions per tile
-constexpr int RAW_SLOT = RAW_INSTR * 1024;   // 21504 bytes (the last instruction's tail is padding)
-constexpr int NRAW = 3;                    // raw tiles in flight
+constexpr int NT = 512;                       // 8 waves, two per SIMD
+constexpr int TILE = 32;                      // rows per tile
+constexpr int RB = MLA_ROW_BYTES;             // 656 bytes = 41 chunks of 16
+constexpr int ROW_CH = RB / 16;               // 41
+constexpr int SCALE_OFF = 512;                // the four fp32 block scales in a row
+constexpr int ROPE_OFF = 528;                 // the 64 bf16 rope dims in a row
+constexpr int TILE_CH = TILE * ROW_CH;        // 1312 chunks of rows per tile
+constexpr int U_OFF = TILE * RB;              // 20992: [row] x 4 fp32, the rows' relative scales u_b
+constexpr int RAW_INSTR = 21;                 // load instructions per tile (64 chunks each)
+constexpr int RAW_SLOT = RAW_INSTR * 1024;    // 21504 bytes: the rows, then the u table
+constexpr int NRAW = 4;                       // tile slots: two computed on, two in flight
 constexpr float LOG2E = 1.4426950408889634f;
 // Softmax reference (log2 units): P = 2^(logit - ref) with ref fixed for the whole split, so the
-// output accumulators are only ever touched by the matrix cores. The first tile with a valid
-// row sets ref = its maximum + REF_MARGIN; a later logit more than REF_HEADROOM above ref would
-// push an fp16 P towards its range limit, and then the split is recomputed with ref = the true
-// maximum, which the first pass has tracked.
+// output accumulators are only ever touched by the matrix cores. The first tile with a valid row
+// sets ref = its maximum + REF_MARGIN; a later logit more than REF_HEADROOM above ref would let P
+// (and the fp32 sums built on it) grow without bound, and then the split is recomputed with
+// ref = the true maximum, which the first pass has tracked.
+// With P <= 2^REF_HEADROOM and u < 2^U_MAX_LOG2, P' stays below 2^14 (fp16 max is 65504).
 constexpr float REF_MARGIN = 4.0f;
-constexpr float REF_HEADROOM = 15.0f;
+constexpr float REF_HEADROOM = 11.0f;
+constexpr float U_MAX = 8.0f;          // 2^3
+constexpr float U_MIN = 0.0009765625f;  // 2^-10: the dominant row's P' (P >= 2^-4) stays normal
 
 struct __align__(16) MlaSmem {
-  unsigned char k[2][K_BYTES];        // K[row][chunk ^ swz(row)], two tiles
-  unsigned char raw[NRAW][RAW_SLOT];  // gathered rows as stored (656 bytes each, back to back)
-  float sx[4][4][64][4];              // per wave: its half of S^T, [i/4][lane][i%4]
+  unsigned char raw[NRAW][RAW_SLOT];  // tiles as gathered (row r at 656 r), then their u tables
+  v4f part[2][4][4][64];              // [row half][head tile][block][lane]: partial logits
+  v4u pp[4][4][4][16];                // [block][head tile][row group][head]: 8 rows of P'
   int idx[TOPK_MAX_K];                // the split's row indices (-1: skip)
+  float xmax[2][MLA_H];               // per row half: logit maxima of each head
+  float xsum[2][MLA_H];               // per row half: softmax denominators of each head
+  int eb[4];                          // E_b of the split (fp16 P'), 0 in the bf16 fallback
 };
-static_assert(sizeof(MlaSmem) <= 160 * 1024 - 16, "LDS budget");
-
-// Row swizzle of 16-byte chunks (a bijection on the low three chunk bits, from row bits 0..3).
-// With 72 chunks per row, rows alternate between the two halves of the 64 banks; the swizzle
-// spreads (a) 32 rows at one chunk, (b) 4 aligned rows x 4 aligned chunks and (c) the
-// dequantiser's writes over all 16 bank groups, so every access is conflict free.
-__device__ __forceinline__ int swz(int row) {
-  return (((row >> 1) & 1) << 2) | (((row >> 2) ^ row) & 1) | (((row >> 3) & 1) << 1);
-}
-__device__ __forceinline__ int k_off(int row, int chunk) { return (row * KCH + (chunk ^ swz(row))) * 16; }
+static_assert(sizeof(MlaSmem) <= 160 * 1024 - 64, "LDS budget");
+static_assert(MLA_H * MLA_DV * 2 <= sizeof(MlaSmem::raw), "output staging");
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   v2f x = {a, b};
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  v2bf y = __builtin_convertvector(x, v2bf);
-  return __builtin_bit_cast(unsigned, y);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, v2bf));
+}
+
+// Eight E4M3 codes (two dwords, code i in byte i) -> eight bf16 values, exactly.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(unsigned lo, unsigned hi) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E4M3 codes -> eight fp16 values, exactly (|code| <= 448, smallest 2^-9).
+__device__ __forceinline__ v8h e4m3x8_to_f16(unsigned lo, unsigned hi) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 __device__ __forceinline__ unsigned pack_f16(float a, float b) {
@@ -93,23 +122,14 @@ __device__ __forceinline__ unsigned pack_f16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(x, v2h));
 }
 
-// Two bf16 (one dword) -> two fp16 (one dword), exact within the fp16 range.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned x) {
-  return pack_f16(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, x & 0xFFFF0000u));
-}
-
-__device__ __forceinline__ float swap_halves_max(float v) {
-  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
-  return __builtin_fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
-}
-__device__ __forceinline__ float swap_halves_sum(float v) {
-  auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
-  return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+// 0xFF in byte i for each set bit i of the four low bits of x.
+__device__ __forceinline__ unsigned byte_mask4(unsigned x) {
+  return (((x & 15u) * 0x00204081u) & 0x01010101u) * 0xFFu;
 }
 
 // Barrier for LDS hand-offs inside the tile loop: waits for this wave's LDS operations only,
-// so the gathers of later tiles keep flying (a full __syncthreads would wait for them too). The empty asm statements keep the compiler from
-// moving memory accesses across it.
+// so the gathers of later tiles keep flying (a full __syncthreads would wait for them too). The
+// empty asm statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -125,14 +145,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-// Gather instructions per tile: instruction q goes to wave q % 4, so wave 0 issues six and the
-// others five. Waits until this wave's gathers of all but the last `later` tiles it issued have
-// landed (`later` at most 2).
+// Gather instructions per tile: instruction q goes to wave q % 8, so waves 0..4 issue three and
+// waves 5..7 two. Waits until this wave's gathers of all but the last `later` tiles it issued
+// have landed (`later` at most 3).
 __device__ __forceinline__ void wait_tiles_but(int later, int wave) {
-  if (wave == 0) {
-    if (later >= 2) wait_vmcnt<12>(); else if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<0>();
+  if (wave < 5) {
+    if (later >= 3) wait_vmcnt<9>(); else if (later == 2) wait_vmcnt<6>();
+    else if (later == 1) wait_vmcnt<3>(); else wait_vmcnt<0>();
   } else {
-    if (later >= 2) wait_vmcnt<10>(); else if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
+    if (later >= 3) wait_vmcnt<6>(); else if (later == 2) wait_vmcnt<4>();
+    else if (later == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
   }
 }
 
@@ -154,109 +176,19 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
       : "memory");
 }
 
-// Gathers one tile (rows sidx[0..TILE)) into a raw slot: chunk c of the tile is the 16 bytes at
-// offset 16 (c % 41) of row c / 41, placed at slot + 16 c. Wave w issues instructions w + 4j
-// (j < 5) and wave 0 also instruction 20, so every wave issues a fixed number (waits count
-// them). Lanes past the tile's last chunk and rows without an index read the request's first
-// row. A lane's chunk positions are the same for every tile: `base[j]` is the request's first
-// row plus the chunk's offset inside its row, `roff[j]` the byte offset of its row's index in
-// the tile's index list.
-struct GatherPlan {
-  const unsigned char* base[6];
-  int roff[6];
-};
-
-__device__ __forceinline__ GatherPlan gather_plan(int wave, const unsigned char* kv_req) {
-  const int lane = threadIdx.x & 63;
-  GatherPlan gp;
-#pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    const int qq = j < 5 ? wave + 4 * j : 20;
-    const int c = 64 * qq + lane;
-    const int row = c < RAW_CHUNKS ? c / ROW_CH : 0;
-    gp.roff[j] = 4 * row;
-    gp.base[j] = kv_req + 16 * (c - ROW_CH * (c / ROW_CH));
-  }
-  return gp;
-}
-
-// The row indices of a lane's chunks (LDS reads) and the loads that use them, separately so that
-// the reads can go out well before the loads.
-__device__ __forceinline__ void gather_rows(const int* sidx, const GatherPlan& gp, int (&ix)[6]) {
-#pragma unroll
-  for (int j = 0; j < 6; ++j)
-    ix[j] = *reinterpret_cast<const int*>(reinterpret_cast<const char*>(sidx) + gp.roff[j]);
-}
-
-__device__ __forceinline__ void gather_issue(unsigned char* slot, const int (&ix)[6],
-                                             const GatherPlan& gp, int wave) {
-#pragma unroll
-  for (int j = 0; j < 6; ++j) {
-    if (j == 5 && wave != 0) break;  // wave-uniform
-    const int qq = j < 5 ? wave + 4 * j : 20;
-    lds_load16(gp.base[j] + (uint64_t)(uint32_t)max(ix[j], 0) * MLA_ROW_BYTES, slot + 1024 * qq);
-  }
-}
-
-__device__ __forceinline__ void tile_gather(unsigned char* slot, const int* sidx,
-                                            const GatherPlan& gp, int wave) {
-  int ix[6];
-  gather_rows(sidx, gp, ix);
-  gather_issue(slot, ix, gp, wave);
-}
-
-// Dequantises a raw tile into the fp16 K tile. Thread (r, m) = (tid / 8, tid % 8) takes 64 e4m3
-// codes of row r (dims 128 i + 16 m .. +16, i < 4) and 8 bf16 rope dims (512 + 8 m .. +8). The
-// scale s = 2^e * mant (1 <= mant < 2): the conversion applies 2^e exactly and a packed multiply
-// fp16(mant); the rope dims are widened. Rows without an index hold the request's first row,
-// which the softmax masks out.
-// The pieces are separate so that the tile loop can place them between the matrix instructions
-// of the previous tile: load() reads the thread's raw bytes, block(i) converts and stores dims
-// 128 i + 16 m .. +16, rope() the rope dims.
-struct Dequant {
-  v4u code[4];
-  v4u scale;
-  v4u rope;
-  __device__ __forceinline__ void load(const unsigned char* slot, int r, int m) {
-    const unsigned char* row = slot + r * MLA_ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) code[i] = *reinterpret_cast<const v4u*>(row + 128 * i + 16 * m);
-    scale = *reinterpret_cast<const v4u*>(row + 512);
-    rope = *reinterpret_cast<const v4u*>(row + 528 + 16 * m);
-  }
-  __device__ __forceinline__ void block(unsigned char* kb, int r, int m, int i) const {
-    // the conversion reads only the exponent of its scale operand
-    const float sc = __builtin_bit_cast(float, scale[i] & 0x7F800000u);
-    const float mt = __builtin_bit_cast(float, (scale[i] & 0x807FFFFFu) | 0x3F800000u);
-    const v2h mm = {(_Float16)mt, (_Float16)mt};
-    unsigned pk[8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code[i][h], sc, false) * mm;
-      const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code[i][h], sc, true) * mm;
-      pk[2 * h] = __builtin_bit_cast(unsigned, lo);
-      pk[2 * h + 1] = __builtin_bit_cast(unsigned, hi);
-    }
-    *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m)) = v4u{pk[0], pk[1], pk[2], pk[3]};
-    *reinterpret_cast<v4u*>(kb + k_off(r, 16 * i + 2 * m + 1)) = v4u{pk[4], pk[5], pk[6], pk[7]};
-  }
-  __device__ __forceinline__ void rope_store(unsigned char* kb, int r, int m) const {
-    *reinterpret_cast<v4u*>(kb + k_off(r, 64 + m)) =
-        v4u{bf16x2_to_f16x2(rope[0]), bf16x2_to_f16x2(rope[1]), bf16x2_to_f16x2(rope[2]), bf16x2_to_f16x2(rope[3])};
-  }
-};
-
-__device__ __forceinline__ void tile_dequant(const unsigned char* slot, unsigned char* kb, int r, int m) {
-  Dequant dq;
-  dq.load(slot, r, m);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dq.block(kb, r, m, i);
-  dq.rope_store(kb, r, m);
-}
-
 // One (token, split): the split's share of the tiles of the token's index list, up to its last
-// valid entry.
-// Writes either the final bf16 output (+ lse) or an fp16 partial (+ lse) for the combine.
+// valid entry. Writes either the final bf16 output (+ lse) or a bf16 partial (+ lse) for the
+// combine.
+//
+// Two teams of four waves, one wave of each on every SIMD, work on consecutive tiles at the same
+// time, so that one team's matrix instructions run while the other's vector instructions do:
+//  - the QK team (waves 0..3, wave b = FP8 block b) computes the partial logits of tile t,
+//    holds them in registers across the middle barrier and then stores them; it also issues
+//    every gather, and its last wave writes each tile's u table;
+//  - the PV team (waves 4..7, wave b) reduces head tile b of tile t - 1 (all 32 rows, so the
+//    softmax state of heads 16b..16b+15 stays inside the wave), writes P', and after the middle
+//    barrier accumulates O for block b's 128 dims of all 64 heads.
+// Per iteration: [QK(t) | reduce(t-1)] barrier [store partials(t), u table(t) | PV(t-1)] barrier.
 __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ toks,
                                                         const __bf16* __restrict__ q,
                                                         const unsigned char* __restrict__ kv,
@@ -264,22 +196,26 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
                                                         int top_k,
                                                         float sm_scale, __bf16* __restrict__ out,
                                                         float* __restrict__ lse_out,
-                                                        _Float16* __restrict__ part_o,
+                                                        __bf16* __restrict__ part_o,
                                                         float* __restrict__ part_lse) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   MlaSmem& sm = *reinterpret_cast<MlaSmem*>(smem_raw);
-  const int64_t t = blockIdx.x;
+  const int64_t t_tok = blockIdx.x;
   const int split = blockIdx.y;
   const int nsplit = gridDim.y;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool qk_team = wave < 4;
+  const int b = wave & 3;
+  const int G = lane >> 4, l16 = lane & 15;
 
-  const int32_t* idx_row = idx + t * top_k;
+  const int32_t* idx_row = idx + t_tok * top_k;
 
   // The split's indices. First guess, right for a list whose last entry is valid: the splits share
   // all of the list's tiles. The last entry is loaded with them to check.
-  __shared__ int last_all, last_valid;
-  if (tid == 0) last_all = -1, last_valid = -1;
+  __shared__ int last_all, last_valid, logit_over, scale_over;
+  if (tid == 0) last_all = -1, last_valid = -1, logit_over = 0, scale_over = 0;
+  if (tid < 4) sm.eb[tid] = 0;
   constexpr int PER = TOPK_MAX_K / NT;
   const int tiles_k = (top_k + TILE - 1) / TILE;
   int per_split = (tiles_k + nsplit - 1) / nsplit;
@@ -292,18 +228,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     ixs[u] = r_begin + j < r_end ? idx_row[r_begin + j] : -1;
   }
   const int32_t last_entry = idx_row[top_k - 1];
-  // this lane's Q^T fragments go out with the indices: head `head`, dims
-  // [288*kh + 16*ks + 8*half, +8), bf16 as loaded (widened to fp16 below)
-  const int hg = wave >> 1, kh = wave & 1;
-  const int col = lane & 31, half = lane >> 5;
-  const int head = 32 * hg + col;
-  v4u qraw[18];
-  {
-    const __bf16* qh = q + (t * MLA_H + head) * MLA_DQK + 288 * kh + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qraw[ks] = *reinterpret_cast<const v4u*>(qh + 16 * ks);
-  }
-  const Tok tk = toks[t];
+  const Tok tk = toks[t_tok];
   __syncthreads();
   {
     int lv = -1;
@@ -347,201 +272,345 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   __syncthreads();
   const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
 
-  v8h qf[18];
+  // Gather plan (QK team): instruction gq = b + 4 j (j < 6, gq <= 20) loads the tile's chunks
+  // 64 gq .. 64 gq + 63 (chunk ci = 16 bytes at offset 16 (ci % 41) of row ci / 41); instruction
+  // 20's upper half would pass the last row, where the u table sits, and loads nothing.
+  const unsigned char* kv_req = kv + tk.row_start * MLA_ROW_BYTES;
+  int grow[6], goff[6];
 #pragma unroll
-  for (int ks = 0; ks < 18; ++ks)
-    qf[ks] = __builtin_bit_cast(v8h, v4u{bf16x2_to_f16x2(qraw[ks][0]), bf16x2_to_f16x2(qraw[ks][1]),
-                                         bf16x2_to_f16x2(qraw[ks][2]), bf16x2_to_f16x2(qraw[ks][3])});
-  // per-lane LDS offsets: S operand (K row `col`, chunk 36*kh + 2u + half (+ 8m)), and the
-  // transposing V reads (16-lane group g: dims +16*(g&1); 4 rows from 4*(g>>1) + lane%16 / 4).
-  // The transposing V reads of (ks, second half, mt = 2m + par) sit at
-  // voff[hi][par] + RB16 * ks + 128 m: rows 16 apart share their swizzle, and the chunk of dim
-  // vdim + 32mt is (vdim >> 3) + 4par + 8m, whose bit 3 and up the swizzle leaves alone.
-  int koff[4];
+  for (int j = 0; j < 6; ++j) {
+    const int ci = min(64 * (b + 4 * j) + lane, TILE_CH - 1);
+    grow[j] = ci / ROW_CH;
+    goff[j] = 16 * (ci - ROW_CH * grow[j]);
+  }
+  auto gather = [&](int tile) {
+    // every row index is read before the first load goes out (a load's asm statement orders the
+    // LDS reads after it behind it)
+    const int* ti = sm.idx + tile * TILE;
+    int ix[6];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = k_off(col, 36 * kh + 2 * u + half);
-  const int grp = lane >> 4, gl = lane & 15;
-  const int vrow = 4 * (grp >> 1) + (gl >> 2);
-  const int vdim = 256 * kh + 16 * (grp & 1) + 4 * (gl & 3);
-  int voff[2][2];
+    for (int j = 0; j < 6; ++j) ix[j] = ti[grow[j]];
+    unsigned char* dst = sm.raw[tile % NRAW];
 #pragma unroll
-  for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      voff[hi][par] = k_off(8 * hi + vrow, (vdim >> 3) + 4 * par) + 2 * (vdim & 7);
+    for (int j = 0; j < 5; ++j)
+      lds_load16(kv_req + (uint64_t)(uint32_t)max(ix[j], 0) * RB + goff[j], dst + 1024 * (b + 4 * j));
+    if (b == 0 && lane < 32)
+      lds_load16(kv_req + (uint64_t)(uint32_t)max(ix[5], 0) * RB + goff[5], dst + 1024 * 20);
+  };
+  // valid-row mask of a tile (bit r: row r has an index); the same in every wave
+  auto tile_valid = [&](int tile) -> uint32_t {
+    return (uint32_t)__ballot(sm.idx[tile * TILE + (lane & 31)] >= 0);
+  };
 
-  // the Q fragments are in registers before any gather goes out (the compiler does not count the
-  // gathers, so a later wait of its own for Q would drain them)
-  wait_vmcnt<0>();
-  // dequantiser's share: tile row tid / 8, pieces m = tid % 8
-  const int pr = tid >> 3, pm = tid & 7;
-  const GatherPlan gp = gather_plan(wave, kv + tk.row_start * MLA_ROW_BYTES);
   const float c = sm_scale * LOG2E;
-  float ref = -INFINITY;     // softmax reference of this lane's head (log2 units)
-  float seen = -INFINITY;    // largest scaled logit of this lane's head so far
-  __shared__ int redo;
-  v16f o[8];
-  float l_run;  // this lane's share of the softmax denominator
+  bool f16 = true;         // P' and V in fp16 (else the bf16 fallback)
+  bool u_out = false;      // scale wave: a row's u outside [U_MIN, U_MAX)
+  const bool scale_wave = wave == 3;
 
-#pragma unroll 1
-  for (int pass = 0;; ++pass) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = v16f{};
-  l_run = 0.f;
-  bool over = false;  // a logit above ref + REF_HEADROOM
-  for (int j = 0; j < NRAW && j < ntiles; ++j) tile_gather(sm.raw[j], sm.idx + j * TILE, gp, wave);
-  if (ntiles > 0) {
-    wait_tiles_but(min(ntiles, NRAW) - 1, wave);
-    lds_barrier();  // every wave's part of tile 0 has landed
-    tile_dequant(sm.raw[0], sm.k[0], pr, pm);
-    if (ntiles > 1) wait_tiles_but(min(ntiles, NRAW) - 2, wave);
-  }
-  if (tid == 0) redo = 0;
-  lds_barrier();  // tile 0 is in K[0], tile 1 in raw slot 1
-
-  // Entering iteration `it`: K[it & 1] holds tile it, raw slot (it+1) % 3 holds tile it+1
-  // (landed and visible), tile it+2 is in flight, slot it % 3 is free.
-#pragma unroll 1
-  for (int it = 0; it < ntiles; ++it) {
-    const unsigned char* kb = sm.k[it & 1];
-    // half of S^T over this wave's dims (one accumulation chain: a dependent 32x32x16 MFMA
-    // issues at full rate). The matrix instructions run on their own while the wave issues the
-    // work placed between them: the gather of tile it+3 and the fp16 copy of tile it+1 (the
-    // latter unconditional: after the last tile it converts a stale slot into the idle buffer,
-    // which nothing reads). Scheduling barriers keep the compiler from regrouping the pieces.
-    v16f s = v16f{};
-    {
-      unsigned char* kn = sm.k[(it + 1) & 1];
-      const bool gather = it + NRAW < ntiles;
-      int ix[6];
-      if (gather) gather_rows(sm.idx + (it + NRAW) * TILE, gp, ix);
-      Dequant dq;
-      // operand reads eight k-steps ahead of their MFMA (LDS latency under load exceeds the
-      // time of a few MFMAs)
-      v8h a[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) a[ks] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * (ks >> 2));
-      dq.load(sm.raw[(it + 1) % NRAW], pr, pm);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 7], qf[ks], s, 0, 0, 0);
-        if (ks + 8 < 18)
-          a[ks & 7] = *reinterpret_cast<const v8h*>(kb + koff[ks & 3] + 128 * ((ks + 8) >> 2));
-        if (ks == 1 && gather) gather_issue(sm.raw[it % NRAW], ix, gp, wave);
-        if (ks == 4 || ks == 7 || ks == 10 || ks == 13) dq.block(kn, pr, pm, (ks - 4) / 3);
-        if (ks == 15) dq.rope_store(kn, pr, pm);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4)
-      *reinterpret_cast<float4*>(&sm.sx[wave][g4][lane][0]) =
-          make_float4(s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]);
-    lds_barrier();
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 o4 = *reinterpret_cast<const float4*>(&sm.sx[wave ^ 1][g4][lane][0]);
-      s[4 * g4] += o4.x;
-      s[4 * g4 + 1] += o4.y;
-      s[4 * g4 + 2] += o4.z;
-      s[4 * g4 + 3] += o4.w;
-    }
-    // lane holds head `head`, rows 8*(i/4) + 4*half + i%4 of the tile; raw logits stay unscaled
-    // (c > 0 keeps their order) and c enters the exponent below
-    const uint64_t valid = __ballot(sm.idx[it * TILE + col] >= 0);  // bit r: row r is valid
-    if ((uint32_t)valid != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * half + (i & 3);
-        if (!((valid >> row) & 1)) s[i] = -INFINITY;
-      }
-    }
-    float tmax = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = __builtin_fmaxf(tmax, s[i]);
-    tmax = swap_halves_max(tmax) * c;
-    // both waves of a head group hold identical logits and take the same decisions
-    seen = __builtin_fmaxf(seen, tmax);
-    ref = ref == -INFINITY && tmax != -INFINITY ? tmax + REF_MARGIN : ref;
-    over |= tmax > ref + REF_HEADROOM;
-    // P in registers, packed as the B operand of the two 16-row k-steps (no valid row so far:
-    // every logit is -inf and P must come out 0, not NaN)
-    const float m_use = ref == -INFINITY ? 0.f : ref;
-    v8h pb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float p8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + j], c, -m_use));  // underflow to 0 is harmless
-        l_run += p8[j];
-      }
-      v4u pk = {pack_f16(p8[0], p8[1]), pack_f16(p8[2], p8[3]), pack_f16(p8[4], p8[5]),
-                pack_f16(p8[6], p8[7])};
-      pb[ks] = __builtin_bit_cast(v8h, pk);
-    }
-    // O^T[dims 256*kh + 32*mt + m][head] += V^T[dim][rows] P^T[rows][head]
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int par = mt & 1, mm = mt >> 1;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(kb + voff[0][par] + RB16 * ks + 128 * mm));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(kb + voff[1][par] + RB16 * ks + 128 * mm));
-        const v8h a = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[ks], o[mt], 0, 0, 0);
-      }
-    }
-    // tile it+2 must have landed before the next iteration dequantises it; only tile it+3 (issued
-    // at the top of this iteration) may still be in flight
-    if (it + 2 < ntiles) wait_tiles_but(it + 3 < ntiles ? 1 : 0, wave);
-    lds_barrier();
-  }
-  wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS
-  if (__any(over)) redo = 1;  // any wave: every wave redoes the split
-  __syncthreads();
-  if (!redo || pass == 1) break;
-  ref = seen;  // the second pass cannot exceed it
-  __syncthreads();
-  }
-
-  // denominator of each head: both lane halves, both waves of the head group hold the same
-  l_run = swap_halves_sum(l_run);
-  const bool empty = !(l_run > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_run;
-  const float lse = empty ? -INFINITY : (ref + log2f(l_run)) * (1.0f / LOG2E);
-
-  // The output goes out through LDS (the K buffers, idle once the tile loop is done) so that every
-  // global store writes whole lines: head h's 512 16-bit values sit at h * 1024 with 16-byte
-  // chunk c at 16 (c ^ (h & 63)), and a wave stores one head's row (1 KB) per instruction.
+  // Each team runs its own pass loop (so that Q and O never share registers); both issue the same
+  // barriers in the same order. A second pass runs when a logit left the reference window
+  // (ref = the true maximum then, P <= 1), and with P' in bf16 when some row's scale left the
+  // fp16 window.
   const bool split_out = part_o != nullptr;
-  unsigned char* stage = &sm.k[0][0];
-  static_assert(sizeof(sm.k) >= MLA_H * MLA_DV * 2, "output staging");
+  unsigned char* stage = &sm.raw[0][0];
+  if (qk_team) {
+  // The QK team's Q fragments go out with the indices (bf16 as given): head tile ht, head
+    // 16 ht + l16; code k-step ks: dims 128 b + 64 (ks >> 1) + 16 G + 8 (ks & 1) .. +8 (the order
+    // in which the K fragments hold them); rope: dims 512 + 16 b + 4 G .. +4 (a 16-deep k-step
+    // covers the block's share of the 64 rope dims).
+    v8bf qc[4][4];
+    v4s qr[4];
+    {
+      const __bf16* qt = q + t_tok * (int64_t)(MLA_H * MLA_DQK);
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+      for (int ht = 0; ht < 4; ++ht) {
+        const __bf16* qh = qt + (16 * ht + l16) * MLA_DQK;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const float v0 = o[mt][4 * g4] * inv, v1 = o[mt][4 * g4 + 1] * inv;
-      const float v2 = o[mt][4 * g4 + 2] * inv, v3 = o[mt][4 * g4 + 3] * inv;
-      const v2u pk = split_out ? v2u{pack_f16(v0, v1), pack_f16(v2, v3)}
-                               : v2u{pack_bf16(v0, v1), pack_bf16(v2, v3)};
-      const int chunk = 32 * kh + 4 * mt + g4;  // dims 256 kh + 32 mt + 8 g4 .. +8
-      *reinterpret_cast<v2u*>(stage + head * 1024 + 16 * (chunk ^ (head & 63)) + 8 * half) = pk;
+        for (int ks = 0; ks < 4; ++ks)
+          qc[ht][ks] = *reinterpret_cast<const v8bf*>(qh + 128 * b + 64 * (ks >> 1) + 16 * G + 8 * (ks & 1));
+        qr[ht] = *reinterpret_cast<const v4s*>(qh + 512 + 16 * b + 4 * G);
+      }
     }
-  __syncthreads();
-  unsigned char* dst = split_out ? reinterpret_cast<unsigned char*>(part_o + (t * nsplit + split) * MLA_H * MLA_DV)
-                                 : reinterpret_cast<unsigned char*>(out + t * MLA_H * MLA_DV);
+  // ---- QK team: one pass over the split's tiles
+    auto qk_pass = [&](auto f16_tag) {
+      constexpr bool F16 = decltype(f16_tag)::value;
+      bool have_e = false;
+      u_out = false;
+      const int first = min(ntiles, NRAW);
+      for (int u = 0; u < first; ++u) gather(u);
+      if (ntiles > 0) wait_tiles_but(first - 1, b);
+      lds_barrier();  // every wave's part of tile 0 has landed
+#pragma unroll 1
+      for (int t = 0; t <= ntiles; ++t) {
+        v4f acc[2][4];
+        if (t < ntiles) {
+          const unsigned char* rt = sm.raw[t % NRAW];
+          v4u k0[2], k1[2];
+          v4s kr[2];
+          float sb[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const unsigned char* rr = rt + RB * (16 * h + l16);
+            k0[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + G));
+            k1[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + 4 + G));
+            kr[h] = *reinterpret_cast<const v4s*>(rr + ROPE_OFF + 32 * b + 8 * G);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sb[h][i] = *reinterpret_cast<const float*>(rt + RB * (16 * h + 4 * G + i) + SCALE_OFF + 4 * b);
+          }
+          if (t >= 2 && t + 2 < ntiles) gather(t + 2);  // its slot held tile t - 2, done with
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) acc[h][ht] = v4f{};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const v4u& kk = ks < 2 ? k0[h] : k1[h];
+              const v8bf a = e4m3x8_to_bf16(kk[2 * (ks & 1)], kk[2 * (ks & 1) + 1]);
+#pragma unroll
+              for (int ht = 0; ht < 4; ++ht)
+                acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qc[ht][ks], acc[h][ht], 0, 0, 0);
+            }
+          }
+          // the block scale multiplies the code part; the rope part then accumulates on top
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[h][ht][i] *= sb[h][i];
+              acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr[h], qr[ht], acc[h][ht], 0, 0, 0);
+            }
+        }
+        lds_barrier();  // the PV team has read the partials of tile t - 1
+        if (t < ntiles) {
+          // lane: head 16 ht + l16, rows 16 h + 4 G + i
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) sm.part[h][ht][b][lane] = acc[h][ht];
+          if (scale_wave) {
+            // u_b[r] = s_b[r] / 2^E_b for the tile's rows (lane: row lane & 31), 0 for rows without
+            // an index; E_b is fixed by the first tile with a valid row (the exponent of its largest
+            // scale of block b), 0 in the bf16 fallback
+            unsigned char* rt = sm.raw[t % NRAW];
+            const int r = lane & 31;
+            const v4f s4 = *reinterpret_cast<const v4f*>(rt + RB * r + SCALE_OFF);
+            const uint32_t vm = tile_valid(t);
+            const bool valid = (vm >> r) & 1u;
+            if (F16 && !have_e && vm != 0) {  // uniform in the wave
+#pragma unroll
+              for (int b2 = 0; b2 < 4; ++b2) {
+                float m = valid ? s4[b2] : 0.f;
+#pragma unroll
+                for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+                if (lane == 0) sm.eb[b2] = m > 0.f && m <= 3.402823466e38f ? __builtin_amdgcn_frexp_expf(m) : 0;
+              }
+              have_e = true;
+            }
+            if (!F16 && lane < 4) sm.eb[lane] = 0;
+            v4f u4;
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) {
+              const float u = valid ? (F16 ? __builtin_amdgcn_ldexpf(s4[b2], -sm.eb[b2]) : s4[b2]) : 0.f;
+              u4[b2] = u;
+              u_out |= F16 && !((u >= U_MIN && u < U_MAX) || u == 0.f);
+            }
+            if (lane < 32) *reinterpret_cast<v4f*>(rt + U_OFF + 16 * r) = u4;
+          }
+        }
+        // tile t + 1 must have landed before the next iteration reads it; later tiles may still be
+        // in flight
+        if (t + 1 < ntiles) {
+          const int last_issued = min(ntiles - 1, max(NRAW - 1, t + 2));
+          wait_tiles_but(last_issued - (t + 1), b);
+        }
+        lds_barrier();
+      }
+      wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS
+    };
+
+#pragma unroll 1
+    for (int pass = 0;; ++pass) {
+      if (f16) qk_pass(std::true_type{});
+      else qk_pass(std::false_type{});
+      if (__any(u_out)) scale_over = 1;
+      __syncthreads();
+      if (!(logit_over || scale_over) || pass == 1) break;
+      f16 = !scale_over;
+      __syncthreads();
+    }
+    __syncthreads();  // the PV team's output is staged
+  } else {
+    float ref = -INFINITY;   // softmax reference of head 16 b + l16 (log2 units)
+    float seen = -INFINITY;  // largest scaled logit of that head in this lane's rows
+    float lsum = 0.f;        // this lane's share of the head's softmax denominator
+    v4f o[8][4];             // O^T [dim tile][head tile] for dims 128 b + 16 dt + 4 G + i
+    bool over = false;       // a logit above ref + REF_HEADROOM
+  // ---- PV team: one pass over the split's tiles, one tile behind the QK team
+    auto pv_pass = [&](auto f16_tag, bool have_ref) {
+      constexpr bool F16 = decltype(f16_tag)::value;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[i][j] = v4f{};
+      lsum = 0.f;
+      lds_barrier();  // tile 0 has landed
+      const int voff = RB * (8 * G + (l16 >> 1)) + 16 * (8 * b) + 8 * (l16 & 1);
+#pragma unroll 1
+      for (int t = 0; t <= ntiles; ++t) {
+        const int u = t - 1;
+        if (t >= 1) {
+          // reduction of tile u, head tile b (lane: head 16 b + l16), rows 16 h + 4 G + i
+          const unsigned char* rt = sm.raw[u % NRAW];
+          // every LDS read of the reduction goes out first
+          v4f ps[2][4], uv[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) ps[h][b2] = sm.part[h][b][b2][lane];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              uv[h][i] = *reinterpret_cast<const v4f*>(rt + U_OFF + 16 * (16 * h + 4 * G + i));
+          const uint32_t vm = tile_valid(u);
+          float x[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const v4f s = ps[h][0] + ps[h][1] + ps[h][2] + ps[h][3];
+            if (vm == 0xFFFFFFFFu) {  // uniform
+#pragma unroll
+              for (int i = 0; i < 4; ++i) x[h][i] = s[i] * c;
+            } else {
+              const unsigned vb = (vm >> (16 * h + 4 * G)) & 15u;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) x[h][i] = (vb >> i) & 1 ? s[i] * c : -INFINITY;
+            }
+          }
+          if (!have_ref && vm != 0) {  // uniform: the first tile with a valid row sets ref
+            float m = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                            fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            ref = m + REF_MARGIN;
+            have_ref = true;
+          }
+          const float m_use = ref == -INFINITY ? 0.f : ref;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              seen = fmaxf(seen, x[h][i]);  // a logit above m_use + REF_HEADROOM asks for a second pass
+              pr[i] = __builtin_amdgcn_exp2f(x[h][i] - m_use);  // -inf -> 0; underflow to 0 is harmless
+              lsum += pr[i];
+            }
+            // P'_b2 = P u_b2[row]; u is 0 for a row without an index, whose P is 0 too
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) {
+              float w[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) w[i] = pr[i] * uv[h][i][b2];
+              unsigned* dst = reinterpret_cast<unsigned*>(&sm.pp[b2][b][2 * h + (G >> 1)][l16]) + 2 * (G & 1);
+              *reinterpret_cast<v2u*>(dst) = F16 ? v2u{pack_f16(w[0], w[1]), pack_f16(w[2], w[3])}
+                                                 : v2u{pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3])};
+            }
+          }
+        }
+        lds_barrier();  // P' of tile u visible; the partials of tile u read
+        if (t >= 1) {
+          // PV of tile u: dims 128 b + 16 dt + 4 G + i of every head
+          const unsigned char* rv = sm.raw[u % NRAW];
+          const uint32_t vm = tile_valid(u);
+          const unsigned vb = (vm >> (8 * G)) & 0xFFu;
+          const unsigned mlo = byte_mask4(vb), mhi = byte_mask4(vb >> 4);
+          v4u pb[4];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) pb[ht] = sm.pp[b][ht][G][l16];
+          v2i fv[8];  // every V fragment is read before the first product
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            fv[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i*)(rv + voff + 16 * dt));
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const v2i f = fv[dt];
+            if constexpr (F16) {
+              const v8h va = e4m3x8_to_f16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
+#pragma unroll
+              for (int ht = 0; ht < 4; ++ht)
+                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(v8h, pb[ht]), o[dt][ht], 0, 0, 0);
+            } else {
+              const v8bf va = e4m3x8_to_bf16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
+#pragma unroll
+              for (int ht = 0; ht < 4; ++ht)
+                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, __builtin_bit_cast(v8bf, pb[ht]), o[dt][ht], 0, 0, 0);
+            }
+          }
+        }
+        lds_barrier();
+      }
+    };
+
+
+#pragma unroll 1
+    for (int pass = 0;; ++pass) {
+      if (f16) pv_pass(std::true_type{}, pass > 0);
+      else pv_pass(std::false_type{}, pass > 0);
+      // denominators and maxima of each head: all 32 rows of a tile are in this wave
+      lsum += __shfl_xor(lsum, 16);
+      lsum += __shfl_xor(lsum, 32);
+      float sn = fmaxf(seen, __shfl_xor(seen, 16));
+      sn = fmaxf(sn, __shfl_xor(sn, 32));
+      if (G == 0) {
+        sm.xsum[0][16 * b + l16] = lsum;
+        sm.xmax[0][16 * b + l16] = sn;
+      }
+      over = seen > (ref == -INFINITY ? 0.f : ref) + REF_HEADROOM;
+      if (__any(over)) logit_over = 1;  // any wave: every wave redoes the split
+      __syncthreads();
+      if (!(logit_over || scale_over) || pass == 1) break;
+      ref = sn;
+      f16 = !scale_over;
+      __syncthreads();
+    }
+    // The output goes out through LDS (the raw slots, idle once the tile loop is done) so that
+    // every global store writes whole lines: head h's 512 16-bit values sit at h * 1024 with
+    // 16-byte chunk c at 16 (c ^ (h & 63)), and a wave stores one head's row (1 KB) per
+    // instruction.
+    const int e_out = sm.eb[b];  // O_b = 2^E_b sum_r P_r u_b[r] code_r / sum_r P_r
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int h = 16 * ht + l16;
+      const float l = sm.xsum[0][h];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int chunk = 16 * b + 2 * dt + (G >> 1);  // dims 128 b + 16 dt + 8 (G >> 1)
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_ldexpf(o[dt][ht][i] * inv, e_out);
+        *reinterpret_cast<v2u*>(stage + h * 1024 + 16 * (chunk ^ (h & 63)) + 8 * (G & 1)) =
+            v2u{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      }
+    }
+    if (G == 0) {
+      const int h = 16 * b + l16;
+      const float l = sm.xsum[0][h];
+      const float m_use = ref == -INFINITY ? 0.f : ref;  // the reference P was formed against
+      const float lse = l > 0.f ? (m_use + __log2f(l)) * (1.0f / LOG2E) : -INFINITY;
+      if (split_out) part_lse[(t_tok * nsplit + split) * MLA_H + h] = lse;
+      else if (lse_out) lse_out[t_tok * MLA_H + h] = lse;
+    }
+    __syncthreads();
+  }
+  unsigned char* dst = split_out ? reinterpret_cast<unsigned char*>(part_o + (t_tok * nsplit + split) * MLA_H * MLA_DV)
+                                 : reinterpret_cast<unsigned char*>(out + t_tok * MLA_H * MLA_DV);
 #pragma unroll 4
   for (int hh = wave; hh < MLA_H; hh += NT / 64)
     *reinterpret_cast<v4u*>(dst + hh * 1024 + 16 * lane) =
         *reinterpret_cast<const v4u*>(stage + hh * 1024 + 16 * (lane ^ (hh & 63)));
-  if (kh == 0 && half == 0) {
-    if (split_out) part_lse[(t * nsplit + split) * MLA_H + head] = lse;
-    else if (lse_out) lse_out[t * MLA_H + head] = lse;
-  }
 }
 
 // Merge split partials by log-sum-exp: one 128-thread block per (token, head), 4 dims per
@@ -550,8 +619,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 // dealt to the XCDs round robin, so with n_tok a multiple of 8 a token's merge runs on the XCD
 // whose L2 holds the partials its splits just wrote (the attention grid puts every split of
 // token t on XCD t % 8 too).
-
-__global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __restrict__ part_o,
+__global__ __launch_bounds__(128) void mla_combine_kernel(const __bf16* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           int nsplit, int n_tok,
                                                           __bf16* __restrict__ out,
@@ -560,14 +628,14 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __rest
   const int h = (int)(blockIdx.x / n_tok);
   const int64_t th = t * MLA_H + h;
   const float* pl = part_lse + t * nsplit * MLA_H + h;
-  const _Float16* po = part_o + (t * nsplit * MLA_H + h) * MLA_DV + 4 * threadIdx.x;
-  v4h v[8];
+  const __bf16* po = part_o + (t * nsplit * MLA_H + h) * MLA_DV + 4 * threadIdx.x;
+  v4bf v[8];
   float lj[8];
   auto load8 = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = min(j0 + u, nsplit - 1);
-      v[u] = *reinterpret_cast<const v4h*>(po + (int64_t)j * MLA_H * MLA_DV);
+      v[u] = *reinterpret_cast<const v4bf*>(po + (int64_t)j * MLA_H * MLA_DV);
       lj[u] = j0 + u < nsplit ? pl[j * MLA_H] : -INFINITY;
     }
   };
@@ -583,7 +651,8 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const _Float16* __rest
       if (j0 > 0) load8(j0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wj = lj[u] != -INFINITY ? __expf(lj[u] - m) : 0.f;
+        if (lj[u] == -INFINITY) continue;  // a split that saw no row: its partial is not read
+        const float wj = __expf(lj[u] - m);
         wsum += wj;
         acc[0] += wj * (float)v[u][0];
         acc[1] += wj * (float)v[u][1];
@@ -671,6 +740,7 @@ __global__ __launch_bounds__(256) void mla_generic_kernel(const Tok* __restrict_
       lse_out[t * H + h] = hsum[h] > 0.f ? hmax[h] + __logf(hsum[h]) : -INFINITY;
 }
 
+
 }  // namespace
 
 int mla_decode_splits(const smla_batch& b, int32_t top_k) {
@@ -686,7 +756,7 @@ size_t mla_workspace_bytes(const smla_batch& b, int32_t H, int32_t D_v, int32_t 
   const int s = mla_decode_splits(b, top_k);
   if (s <= 1) return 0;
   const size_t n = (size_t)b.total_q * s * H;
-  return align_up(n * D_v * sizeof(_Float16), 256) + align_up(n * sizeof(float), 256);
+  return align_up(n * D_v * sizeof(__bf16), 256) + align_up(n * sizeof(float), 256);
 }
 
 hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, const int32_t* idx,
@@ -701,12 +771,12 @@ hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, co
     return true;
   }();
   (void)lds_set;
-  _Float16* part_o = nullptr;
+  __bf16* part_o = nullptr;
   float* part_lse = nullptr;
   if (nsplit > 1) {
-    part_o = static_cast<_Float16*>(ws);
+    part_o = static_cast<__bf16*>(ws);
     part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                        align_up((size_t)b.total_q * nsplit * MLA_H * MLA_DV * sizeof(_Float16), 256));
+                                        align_up((size_t)b.total_q * nsplit * MLA_H * MLA_DV * sizeof(__bf16), 256));
   }
   mark_stage(STAGE_MLA, false, s);
   hipLaunchKernelGGL(mla_fp8_kernel, dim3(b.total_q, nsplit), dim3(NT), lds, s, tv.tok,
