@@ -262,6 +262,23 @@ int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, i
                            size_t ws_bytes, void* stream);
 
 /*
+ * smla_sparse_mla_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, results and errors are those of smla_sparse_mla_decode. The split partials live in
+ * a scratch array built into the library: 512 (token, split) pairs, 33,685,504 bytes per GPU,
+ * held from the first call on that GPU until the process ends. The split rule needs at most 510
+ * pairs for the FP8_656 shape (and none from 256 query tokens up); a call whose partials would
+ * not fit fails with SMLA_E_UNSUPPORTED. BF16 rows need no scratch. Allocates nothing.
+ * Every call on one GPU shares that GPU's scratch: calls whose executions overlap on one GPU
+ * (different streams, or threads without ordering) race and give wrong results; calls ordered
+ * on one stream are safe. The scratch needs no clearing: each call writes the partials it reads.
+ */
+int smla_sparse_mla_decode_noalloc(const smla_batch* b, const void* q, const void* kv,
+                                   int32_t kv_format, int32_t H, int32_t D_qk, int32_t D_v,
+                                   const int32_t* idx, int32_t top_k, float sm_scale, void* out,
+                                   float* lse, void* stream);
+
+/*
  * New tokens into the caches (the step before scoring and attention in each decode or prefill
  * chunk): token i's latent row becomes row rows[i] of the FP8_656 latent cache, and its indexer
  * key row rows[i] of the key cache. The pages size the latent row at 656 bytes (FlashMLA's

@@ -36,6 +36,7 @@ EXPORTS = (
     "smla_sparse_mla_workspace_bytes",
     "smla_sparse_mla_prefill",
     "smla_sparse_mla_decode",
+    "smla_sparse_mla_decode_noalloc",
     "smla_kv_append",
     "smla_set_stage_events",
     "smla_status_str",
@@ -95,6 +96,8 @@ def lib():
         for fn in ("smla_sparse_mla_prefill", "smla_sparse_mla_decode"):
             getattr(L, fn).argtypes = [BP, P, P, i32, i32, i32, i32, P, i32, ctypes.c_float, P, P,
                                        P, sz, P]
+        L.smla_sparse_mla_decode_noalloc.argtypes = [BP, P, P, i32, i32, i32, i32, P, i32,
+                                                      ctypes.c_float, P, P, P]
         L.smla_kv_append.argtypes = [i64, P, P, i32, P, P, P, P]
         L.smla_set_stage_events.argtypes = [P, P, i32]
         L.smla_status_str.argtypes = [ctypes.c_int]

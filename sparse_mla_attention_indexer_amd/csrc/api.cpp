@@ -484,6 +484,30 @@ int smla_sparse_mla_decode(const smla_batch* b, const void* q, const void* kv, i
                     ws_bytes, stream, 1);
 }
 
+int smla_sparse_mla_decode_noalloc(const smla_batch* b, const void* q, const void* kv,
+                                   int32_t kv_format, int32_t H, int32_t D_qk, int32_t D_v,
+                                   const int32_t* idx, int32_t top_k, float sm_scale, void* out,
+                                   float* lse, void* stream) {
+  g_err.clear();
+  bool fp8 = false;
+  int rc = check_mla_args(b, q, kv, kv_format, H, D_qk, D_v, idx, top_k, out, &fp8);
+  if (rc) return rc;
+  void* ws = nullptr;
+  size_t need = 0;
+  if (fp8) {
+    need = smla::mla_workspace_bytes(*b, H, D_v, top_k, 1);
+    if (need > smla::mla_scratch_bytes())
+      return fail(SMLA_E_UNSUPPORTED, "decode split partials need %zu bytes, the built-in scratch holds %zu",
+                  need, smla::mla_scratch_bytes());
+    if (need) {
+      hipError_t e = smla::mla_scratch(&ws);
+      if (e != hipSuccess) return hip_fail(e, "scratch address");
+    }
+  }
+  return sparse_mla(b, q, kv, kv_format, H, D_qk, D_v, idx, top_k, sm_scale, out, lse, ws, need,
+                    stream, 1);
+}
+
 int smla_kv_append(int64_t n, const void* latent, const int8_t* k_new, int32_t D_I,
                    const int64_t* rows, void* kv, int8_t* k_idx, void* stream) {
   g_err.clear();

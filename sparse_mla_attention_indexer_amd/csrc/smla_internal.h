@@ -166,6 +166,10 @@ int mla_decode_splits(const smla_batch& b, int32_t top_k);
 hipError_t launch_mla_fp8(const smla_batch& b, const void* q, const void* kv, const int32_t* idx,
                           int32_t top_k, float sm_scale, void* out, float* lse, void* ws,
                           int decode, hipStream_t s);
+// The decode split-partial scratch of the allocation-free entry point: its size, and its address
+// on the current device (looked up once per device).
+size_t mla_scratch_bytes();
+hipError_t mla_scratch(void** ptr);
 hipError_t launch_kv_append(int64_t n, const void* latent, const int64_t* rows, void* kv,
                             const int8_t* k_new, int32_t D_I, int8_t* k_idx, hipStream_t s);
 // DCP merges on one GPU (topk.hip, dcp.hip). The top-k merge holds at most MERGE_MAX_CAND

@@ -39,6 +39,7 @@
 // The reduction of tile t and the products of tile t-1 share one phase between barriers, so the
 // matrix cores and the vector ALUs overlap across the two waves of each SIMD.
 // Decode splits a token's rows across workgroups and merges bf16 partials by log-sum-exp.
+#include <mutex>
 #include <type_traits>
 
 #include "smla_internal.h"
@@ -742,6 +743,36 @@ __global__ __launch_bounds__(256) void mla_generic_kernel(const Tok* __restrict_
 
 
 }  // namespace
+
+// Scratch for callers that cannot allocate (smla_sparse_mla_decode_noalloc): the decode split
+// partials of up to MLA_SCRATCH_SPLITS (token, split) pairs, laid out as a workspace of that size
+// (bf16 partial outputs, then fp32 lse). The split rule below never needs more than 510 pairs.
+// Each GPU that runs the library holds one copy for the life of the process; the host reaches
+// it only through the address hipGetSymbolAddress returns for the current device.
+constexpr int MLA_SCRATCH_SPLITS = 512;
+constexpr size_t MLA_SCRATCH_BYTES =
+    (size_t)MLA_SCRATCH_SPLITS * MLA_H * MLA_DV * 2 + (size_t)MLA_SCRATCH_SPLITS * MLA_H * 4;
+static __device__ __align__(256) unsigned char scratch[MLA_SCRATCH_BYTES];
+
+size_t mla_scratch_bytes() { return MLA_SCRATCH_BYTES; }
+
+hipError_t mla_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 int mla_decode_splits(const smla_batch& b, int32_t top_k) {
   const int tiles = (top_k + TILE - 1) / TILE;

@@ -297,8 +297,11 @@ def mla_workspace(plan: BatchPlan, H: int, D_v: int, top_k: int, decode: bool) -
 
 
 def sparse_mla(plan: BatchPlan, q, kv, kv_format: int, D_v: int, idx, sm_scale: float,
-               decode=False, with_lse=True, out=None, lse=None, workspace=None):
+               decode=False, with_lse=True, out=None, lse=None, workspace=None, noalloc=False):
     """Sparse MLA over the selected rows: out [total_q, H, D_v] bf16 (+ lse [total_q, H] fp32).
+
+    noalloc (decode only): smla_sparse_mla_decode_noalloc, whose split partials live in the
+    library's built-in scratch; the caller passes out (and lse) to allocate nothing at all.
 
     q is [total_q, H, D_qk] bf16; kv is [>= total_rows, row_bytes] uint8 (656-byte FP8 rows) or
     [>= total_rows, D_qk] bf16; idx is [total_q, top_k] int32."""
@@ -328,6 +331,16 @@ def sparse_mla(plan: BatchPlan, q, kv, kv_format: int, D_v: int, idx, sm_scale: 
         lse = torch.empty((plan.total_q, H), dtype=torch.float32, device=d)
     if lse is not None:
         _req(lse, "lse", torch.float32, (plan.total_q, H), d)
+    if noalloc:
+        if not decode:
+            raise ValueError("noalloc is the decode entry point")
+        with torch.cuda.device(d):
+            check("smla_sparse_mla_decode_noalloc",
+                  lib().smla_sparse_mla_decode_noalloc(
+                      plan.ref, q.data_ptr(), kv.data_ptr(), kv_format, H, D_qk, D_v, idx.data_ptr(),
+                      top_k, float(sm_scale), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, _stream(d)))
+        return out, lse
     if workspace is None:
         workspace = mla_workspace(plan, H, D_v, top_k, decode)
     fn = "smla_sparse_mla_decode" if decode else "smla_sparse_mla_prefill"
