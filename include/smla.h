@@ -199,9 +199,11 @@ int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, con
  *
  * idx (device) [total_q, top_k]: the step's selections (local rows, -1 padding). Per request b
  * (device arrays of `batch` entries): resident_from[b] = first resident local row (rows below
- * it are offloaded; 0 = fully resident, nothing to do); hot_base[b] = local row of hot slot 0,
- * with 0 <= hot_base and hot_base + n_slots <= resident_from (the hot buffer sits in the
- * request's released rows); host_row0[b] = host row of the request's local row 0.
+ * it are offloaded; 0 = fully resident, nothing to do), at most kv_len - n_q + 1 so that every
+ * query token of the request (the first sits at position kv_len - n_q) sees every offloaded
+ * row; hot_base[b] = local row of hot slot 0, with 0 <= hot_base and hot_base + n_slots <=
+ * resident_from (the hot buffer sits in the request's released rows); host_row0[b] = host row
+ * of the request's local row 0.
  * hot_tok / hot_age (device) [batch, n_slots]: the slots' token (-1 empty) and step of last use
  * (-1 never), initialised by the caller to -1 and updated in place; step >= 0 is this call's
  * and must grow from call to call for the least-recently-used order to hold.

@@ -54,7 +54,7 @@ def lib():
         L.smla_oracle_topk.argtypes = [P, i64, i32, P, P]
         L.smla_oracle_topk_merge.argtypes = [P, P, i32, i32, i32, P, P]
         L.smla_oracle_lse_merge.argtypes = [i32, i32, i32, P, P, P, P]
-        L.smla_oracle_hot_resolve.argtypes = [i32, i32, P, i64, i32, P, P, i32, i64, P, P, P]
+        L.smla_oracle_hot_resolve.argtypes = [i32, i32, P, i64, i64, i32, P, P, i32, i64, P, P, P]
         L.smla_oracle_attend.argtypes = [P, P, i32, i32, i32, i32, i32, P, i32, ctypes.c_double,
                                          P, P]
         L.smla_oracle_indexer_topk_batch.argtypes = [i32, P, P, P, P, P, i32, i32, i32, P, i64, P,
@@ -179,9 +179,19 @@ def lse_merge(outs, lses):
     return out, lse
 
 
-def hot_resolve(idx, resident_from: int, hot_tok, hot_age, step: int, hot_base: int):
+class HotResolveOverflow(ValueError):
+    """The request's distinct offloaded selections outnumber the hot buffer's slots."""
+
+
+class HotResolveBounds(ValueError):
+    """resident_from / hot_base out of the request's bounds."""
+
+
+def hot_resolve(idx, resident_from: int, hot_tok, hot_age, step: int, hot_base: int,
+                kv_len: int = -1):
     """Hot-buffer resolve of one request: idx [n_q, top_k]; hot_tok / hot_age [H] int32 are
-    updated in place. Returns (idx_out [n_q, top_k], copies [(token, slot), ...])."""
+    updated in place. kv_len >= 0 also checks the request's bounds (HotResolveBounds).
+    Returns (idx_out [n_q, top_k], copies [(token, slot), ...])."""
     idx = _c(idx, np.int32)
     assert hot_tok.dtype == np.int32 and hot_age.dtype == np.int32
     assert hot_tok.flags.c_contiguous and hot_age.flags.c_contiguous
@@ -190,10 +200,13 @@ def hot_resolve(idx, resident_from: int, hot_tok, hot_age, step: int, hot_base: 
     out = np.empty_like(idx)
     copies = np.empty((n_q * top_k + 1, 2), np.int32)
     nc = ctypes.c_int32(0)
-    rc = lib().smla_oracle_hot_resolve(n_q, top_k, _p(idx), resident_from, H, _p(hot_tok), _p(hot_age),
-                                       step, hot_base, _p(out), _p(copies), ctypes.byref(nc))
+    rc = lib().smla_oracle_hot_resolve(n_q, top_k, _p(idx), kv_len, resident_from, H, _p(hot_tok),
+                                       _p(hot_age), step, hot_base, _p(out), _p(copies),
+                                       ctypes.byref(nc))
     if rc == -2:
-        raise ValueError("hot_resolve: more distinct offloaded rows than slots")
+        raise HotResolveOverflow("hot_resolve: more distinct offloaded rows than slots")
+    if rc == -3:
+        raise HotResolveBounds("hot_resolve: resident_from / hot_base out of the request's bounds")
     if rc != 0:
         raise ValueError("hot_resolve failed")
     return out, [tuple(int(v) for v in copies[i]) for i in range(nc.value)]

@@ -241,9 +241,17 @@ static int cmp_i64(const void* a, const void* b) {
   return x < y ? -1 : (x > y ? 1 : 0);
 }
 
-int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t resident_from,
-                            int32_t H, int32_t* hot_tok, int32_t* hot_age, int32_t step,
-                            int64_t hot_base, int32_t* idx_out, int32_t* copy_src, int32_t* n_copy) {
+int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t kv_len,
+                            int64_t resident_from, int32_t H, int32_t* hot_tok, int32_t* hot_age,
+                            int32_t step, int64_t hot_base, int32_t* idx_out, int32_t* copy_src,
+                            int32_t* n_copy) {
+  /* the hot buffer must lie in rows every query token of the request sees: token j sits at
+   * position kv_len - n_q + j and attends to rows up to it, so the offloaded prefix (and the
+   * buffer inside it) ends at or before the first token's position */
+  if (kv_len >= 0) {
+    if (resident_from < 0 || resident_from > kv_len - n_q + 1) return -3;
+    if (resident_from > 0 && (hot_base < 0 || hot_base + H > resident_from)) return -3;
+  }
   /* the distinct offloaded selections of the request, ascending */
   int64_t* u = (int64_t*)malloc(sizeof(int64_t) * ((size_t)n_q * top_k + 1));
   int32_t* slot_of = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n_q * top_k + 1));

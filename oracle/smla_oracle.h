@@ -100,10 +100,16 @@ int smla_oracle_lse_merge(int32_t n_parts, int32_t H, int32_t D_v, const double*
  *    (least recently used first, ties to the lower slot); each gets the token and age `step`,
  *    and its row is to be copied from host memory (copy_src: pairs (token, slot), n_copy of them);
  *  - idx_out: -1 stays -1, a resident row stays, an offloaded row becomes hot_base + its slot.
- * Returns -2, with nothing changed, when the distinct offloaded rows outnumber the H slots. */
-int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t resident_from,
-                            int32_t H, int32_t* hot_tok, int32_t* hot_age, int32_t step,
-                            int64_t hot_base, int32_t* idx_out, int32_t* copy_src, int32_t* n_copy);
+ * Returns -2, with nothing changed, when the distinct offloaded rows outnumber the H slots.
+ * kv_len >= 0 (the request's rows, its n_q query tokens last) also bounds the request: the
+ * first token sits at position kv_len - n_q and attends only to rows up to it, so the offloaded
+ * prefix must end there (resident_from <= kv_len - n_q + 1) and the hot buffer must lie inside
+ * it (0 <= hot_base, hot_base + H <= resident_from); otherwise -3, nothing changed. kv_len < 0
+ * skips these bounds (a request whose length is not given). */
+int smla_oracle_hot_resolve(int32_t n_q, int32_t top_k, const int32_t* idx, int64_t kv_len,
+                            int64_t resident_from, int32_t H, int32_t* hot_tok, int32_t* hot_age,
+                            int32_t step, int64_t hot_base, int32_t* idx_out, int32_t* copy_src,
+                            int32_t* n_copy);
 
 /* Attention of one query token q_tok [H, D_qk] (bf16 bits) over rows[idx[i]] (row_bytes each),
  * skipping idx < 0; out [H, D_v], lse [H] (either may be NULL). Returns -1 if no row is valid. */

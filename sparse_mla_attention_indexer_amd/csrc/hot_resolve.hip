@@ -112,7 +112,9 @@ __global__ __launch_bounds__(HR_THREADS) void hot_resolve_kernel(
   int32_t* age = hot_age + (int64_t)b * n_slots;
 
   int status = 0;
-  if (rf < 0 || rf > rq.kv_len) status = -2;
+  // the offloaded prefix (and the hot buffer inside it) must end at or before the first query
+  // token's position kv_len - n_q: every token of the request then sees every hot row
+  if (rf < 0 || (int64_t)rf > rq.kv_len - rq.n_q + 1) status = -2;
   else if (rf > 0 && (hb < 0 || (int64_t)hb + n_slots > rf)) status = -2;
   else if (rf > 0 && (hr0 < 0 || hr0 + rf > host_n_rows)) status = -3;
   if (status < 0 || rf == 0) {  // nothing offloaded, or a bad request: no state is touched

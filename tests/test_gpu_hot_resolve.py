@@ -26,7 +26,8 @@ class Offload:
     """A batch whose rows below resident_from[b] are only in pinned host memory (the device
     copies are overwritten with POISON), with a hot buffer of n_slots rows at hot_base[b]."""
 
-    def __init__(self, n_q, kv_len, rows, resident_from, hot_base, n_slots, device="cuda:0"):
+    def __init__(self, n_q, kv_len, rows, resident_from, hot_base, n_slots, device="cuda:0",
+                 poison=POISON):
         self.dv = torch.device(device)
         self.plan = ops.BatchPlan(n_q, kv_len, self.dv)
         self.n_q, self.kv_len = np.asarray(n_q), np.asarray(kv_len, np.int64)
@@ -35,7 +36,7 @@ class Offload:
         self.host = torch.from_numpy(rows).pin_memory()
         dev_rows = rows.copy()
         for b, rf in enumerate(resident_from):
-            dev_rows[self.row0[b]: self.row0[b] + rf] = POISON
+            dev_rows[self.row0[b]: self.row0[b] + rf] = poison
         self.kv = torch.from_numpy(dev_rows).to(self.dv)
         self.rf = np.asarray(resident_from, np.int32)
         self.hb = np.asarray(hot_base, np.int32)
@@ -62,10 +63,12 @@ class Offload:
             sel = idx_np[q0: q0 + nq]
             try:
                 ref, cp = oracle.hot_resolve(sel, int(self.rf[b]), self.o_tok[b], self.o_age[b], step,
-                                             int(self.hb[b]))
+                                             int(self.hb[b]), kv_len=int(self.kv_len[b]))
                 want_nc = len(cp)
-            except ValueError:
+            except oracle.HotResolveOverflow:
                 ref, want_nc = np.full_like(sel, -1), -1
+            except oracle.HotResolveBounds:
+                ref, want_nc = np.full_like(sel, -1), -2
             assert np.array_equal(got[q0: q0 + nq], ref), f"{label}: request {b} selections differ"
             assert nc[b] == want_nc, f"{label}: request {b} copied {nc[b]}, oracle {want_nc}"
             q0 += nq
@@ -146,6 +149,67 @@ def test_hot_resolve_rejections():
     with pytest.raises(ValueError):
         ops.hot_resolve(off.plan, torch.from_numpy(idx).to(off.dv), off.t_rf, off.t_hb, off.tok,
                         off.age, 1, torch.from_numpy(rows), off.t_h0, off.kv)
+
+
+def test_hot_resolve_request_bound_two_tokens():
+    # two query tokens per request (positions kv_len - 2 and kv_len - 1): the offloaded prefix
+    # may end at the first token's own row (resident_from = kv_len - 1) but not past it
+    rng = np.random.default_rng(0x40B)
+    n_q = np.array([2, 2], np.int32)
+    kv_len = np.array([3000, 3000], np.int64)
+    rows = rng.integers(0, 256, size=(6000, 656), dtype=np.uint8)
+    off = Offload(n_q, kv_len, rows, [2999, 3000], [100, 100], 256)
+    idx = np.full((4, 128), -1, np.int32)
+    for t, p in enumerate((2998, 2999, 2998, 2999)):
+        idx[t, :100] = np.arange(100) * 7
+        idx[t, 100] = p
+    say("[case] hot resolve: resident_from at kv_len - n_q + 1 and one past it")
+    nc = off.check_against_oracle(idx, 0, "request bound")
+    assert nc.tolist() == [101, -2]
+
+
+def _nan_row():
+    """A 656-byte row of NaN codes, non-finite block scales and NaN rope dims."""
+    r = np.full(656, 0x7F, np.uint8)
+    r[512:528] = np.array([np.nan, np.inf, -np.inf, np.nan], np.float32).view(np.uint8)
+    r[528:656] = np.full(64, 0x7FC0, np.uint16).view(np.uint8)
+    return r
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_hot_resolve_hot_base_padded_lists_attention(decode):
+    # hot buffers at hot_base > 0 inside offloaded prefixes whose device rows (row 0 included)
+    # hold NaN rows; selections with -1 holes in the middle, lists cut short, and a request whose
+    # kv_len is below top_k (its lists are padded by the selection itself); the attention over
+    # the resolved selections must match the oracle's over the original ones and the clean cache
+    x = W.generate(W.small_big_dims(batch=3, n_q=2, cached=5000, seed=0x5EED4200))
+    d = x.dims
+    n_q = np.array([2, 2, 2], np.int32)
+    kv_len = np.array([5002, 1500, 5002], np.int64)
+    dev = Dev(x, n_q=n_q, kv_len=kv_len)
+    idx, _ = dev.topk(with_scores=False)
+    assert (idx[2:4] < 0).any(axis=1).all(), "request 1 should have padded lists"
+    rng = np.random.default_rng(0x40C)
+    sel = idx.copy()
+    sel[rng.random(sel.shape) < 0.12] = -1
+    sel[0, 1300:] = -1
+    sel[5, 900:] = -1
+    rf = [4600, 0, 4700]
+    hb = [300, 0, 500]
+    say(f"[case] hot resolve at hot_base {hb} over NaN rows, padded lists, decode={decode}")
+    off = Offload(n_q, kv_len, x.kv, rf, hb, 4096, poison=_nan_row())
+    nc = off.check_against_oracle(sel, 0, "hot_base > 0, step 0")
+    assert nc[0] > 0 and nc[2] > 0 and nc[1] == 0
+    got_idx, nc = off.step(sel, 1)
+    assert (nc == 0).all()
+    idx_t = torch.from_numpy(got_idx).to(off.dv)
+    out, lse = ops.sparse_mla(off.plan, dev.q, off.kv, d.kv_format, d.D_v, idx_t, d.sm_scale,
+                              decode=decode)
+    torch.cuda.synchronize()
+    tokens = np.arange(int(n_q.sum()))
+    ref_o, ref_l = oracle_mla(x, sel, tokens, n_q=n_q, kv_len=kv_len)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_attn_close(got, ref_o, lse.cpu().numpy(), ref_l, f"hot_base > 0 decode={decode}")
 
 
 def test_hot_resolve_then_attention_decode():

@@ -578,6 +578,24 @@ def test_hot_resolve_worked_example():
     assert out.tolist() == [[2, 5, -1]] and cp == [] and tok.tolist() == [2, 7, 5, 11]
 
 
+def test_hot_resolve_request_bounds():
+    # a request of 12 rows whose last 2 are query tokens (positions 10 and 11): the offloaded
+    # prefix may reach row 10, the first token's own row, and no further; the 4-slot buffer at
+    # hot_base 2 lies inside it
+    tok = np.full(4, -1, np.int32)
+    age = np.full(4, -1, np.int32)
+    idx = np.array([[3, 10], [4, 11]])
+    out, cp = oracle.hot_resolve(idx, 11, tok, age, 0, 2, kv_len=12)
+    assert out.tolist() == [[2, 4], [3, 11]] and cp == [(3, 0), (4, 1), (10, 2)]
+    for rf, hb in ((12, 2), (-1, 2), (11, 8), (11, -1)):
+        t0, a0 = tok.copy(), age.copy()
+        with pytest.raises(oracle.HotResolveBounds):
+            oracle.hot_resolve(idx, rf, tok, age, 1, hb, kv_len=12)
+        assert np.array_equal(tok, t0) and np.array_equal(age, a0)
+    # without the request's length only the slot count is checked (the worked example above)
+    oracle.hot_resolve(idx, 12, np.full(4, -1, np.int32), np.full(4, -1, np.int32), 0, 500)
+
+
 def test_hot_resolve_one_row_per_step_is_textbook_lru():
     # with one offloaded selection per step every last-use step differs, and the rule is the
     # textbook least-recently-used cache: free slots first (lowest first), else the slot of the
