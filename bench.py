@@ -4,16 +4,25 @@ MI355X, in query tokens per second, with the dominant kernel's roofline fraction
 oracle timed on the host beside it.
 
 A step is one pass of the whole path over one batch of seeded synthetic inputs resident in HBM:
-smla_indexer_scores_topk then smla_sparse_mla_decode (decode workloads) or _prefill. The default
-workload is the decode batch: 32 requests x 1 query token over 65,536 cached tokens each.
+smla_indexer_scores_topk then smla_sparse_mla_decode (decode workloads) or _prefill. The headline
+workload is the largest: one 32,768-token prompt, fully causal. The decode batch (32 x 1 token
+after 65,536), the 2,048-token chunk after 65,536 and the million-token MTP decode (4 x 4 after
+1,048,576) run beside it as legs, each with its own roofline.
 
-    python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
+Steps are timed cold: before each step, outside its timed span, a 1 GiB buffer is written so that
+neither the L2 caches nor the 256 MB last-level cache hold anything of the previous step; each
+step's span is taken with HIP events on the stream the library launches on. Decode legs also
+rotate among four seeded query sets, so consecutive steps select different rows. The warm figure
+(steps back to back, no scrub) is reported beside the cold one.
+
+    python bench.py [--steps K] [--warmup W] [--config 0..4] [--legs 1,2,4 | --legs none]
+                    [--no-cpu-baseline]
     python bench.py --copy-calibration    # a plain 256 MiB device copy, for counter scaling
 
-HBM traffic of the dominant kernel comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters taken
-on this same command and scaled by what the counters read for the plain copy; the summary under
-profiles/ records the hash of the kernel's sources, and the figure is reported only while the
-sources still match.
+HBM traffic of a dominant kernel comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters taken
+on `bench.py --config N --legs none` and scaled by what the counters read for the plain copy; the
+summary under profiles/ records the hash of the kernel's sources, and the figure is reported only
+while the sources still match.
 """
 from __future__ import annotations
 
@@ -35,6 +44,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 DECODE_CONFIGS = (1, 4)
+HEADLINE_CONFIG = 3
+SIDE_LEGS = (1, 2, 4)
+SCRUB_BYTES = 1 << 30        # written between timed steps: > 4 x the 256 MB last-level cache
+ROTATIONS = 4                # seeded query sets a decode leg cycles through
 # file-name tags of the workloads in profiles/
 WORKLOAD_TAGS = {0: "tiny_1x512", 1: "decode_32x65536", 2: "chunk_2048after65536",
                  3: "prefill_32768", 4: "decode_4x4after1048576"}
@@ -83,6 +96,10 @@ class HipEvents:
 KERNEL_SOURCES = {
     "indexer_mfma_kernel": ("sparse_mla_attention_indexer_amd/csrc/indexer.hip",
                             "sparse_mla_attention_indexer_amd/csrc/smla_internal.h"),
+    "indexer_mfma_kernel_multi": ("sparse_mla_attention_indexer_amd/csrc/indexer.hip",
+                                  "sparse_mla_attention_indexer_amd/csrc/smla_internal.h"),
+    "mla_fp8_kernel": ("sparse_mla_attention_indexer_amd/csrc/sparse_mla.hip",
+                       "sparse_mla_attention_indexer_amd/csrc/smla_internal.h"),
 }
 
 
@@ -157,9 +174,10 @@ def append_measurement(dev, steps):
     return out
 
 
-def stage_times(step, steps):
-    """Average per-stage kernel time (ms) over `steps` calls of step(), from HIP events the library
-    records on its own launch stream around each stage."""
+def stage_times(step, steps, before=None):
+    """Average per-stage kernel time (ms) over `steps` calls of step(k), from HIP events the
+    library records on its own launch stream around each stage; before(k) (the cache scrub) runs
+    ahead of each step, outside every stage's span."""
     from sparse_mla_attention_indexer_amd import _lib
 
     hip = HipEvents()
@@ -169,10 +187,12 @@ def stage_times(step, steps):
 
     torch.cuda.synchronize()
     for k in range(steps):
+        if before is not None:
+            before(k)
         begin = (ctypes.c_void_p * len(STAGES))(*[e[0] for e in ev[k]])
         end = (ctypes.c_void_p * len(STAGES))(*[e[1] for e in ev[k]])
         _lib.check("smla_set_stage_events", L.smla_set_stage_events(begin, end, len(STAGES)))
-        step()
+        step(k)
     torch.cuda.synchronize()
     L.smla_set_stage_events(None, None, 0)
     return ev, hip
@@ -201,7 +221,7 @@ def fp8_indexer_measurement(dev, d, plan, steps, warmup, attend):
     idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
     ws = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
 
-    def step():
+    def step(k=0):
         ops.indexer_topk_fp8(plan, q8, k8, ks, w8, d.top_k, with_scores=False, idx=idx, workspace=ws)
         attend(idx)
 
@@ -417,14 +437,72 @@ def algorithmic(d, positions):
 
     rows_sel = np.minimum(positions + 1, d.top_k)
     pairs = float(np.sum(positions + 1))
+    n_rows = float(np.sum(rows_sel))
+    qo = d.total_q * d.H * 2 * (d.D_qk + d.D_v)
     return {
         # every key read once per request, every query once, the weights
         "indexer_bytes": d.total_rows * d.D_I + d.total_q * d.H_I * d.D_I + 4 * d.H_I,
         "indexer_ops": 2.0 * d.H_I * d.D_I * pairs,
-        # the pages' accounting per query: selected rows (656 B + 4 B index) + bf16 q and out
-        "mla_bytes": float(np.sum(rows_sel)) * (d.row_bytes + 4) + d.total_q * d.H * 2 * (d.D_qk + d.D_v),
-        "mla_flops": float(np.sum(rows_sel)) * d.H * 2.0 * (d.D_qk + d.D_v),
+        # the pages' accounting per query: selected rows (656 B + 4 B index) + bf16 q and out;
+        # every gathered row counts as read from HBM
+        "mla_bytes": n_rows * (d.row_bytes + 4) + qo,
+        # unique bytes: q and out, the indices, and every latent row of the batch once (prefill
+        # re-reads its few MB of rows from cache)
+        "mla_unique_bytes": qo + n_rows * 4 + d.total_rows * d.row_bytes,
+        "mla_flops": n_rows * d.H * 2.0 * (d.D_qk + d.D_v),
     }
+
+
+def rooflines(d, positions, stage_ms, decode, tag):
+    """Roofline objects of the indexer and the sparse MLA, the dominant kernel's, and the step's
+    roofline ceiling (indexer and MLA each at its bound, top-k counted as free)."""
+    alg = algorithmic(d, positions)
+    ridge_i8 = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge_bf16 = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    multi = d.n_q > 1
+    idx_kernel = "indexer_mfma_kernel_multi" if multi else "indexer_mfma_kernel"
+    idx_s = stage_ms["indexer"] * 1e-3
+    if alg["indexer_ops"] / alg["indexer_bytes"] < ridge_i8:
+        a = alg["indexer_bytes"] / idx_s / 1e9
+        idx = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(a / HBM_PEAK_GBS, 4)}
+        idx_floor = alg["indexer_bytes"] / (HBM_PEAK_GBS * 1e9)
+    else:
+        a = alg["indexer_ops"] / idx_s / 1e12
+        idx = {"bound": "mfma", "achieved": round(a, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s (int8)",
+               "frac": round(a / INT8_PEAK_TOPS, 4)}
+        idx_floor = alg["indexer_ops"] / (INT8_PEAK_TOPS * 1e12)
+    idx.update({"traffic": profiled_traffic(idx_kernel, tag), "kernel": idx_kernel,
+                "kernel_ms": round(stage_ms["indexer"], 4), "algorithmic_bytes": alg["indexer_bytes"],
+                "ops": alg["indexer_ops"]})
+    mla_ms = stage_ms["mla"] + stage_ms.get("combine", 0.0)
+    mla_s = mla_ms * 1e-3
+    if decode:  # no reuse between tokens: every gathered row from HBM (footnote accounting)
+        nbytes = alg["mla_bytes"]
+        a = nbytes / mla_s / 1e9
+        mla = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(a / HBM_PEAK_GBS, 4), "accounting": "selected rows + q + out per token"}
+        mla_floor = max(nbytes / (HBM_PEAK_GBS * 1e9), alg["mla_flops"] / (BF16_PEAK_TFLOPS * 1e12))
+    else:
+        nbytes = alg["mla_unique_bytes"]
+        bound_hbm = alg["mla_flops"] / nbytes < ridge_bf16
+        if bound_hbm:
+            a = nbytes / mla_s / 1e9
+            mla = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(a / HBM_PEAK_GBS, 4)}
+        else:
+            a = alg["mla_flops"] / mla_s / 1e12
+            mla = {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+                   "unit": "TFLOP/s (bf16)", "frac": round(a / BF16_PEAK_TFLOPS, 4)}
+        mla["accounting"] = "unique bytes: q + out + indices + every latent row once"
+        mla["footnote_hbm_GBps"] = round(alg["mla_bytes"] / mla_s / 1e9, 1)
+        mla_floor = max(nbytes / (HBM_PEAK_GBS * 1e9), alg["mla_flops"] / (BF16_PEAK_TFLOPS * 1e12))
+    mla.update({"traffic": profiled_traffic("mla_fp8_kernel", tag) if not decode or "combine" not in stage_ms
+                else None,
+                "kernel": "mla_fp8_kernel" + (" + mla_combine_kernel" if "combine" in stage_ms else ""),
+                "kernel_ms": round(mla_ms, 4), "algorithmic_bytes": nbytes, "flops": alg["mla_flops"]})
+    dominant = idx if stage_ms["indexer"] >= mla_ms else mla
+    return idx, mla, dict(dominant), (idx_floor + mla_floor) * 1e3
 
 
 def cpu_baseline(x, d, sample_tokens):
@@ -454,13 +532,252 @@ def cpu_baseline(x, d, sample_tokens):
                       f"{threads} threads"}
 
 
+def measured_peaks(dev):
+    """What this GPU reaches on plain library work, for context beside the nominal peaks: a 1 GiB
+    device copy (read + write bytes / time) and square bf16 and int8 GEMMs of 8,192 (hipBLASLt)."""
+    import torch
+
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_GBps"] = round(2 * n * 10 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, dst
+    m = 8192
+    x = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    y = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_TFLOPs"] = round(2.0 * m ** 3 * 10 / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+    del x, y
+    try:
+        xi = torch.randint(-8, 8, (m, m), dtype=torch.int8, device=dev)
+        yi = torch.randint(-8, 8, (m, m), dtype=torch.int8, device=dev)
+        for _ in range(3):
+            torch._int_mm(xi, yi)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            torch._int_mm(xi, yi)
+        b.record()
+        torch.cuda.synchronize()
+        out["int8_gemm_TOPs"] = round(2.0 * m ** 3 * 10 / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+        del xi, yi
+    except Exception as e:  # int8 GEMM may be missing from this torch build
+        out["int8_gemm_TOPs"] = None
+        out["int8_gemm_note"] = f"torch._int_mm unavailable: {type(e).__name__}"
+    torch.cuda.empty_cache()
+    out["note"] = "library kernels (torch copy, hipBLASLt GEMMs); frac is taken against the nominal peaks"
+    return out
+
+
+def run_metadata():
+    import platform
+    import subprocess
+
+    import torch
+
+    meta = {"python": platform.python_version(), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
+    try:
+        meta["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        meta["rocm"] = None
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    meta["cpu_model"] = cpu
+    meta["host_cpus"] = os.cpu_count()
+    meta["host_cpus_allowed"] = len(os.sched_getaffinity(0))
+    p = torch.cuda.get_device_properties(0)
+    meta["gpu"] = {"name": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", None),
+                   "cus": p.multi_processor_count, "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        rev = subprocess.run(["git", "rev-parse", "HEAD"], cwd=ROOT, capture_output=True, text=True,
+                             timeout=10)
+        meta["git_rev"] = rev.stdout.strip() if rev.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        meta["git_rev"] = None
+    h = hashlib.sha256()
+    for sub in ("include", "sparse_mla_attention_indexer_amd/csrc"):
+        base = os.path.join(ROOT, sub)
+        for name in sorted(os.listdir(base)):
+            if name.endswith((".h", ".hip", ".cpp")):
+                with open(os.path.join(base, name), "rb") as f:
+                    h.update(name.encode() + b"\0" + f.read())
+    meta["src_sha256"] = h.hexdigest()
+    return meta
+
+
+class Leg:
+    """One workload on the GPU: inputs, buffers and the step (indexer + top-k, then sparse MLA)."""
+
+    def __init__(self, config, dev, log):
+        import numpy as np
+        import torch
+
+        from sparse_mla_attention_indexer_amd import ops
+        from sparse_mla_attention_indexer_amd import workload as W
+
+        self.config, self.dev = config, dev
+        d = self.d = W.config_dims(config)
+        self.decode = config in DECODE_CONFIGS
+        log(f"generating workload {config} ({W.CONFIG_NAMES[config]})")
+        x = self.x = W.generate(d)
+        self.plan = ops.BatchPlan(x.n_q, x.kv_len, dev)
+        as_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if d.kv_format == W.KV_FP8_656:
+            self.kv = torch.from_numpy(x.kv).to(dev)
+        else:
+            self.kv = torch.from_numpy(x.kv.view(np.int16).reshape(d.total_rows, d.D_qk)).view(
+                torch.bfloat16).to(dev)
+        self.k_idx = torch.from_numpy(x.k_idx).to(dev)
+        self.w = torch.from_numpy(x.w).to(dev)
+        # query sets: the workload's own, and for decode legs three more seeded ones, so that
+        # consecutive steps select different rows
+        self.q = [as_bf16(x.q)]
+        self.q_idx = [torch.from_numpy(x.q_idx).to(dev)]
+        if self.decode:
+            for r in range(1, ROTATIONS):
+                xr = W.generate(d, seed=int(d.seed) + 0x1000 * r, parts=("q", "q_idx"))
+                self.q.append(as_bf16(xr.q))
+                self.q_idx.append(torch.from_numpy(xr.q_idx).to(dev))
+        self.idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((d.total_q, d.H), dtype=torch.float32, device=dev)
+        self.ws_topk = ops.topk_workspace(self.plan, d.H_I, d.D_I, d.top_k)
+        self.ws_mla = ops.mla_workspace(self.plan, d.H, d.D_v, d.top_k, self.decode)
+        torch.cuda.synchronize()
+
+    def step(self, k=0):
+        from sparse_mla_attention_indexer_amd import ops
+
+        d, r = self.d, k % len(self.q)
+        ops.indexer_topk(self.plan, self.q_idx[r], self.k_idx, self.w, d.top_k, with_scores=False,
+                         idx=self.idx, workspace=self.ws_topk)
+        ops.sparse_mla(self.plan, self.q[r], self.kv, d.kv_format, d.D_v, self.idx, d.sm_scale,
+                       decode=self.decode, out=self.out, lse=self.lse, workspace=self.ws_mla)
+
+    def attend(self, sel, kv=None, k=0):
+        from sparse_mla_attention_indexer_amd import ops
+
+        d = self.d
+        ops.sparse_mla(self.plan, self.q[k % len(self.q)], self.kv if kv is None else kv, d.kv_format,
+                       d.D_v, sel, d.sm_scale, decode=self.decode, out=self.out, lse=self.lse,
+                       workspace=self.ws_mla)
+
+
+def time_leg(leg, steps, warmup, scrub, log):
+    """Cold per-step spans (the reported figures), cold per-stage kernel times, and the warm rate
+    of steps back to back."""
+    import numpy as np
+    import torch
+
+    for k in range(warmup):
+        leg.step(k)
+    torch.cuda.synchronize()
+
+    def cold(k):
+        scrub.fill_(k & 0x7F)
+
+    log(f"timing {steps} cold steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        cold(k)
+        ev[k][0].record()
+        leg.step(k)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    spans = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # per-stage kernel time: as many cold steps again with HIP events the library records on its
+    # own launch stream around each stage (kept out of the spans above)
+    sev, hip = stage_times(leg.step, steps, before=cold)
+    stage_ms = {}
+    has_combine = leg.decode and leg.ws_mla.numel() > 256
+    for s, name in enumerate(STAGES):
+        if name == "combine" and not has_combine:
+            continue
+        stage_ms[name] = sum(hip.elapsed_ms(*sev[k][s]) for k in range(steps)) / steps
+    for row in sev:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
+
+    log(f"timing {steps} warm steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        leg.step(k)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms": float(spans.mean()), "median_ms": float(np.median(spans)), "min_ms": float(spans.min()),
+            "wall_ms_incl_scrub": wall * 1e3 / steps, "warm_ms": warm_ms, "stage_ms": stage_ms}
+
+
+def leg_result(leg, t, steps, warmup):
+    d = leg.d
+    tag = WORKLOAD_TAGS.get(leg.config, "")
+    idx_roof, mla_roof, dominant, ceiling_ms = rooflines(d, leg.plan.positions, t["stage_ms"],
+                                                         leg.decode, tag)
+    return {
+        "config": {"workload": workload_name(d), "config_id": leg.config, "batch": d.batch,
+                   "query_tokens": d.total_q, "cached_tokens": d.cached, "heads": d.H,
+                   "top_k": d.top_k, "decode_entry": leg.decode, "seed": hex(int(d.seed)),
+                   "query_sets": len(leg.q)},
+        "value": round(d.total_q / (t["ms"] * 1e-3), 1), "unit": "query-tokens/s",
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": round(t["ms"], 4), "median_ms": round(t["median_ms"], 4),
+        "min_ms": round(t["min_ms"], 4),
+        "warm": {"ms_per_step": round(t["warm_ms"], 4),
+                 "value": round(d.total_q / (t["warm_ms"] * 1e-3), 1)},
+        "stages_ms": {k: round(v, 4) for k, v in t["stage_ms"].items()},
+        "roofline": dominant,
+        "indexer_roofline": idx_roof,
+        "mla_roofline": mla_roof,
+        "step_roofline": {"ceiling_ms": round(ceiling_ms, 4),
+                          "frac": round(ceiling_ms / t["ms"], 4),
+                          "note": "indexer and sparse MLA each at its bound, top-k free"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1, help="workload 0..4 (default 1: decode)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=HEADLINE_CONFIG,
+                    help="headline workload 0..4 (default 3: the 32,768-token prefill)")
+    ap.add_argument("--legs", default=",".join(map(str, SIDE_LEGS)),
+                    help="comma-separated side workloads, or 'none'")
+    ap.add_argument("--leg-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cache-append, DCP, hybrid-offload and FP8-key measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter scaling reference)")
     args = ap.parse_args()
@@ -472,7 +789,7 @@ def main():
     import numpy as np
     import torch
 
-    from sparse_mla_attention_indexer_amd import _lib, ops
+    from sparse_mla_attention_indexer_amd import _lib, ops  # noqa: F401  (loads the library)
     from sparse_mla_attention_indexer_amd import workload as W
 
     if not torch.cuda.is_available():
@@ -481,135 +798,77 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    _lib.lib()
     dev = torch.device("cuda:0")
-    d = W.config_dims(args.config)
-    decode = args.config in DECODE_CONFIGS
-    print(f"[bench] generating workload {args.config} ({W.CONFIG_NAMES[args.config]})", file=sys.stderr, flush=True)
-    x = W.generate(d)
-    plan = ops.BatchPlan(x.n_q, x.kv_len, dev)
-    q = torch.from_numpy(x.q.view(np.int16)).view(torch.bfloat16).to(dev)
-    if d.kv_format == W.KV_FP8_656:
-        kv = torch.from_numpy(x.kv).to(dev)
-    else:
-        kv = torch.from_numpy(x.kv.view(np.int16).reshape(d.total_rows, d.D_qk)).view(torch.bfloat16).to(dev)
-    q_idx = torch.from_numpy(x.q_idx).to(dev)
-    k_idx = torch.from_numpy(x.k_idx).to(dev)
-    w = torch.from_numpy(x.w).to(dev)
-    idx = torch.empty((d.total_q, d.top_k), dtype=torch.int32, device=dev)
-    out = torch.empty((d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((d.total_q, d.H), dtype=torch.float32, device=dev)
-    ws_topk = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
-    ws_mla = ops.mla_workspace(plan, d.H, d.D_v, d.top_k, decode)
-    torch.cuda.synchronize()
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    legs = [] if args.legs.strip() in ("", "none") else [int(c) for c in args.legs.split(",")]
+    legs = [c for c in legs if c != args.config]
 
-    def step():
-        ops.indexer_topk(plan, q_idx, k_idx, w, d.top_k, with_scores=False, idx=idx,
-                         workspace=ws_topk)
-        ops.sparse_mla(plan, q, kv, d.kv_format, d.D_v, idx, d.sm_scale, decode=decode, out=out,
-                       lse=lse, workspace=ws_mla)
+    meta = run_metadata()
+    log("measuring copy and GEMM rates")
+    meta["measured_peaks"] = measured_peaks(dev)
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # headline: K steps back to back, nothing but the library's launches in the timed region
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # per-stage kernel time: K more steps with HIP events the library records on its own launch
-    # stream around each stage (event markers cost a few microseconds each, so they stay out of
-    # the headline region)
-    ev, hip = stage_times(step, args.steps)
-
-    stage_ms = {}
-    for s, name in enumerate(STAGES):
-        if name == "combine" and not (decode and ws_mla.numel() > 256):
-            continue
-        stage_ms[name] = sum(hip.elapsed_ms(*ev[k][s]) for k in range(args.steps)) / args.steps
-    for row in ev:
-        for a, b in row:
-            hip.destroy(a)
-            hip.destroy(b)
-
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = d.total_q / (ms_per_step * 1e-3)
-    alg = algorithmic(d, plan.positions)
-    idx_gbs = alg["indexer_bytes"] / (stage_ms["indexer"] * 1e-3) / 1e9
-    idx_tops = alg["indexer_ops"] / (stage_ms["indexer"] * 1e-3) / 1e12
-    mla_ms = stage_ms["mla"] + stage_ms.get("combine", 0.0)
-    mla_gbs = alg["mla_bytes"] / (mla_ms * 1e-3) / 1e9
-    mla_tflops = alg["mla_flops"] / (mla_ms * 1e-3) / 1e12
-    # the indexer dominates the step; it is HBM-bound when its ops per key byte fall below the
-    # int8 ridge (5.0 POP/s / 8 TB/s = 625)
-    idx_hbm = alg["indexer_ops"] / alg["indexer_bytes"] < INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = profiled_traffic("indexer_mfma_kernel", WORKLOAD_TAGS.get(args.config, ""))
-    if idx_hbm:
-        roof = {"bound": "hbm", "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else round(traffic),
-                "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(idx_tops, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s (int8)", "frac": round(idx_tops / INT8_PEAK_TOPS, 4),
-                "traffic": None if traffic is None else round(traffic),
-                "kernel": "indexer_mfma_kernel", "kernel_ms": round(stage_ms["indexer"], 4)}
-    mla_hbm = alg["mla_flops"] / alg["mla_bytes"] < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    mla_roof = ({"bound": "hbm", "achieved": round(mla_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": round(mla_gbs / HBM_PEAK_GBS, 4)} if mla_hbm else
-                {"bound": "mfma", "achieved": round(mla_tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": round(mla_tflops / BF16_PEAK_TFLOPS, 4)})
-    mla_roof["kernel_ms"] = round(mla_ms, 4)
-
+    leg = Leg(args.config, dev, log)
+    d = leg.d
+    t = time_leg(leg, args.steps, args.warmup, scrub, log)
+    head = leg_result(leg, t, args.steps, args.warmup)
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+fp16",
-        "dtypes": {"indexer": "int8 x int8 -> int32", "kv": "fp8 e4m3 + fp32 block scales",
-                   "attention": "fp16 MFMA on dequantised rows, fp32 accumulate and softmax"},
+        "metric": METRIC, "value": head["value"], "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16",
+        "dtypes": {"indexer": "int8 x int8 -> int32 (MFMA)",
+                   "kv": "fp8 e4m3 codes + fp32 block scales per 128 dims",
+                   "attention": "bf16 MFMA of bf16 q with exact e4m3 codes, fp32 block scales and "
+                                "softmax; PV in fp16 (bf16 fallback), fp32 accumulate"},
         "data": "synthetic",
-        "config": {"workload": workload_name(d), "config_id": args.config, "batch": d.batch,
-                   "query_tokens": d.total_q, "cached_tokens": d.cached, "heads": d.H,
-                   "top_k": d.top_k, "decode_entry": decode},
-        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": roof,
-        "mla_roofline": mla_roof,
+        "config": head["config"],
+        "timing": "cold: 1 GiB scrub before each step, outside its HIP-event span"
+                  + ("; 4 rotating query sets" if leg.decode else ""),
+        "median_ms": head["median_ms"], "min_ms": head["min_ms"], "warm": head["warm"],
+        "stages_ms": head["stages_ms"],
+        "roofline": head["roofline"],
+        "indexer_roofline": head["indexer_roofline"],
+        "mla_roofline": head["mla_roofline"],
+        "step_roofline": head["step_roofline"],
+        "meta": meta,
     }
-    if d.kv_format == W.KV_FP8_656:
-        result["append"] = append_measurement(dev, args.steps)
-    if decode and (x.n_q == 1).all() and d.kv_format == W.KV_FP8_656:
-        print("[bench] DCP simulation", file=sys.stderr, flush=True)
-        result["dcp_sim"] = dcp_measurement(dev, x, d, args.steps, args.warmup)
-    if decode and (x.n_q == 1).all() and d.kv_format == W.KV_FP8_656:
-        print("[bench] hybrid offload resolve", file=sys.stderr, flush=True)
-
-        def select():
-            ops.indexer_topk(plan, q_idx, k_idx, w, d.top_k, with_scores=False, idx=idx,
-                             workspace=ws_topk)
-            return idx
-
-        hot = hot_resolve_measurement(
-            dev, x, d, plan, q, select,
-            lambda sel, kv_h: ops.sparse_mla(plan, q, kv_h, d.kv_format, d.D_v, sel, d.sm_scale,
-                                             decode=True, out=out, lse=lse, workspace=ws_mla),
-            args.steps, args.warmup)
-        if hot is not None:
-            result["hot_resolve"] = hot
-    if d.H_I == 64 and d.D_I == 128:
-        print("[bench] FP8-key indexer", file=sys.stderr, flush=True)
-        result["indexer_fp8"] = fp8_indexer_measurement(
-            dev, d, plan, args.steps, args.warmup,
-            lambda sel: ops.sparse_mla(plan, q, kv, d.kv_format, d.D_v, sel, d.sm_scale, decode=decode,
-                                       out=out, lse=lse, workspace=ws_mla))
+    extras = not args.no_extras and d.kv_format == W.KV_FP8_656
+    if extras and d.H_I == 64 and d.D_I == 128:
+        log("FP8-key indexer")
+        result["indexer_fp8"] = fp8_indexer_measurement(dev, d, leg.plan, min(args.steps, 10), 2,
+                                                        leg.attend)
     if not args.no_cpu_baseline:
         sample = np.arange(d.total_q) if d.total_q <= 32 else np.linspace(0, d.total_q - 1, 32).astype(np.int64)
-        print(f"[bench] oracle on {sample.size} tokens", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(x, d, sample)
+        log(f"oracle on {sample.size} tokens")
+        result["cpu_baseline"] = cpu_baseline(leg.x, d, sample)
+    del leg
+    torch.cuda.empty_cache()
+
+    result["legs"] = {}
+    for c in legs:
+        lg = Leg(c, dev, log)
+        tl = time_leg(lg, args.leg_steps, 3, scrub, log)
+        r = leg_result(lg, tl, args.leg_steps, 3)
+        if extras and lg.decode and (lg.x.n_q == 1).all() and lg.d.kv_format == W.KV_FP8_656:
+            log("DCP simulation")
+            r["dcp_sim"] = dcp_measurement(dev, lg.x, lg.d, args.leg_steps, 3)
+            log("hybrid offload resolve")
+
+            def select():
+                ops.indexer_topk(lg.plan, lg.q_idx[0], lg.k_idx, lg.w, lg.d.top_k, with_scores=False,
+                                 idx=lg.idx, workspace=lg.ws_topk)
+                return lg.idx
+
+            hot = hot_resolve_measurement(dev, lg.x, lg.d, lg.plan, lg.q[0], select,
+                                          lambda sel, kv_h: lg.attend(sel, kv_h), args.leg_steps, 3)
+            if hot is not None:
+                r["hot_resolve"] = hot
+        result["legs"][WORKLOAD_TAGS[c]] = r
+        del lg
+        torch.cuda.empty_cache()
+    if extras:
+        result["append"] = append_measurement(dev, args.leg_steps)
     print(json.dumps(result), flush=True)
 
 
