@@ -3,7 +3,9 @@
 The FP8 matrix cores sum a head's 128 exact products in a narrower accumulator than IEEE fp32,
 so scores are compared with the oracle within a bound derived from that (below), while the
 selection is compared exactly: the top-k the library returns must be the oracle's top-k of the
-library's own fp32 scores (the decision taken on the same values, in the same precision). With
+library's own fp32 scores (the decision taken on the same values, in the same precision). Against
+the oracle's own fp64 scores the selection must lie within the band that bound allows around the
+oracle's cut. With
 integer-valued codes every partial sum is a small integer, which any accumulator holds exactly:
 then the FP8 path must reproduce the int8 path bit for bit, scores and indices.
 """
@@ -98,6 +100,38 @@ def _check_scores_against_oracle(full, x, toks, label, tokens=None, key_step=1):
     say(f"  {label}: largest |score - oracle| / magnitude = {worst_ratio:.3e} (bound {SCORE_RTOL:.3e})")
 
 
+def _check_band_against_oracle(idx, x, toks, top_k, label, tokens=None):
+    """The selection against the oracle's own fp64 scores. With every library score within b_s of
+    the oracle's (b_s = SCORE_RTOL x magnitude, B = the row's largest b_s) and c the oracle's k-th
+    largest score, the library's k-th largest score lies within B of c, so a selected key has an
+    oracle score >= c - b_s - B and an unselected one <= c + b_s + B. Keys inside that band may
+    swap with the oracle's selection; the count of swaps is reported."""
+    swaps = rows = 0
+    for t, row0, p in toks:
+        if tokens is not None and t not in tokens:
+            continue
+        keys = np.arange(p + 1)
+        ref, mag = oracle.indexer_scores_fp8(x.q[t], x.k[row0 + keys], x.k_scale[row0 + keys], x.w[t])
+        b = SCORE_RTOL * mag
+        B = float(b.max())
+        n = min(top_k, p + 1)
+        sel = idx[t][idx[t] >= 0]
+        assert sel.size == n and np.unique(sel).size == n, f"{label}: row {t} has {sel.size} picks"
+        order = np.lexsort((keys, -ref))  # oracle order: score desc, index asc
+        ref_sel = order[:n]
+        picked = np.zeros(p + 1, bool)
+        picked[sel] = True
+        c = ref[order[n - 1]]
+        lo = ref[picked] < c - b[picked] - B
+        hi = ref[~picked] > c + b[~picked] + B
+        assert not lo.any(), f"{label}: row {t}: selected key {keys[picked][lo][0]} far below the cut"
+        assert not hi.any(), f"{label}: row {t}: unselected key {keys[~picked][hi][0]} far above the cut"
+        swaps += n - int(picked[ref_sel].sum())
+        rows += 1
+    say(f"  {label}: {rows} rows within the band of the oracle's scores; {swaps} selections swap "
+        f"with the oracle's own top-{top_k}")
+
+
 @pytest.mark.parametrize("shape", ["decode", "multi"])
 def test_fp8_integer_codes_reproduce_int8_path(shape):
     # decode: one token per request (the single-token kernel, segmented and LDS top-k paths);
@@ -148,6 +182,7 @@ def test_fp8_random_codes_against_oracle(shape):
     for top_k in (2048, 100):
         idx, sc = dev.topk(top_k)
         _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"{shape} k={top_k}")
+        _check_band_against_oracle(idx, x, toks, top_k, f"{shape} k={top_k}")
     idx2, sc2 = dev.topk(2048)
     assert np.array_equal(idx2, dev.topk(2048)[0]), "FP8 top-k not deterministic"
 
@@ -189,3 +224,4 @@ def test_fp8_decode_batch_full_size():
     toks = _token_rows(n_q, kv_len)
     _check_topk_on_own_scores(idx, sc, full, toks, d.top_k, "fp8 decode full")
     _check_scores_against_oracle(full, x, toks, "fp8 decode full", tokens={0, 13, 31})
+    _check_band_against_oracle(idx, x, toks, d.top_k, "fp8 decode full", tokens={0, 5, 13, 21, 31})

@@ -221,6 +221,7 @@ def _sampled_full_config(cid, tokens, decode):
     say(f"[case] config {cid}: top-k")
     idx, sc = dev.topk()
     tokens = np.asarray(sorted(set(int(t) for t in tokens if 0 <= t < d.total_q)))
+    assert tokens.size >= min(256, d.total_q), tokens.size
     say(f"[case] config {cid}: oracle on {tokens.size} tokens")
     ref_idx, ref_sc = oracle_topk(x, tokens)
     assert_topk_equal(idx[tokens], sc[tokens], ref_idx, ref_sc, f"config {cid}")
@@ -285,13 +286,26 @@ def test_config1_decode_full_size():
     _sampled_full_config(1, range(32), decode=True)
 
 
+def _spread_and_seams(n_tok, n_even, extra):
+    """n_even tokens spread evenly over [0, n_tok), plus `extra`: the query-tile seams (tiles of 4
+    tokens, tile i paired with tile n - 1 - i, so the middle pair shares a seam), the ends."""
+    tiles = n_tok // 4
+    mid = 4 * (tiles // 2)
+    seams = [3, 4, 7, 8, mid - 5, mid - 4, mid - 1, mid, mid + 3, mid + 4, n_tok - 5, n_tok - 4]
+    ends = [0, 1, 2, n_tok - 2, n_tok - 1]
+    return np.linspace(0, n_tok - 1, n_even).astype(np.int64).tolist() + seams + ends + list(extra)
+
+
 def test_config2_chunked_full_size():
-    _sampled_full_config(2, [0, 1, 2, 511, 1024, 1535, 2046, 2047], decode=False)
+    # 2,048 tokens after 65,536 cached: every row spans many 4,096-key chunks of the plan
+    _sampled_full_config(2, _spread_and_seams(2048, 248, []), decode=False)
 
 
 def test_config3_prefill_full_size():
-    _sampled_full_config(3, [0, 1, 63, 2045, 2046, 2047, 2048, 4097, 16000, 32766, 32767],
-                         decode=False)
+    # p + 1 = 2,047 / 2,048 / 2,049 (the top-k fills exactly), rows ending on both sides of every
+    # 4,096-key chunk edge up to 32K, and the tile-pair seams
+    edges = [e + o for e in range(4096, 32768, 4096) for o in (-1, 0)]
+    _sampled_full_config(3, _spread_and_seams(32768, 232, [2046, 2047, 2048] + edges), decode=False)
 
 
 def test_config4_million_full_size():
