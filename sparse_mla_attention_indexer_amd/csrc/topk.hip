@@ -10,7 +10,8 @@
 //     6 bits below the leading one) locates the bin b* that holds the k-th largest key;
 //     everything in higher bins is selected;
 //  2. inside b* an MSD radix select over 8-bit digits of the 64-bit key finds the exact cut.
-// Rows of up to 32,768 candidates are selected by one workgroup with the scores held in LDS.
+// Rows of up to 32,768 candidates are selected by one 512-thread workgroup with the scores held
+// in registers and the histogram built in LDS (two rows per CU).
 // Longer rows use the histogram the indexer kernel accumulated while scoring: in batches with
 // many query tokens, rows of up to 73,728 candidates are held in one workgroup's registers;
 // otherwise (and for longer rows) rows are cut into 4,096-candidate segments handled by three
@@ -209,146 +210,7 @@ __device__ void wave_radix_cut(KeyAt key_at, int n, int need, int* h, uint64_t* 
   *mask_out = mask;
 }
 
-// Ordered emission: the block's NW waves each own a contiguous chunk of [0, len); a first pass
-// counts the selected elements per wave, a second writes each at its rank (ballot prefix), so
-// the output keeps ascending index order with conflict-free, consecutive LDS reads.
-template <int NT, typename Sel, typename Emit>
-__device__ void emit_in_order(int len, int base, Sel sel, Emit emit, int* wcnt) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int chunk = ((len + NW - 1) / NW + 63) & ~63;
-  const int c0 = min(len, wv * chunk), c1 = min(len, c0 + chunk);
-  int cnt = 0;
-  for (int i0 = c0; i0 < c1; i0 += 64) {
-    const int i = i0 + lane;
-    cnt += __popcll(__ballot(i < c1 && sel(i)));
-  }
-  if (lane == 0) wcnt[wv] = cnt;
-  __syncthreads();
-  int pos = base;
-  for (int w = 0; w < wv; ++w) pos += wcnt[w];
-  for (int i0 = c0; i0 < c1; i0 += 64) {
-    const int i = i0 + lane;
-    const bool f = i < c1 && sel(i);
-    const uint64_t m = __ballot(f);
-    if (f) emit(i, pos + __popcll(m & ((1ull << lane) - 1)));
-    pos += __popcll(m);
-  }
-}
-
-// ---- path A: rows of n <= TOPK_LDS_MAX, one 1024-thread workgroup per row ----------------
-constexpr int NT_A = 1024;
-
-template <bool FB>
-__global__ __launch_bounds__(NT_A) void topk_lds_kernel(const Tok* __restrict__ toks,
-                                                        const int32_t* __restrict__ scores,
-                                                        int top_k, int32_t* __restrict__ idx_out,
-                                                        int32_t* __restrict__ score_out,
-                                                        int32_t pad_score) {
-  extern __shared__ int smem[];
-  int* sc = smem;                 // [TOPK_LDS_MAX]
-  int* hist = sc + TOPK_LDS_MAX;  // [TOPK_BINS]
-  __shared__ int hist2[256];
-  __shared__ int red[NT_A / 64 + 1];
-  __shared__ int cut[2];
-  __shared__ uint64_t pm[2];
-
-  const int64_t t = blockIdx.x;
-  const Tok tk = toks[t];
-  const int n = tk.pos + 1;
-  if (n > TOPK_LDS_MAX) return;
-  int32_t* oi = idx_out + t * top_k;
-  int32_t* os = score_out ? score_out + t * top_k : nullptr;
-  const int32_t* row = scores + tk.cand_off;
-  if (n <= top_k) {
-    for (int j = threadIdx.x; j < top_k; j += NT_A) {
-      oi[j] = j < n ? j : -1;
-      if (os) os[j] = j < n ? row[j] : pad_score;
-    }
-    return;
-  }
-  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_A) hist[i] = 0;
-  __syncthreads();
-  {
-    // every load of the row in flight before any is used
-    constexpr int PER = TOPK_LDS_MAX / NT_A;
-    int vals[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * NT_A + threadIdx.x;
-      vals[j] = i < n ? row[i] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int i = j * NT_A + threadIdx.x;
-      if (i < n) {
-        sc[i] = vals[j];
-        atomicAdd(&hist[score_bin<FB>((uint32_t)vals[j])], 1);
-      }
-    }
-  }
-  __syncthreads();
-  find_cut<NT_A>(hist, TOPK_BINS, top_k, red, cut);
-  const int bstar = cut[0];
-  const int above = cut[1];
-  const int need = top_k - above;
-  __syncthreads();
-  uint64_t prefix = 0, mask = 0;
-  if (hist[bstar] != need) {
-    const int ncand = hist[bstar];
-    if (ncand <= TOPK_MAX_K) {
-      // gather the b* candidates' keys, then one wave finds the exact cut among them
-      __shared__ uint64_t keys[TOPK_MAX_K];
-      __shared__ int nk;
-      if (threadIdx.x == 0) nk = 0;
-      __syncthreads();
-      const int lane = threadIdx.x & 63;
-      for (int i0 = 0; i0 < n; i0 += NT_A) {
-        const int i = i0 + threadIdx.x;
-        const bool f = i < n && score_bin<FB>((uint32_t)sc[i]) == bstar;
-        const uint64_t m = __ballot(f);
-        if (m) {
-          int base = 0;
-          const int leader = __builtin_ctzll(m);
-          if (lane == leader) base = atomicAdd(&nk, __popcll(m));
-          base = __shfl(base, leader);
-          if (f) keys[base + __popcll(m & ((1ull << lane) - 1))] = sel_key(sc[i], i);
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        uint64_t pf, mk;
-        wave_radix_cut([&](int i) { return keys[i]; }, ncand, need, hist2, &pf, &mk);
-        if (threadIdx.x == 0) {
-          pm[0] = pf;
-          pm[1] = mk;
-        }
-      }
-      __syncthreads();
-    } else {
-      radix_cut<NT_A>(
-          n, need, [&](int i) { return sel_key(sc[i], i); },
-          [&](int i) { return score_bin<FB>((uint32_t)sc[i]) == bstar; }, hist2, red, cut, pm);
-    }
-    prefix = pm[0];
-    mask = pm[1];
-  }
-  // emit in ascending index order
-  __shared__ int wcnt[NT_A / 64];
-  emit_in_order<NT_A>(
-      n, 0,
-      [&](int i) {
-        const int bn = score_bin<FB>((uint32_t)sc[i]);
-        return bn > bstar || (bn == bstar && (sel_key(sc[i], i) & mask) >= prefix);
-      },
-      [&](int i, int pos) {
-        if (pos < top_k) {  // exactly top_k are selected; the guard only bounds the writes
-          oi[pos] = i;
-          if (os) os[pos] = sc[i];
-        }
-      },
-      wcnt);
-}
+constexpr int NT_A = 1024;  // the DCP merge's workgroup
 
 // ---- DCP top-k merge: the union of per-shard lists, one 1024-thread workgroup per token ----
 // Shard l of n_lists holds the tokens l, l + n_lists, ...; list entry (local j, score) is global
@@ -580,6 +442,7 @@ __device__ __forceinline__ int pass_gather(const uint32_t (&v)[V], int i0, int r
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // one element's masks live at a time (SGPR pressure)
   }
   return above;
 }
@@ -600,7 +463,10 @@ __device__ __forceinline__ int pass_count(const uint32_t (&v)[V], int i0, int re
                                           uint32_t tl) {
   int c = 0;
 #pragma unroll
-  for (int u = 0; u < V; ++u) c += __popcll(sel_mask<FULL>(v[u], i0 + 64 * u, u, rem, th, tl));
+  for (int u = 0; u < V; ++u) {
+    c += __popcll(sel_mask<FULL>(v[u], i0 + 64 * u, u, rem, th, tl));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   return c;
 }
 
@@ -624,6 +490,7 @@ __device__ __forceinline__ void pass_write(const uint32_t (&v)[V], int i0, int r
       }
       pos += __popcll(m);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -804,6 +671,128 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
     }
     pos += __popcll(m);
   }
+}
+
+// ---- rows of top_k < n <= TOPK_LDS_MAX: one 512-thread workgroup per row, in registers -------
+// Each of the 8 waves owns a contiguous chunk of 64 V scores of the row (V = 8, 16, 32 or 64, the
+// smallest that covers the row), held in registers; the score histogram is built in LDS from
+// them; then, as for the longer rows, one pass counts the elements above b* and gathers the b*
+// candidates, one wave finds the exact cut among them, and a second pass over the registers
+// writes every selected index at its rank. 40 KB of LDS, so two rows share a CU and hide each
+// other's latencies.
+constexpr int NT_B = 512;
+constexpr int NW_B = NT_B / 64;
+
+template <bool FB, int V>
+__device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, int n, int top_k,
+                                               int32_t* __restrict__ oi, int32_t* __restrict__ os,
+                                               int* hist, uint32_t* klo, uint32_t* khi,
+                                               int* hist2, int* red, int* cut, uint64_t* pm,
+                                               int* nk, int* wsel, int* woff) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ib = wv * (64 * V) + lane;
+  const int rem = n - ib;
+  const bool full = n >= (wv + 1) * (64 * V);
+  uint32_t v[V];
+  lane_load<V>(v, row, n, ib, 0);
+  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = 0;
+  if (threadIdx.x == 0) *nk = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < V; ++u)
+    if (64 * u < rem) atomicAdd(&hist[score_bin<FB>(v[u])], 1);
+  __syncthreads();
+  find_cut<NT_B>(hist, TOPK_BINS, top_k, red, cut);
+  const int bstar = cut[0];
+  const int need = top_k - cut[1];
+  const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
+  const uint32_t hm1 = bin_hm1<FB>(bstar);
+  const int above = full ? pass_gather<V, true>(v, ib, rem, lo, hm1, klo, khi, nk, TOPK_CAND_CAP)
+                         : pass_gather<V, false>(v, ib, rem, lo, hm1, klo, khi, nk, TOPK_CAND_CAP);
+  if (lane == 0) wsel[wv] = above;
+  __syncthreads();
+  const int ncand = *nk;
+  uint64_t ck;
+  if (ncand <= TOPK_CAND_CAP) {
+    if (wv == 0) {
+      uint64_t pf, mk;
+      wave_radix_cut([&](int i) { return ((uint64_t)khi[i] << 32) | klo[i]; }, ncand, need, hist2,
+                     &pf, &mk);
+      if (lane == 0) pm[0] = cut_key(pf, lo);
+      (void)mk;
+    }
+    __syncthreads();
+    ck = pm[0];
+    // selected candidates per owning wave (the index says which wave holds the score)
+    for (int c = threadIdx.x; c < ncand; c += NT_B) {
+      const uint64_t key = ((uint64_t)khi[c] << 32) | klo[c];
+      if (key >= ck) atomicAdd(&wsel[(int)(0xFFFFFFFFu - klo[c]) / (64 * V)], 1);
+    }
+  } else {
+    // more candidates than LDS holds (heavy ties): the exact cut by radix select over the row,
+    // then every wave counts its own selected elements
+    radix_cut<NT_B>(
+        n, need, [&](int i) { return sel_key(row[i], i); },
+        [&](int i) { return score_bin<FB>((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
+    ck = cut_key(pm[0], lo);
+    const int cnt = full ? pass_count<V, true>(v, ib, rem, (uint32_t)(ck >> 32), (uint32_t)ck)
+                         : pass_count<V, false>(v, ib, rem, (uint32_t)(ck >> 32), (uint32_t)ck);
+    if (lane == 0) wsel[wv] = cnt;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < NW_B; ++w) {
+      woff[w] = acc;
+      acc += wsel[w];
+    }
+  }
+  __syncthreads();
+  const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
+  const int pos = __builtin_amdgcn_readfirstlane(woff[wv]);
+  if (full)
+    pass_write<V, true>(v, ib, rem, th, tl, pos, top_k, oi, os);
+  else
+    pass_write<V, false>(v, ib, rem, th, tl, pos, top_k, oi, os);
+}
+
+template <bool FB>
+__global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restrict__ toks,
+                                                          const int32_t* __restrict__ scores,
+                                                          int top_k, int32_t* __restrict__ idx_out,
+                                                          int32_t* __restrict__ score_out,
+                                                          int32_t pad_score) {
+  __shared__ int hist[TOPK_BINS];
+  __shared__ uint32_t klo[TOPK_CAND_CAP], khi[TOPK_CAND_CAP];
+  __shared__ int hist2[256];
+  __shared__ int red[NW_B + 1];
+  __shared__ int cut[2];
+  __shared__ uint64_t pm[2];
+  __shared__ int nk;
+  __shared__ int wsel[NW_B], woff[NW_B];
+  const int64_t t = blockIdx.x;
+  const Tok tk = toks[t];
+  const int n = tk.pos + 1;
+  if (n > TOPK_LDS_MAX) return;
+  int32_t* oi = idx_out + t * top_k;
+  int32_t* os = score_out ? score_out + t * top_k : nullptr;
+  const int32_t* row = scores + tk.cand_off;
+  if (n <= top_k) {  // every row is taken, in order
+    for (int j = threadIdx.x; j < top_k; j += NT_B) {
+      oi[j] = j < n ? j : -1;
+      if (os) os[j] = j < n ? row[j] : pad_score;
+    }
+    return;
+  }
+  static_assert(NT_B * 64 == TOPK_LDS_MAX, "8 waves x 64 x 64 scores cover the longest short row");
+  if (n <= NT_B * 8)
+    topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+  else if (n <= NT_B * 16)
+    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+  else if (n <= NT_B * 32)
+    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+  else
+    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
 }
 
 // ---- segmented rows: count / resolve / emit over TOPK_SEG-candidate segments ---------------
@@ -1034,17 +1023,10 @@ template <bool FB>
 hipError_t launch_topk_t(const smla_batch& b, const int32_t* scores, int32_t top_k, int32_t* idx,
                          int32_t* score, const TopkWs& w, hipStream_t s) {
   TableView tv = table_view(b.table, b.batch, b.total_q);
-  const size_t lds_a = sizeof(int) * (TOPK_LDS_MAX + TOPK_BINS);
-  static const bool lds_set = [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_lds_kernel<FB>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_a);
-    return true;
-  }();
-  (void)lds_set;
   const int32_t pad = FB ? (int32_t)0xBF800000u : -1;  // -1.0f or -1
   hipError_t e = hipSuccess;
   if (b.min_cand <= TOPK_LDS_MAX) {
-    hipLaunchKernelGGL(topk_lds_kernel<FB>, dim3(b.total_q), dim3(NT_A), lds_a, s, tv.tok, scores,
+    hipLaunchKernelGGL(topk_short_kernel<FB>, dim3(b.total_q), dim3(NT_B), 0, s, tv.tok, scores,
                        top_k, idx, score, pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
