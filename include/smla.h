@@ -246,8 +246,9 @@ size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D
  * both exact in bf16, with fp32 accumulation; each 128-dim block's fp32 scale is applied to its
  * part of the logit in fp32, so any finite scale and the whole bf16 range of q are supported.
  * Softmax in fp32. The output products use P' = P * scale relative to a power of two chosen per
- * split, in fp16 (11 significant bits) while every row's scale stays within [2^-10, 2^3] of it,
- * otherwise in bf16 (the split is recomputed); fp32 accumulation; bf16 outputs. Intermediate sums
+ * split: P and the relative scale each rounded to fp16 and multiplied in fp16 (11 significant
+ * bits per rounding) while every row's scale stays within [2^-10, 2^3] of it, otherwise
+ * P * scale in fp32 rounded to bf16 (the split is recomputed); fp32 accumulation; bf16 outputs. Intermediate sums
  * are fp32: finite results need |q . v| and |v| well inside the fp32 range (|v| < 2^90).
  * Entries that are -1 (or above p) never reach the output, whatever their placeholder row holds
  * (NaN codes or scales included).

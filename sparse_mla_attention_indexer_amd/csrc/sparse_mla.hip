@@ -7,32 +7,34 @@
 // rows). Partial results over disjoint row sets merge by log-sum-exp (section "DCP").
 //
 // FP8 kernel (64 heads, 576/512 dims, 656-byte rows): one workgroup of 8 waves (two per SIMD)
-// per (token, split), over 32-row tiles. Wave w owns FP8 block b = w & 3 (value dims
-// 128b..128b+127) and half h = w >> 2:
-//  - gather: the rows of a tile move from HBM straight into LDS by the load-to-LDS path, two
-//    tiles ahead, as stored (row r at 656 r): each load instruction covers 1 KB of consecutive
-//    row bytes, and since a row is an odd number (41) of 16-byte chunks, one chunk of 16
-//    consecutive rows falls on 16 distinct bank groups, so every operand read below is free of
+// per (token, split), over 32-row tiles, in two teams of four waves (wave b of each team on
+// SIMD b; b is also the FP8 block of value dims 128b..128b+127 the wave owns):
+//  - gather (QK team): the rows of a tile move from HBM straight into LDS by the load-to-LDS
+//    path, two tiles ahead, as stored (row r at 656 r): each load instruction covers 1 KB of
+//    consecutive row bytes, and since a row is an odd number (41) of 16-byte chunks, one chunk of
+//    16 consecutive rows falls on 16 distinct bank groups, so every operand read below is free of
 //    bank conflicts;
-//  - QK: the wave multiplies rows 16h..16h+15 of the tile by all 64 heads over block b's 128 E4M3
-//    codes, converted exactly to bf16 without their scale (v_cvt_scalef32_pk_bf16_fp8 with scale
-//    1), on v_mfma_f32_16x16x32_bf16 with rows as M and heads as N (four head tiles share each
-//    converted fragment). The block's fp32 scale then multiplies the code part of each row's
-//    partial logit, and a 16-deep k-step (v_mfma_f32_16x16x16_bf16) adds 16 of the 64 bf16 rope
-//    dims: partial_b = s_b[row] * (q_b . code_b) + q_rope_b . rope_b;
-//  - reduce: after a barrier, wave (b, h) sums the four block partials of head tile b, rows of
-//    half h, and forms P = 2^(logit * c - ref) in fp32; for each block b' it writes
-//    P'_b' = P * u_b'[row] in fp16, where u_b = s_b / 2^E_b is the scale relative to a power of
-//    two fixed per split (the first tile's largest scale of the block), zero for rows without an
-//    index;
-//  - PV: wave (b, h) accumulates O^T for dims 128b + 64h .. +64 of all 64 heads over the 32 rows
-//    on v_mfma_f32_16x16x32_f16: V^T comes from the raw codes through transposing 8-bit LDS reads
+//  - QK (QK wave b): all 32 rows of a tile times all 64 heads over block b's 128 E4M3 codes,
+//    converted exactly to bf16 without their scale (v_cvt_scalef32_pk_bf16_fp8, scale 1), on
+//    v_mfma_f32_16x16x32_bf16 with rows as M and heads as N (four head tiles share each converted
+//    fragment). The block's fp32 scale then multiplies the code part of each row's partial logit,
+//    and a 16-deep k-step (v_mfma_f32_16x16x16_bf16) adds 16 of the 64 bf16 rope dims:
+//    partial_b = s_b[row] * (q_b . code_b) + q_rope_b . rope_b. The wave reads and converts a
+//    tile's K fragments in the phase before its products, and writes block b's column of the
+//    tile's u table: u_b = s_b / 2^E_b, the scale relative to a power of two fixed per split (the
+//    first tile's largest scale of the block), zero for rows without an index;
+//  - reduce (PV wave b): head tile b over all 32 rows, so a head's softmax state never leaves
+//    its wave: the four block partials summed, P = 2^(logit * c - ref) in fp32, then
+//    P'_b' = P u_b'[row] for each block b' as the product of P and u rounded to fp16, in fp16;
+//  - PV (PV wave b): O^T for block b's 128 dims of all 64 heads over the 32 rows on
+//    v_mfma_f32_16x16x32_f16: V^T comes from the raw codes through transposing 8-bit LDS reads
 //    (ds_read_b64_tr_b8) and the exact conversion to fp16, P'_b^T from LDS, so
 //    O_b = 2^E_b sum_r P_r u_b[r] code_r / sum_r P_r.
 // The K and V operands are therefore exact (an E4M3 code is a bf16 and an fp16 value, and q is
-// bf16 as given) and the scales are applied in fp32. P' keeps fp16's 11 significant bits while
-// every row's u stays within [2^-10, 2^3] (or is 0); one wave checks that for each tile, and a
-// split whose rows fall outside is recomputed with P' = P * s in bf16 (full range, 8 bits).
+// bf16 as given) and the scales are applied in fp32 (logits) or as fp16 numbers (P'). P' is
+// fp16 while every row's u stays within [2^-10, 2^3] (or is 0); the QK waves check that for each
+// tile, and a split whose rows fall outside is recomputed with P' = P * s in fp32, rounded to bf16
+// (full range, 8 bits).
 // Rows without an index (padding) are masked: their logits become -inf, their P' is zero and
 // their V codes are zeroed before the products, so a padding row's bytes (which may be NaN)
 // never reach an output.
@@ -67,7 +69,8 @@ constexpr int ROW_CH = RB / 16;               // 41
 constexpr int SCALE_OFF = 512;                // the four fp32 block scales in a row
 constexpr int ROPE_OFF = 528;                 // the 64 bf16 rope dims in a row
 constexpr int TILE_CH = TILE * ROW_CH;        // 1312 chunks of rows per tile
-constexpr int U_OFF = TILE * RB;              // 20992: [row] x 4 fp32, the rows' relative scales u_b
+// The rows' relative scales u_b of a tile: fp16 [block][row] (fp16 P'), fp32 [row][block] (bf16)
+constexpr int U_OFF = TILE * RB;              // 20992
 constexpr int RAW_INSTR = 21;                 // load instructions per tile (64 chunks each)
 constexpr int RAW_SLOT = RAW_INSTR * 1024;    // 21504 bytes: the rows, then the u table
 constexpr int NRAW = 4;                       // tile slots: two computed on, two in flight
@@ -146,16 +149,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
-// Gather instructions per tile: instruction q goes to wave q % 8, so waves 0..4 issue three and
-// waves 5..7 two. Waits until this wave's gathers of all but the last `later` tiles it issued
-// have landed (`later` at most 3).
+// Gather instructions per tile (the QK team issues them all): wave b issues instructions b + 4 j,
+// j < 6, of the tile's 21, so wave 0 issues six and waves 1..3 five. Waits until this wave's
+// gathers of all but the last `later` tiles it issued have landed (`later` at most 3).
 __device__ __forceinline__ void wait_tiles_but(int later, int wave) {
-  if (wave < 5) {
-    if (later >= 3) wait_vmcnt<9>(); else if (later == 2) wait_vmcnt<6>();
-    else if (later == 1) wait_vmcnt<3>(); else wait_vmcnt<0>();
+  if (wave == 0) {
+    if (later >= 3) wait_vmcnt<18>(); else if (later == 2) wait_vmcnt<12>();
+    else if (later == 1) wait_vmcnt<6>(); else wait_vmcnt<0>();
   } else {
-    if (later >= 3) wait_vmcnt<6>(); else if (later == 2) wait_vmcnt<4>();
-    else if (later == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
+    if (later >= 3) wait_vmcnt<15>(); else if (later == 2) wait_vmcnt<10>();
+    else if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
   }
 }
 
@@ -284,13 +287,14 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     grow[j] = ci / ROW_CH;
     goff[j] = 16 * (ci - ROW_CH * grow[j]);
   }
-  auto gather = [&](int tile) {
-    // every row index is read before the first load goes out (a load's asm statement orders the
-    // LDS reads after it behind it)
+  // the row indices of a tile's gather, read ahead of it (a load's asm statement orders the LDS
+  // reads after it behind it, so they must not sit between the loads)
+  auto gather_ix = [&](int tile, int (&ix)[6]) {
     const int* ti = sm.idx + tile * TILE;
-    int ix[6];
 #pragma unroll
     for (int j = 0; j < 6; ++j) ix[j] = ti[grow[j]];
+  };
+  auto gather_go = [&](int tile, const int (&ix)[6]) {
     unsigned char* dst = sm.raw[tile % NRAW];
 #pragma unroll
     for (int j = 0; j < 5; ++j)
@@ -298,15 +302,26 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     if (b == 0 && lane < 32)
       lds_load16(kv_req + (uint64_t)(uint32_t)max(ix[5], 0) * RB + goff[5], dst + 1024 * 20);
   };
-  // valid-row mask of a tile (bit r: row r has an index); the same in every wave
+  auto gather = [&](int tile) {
+    int ix[6];
+    gather_ix(tile, ix);
+    gather_go(tile, ix);
+  };
+  // valid-row masks of the split's tiles (bit r: row r has an index), lane i holding tile i's
+  // (at most 64 tiles): the same in every wave, read with a lane read instead of LDS
+  uint32_t vmr = 0;
+#pragma unroll 4
+  for (int tl = 0; tl < ntiles; ++tl) {
+    const uint32_t m = (uint32_t)__ballot(sm.idx[tl * TILE + (lane & 31)] >= 0);
+    if (lane == tl) vmr = m;
+  }
   auto tile_valid = [&](int tile) -> uint32_t {
-    return (uint32_t)__ballot(sm.idx[tile * TILE + (lane & 31)] >= 0);
+    return (uint32_t)__builtin_amdgcn_readlane((int)vmr, tile);
   };
 
   const float c = sm_scale * LOG2E;
   bool f16 = true;         // P' and V in fp16 (else the bf16 fallback)
-  bool u_out = false;      // scale wave: a row's u outside [U_MIN, U_MAX)
-  const bool scale_wave = wave == 3;
+  bool u_out = false;      // QK team: a row's u of its block outside [U_MIN, U_MAX)
 
   // Each team runs its own pass loop (so that Q and O never share registers); both issue the same
   // barriers in the same order. A second pass runs when a logit left the reference window
@@ -331,47 +346,93 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
           qc[ht][ks] = *reinterpret_cast<const v8bf*>(qh + 128 * b + 64 * (ks >> 1) + 16 * G + 8 * (ks & 1));
         qr[ht] = *reinterpret_cast<const v4s*>(qh + 512 + 16 * b + 4 * G);
       }
+      // Q is in before the first gather goes out, visibly to the compiler: it then adds no waits
+      // of its own for these loads inside the tile loop, where the vector-memory counter also
+      // counts the gathers (a compiler wait there would drain gathers still in flight)
+      wait_vmcnt<0>();
     }
-  // ---- QK team: one pass over the split's tiles
+  // ---- QK team: one pass over the split's tiles. Phase 1 of iteration t issues only the
+    // products of tile t (its K fragments were read and converted in the phase before); phase 2
+    // stores the partials, then reads and converts tile t + 1 and writes its block's column of
+    // tile t + 1's u table, so the conversions run beside the PV team's products.
     auto qk_pass = [&](auto f16_tag) {
       constexpr bool F16 = decltype(f16_tag)::value;
       bool have_e = false;
+      int e_b = 0;  // E_b of this wave's block
+      int gix[6];   // row indices of the next tile to gather
       u_out = false;
+      v8bf kc[2][4];     // tile's K codes as bf16: [row half][k-step]
+      v4s kr[2];         // tile's rope dims: [row half]
+      float sb[2][4];    // tile's block-b scales: [row half][i], rows 16 h + 4 G + i
+      auto load_k = [&](int tile) {
+        const unsigned char* rt = sm.raw[tile % NRAW];
+        v4u k0[2], k1[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned char* rr = rt + RB * (16 * h + l16);
+          k0[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + G));
+          k1[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + 4 + G));
+          kr[h] = *reinterpret_cast<const v4s*>(rr + ROPE_OFF + 32 * b + 8 * G);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sb[h][i] = *reinterpret_cast<const float*>(rt + RB * (16 * h + 4 * G + i) + SCALE_OFF + 4 * b);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const v4u& kk = ks < 2 ? k0[h] : k1[h];
+            kc[h][ks] = e4m3x8_to_bf16(kk[2 * (ks & 1)], kk[2 * (ks & 1) + 1]);
+          }
+      };
+      // u_b[r] = s_b[r] / 2^E_b for a tile's rows (lane: row lane & 31), 0 for rows without an
+      // index; E_b is fixed by the first tile with a valid row (the exponent of its largest scale
+      // of block b), 0 in the bf16 fallback. Wave b writes block b's column.
+      auto u_col = [&](int tile) {
+        unsigned char* rt = sm.raw[tile % NRAW];
+        const int r = lane & 31;
+        const float sc = *reinterpret_cast<const float*>(rt + RB * r + SCALE_OFF + 4 * b);
+        const uint32_t vm = tile_valid(tile);
+        const bool valid = (vm >> r) & 1u;
+        if (F16 && !have_e && vm != 0) {  // uniform in the wave
+          float m = valid ? sc : 0.f;
+#pragma unroll
+          for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+          e_b = m > 0.f && m <= 3.402823466e38f ? __builtin_amdgcn_frexp_expf(m) : 0;
+          have_e = true;
+        }
+        const float uu = valid ? (F16 ? __builtin_amdgcn_ldexpf(sc, -e_b) : sc) : 0.f;
+        u_out |= F16 && !((uu >= U_MIN && uu < U_MAX) || uu == 0.f);
+        if (lane < 32) {
+          if (F16)  // u < 2^3 or 0, and >= 2^-10: an fp16 normal number
+            *reinterpret_cast<_Float16*>(rt + U_OFF + 2 * (32 * b + r)) = (_Float16)uu;
+          else
+            *reinterpret_cast<float*>(rt + U_OFF + 16 * r + 4 * b) = uu;
+        }
+      };
       const int first = min(ntiles, NRAW);
       for (int u = 0; u < first; ++u) gather(u);
       if (ntiles > 0) wait_tiles_but(first - 1, b);
       lds_barrier();  // every wave's part of tile 0 has landed
+      if (ntiles > 0) {
+        load_k(0);
+        u_col(0);
+      }
+      if (ntiles > 4) gather_ix(4, gix);
 #pragma unroll 1
       for (int t = 0; t <= ntiles; ++t) {
         v4f acc[2][4];
         if (t < ntiles) {
-          const unsigned char* rt = sm.raw[t % NRAW];
-          v4u k0[2], k1[2];
-          v4s kr[2];
-          float sb[2][4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const unsigned char* rr = rt + RB * (16 * h + l16);
-            k0[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + G));
-            k1[h] = *reinterpret_cast<const v4u*>(rr + 16 * (8 * b + 4 + G));
-            kr[h] = *reinterpret_cast<const v4s*>(rr + ROPE_OFF + 32 * b + 8 * G);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sb[h][i] = *reinterpret_cast<const float*>(rt + RB * (16 * h + 4 * G + i) + SCALE_OFF + 4 * b);
-          }
-          if (t >= 2 && t + 2 < ntiles) gather(t + 2);  // its slot held tile t - 2, done with
+          if (t >= 2 && t + 2 < ntiles) gather_go(t + 2, gix);  // its slot held tile t - 2, done with
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) acc[h][ht] = v4f{};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const v4u& kk = ks < 2 ? k0[h] : k1[h];
-              const v8bf a = e4m3x8_to_bf16(kk[2 * (ks & 1)], kk[2 * (ks & 1) + 1]);
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
               for (int ht = 0; ht < 4; ++ht)
-                acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qc[ht][ks], acc[h][ht], 0, 0, 0);
-            }
+                acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[h][ks], qc[ht][ks], acc[h][ht], 0, 0, 0);
           }
           // the block scale multiplies the code part; the rope part then accumulates on top
 #pragma unroll
@@ -382,53 +443,29 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
               for (int i = 0; i < 4; ++i) acc[h][ht][i] *= sb[h][i];
               acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr[h], qr[ht], acc[h][ht], 0, 0, 0);
             }
+          // tile t + 1 must have landed before phase 2 reads it; later tiles may still be in flight
+          if (t + 1 < ntiles) {
+            const int last_issued = min(ntiles - 1, max(NRAW - 1, t + 2));
+            wait_tiles_but(last_issued - (t + 1), b);
+          }
         }
-        lds_barrier();  // the PV team has read the partials of tile t - 1
+        lds_barrier();  // the PV team has read the partials of tile t - 1; tile t + 1 has landed
         if (t < ntiles) {
           // lane: head 16 ht + l16, rows 16 h + 4 G + i
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) sm.part[h][ht][b][lane] = acc[h][ht];
-          if (scale_wave) {
-            // u_b[r] = s_b[r] / 2^E_b for the tile's rows (lane: row lane & 31), 0 for rows without
-            // an index; E_b is fixed by the first tile with a valid row (the exponent of its largest
-            // scale of block b), 0 in the bf16 fallback
-            unsigned char* rt = sm.raw[t % NRAW];
-            const int r = lane & 31;
-            const v4f s4 = *reinterpret_cast<const v4f*>(rt + RB * r + SCALE_OFF);
-            const uint32_t vm = tile_valid(t);
-            const bool valid = (vm >> r) & 1u;
-            if (F16 && !have_e && vm != 0) {  // uniform in the wave
-#pragma unroll
-              for (int b2 = 0; b2 < 4; ++b2) {
-                float m = valid ? s4[b2] : 0.f;
-#pragma unroll
-                for (int sh = 1; sh < 32; sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
-                if (lane == 0) sm.eb[b2] = m > 0.f && m <= 3.402823466e38f ? __builtin_amdgcn_frexp_expf(m) : 0;
-              }
-              have_e = true;
-            }
-            if (!F16 && lane < 4) sm.eb[lane] = 0;
-            v4f u4;
-#pragma unroll
-            for (int b2 = 0; b2 < 4; ++b2) {
-              const float u = valid ? (F16 ? __builtin_amdgcn_ldexpf(s4[b2], -sm.eb[b2]) : s4[b2]) : 0.f;
-              u4[b2] = u;
-              u_out |= F16 && !((u >= U_MIN && u < U_MAX) || u == 0.f);
-            }
-            if (lane < 32) *reinterpret_cast<v4f*>(rt + U_OFF + 16 * r) = u4;
+          if (t + 1 < ntiles) {
+            load_k(t + 1);
+            u_col(t + 1);
           }
-        }
-        // tile t + 1 must have landed before the next iteration reads it; later tiles may still be
-        // in flight
-        if (t + 1 < ntiles) {
-          const int last_issued = min(ntiles - 1, max(NRAW - 1, t + 2));
-          wait_tiles_but(last_issued - (t + 1), b);
+          if (t >= 2 && t + 3 < ntiles) gather_ix(t + 3, gix);  // gathered in the next phase 1
         }
         lds_barrier();
       }
       wait_vmcnt<0>();  // no gather may still be writing this workgroup's LDS
+      if (lane == 0) sm.eb[b] = F16 ? e_b : 0;
     };
 
 #pragma unroll 1
@@ -444,7 +481,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     __syncthreads();  // the PV team's output is staged
   } else {
     float ref = -INFINITY;   // softmax reference of head 16 b + l16 (log2 units)
-    float seen = -INFINITY;  // largest scaled logit of that head in this lane's rows
+    float seen = -INFINITY;  // largest logit (before the scale c) of that head in this lane's rows
     float lsum = 0.f;        // this lane's share of the head's softmax denominator
     v4f o[8][4];             // O^T [dim tile][head tile] for dims 128 b + 16 dt + 4 G + i
     bool over = false;       // a logit above ref + REF_HEADROOM
@@ -458,6 +495,8 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
       lsum = 0.f;
       lds_barrier();  // tile 0 has landed
       const int voff = RB * (8 * G + (l16 >> 1)) + 16 * (8 * b) + 8 * (l16 & 1);
+      v2i fv[8];          // V fragments of tile u, read at the end of phase 1
+      uint32_t vm_u = 0;  // valid rows of tile u
 #pragma unroll 1
       for (int t = 0; t <= ntiles; ++t) {
         const int u = t - 1;
@@ -465,36 +504,48 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
           // reduction of tile u, head tile b (lane: head 16 b + l16), rows 16 h + 4 G + i
           const unsigned char* rt = sm.raw[u % NRAW];
           // every LDS read of the reduction goes out first
-          v4f ps[2][4], uv[2][4];
+          v4f ps[2][4];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int b2 = 0; b2 < 4; ++b2) ps[h][b2] = sm.part[h][b][b2][lane];
+          // u of the lane's rows 16 h + 4 G .. +3: fp16 per block (fp16 P'), fp32 per row (bf16)
+          v2u uh[2][4];
+          v4f uv[2][4];
+          if constexpr (F16) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              uv[h][i] = *reinterpret_cast<const v4f*>(rt + U_OFF + 16 * (16 * h + 4 * G + i));
-          const uint32_t vm = tile_valid(u);
-          float x[2][4];
+              for (int b2 = 0; b2 < 4; ++b2)
+                uh[h][b2] = *reinterpret_cast<const v2u*>(rt + U_OFF + 2 * (32 * b2 + 16 * h + 4 * G));
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                uv[h][i] = *reinterpret_cast<const v4f*>(rt + U_OFF + 16 * (16 * h + 4 * G + i));
+          }
+          vm_u = tile_valid(u);
+          const uint32_t vm = vm_u;
+          float y[2][4];  // logits before the scale c (c > 0); -inf for rows without an index
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const v4f s = ps[h][0] + ps[h][1] + ps[h][2] + ps[h][3];
+            const v4f sum = ps[h][0] + ps[h][1] + ps[h][2] + ps[h][3];
             if (vm == 0xFFFFFFFFu) {  // uniform
 #pragma unroll
-              for (int i = 0; i < 4; ++i) x[h][i] = s[i] * c;
+              for (int i = 0; i < 4; ++i) y[h][i] = sum[i];
             } else {
               const unsigned vb = (vm >> (16 * h + 4 * G)) & 15u;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) x[h][i] = (vb >> i) & 1 ? s[i] * c : -INFINITY;
+              for (int i = 0; i < 4; ++i) y[h][i] = (vb >> i) & 1 ? sum[i] : -INFINITY;
             }
           }
           if (!have_ref && vm != 0) {  // uniform: the first tile with a valid row sets ref
-            float m = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                            fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            float m = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), fmaxf(y[0][2], y[0][3])),
+                            fmaxf(fmaxf(y[1][0], y[1][1]), fmaxf(y[1][2], y[1][3])));
             m = fmaxf(m, __shfl_xor(m, 16));
             m = fmaxf(m, __shfl_xor(m, 32));
-            ref = m + REF_MARGIN;
+            ref = m * c + REF_MARGIN;
             have_ref = true;
           }
           const float m_use = ref == -INFINITY ? 0.f : ref;
@@ -503,52 +554,70 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              seen = fmaxf(seen, x[h][i]);  // a logit above m_use + REF_HEADROOM asks for a second pass
-              pr[i] = __builtin_amdgcn_exp2f(x[h][i] - m_use);  // -inf -> 0; underflow to 0 is harmless
+              seen = fmaxf(seen, y[h][i]);  // a logit above m_use + REF_HEADROOM asks for a second pass
+              // P = 2^(y c - ref): -inf -> 0; underflow to 0 is harmless
+              pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[h][i], c, -m_use));
               lsum += pr[i];
             }
-            // P'_b2 = P u_b2[row]; u is 0 for a row without an index, whose P is 0 too
+            // P'_b2 = P u_b2[row]; u is 0 for a row without an index, whose P is 0 too. fp16: P
+            // (<= 2^11) and u (in [2^-10, 2^3]) are fp16 numbers, multiplied in pairs of rows
+            if constexpr (F16) {
+              const v2h p01 = __builtin_bit_cast(v2h, pack_f16(pr[0], pr[1]));
+              const v2h p23 = __builtin_bit_cast(v2h, pack_f16(pr[2], pr[3]));
 #pragma unroll
-            for (int b2 = 0; b2 < 4; ++b2) {
-              float w[4];
+              for (int b2 = 0; b2 < 4; ++b2) {
+                const unsigned u01 = uh[h][b2].x, u23 = uh[h][b2].y;
+                const v2h w01 = p01 * __builtin_bit_cast(v2h, u01);
+                const v2h w23 = p23 * __builtin_bit_cast(v2h, u23);
+                unsigned* dst = reinterpret_cast<unsigned*>(&sm.pp[b2][b][2 * h + (G >> 1)][l16]) + 2 * (G & 1);
+                *reinterpret_cast<v2u*>(dst) = v2u{__builtin_bit_cast(unsigned, w01), __builtin_bit_cast(unsigned, w23)};
+              }
+            } else {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) w[i] = pr[i] * uv[h][i][b2];
-              unsigned* dst = reinterpret_cast<unsigned*>(&sm.pp[b2][b][2 * h + (G >> 1)][l16]) + 2 * (G & 1);
-              *reinterpret_cast<v2u*>(dst) = F16 ? v2u{pack_f16(w[0], w[1]), pack_f16(w[2], w[3])}
-                                                 : v2u{pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3])};
+              for (int b2 = 0; b2 < 4; ++b2) {
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = pr[i] * uv[h][i][b2];
+                unsigned* dst = reinterpret_cast<unsigned*>(&sm.pp[b2][b][2 * h + (G >> 1)][l16]) + 2 * (G & 1);
+                *reinterpret_cast<v2u*>(dst) = v2u{pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3])};
+              }
             }
           }
-        }
-        lds_barrier();  // P' of tile u visible; the partials of tile u read
-        if (t >= 1) {
-          // PV of tile u: dims 128 b + 16 dt + 4 G + i of every head
+          // the V fragments of tile u go out now, to land during the barrier
           const unsigned char* rv = sm.raw[u % NRAW];
-          const uint32_t vm = tile_valid(u);
-          const unsigned vb = (vm >> (8 * G)) & 0xFFu;
-          const unsigned mlo = byte_mask4(vb), mhi = byte_mask4(vb >> 4);
-          v4u pb[4];
-#pragma unroll
-          for (int ht = 0; ht < 4; ++ht) pb[ht] = sm.pp[b][ht][G][l16];
-          v2i fv[8];  // every V fragment is read before the first product
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
             fv[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (__attribute__((address_space(3))) v2i*)(rv + voff + 16 * dt));
+        }
+        lds_barrier();  // P' of tile u visible; the partials of tile u read
+        if (t >= 1) {
+          // PV of tile u: dims 128 b + 16 dt + 4 G + i of every head
+          const unsigned vb = (vm_u >> (8 * G)) & 0xFFu;
+          const unsigned mlo = byte_mask4(vb), mhi = byte_mask4(vb >> 4);
+          v4u pb[4];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) pb[ht] = sm.pp[b][ht][G][l16];
+          // every V fragment is converted while P' is in flight; then the products go out back to
+          // back (converting between them would leave the matrix core idle)
+          using VT = std::conditional_t<F16, v8h, v8bf>;
+          VT va[8];
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
             const v2i f = fv[dt];
-            if constexpr (F16) {
-              const v8h va = e4m3x8_to_f16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht)
-                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, __builtin_bit_cast(v8h, pb[ht]), o[dt][ht], 0, 0, 0);
-            } else {
-              const v8bf va = e4m3x8_to_bf16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
-#pragma unroll
-              for (int ht = 0; ht < 4; ++ht)
-                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, __builtin_bit_cast(v8bf, pb[ht]), o[dt][ht], 0, 0, 0);
-            }
+            if constexpr (F16) va[dt] = e4m3x8_to_f16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
+            else va[dt] = e4m3x8_to_bf16((unsigned)f[0] & mlo, (unsigned)f[1] & mhi);
           }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+              if constexpr (F16)
+                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], __builtin_bit_cast(v8h, pb[ht]), o[dt][ht], 0, 0, 0);
+              else
+                o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(v8bf, pb[ht]), o[dt][ht], 0, 0, 0);
+            }
         }
         lds_barrier();
       }
@@ -564,11 +633,12 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
       lsum += __shfl_xor(lsum, 32);
       float sn = fmaxf(seen, __shfl_xor(seen, 16));
       sn = fmaxf(sn, __shfl_xor(sn, 32));
+      sn *= c;  // the largest scaled logit
       if (G == 0) {
         sm.xsum[0][16 * b + l16] = lsum;
         sm.xmax[0][16 * b + l16] = sn;
       }
-      over = seen > (ref == -INFINITY ? 0.f : ref) + REF_HEADROOM;
+      over = seen * c > (ref == -INFINITY ? 0.f : ref) + REF_HEADROOM;
       if (__any(over)) logit_over = 1;  // any wave: every wave redoes the split
       __syncthreads();
       if (!(logit_over || scale_over) || pass == 1) break;
