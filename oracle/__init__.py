@@ -13,7 +13,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsmla_oracle.so")
+# SMLA_ORACLE_LIB names another build of the same sources (the sanitizer test uses it)
+LIB_PATH = os.environ.get("SMLA_ORACLE_LIB") or os.path.join(_HERE, "libsmla_oracle.so")
 SRC = os.path.join(_HERE, "smla_oracle.c")
 
 

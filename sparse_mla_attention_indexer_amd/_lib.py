@@ -9,7 +9,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsmla.so")
+# SMLA_LIB names another build of the same sources (the sanitizer test uses it)
+LIB_PATH = os.environ.get("SMLA_LIB") or os.path.join(_HERE, "libsmla.so")
 
 SMLA_OK = 0
 SMLA_E_INVALID = -1

@@ -14,7 +14,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsmla_workload.so")
+# SMLA_WORKLOAD_LIB names another build of the same sources (the sanitizer test uses it)
+LIB_PATH = os.environ.get("SMLA_WORKLOAD_LIB") or os.path.join(_HERE, "libsmla_workload.so")
 
 KV_BF16 = 0
 KV_FP8_656 = 1
