@@ -261,9 +261,10 @@ def fp8_indexer_measurement(dev, d, plan, steps, warmup, attend):
 
 
 def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
-    """The single-GPU DCP simulation on the decode batch: the KV cache of every request cut round
-    robin into n_sh shards (shard l holds tokens l, l + n_sh, ...), each shard's indexer + top-k and
-    sparse MLA at its real shape, and the exact merges (top-k merge, local indices, LSE merge).
+    """The single-GPU DCP simulation on a decode batch: the KV cache of every request cut round
+    robin into n_sh shards (shard l holds tokens l, l + n_sh, ...; a request's several query
+    tokens get their local positions), each shard's indexer + top-k and sparse MLA at its real
+    shape, and the exact merges (top-k merge with the shards' local lists, LSE merge).
     Reports one shard's step, the merges, and their sum: what one GPU of a DCP group would spend
     on compute per step (the all-gathers between GPUs are not modelled)."""
     import numpy as np
@@ -277,13 +278,9 @@ def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
     row0 = np.concatenate([[0], np.cumsum(x.kv_len)[:-1]])
     shards = []
     for sh in range(n_sh):
-        lens, rows = [], []
-        for b, kl in enumerate(x.kv_len):
-            g = np.arange(sh, int(kl), n_sh)
-            lens.append(g.size)
-            rows.append(row0[b] + g)
-        rows = np.concatenate(rows)
-        plan = ops.BatchPlan(np.ones(d.batch, np.int32), np.array(lens, np.int64), dev)
+        lens, pos = ops.dcp_shard_positions(x.n_q, x.kv_len, n_sh, sh)
+        rows = np.concatenate([row0[b] + np.arange(sh, int(kl), n_sh) for b, kl in enumerate(x.kv_len)])
+        plan = ops.BatchPlan(x.n_q, lens, dev, positions=pos)
         kv = torch.from_numpy(np.ascontiguousarray(x.kv[rows])).to(dev)
         k_idx = torch.from_numpy(np.ascontiguousarray(x.k_idx[rows])).to(dev)
         ws_t = ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k)
@@ -309,8 +306,7 @@ def dcp_measurement(dev, x, d, steps, warmup, n_sh=8):
                        out=outs[sh], lse=lses[sh], workspace=ws_m)
 
     def merge_select():
-        ops.topk_merge(lists_i, lists_s, d.top_k, idx=idx, score=sc)
-        ops.dcp_local_indices(idx, n_sh, out=local)
+        ops.topk_merge(lists_i, lists_s, d.top_k, idx=idx, score=sc, local=local)
 
     def merge_attend():
         ops.lse_merge(outs, lses, out=out, lse=lse)
@@ -850,9 +846,10 @@ def main():
         lg = Leg(c, dev, log)
         tl = time_leg(lg, args.leg_steps, 3, scrub, log)
         r = leg_result(lg, tl, args.leg_steps, 3)
-        if extras and lg.decode and (lg.x.n_q == 1).all() and lg.d.kv_format == W.KV_FP8_656:
+        if extras and lg.decode and lg.d.kv_format == W.KV_FP8_656:
             log("DCP simulation")
             r["dcp_sim"] = dcp_measurement(dev, lg.x, lg.d, args.leg_steps, 3)
+        if extras and lg.decode and (lg.x.n_q == 1).all() and lg.d.kv_format == W.KV_FP8_656:
             log("hybrid offload resolve")
 
             def select():

@@ -28,7 +28,8 @@
  * Batch layout (all entry points): request b owns query tokens [Q_b, Q_b + n_q[b]) and latent
  * rows / indexer keys [R_b, R_b + kv_len[b]), Q and R being exclusive prefix sums. Query j of
  * request b sits at position p = kv_len[b] - n_q[b] + j (its own row is already in the cache)
- * and may use rows s <= p; s is local to the request.
+ * and may use rows s <= p; s is local to the request. smla_batch_build_pos takes the positions
+ * explicitly instead (a DCP shard's tokens, below).
  */
 #ifndef SMLA_H
 #define SMLA_H
@@ -81,6 +82,19 @@ size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv);
  */
 int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
                      size_t table_bytes, void* stream, smla_batch* out);
+
+/*
+ * smla_batch_build with every query token's position given: pos (host) [total_q], token j of
+ * request b at pos[Q_b + j] with 0 <= pos < kv_len[b], non-decreasing within a request; the
+ * token uses rows s <= pos. With pos = NULL it is smla_batch_build. Under decode context
+ * parallelism ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "DCP") a shard holds
+ * every n-th row, so the consecutive global positions of a request's tokens (MTP drafts) become
+ * local positions that repeat or step by one: shard l of n gives global position P the local
+ * position floor((P - l) / n), which needs P >= l. Same table size bound and contract otherwise.
+ */
+int smla_batch_build_pos(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                         const int64_t* pos, void* table, size_t table_bytes, void* stream,
+                         smla_batch* out);
 
 /*
  * Indexer scores, full matrix (parity and debugging; O(total_q * max_kv) memory).
@@ -162,12 +176,18 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
  * smla_indexer_scores_topk_fp8 returns them, with float_scores = 1). idx (device)
  * [total_q, top_k]: the top_k global indices by (score desc, index asc), in ascending index
  * order, -1 padded; score (device, optional) [total_q, top_k] likewise, -1 (-1.0f) on padding. The merge
- * is exact because a member of the global top-k is in its own shard's top-k. 1 <= n_lists,
- * 1 <= k_in, n_lists * k_in <= 16,384, 1 <= top_k <= 2,048; global indices must stay below 2^31.
+ * is exact because a member of the global top-k is in its own shard's top-k. local_idx (device,
+ * optional) [n_lists, total_q, top_k]: every shard's part of the merged selection, as
+ * smla_dcp_local_indices would return it for n_shards = n_lists (ascending local indices, then -1),
+ * written by the same launch; it needs n_lists <= 64 (SMLA_E_UNSUPPORTED otherwise).
+ * 1 <= n_lists, 1 <= k_in, n_lists * k_in <= 16,384, 1 <= top_k <= 2,048; global indices must stay
+ * below 2^31. Lists in the order the indexer's top-k returns them (each list's valid entries in
+ * ascending local index, then only padding) take a sort-free path; any other order is accepted
+ * and sorted.
  */
 int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
                     const int32_t* score_lists, int64_t list_stride, int32_t float_scores,
-                    int32_t top_k, int32_t* idx, int32_t* score, void* stream);
+                    int32_t top_k, int32_t* idx, int32_t* score, int32_t* local_idx, void* stream);
 
 /*
  * smla_dcp_local_indices: every shard's part of a global selection. idx (device)
@@ -199,9 +219,9 @@ int smla_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts, con
  *
  * idx (device) [total_q, top_k]: the step's selections (local rows, -1 padding). Per request b
  * (device arrays of `batch` entries): resident_from[b] = first resident local row (rows below
- * it are offloaded; 0 = fully resident, nothing to do), at most kv_len - n_q + 1 so that every
- * query token of the request (the first sits at position kv_len - n_q) sees every offloaded
- * row; hot_base[b] = local row of hot slot 0, with 0 <= hot_base and hot_base + n_slots <=
+ * it are offloaded; 0 = fully resident, nothing to do), at most p_0 + 1, p_0 the position of the
+ * request's first query token (kv_len - n_q unless given to smla_batch_build_pos), so that every
+ * query token of the request sees every offloaded row; hot_base[b] = local row of hot slot 0, with 0 <= hot_base and hot_base + n_slots <=
  * resident_from (the hot buffer sits in the request's released rows); host_row0[b] = host row
  * of the request's local row 0.
  * hot_tok / hot_age (device) [batch, n_slots]: the slots' token (-1 empty) and step of last use

@@ -25,6 +25,7 @@ KV_FP8_656 = 1
 EXPORTS = (
     "smla_batch_table_bytes",
     "smla_batch_build",
+    "smla_batch_build_pos",
     "smla_indexer_scores",
     "smla_indexer_topk_workspace_bytes",
     "smla_indexer_scores_topk",
@@ -82,13 +83,14 @@ def lib():
         L.smla_batch_table_bytes.argtypes = [i32, i32, i64]
         L.smla_batch_table_bytes.restype = sz
         L.smla_batch_build.argtypes = [i32, P, P, P, sz, P, BP]
+        L.smla_batch_build_pos.argtypes = [i32, P, P, P, P, sz, P, BP]
         L.smla_indexer_scores.argtypes = [BP, P, P, P, i32, i32, P, P]
         L.smla_indexer_topk_workspace_bytes.argtypes = [BP, i32, i32, i32]
         L.smla_indexer_topk_workspace_bytes.restype = sz
         L.smla_indexer_scores_topk.argtypes = [BP, P, P, P, i32, i32, i32, P, P, P, sz, P]
         L.smla_indexer_scores_fp8.argtypes = [BP, P, P, P, P, i32, i32, P, P]
         L.smla_indexer_scores_topk_fp8.argtypes = [BP, P, P, P, P, i32, i32, i32, P, P, P, sz, P]
-        L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, i32, P, P, P]
+        L.smla_topk_merge.argtypes = [i32, i32, i32, P, P, i64, i32, i32, P, P, P, P]
         L.smla_dcp_local_indices.argtypes = [i32, i32, P, i32, P, P]
         L.smla_lse_merge.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         L.smla_hot_resolve.argtypes = [BP, P, i32, P, P, i32, P, P, i32, P, i64, P, i32, P, P, P, P]

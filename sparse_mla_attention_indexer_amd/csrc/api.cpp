@@ -90,20 +90,20 @@ int check_mla_args(const smla_batch* b, const void* q, const void* kv, int32_t f
 }
 
 // Indexer work plan: query tiles of up to QT tokens, tile i paired with tile n-1-i, each pair's
-// combined key range (front tile's keys, then back tile's) cut into C-key items.
-void plan_items_chunk(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+// combined key range (front tile's keys, then back tile's) cut into C-key items. pos: every
+// token's position (non-decreasing within a request).
+void plan_items_chunk(int32_t batch, const int32_t* n_q, const std::vector<int32_t>& pos,
                       const std::vector<int32_t>& q_start, int64_t C, std::vector<smla::Item>* items) {
   using smla::Item;
   using smla::Seg;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t base = kv_len[b] - n_q[b];
     const int32_t nt = (n_q[b] + smla::QT - 1) / smla::QT;
     auto tile = [&](int32_t i, int64_t* extent, int32_t* q0, int32_t* nq) {
       const int32_t lo = i * smla::QT;
       const int32_t hi = std::min<int32_t>(n_q[b], lo + smla::QT);
       *q0 = q_start[b] + lo;
       *nq = hi - lo;
-      *extent = base + hi;  // keys [0, extent) cover every position of the tile
+      *extent = (int64_t)pos[(size_t)(q_start[b] + hi - 1)] + 1;  // keys [0, extent) cover the tile
     };
     for (int32_t i = 0; i < (nt + 1) / 2; ++i) {
       const int32_t j = nt - 1 - i;
@@ -128,12 +128,12 @@ void plan_items_chunk(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
   }
 }
 
-void plan_items(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+void plan_items(int32_t batch, const int32_t* n_q, const std::vector<int32_t>& pos,
                 const std::vector<int32_t>& q_start, std::vector<smla::Item>* items) {
-  plan_items_chunk(batch, n_q, kv_len, q_start, smla::KEY_CHUNK, items);
+  plan_items_chunk(batch, n_q, pos, q_start, smla::KEY_CHUNK, items);
   if ((int64_t)items->size() < smla::ITEMS_FILL) {
     items->clear();
-    plan_items_chunk(batch, n_q, kv_len, q_start, smla::KEY_CHUNK_SMALL, items);
+    plan_items_chunk(batch, n_q, pos, q_start, smla::KEY_CHUNK_SMALL, items);
   }
 }
 
@@ -176,11 +176,17 @@ size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv) {
 
 int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
                      size_t table_bytes, void* stream, smla_batch* out) {
+  return smla_batch_build_pos(batch, n_q, kv_len, nullptr, table, table_bytes, stream, out);
+}
+
+int smla_batch_build_pos(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
+                         const int64_t* pos, void* table, size_t table_bytes, void* stream,
+                         smla_batch* out) {
   g_err.clear();
   if (batch < 1 || !n_q || !kv_len || !table || !out)
     return fail(SMLA_E_INVALID, "batch >= 1 and non-NULL n_q, kv_len, table, out required");
   if (!aligned(table, 256)) return fail(SMLA_E_INVALID, "table must be 256-byte aligned");
-  int64_t total_q = 0, total_rows = 0, max_kv = 0, total_cand = 0, min_cand = INT64_MAX;
+  int64_t total_q = 0, total_rows = 0, max_kv = 0;
   int32_t max_q = 0;
   for (int32_t b = 0; b < batch; ++b) {
     if (n_q[b] < 1 || kv_len[b] < n_q[b] || kv_len[b] >= (int64_t(1) << 31))
@@ -190,12 +196,26 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
     total_rows += kv_len[b];
     max_kv = std::max<int64_t>(max_kv, kv_len[b]);
     max_q = std::max(max_q, n_q[b]);
-    // positions kv_len - n_q .. kv_len - 1 see (p + 1) candidates each
-    total_cand += (int64_t)n_q[b] * (2 * kv_len[b] - n_q[b] + 1) / 2;
-    min_cand = std::min<int64_t>(min_cand, kv_len[b] - n_q[b] + 1);
   }
   if (total_q >= (int64_t(1) << 31)) return fail(SMLA_E_INVALID, "too many query tokens");
   if (total_rows >= (int64_t(1) << 40)) return fail(SMLA_E_INVALID, "too many rows");
+  // every token's position: given, or kv_len - n_q + j; token t sees (p + 1) candidates
+  std::vector<int32_t> P((size_t)total_q);
+  int64_t total_cand = 0, min_cand = INT64_MAX;
+  {
+    int64_t t = 0;
+    for (int32_t b = 0; b < batch; ++b)
+      for (int32_t j = 0; j < n_q[b]; ++j, ++t) {
+        const int64_t p = pos ? pos[t] : kv_len[b] - n_q[b] + j;
+        if (p < 0 || p >= kv_len[b] || (j > 0 && p < P[(size_t)t - 1]))
+          return fail(SMLA_E_INVALID,
+                      "request %d token %d: position %lld outside [0, kv_len) or below the token "
+                      "before it", b, j, (long long)p);
+        P[(size_t)t] = (int32_t)p;
+        total_cand += p + 1;
+        min_cand = std::min<int64_t>(min_cand, p + 1);
+      }
+  }
   std::vector<smla::Req> req(batch);
   std::vector<smla::Tok> tok((size_t)total_q);
   std::vector<int32_t> q_start(batch);
@@ -204,15 +224,15 @@ int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, v
     q_start[b] = (int32_t)q0;
     req[b] = smla::Req{r0, kv_len[b], (int32_t)q0, n_q[b], 0};
     for (int32_t j = 0; j < n_q[b]; ++j) {
-      const int64_t p = kv_len[b] - n_q[b] + j;
-      tok[(size_t)(q0 + j)] = smla::Tok{r0, cand, (int32_t)p, b, 0};
-      cand += p + 1;
+      const int32_t p = P[(size_t)(q0 + j)];
+      tok[(size_t)(q0 + j)] = smla::Tok{r0, cand, p, b, 0};
+      cand += (int64_t)p + 1;
     }
     q0 += n_q[b];
     r0 += kv_len[b];
   }
   std::vector<smla::Item> items;
-  plan_items(batch, n_q, kv_len, q_start, &items);
+  plan_items(batch, n_q, P, q_start, &items);
   const size_t need = table_layout(batch, (int32_t)total_q, (int64_t)items.size());
   if (table_bytes < need)
     return fail(SMLA_E_WORKSPACE, "table needs %zu bytes, got %zu", need, table_bytes);
@@ -354,7 +374,7 @@ int smla_indexer_scores_topk_fp8(const smla_batch* b, const uint8_t* q, const ui
 
 int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
                     const int32_t* score_lists, int64_t list_stride, int32_t float_scores,
-                    int32_t top_k, int32_t* idx, int32_t* score, void* stream) {
+                    int32_t top_k, int32_t* idx, int32_t* score, int32_t* local_idx, void* stream) {
   g_err.clear();
   if (total_q < 1 || n_lists < 1 || k_in < 1 || top_k < 1)
     return fail(SMLA_E_INVALID, "total_q, n_lists, k_in and top_k must be >= 1");
@@ -367,8 +387,12 @@ int smla_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_
       !aligned(idx, 4) || (score && !aligned(score, 4)))
     return fail(SMLA_E_INVALID, "idx_lists, score_lists and idx must be non-NULL, all 4-byte aligned");
   if (float_scores != 0 && float_scores != 1) return fail(SMLA_E_INVALID, "float_scores must be 0 or 1");
+  if (local_idx && !aligned(local_idx, 4)) return fail(SMLA_E_INVALID, "local_idx must be 4-byte aligned");
+  if (local_idx && n_lists > smla::MERGE_FAST_LISTS)
+    return fail(SMLA_E_UNSUPPORTED, "local_idx needs n_lists <= %d (got %d)", smla::MERGE_FAST_LISTS,
+                n_lists);
   hipError_t e = smla::launch_topk_merge(total_q, n_lists, k_in, idx_lists, score_lists, list_stride,
-                                         top_k, idx, score, float_scores != 0,
+                                         top_k, idx, score, local_idx, float_scores != 0,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMLA_OK : hip_fail(e, "top-k merge launch");
 }

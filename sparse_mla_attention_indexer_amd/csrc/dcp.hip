@@ -12,6 +12,8 @@
 //  - local_indices_kernel: each shard's part of a global selection, as ascending local indices,
 //    compacted to the front (the attention kernel skips trailing padding tiles).
 //  - lse_merge_kernel: per (token, head), weights exp(lse_i - max) over the parts, bf16 in and out.
+//  - the top-k merge can also write every shard's local list itself (topk_merge_kernel); the
+//    local-indices kernel here serves selections from anywhere else.
 #include "smla_internal.h"
 
 namespace smla {
@@ -62,44 +64,70 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (bf)f);
 }
 
-// One 128-thread block per (token, head); thread x covers dims 4x .. 4x + 3, then 512 further on.
-// All parts' lse values and the first eight parts' outputs go out together.
-__global__ __launch_bounds__(128) void lse_merge_kernel(int total_q, int H, int D_v, int n_parts,
-                                                        const uint16_t* __restrict__ outs,
-                                                        const float* __restrict__ lses,
-                                                        uint16_t* __restrict__ out,
-                                                        float* __restrict__ lse_out) {
-  const int64_t th = blockIdx.x;  // token * H + head
+// One wave per (token, head), four per workgroup. Lane i < n_parts holds part i's lse; the max,
+// the weights exp(lse_i - max) and their sum come from wave reductions, and lane x then covers
+// dims 8x .. 8x + 7 (then 512 further on), reading every part's eight bf16 values in one 16-byte
+// load when rows are 16-byte aligned.
+constexpr int LM_WAVES = 4;
+__global__ __launch_bounds__(64 * LM_WAVES) void lse_merge_kernel(int total_q, int H, int D_v,
+                                                                  int n_parts,
+                                                                  const uint16_t* __restrict__ outs,
+                                                                  const float* __restrict__ lses,
+                                                                  uint16_t* __restrict__ out,
+                                                                  float* __restrict__ lse_out) {
+  const int64_t th = (int64_t)blockIdx.x * LM_WAVES + (threadIdx.x >> 6);  // token * H + head
   const int64_t plane_o = (int64_t)total_q * H * D_v, plane_l = (int64_t)total_q * H;
-  float m = -INFINITY;
-  for (int i = 0; i < n_parts; ++i) m = fmaxf(m, lses[i * plane_l + th]);
-  float z = 0.f;
-  for (int i = 0; i < n_parts; ++i) {
-    const float li = lses[i * plane_l + th];
-    z += li == -INFINITY ? 0.f : __expf(li - m);
-  }
+  if (th >= plane_l) return;  // whole waves
+  const int lane = threadIdx.x & 63;
+  const float li = lane < n_parts ? lses[lane * plane_l + th] : -INFINITY;
+  float m = li;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const float wi = li == -INFINITY ? 0.f : __expf(li - m);
+  float z = wi;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  const bool vec = (D_v & 3) == 0 && ((uintptr_t)outs & 7) == 0;  // 8-byte loads
-  for (int d0 = 4 * threadIdx.x; d0 < D_v; d0 += 512) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < n_parts; ++i) {
-      const float li = lses[i * plane_l + th];
-      if (li == -INFINITY) continue;
-      const float wi = __expf(li - m);
-      const uint16_t* src = outs + i * plane_o + th * D_v + d0;
-      if (vec) {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        acc[0] += wi * __uint_as_float(v.x << 16);
-        acc[1] += wi * __uint_as_float(v.x & 0xFFFF0000u);
-        acc[2] += wi * __uint_as_float(v.y << 16);
-        acc[3] += wi * __uint_as_float(v.y & 0xFFFF0000u);
-      } else {
-        for (int e = 0; e < 4 && d0 + e < D_v; ++e) acc[e] += wi * bf16_to_f32(src[e]);
+  const bool vec = (D_v & 7) == 0 && ((uintptr_t)outs & 15) == 0 && ((uintptr_t)out & 15) == 0;
+  for (int d0 = 8 * lane; d0 < D_v; d0 += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < n_parts; i0 += 8) {  // up to eight parts' loads in flight
+      uint4 v[8];
+      float w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k;
+        w[k] = i < n_parts ? __shfl(wi, i) : 0.f;
+        if (vec && w[k] != 0.f)
+          v[k] = *reinterpret_cast<const uint4*>(outs + i * plane_o + th * D_v + d0);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (w[k] == 0.f) continue;  // an empty part (or none)
+        if (vec) {
+          const uint32_t u[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w[k] * __uint_as_float(u[e] << 16);
+            acc[2 * e + 1] += w[k] * __uint_as_float(u[e] & 0xFFFF0000u);
+          }
+        } else {
+          const uint16_t* src = outs + (i0 + k) * plane_o + th * D_v + d0;
+          for (int e = 0; e < 8 && d0 + e < D_v; ++e) acc[e] += w[k] * bf16_to_f32(src[e]);
+        }
       }
     }
-    for (int e = 0; e < 4 && d0 + e < D_v; ++e) out[th * D_v + d0 + e] = f32_to_bf16(acc[e] * inv);
+    if (vec) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[e] = (uint32_t)f32_to_bf16(acc[2 * e] * inv) | ((uint32_t)f32_to_bf16(acc[2 * e + 1] * inv) << 16);
+      *reinterpret_cast<uint4*>(out + th * D_v + d0) = make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      for (int e = 0; e < 8 && d0 + e < D_v; ++e) out[th * D_v + d0 + e] = f32_to_bf16(acc[e] * inv);
+    }
   }
-  if (lse_out && threadIdx.x == 0) lse_out[th] = z > 0.f ? m + __logf(z) : -INFINITY;
+  if (lse_out && lane == 0) lse_out[th] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
 }  // namespace
@@ -114,7 +142,9 @@ hipError_t launch_local_indices(int32_t total_q, int32_t top_k, const int32_t* i
 hipError_t launch_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts,
                             const void* outs, const float* lses, void* out, float* lse,
                             hipStream_t s) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((int64_t)total_q * H)), dim3(128), 0, s,
+  const int64_t waves = (int64_t)total_q * H;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((waves + LM_WAVES - 1) / LM_WAVES)),
+                     dim3(64 * LM_WAVES), 0, s,
                      total_q, H, D_v, n_parts, static_cast<const uint16_t*>(outs), lses,
                      static_cast<uint16_t*>(out), lse);
   return hipGetLastError();

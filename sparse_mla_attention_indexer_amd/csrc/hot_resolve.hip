@@ -92,7 +92,8 @@ struct HrLds {
 };
 
 __global__ __launch_bounds__(HR_THREADS) void hot_resolve_kernel(
-    const Req* __restrict__ reqs, const int32_t* __restrict__ idx, int top_k,
+    const Req* __restrict__ reqs, const Tok* __restrict__ toks, const int32_t* __restrict__ idx,
+    int top_k,
     const int32_t* __restrict__ resident_from, const int32_t* __restrict__ hot_base, int n_slots,
     int32_t* __restrict__ hot_tok, int32_t* __restrict__ hot_age, int step,
     const unsigned char* __restrict__ host_rows, int64_t host_n_rows,
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(HR_THREADS) void hot_resolve_kernel(
 
   int status = 0;
   // the offloaded prefix (and the hot buffer inside it) must end at or before the first query
-  // token's position kv_len - n_q: every token of the request then sees every hot row
-  if (rf < 0 || (int64_t)rf > rq.kv_len - rq.n_q + 1) status = -2;
+  // token's position (kv_len - n_q by default): every token of the request sees every hot row
+  if (rf < 0 || rf > toks[rq.q_start].pos + 1) status = -2;
   else if (rf > 0 && (hb < 0 || (int64_t)hb + n_slots > rf)) status = -2;
   else if (rf > 0 && (hr0 < 0 || hr0 + rf > host_n_rows)) status = -3;
   if (status < 0 || rf == 0) {  // nothing offloaded, or a bad request: no state is touched
@@ -270,7 +271,8 @@ hipError_t launch_hot_resolve(const void* table, int32_t batch, const int32_t* i
     attr = true;
   }
   hipLaunchKernelGGL(hot_resolve_kernel, dim3((unsigned)batch), dim3(HR_THREADS), sizeof(HrLds), s,
-                     reinterpret_cast<const Req*>(table), idx, top_k, resident_from, hot_base,
+                     reinterpret_cast<const Req*>(table), table_view(table, batch, 0).tok, idx, top_k,
+                     resident_from, hot_base,
                      n_slots, hot_tok, hot_age, step, static_cast<const unsigned char*>(host_rows),
                      host_n_rows, host_row0, row_bytes, static_cast<unsigned char*>(kv), idx_out,
                      n_copied);

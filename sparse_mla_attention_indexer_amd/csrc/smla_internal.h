@@ -173,11 +173,14 @@ hipError_t mla_scratch(void** ptr);
 hipError_t launch_kv_append(int64_t n, const void* latent, const int64_t* rows, void* kv,
                             const int8_t* k_new, int32_t D_I, int8_t* k_idx, hipStream_t s);
 // DCP merges on one GPU (topk.hip, dcp.hip). The top-k merge holds at most MERGE_MAX_CAND
-// candidates; fscores: the scores are fp32 bit patterns.
+// candidates; fscores: the scores are fp32 bit patterns. Its per-shard local lists (local_idx,
+// optional) are supported up to MERGE_FAST_LISTS lists, the most its search-based order handles.
 constexpr int MERGE_MAX_CAND = 16384;
+constexpr int MERGE_FAST_LISTS = 64;
 hipError_t launch_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
                              const int32_t* score_lists, int64_t list_stride, int32_t top_k,
-                             int32_t* idx, int32_t* score, bool fscores, hipStream_t s);
+                             int32_t* idx, int32_t* score, int32_t* local_idx, bool fscores,
+                             hipStream_t s);
 hipError_t launch_local_indices(int32_t total_q, int32_t top_k, const int32_t* idx, int32_t n_shards,
                                 int32_t* local_idx, hipStream_t s);
 hipError_t launch_lse_merge(int32_t total_q, int32_t H, int32_t D_v, int32_t n_parts,

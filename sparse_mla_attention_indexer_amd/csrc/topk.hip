@@ -34,9 +34,13 @@ __device__ __forceinline__ uint64_t sel_key(int32_t score, int64_t s) {
   return ((uint64_t)(uint32_t)score << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)s);
 }
 
-// Inclusive scan over the block (NT threads, multiple of 64); `red` holds NT/64 + 1 ints.
+// Inclusive scan over the block (NT threads, multiple of 64); `red` holds NT/64 + 1 ints and
+// red[NT/64] holds the block total on return. Every wave reads all wave totals and reduces the
+// ones before it itself (a butterfly over the first NT/64 lanes), so no thread walks them.
 template <int NT>
 __device__ int block_incl_scan(int v, int* red) {
+  constexpr int NW = NT / 64;
+  static_assert((NW & (NW - 1)) == 0 && NW <= 64, "a power-of-two number of waves");
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -45,18 +49,16 @@ __device__ int block_incl_scan(int v, int* red) {
   }
   if (lane == 63) red[wv] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int i = 0; i < NT / 64; ++i) {
-      int x = red[i];
-      red[i] = acc;
-      acc += x;
-    }
-    red[NT / 64] = acc;
+  const int s = lane < NW ? red[lane] : 0;
+  int before = lane < wv ? s : 0, all = s;
+#pragma unroll
+  for (int o = 1; o < NW; o <<= 1) {
+    before += __shfl_xor(before, o);
+    all += __shfl_xor(all, o);
   }
-  __syncthreads();
-  v += red[wv];
-  __syncthreads();
+  v += __shfl(before, 0);
+  if (threadIdx.x == 0) red[NW] = all;
+  __syncthreads();  // red[NW] visible; red is free for the next scan
   return v;
 }
 
@@ -210,63 +212,156 @@ __device__ void wave_radix_cut(KeyAt key_at, int n, int need, int* h, uint64_t* 
   *mask_out = mask;
 }
 
-constexpr int NT_A = 1024;  // the DCP merge's workgroup
+constexpr int NT_A = 1024;                          // the DCP merge's workgroup
+constexpr int MERGE_PER = MERGE_MAX_CAND / NT_A;    // candidates per thread, in registers
+constexpr int MERGE_WORDS = MERGE_MAX_CAND / 32;    // selection bitmap words
+
+// MSD radix select as radix_cut, over the PER keys each thread holds in registers; element u
+// takes part iff member(u).
+template <int NT, int PER, typename Member>
+__device__ void radix_cut_regs(const uint64_t (&key)[PER], Member member, int need, int* hist2,
+                               int* red, int* cut, uint64_t* pm) {
+  uint64_t prefix = 0, mask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist2[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (member(u) && (key[u] & mask) == prefix)
+        atomicAdd(&hist2[(int)((key[u] >> shift) & 255u)], 1);
+    __syncthreads();
+    find_cut<NT>(hist2, 256, need, red, cut);
+    const int dg = cut[0];
+    const int gt = cut[1];
+    const int eq = hist2[dg];
+    need -= gt;
+    prefix |= (uint64_t)dg << shift;
+    mask |= (uint64_t)255u << shift;
+    __syncthreads();
+    if (eq == need) break;
+  }
+  if (threadIdx.x == 0) {
+    pm[0] = prefix;
+    pm[1] = mask;
+  }
+  __syncthreads();
+}
 
 // ---- DCP top-k merge: the union of per-shard lists, one 1024-thread workgroup per token ----
 // Shard l of n_lists holds the tokens l, l + n_lists, ...; list entry (local j, score) is global
-// index j n_lists + l. The union's keys sit in LDS; the cut is found as for a row (histogram of
-// score codes, then an exact radix select inside the cut bin), and the selected (index, score)
-// pairs are sorted by index (bitonic) before they are written.
-template <bool FB>
+// index g = j n_lists + l. Candidate c = l k_in + (position in list l); thread tid holds the
+// candidates u NT_A + tid in registers, with their keys and score codes (AL: k_in is a multiple
+// of NT_A, so each u lies in one list for the whole workgroup). The cut is found as for a row: a
+// histogram of score codes locates the bin of the take-th key, an exact radix select inside that
+// bin finds the key itself. The selection is kept as a bitmap over c, and F(c), the number of
+// selected candidates before c, is a popcount away. Per-candidate steps are written without
+// branches (invalid entries go to a spare histogram bin and spare LDS slots), since the
+// workgroup's time is the instructions its 16 waves issue on one CU.
+// Output order: for g = j n + l, ascending g is ascending (j, l). When every list holds its
+// valid entries in ascending order followed only by padding (what the indexer's top-k returns),
+// the selected entries, numbered F(c), are list after list and ascending inside each list. The
+// entry numbered r of list l then has output position (r - F(l k_in)) plus, for each other list
+// l', the number of l''s selected entries with local index below j (l' > l) or at most j (l' <
+// l), no sort: the local indices are cut into NBK buckets of width W, a table holds every list's
+// count of selected entries below each bucket (a histogram and one block scan), and an entry
+// reads that count for its own bucket and then compares only the few entries of that bucket.
+// r - F(l k_in) is also its position in its shard's local list. Each thread ranks the entries
+// numbered tid and tid + 1024.
+// Otherwise the selected (index, score) pairs are sorted by index (bitonic), and each shard's
+// local list is cut out of the sorted selection by one block scan per shard.
+template <bool FB, bool AL>
 __global__ __launch_bounds__(NT_A) void topk_merge_kernel(int n_lists, int k_in,
                                                           const int32_t* __restrict__ idx_lists,
                                                           const int32_t* __restrict__ score_lists,
                                                           int64_t list_stride, int top_k,
                                                           int32_t* __restrict__ idx_out,
-                                                          int32_t* __restrict__ score_out) {
+                                                          int32_t* __restrict__ score_out,
+                                                          int32_t* __restrict__ local_out,
+                                                          int64_t local_stride) {
   extern __shared__ __align__(16) unsigned char smem_m[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem_m);  // [MERGE_MAX_CAND], 0: no entry
-  int* hist = reinterpret_cast<int*>(keys + MERGE_MAX_CAND);  // [TOPK_BINS]
-  uint64_t* work = reinterpret_cast<uint64_t*>(hist + TOPK_BINS);  // [TOPK_MAX_K]: b* keys, then the selection
+  uint64_t* work = reinterpret_cast<uint64_t*>(smem_m);  // [TOPK_MAX_K + 1], the last a spare
+  uint64_t* sel = work + TOPK_MAX_K + 1;  // [TOPK_MAX_K + 1] numbered entries (score, j); spare
+  int32_t* lidx = reinterpret_cast<int32_t*>(sel + TOPK_MAX_K + 1);  // [MERGE_MAX_CAND] local j
+  int* hist = reinterpret_cast<int*>(lidx + MERGE_MAX_CAND);         // [TOPK_BINS + 1]; spare
+  uint32_t* bits = reinterpret_cast<uint32_t*>(hist + TOPK_BINS + 1);  // [MERGE_WORDS]
+  int* wpre = reinterpret_cast<int*>(bits + MERGE_WORDS);              // [MERGE_WORDS + 1]
   __shared__ int hist2[256];
   __shared__ int red[NT_A / 64 + 1];
   __shared__ int cut[2];
   __shared__ uint64_t pm[2];
-  __shared__ int nvalid, nk, nsel;
+  __shared__ int nval[MERGE_FAST_LISTS], lbase[MERGE_FAST_LISTS + 1];
+  __shared__ uint8_t sel_list[TOPK_MAX_K + 1];  // list of each numbered entry; spare
+  __shared__ int nvalid, unsorted;
   const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid == 0) nvalid = 0, nk = 0, nsel = 0;
-  for (int i = tid; i < TOPK_BINS; i += NT_A) hist[i] = 0;
-  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ncand = n_lists * k_in;
-  int mine = 0;
-  {
-    // every load of the thread's candidates in flight before any is used
-    constexpr int PER = MERGE_MAX_CAND / NT_A;
-    int32_t lv[PER], sv[PER];
+  const bool fast_ok = n_lists <= MERGE_FAST_LISTS;
+  if (tid == 0) nvalid = 0, unsorted = fast_ok ? 0 : 1;
+  if (tid < MERGE_FAST_LISTS) nval[tid] = 0;
+  for (int i = tid; i <= TOPK_BINS; i += NT_A) hist[i] = 0;
+  // list of candidate c: floor((c + 0.5) / k_in) in fp32 is exact here, since the quotient's
+  // distance to an integer (>= 0.5 / k_in) exceeds its rounding error ((c + 0.5) 2^-23 / k_in)
+  // for every c < 2^22
+  const float inv_k = 1.0f / (float)k_in;
+  auto list_of = [&](int c) { return (int)(((float)c + 0.5f) * inv_k); };
+  int lu[MERGE_PER];  // AL: list of slot u, the same for every thread
+  if (AL) {
+    const int per_list = k_in / NT_A;
+    int l = 0, left = per_list;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = u * NT_A + tid;
-      const int l = c / k_in;
-      const int64_t off = l * list_stride + t * k_in + (c - l * k_in);
-      lv[u] = c < ncand ? idx_lists[off] : -1;
-      sv[u] = c < ncand ? score_lists[off] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = u * NT_A + tid;
-      if (c >= ncand) break;
-      uint64_t key = 0;  // valid keys have ~index >= 2^31, so 0 is below all of them
-      if (lv[u] >= 0) {
-        key = sel_key(sv[u], (int64_t)lv[u] * n_lists + c / k_in);
-        atomicAdd(&hist[score_bin<FB>((uint32_t)sv[u])], 1);
-        ++mine;
-      }
-      keys[c] = key;
+    for (int u = 0; u < MERGE_PER; ++u) {
+      lu[u] = l;
+      if (--left == 0) left = per_list, ++l;
     }
   }
-  if (mine) atomicAdd(&nvalid, mine);
+  auto list_u = [&](int u, int c) { return AL ? lu[u] : list_of(c); };
+  int32_t li[MERGE_PER];
+  uint64_t key[MERGE_PER];  // 0: no candidate (valid keys have ~index >= 2^31)
+  int bin[MERGE_PER];       // score code; TOPK_BINS (the spare bin) for no candidate
+  {
+    int32_t sv[MERGE_PER];
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) {  // every load in flight before any is used
+      const int c = u * NT_A + tid;
+      const int l = list_u(u, c);
+      const int64_t off = l * list_stride + t * k_in + (c - l * k_in);
+      li[u] = c < ncand ? idx_lists[off] : -1;
+      sv[u] = c < ncand ? score_lists[off] : 0;
+    }
+    __syncthreads();  // hist and the counters are cleared
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) {
+      const int c = u * NT_A + tid;
+      if (c < ncand) lidx[c] = li[u];
+      const bool v = li[u] >= 0;
+      key[u] = v ? sel_key(sv[u], (int64_t)li[u] * n_lists + list_u(u, c)) : 0ull;
+      bin[u] = v ? score_bin<FB>((uint32_t)sv[u]) : TOPK_BINS;
+      atomicAdd(&hist[bin[u]], 1);
+      cnt += __popcll(__ballot(v));
+    }
+    if (lane == 0 && cnt) atomicAdd(&nvalid, cnt);
+  }
   __syncthreads();
+  // the fast order needs every list ascending, then padding; nval[l] = its valid entries
+  if (fast_ok) {
+    int32_t nb[MERGE_PER];
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) {  // the next entries first, all reads in flight
+      const int c = u * NT_A + tid;
+      nb[u] = c + 1 < ncand ? lidx[c + 1] : -1;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) {
+      const int c = u * NT_A + tid;
+      const int l = list_u(u, c), j = c - l * k_in;
+      const int32_t a = li[u], b = j + 1 < k_in ? nb[u] : -1;
+      bad |= c < ncand && !(b < 0 || (a >= 0 && a < b));
+      if (c < ncand && a >= 0 && b < 0) nval[l] = j + 1;
+    }
+    if (__ballot(bad) && lane == 0) unsorted = 1;
+  }
   const int n = nvalid;
   const int take = min(top_k, n);
   int bstar = -1;  // every valid key selected
@@ -275,89 +370,207 @@ __global__ __launch_bounds__(NT_A) void topk_merge_kernel(int n_lists, int k_in,
     find_cut<NT_A>(hist, TOPK_BINS, take, red, cut);
     bstar = cut[0];
     const int need = take - cut[1];
-    if (hist[bstar] != need) {
-      const int nb = hist[bstar];
-      if (nb <= TOPK_MAX_K) {
-        const int lane = tid & 63;
-        for (int i0 = 0; i0 < ncand; i0 += NT_A) {
-          const int i = i0 + tid;
-          const bool f = i < ncand && keys[i] != 0 && score_bin<FB>((uint32_t)(keys[i] >> 32)) == bstar;
-          const uint64_t m = __ballot(f);
-          if (m) {
-            int base = 0;
-            const int leader = __builtin_ctzll(m);
-            if (lane == leader) base = atomicAdd(&nk, __popcll(m));
-            base = __shfl(base, leader);
-            if (f) work[base + __popcll(m & ((1ull << lane) - 1))] = keys[i];
-          }
+    const int nbin = hist[bstar];
+    if (nbin != need) {
+      if (nbin <= TOPK_MAX_K) {  // the bin's keys to LDS, then one wave selects inside them
+        int mine = 0;
+#pragma unroll
+        for (int u = 0; u < MERGE_PER; ++u) mine += bin[u] == bstar;
+        int pos = block_incl_scan<NT_A>(mine, red) - mine;
+#pragma unroll
+        for (int u = 0; u < MERGE_PER; ++u) {
+          const bool in = bin[u] == bstar;
+          work[in ? pos : TOPK_MAX_K] = key[u];
+          pos += in;
         }
         __syncthreads();
-        if (tid < 64) {
+        if (wave == 0) {
           uint64_t pf, mk;
-          wave_radix_cut([&](int i) { return work[i]; }, nb, need, hist2, &pf, &mk);
-          if (tid == 0) {
+          wave_radix_cut([&](int i) { return work[i]; }, nbin, need, hist2, &pf, &mk);
+          if (lane == 0) {
             pm[0] = pf;
             pm[1] = mk;
           }
         }
         __syncthreads();
       } else {
-        radix_cut<NT_A>(
-            ncand, need, [&](int i) { return keys[i]; },
-            [&](int i) { return keys[i] != 0 && score_bin<FB>((uint32_t)(keys[i] >> 32)) == bstar; },
-            hist2, red, cut, pm);
+        radix_cut_regs<NT_A, MERGE_PER>(key, [&](int u) { return bin[u] == bstar; }, need, hist2,
+                                        red, cut, pm);
       }
       prefix = pm[0];
       mask = pm[1];
     }
   }
-  __syncthreads();  // `work` is reused for the selection
+  // the selection as a bitmap over c: each wave's 64 candidates of a u are two aligned words
+  uint64_t msk[MERGE_PER];  // the same words, per wave (uniform)
+#pragma unroll
+  for (int u = 0; u < MERGE_PER; ++u) {
+    const bool s = key[u] != 0 &&
+                   (bstar < 0 || bin[u] > bstar || (bin[u] == bstar && (key[u] & mask) >= prefix));
+    const uint64_t m = __ballot(s);
+    msk[u] = m;
+    const int w0 = (u * NT_A + wave * 64) >> 5;
+    if (lane < 2) bits[w0 + lane] = (uint32_t)(lane ? m >> 32 : m);
+  }
+  __syncthreads();
   {
-    const int lane = tid & 63;
-    for (int c0 = 0; c0 < ncand; c0 += NT_A) {  // one counter update per wave and pass
-      const int c = c0 + tid;
-      const uint64_t key = c < ncand ? keys[c] : 0;
-      bool f = key != 0;
-      if (f && bstar >= 0) {
-        const int b = score_bin<FB>((uint32_t)(key >> 32));
-        f = b > bstar || (b == bstar && (key & mask) >= prefix);
-      }
-      const uint64_t m = __ballot(f);
-      if (m) {
-        int base = 0;
-        const int leader = __builtin_ctzll(m);
-        if (lane == leader) base = atomicAdd(&nsel, __popcll(m));
-        base = __shfl(base, leader);
-        const int slot = base + __popcll(m & ((1ull << lane) - 1));
-        if (f && slot < TOPK_MAX_K)  // exactly `take` for valid input; duplicates cannot overrun
-          work[slot] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)key) << 32) | (key >> 32);
-      }
-    }
+    const int pc = tid < MERGE_WORDS ? __popc(bits[tid]) : 0;
+    const int incl = block_incl_scan<NT_A>(pc, red);
+    if (tid < MERGE_WORDS) wpre[tid] = incl - pc;
+    if (tid == MERGE_WORDS - 1) wpre[MERGE_WORDS] = incl;
   }
   __syncthreads();
-  // ascending global index: bitonic sort of the selected (index, score) pairs
-  int m = 1;
-  while (m < take) m <<= 1;
-  for (int i = take + tid; i < m; i += NT_A) work[i] = ~0ull;
-  __syncthreads();
-  for (int size = 2; size <= m; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < m / 2; i += NT_A) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t a = work[lo], b = work[hi];
-        if ((a > b) == up) {
-          work[lo] = b;
-          work[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
+  // F(c): selected candidates before c (0 <= c <= MERGE_MAX_CAND)
+  auto F = [&](int c) {
+    const int w = c >> 5, r = c & 31;
+    return r ? wpre[w] + __popc(bits[w] & ((1u << r) - 1u)) : wpre[w];
+  };
+  auto selected = [&](int c) { return (bits[c >> 5] >> (c & 31)) & 1u; };
   int32_t* oi = idx_out + t * top_k;
   int32_t* os = score_out ? score_out + t * top_k : nullptr;
   const int32_t pad = FB ? (int32_t)0xBF800000u : -1;
+  if (!unsorted) {
+    if (tid <= n_lists) lbase[tid] = F(tid * k_in);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int wp[MERGE_PER];
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) wp[u] = wpre[(u * NT_A + wave * 64) >> 5];
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) {  // number the selected entries: sel[F(c)]
+      const int r = wp[u] + __popcll(msk[u] & below);
+      const int dst = ((msk[u] >> lane) & 1ull) && r < TOPK_MAX_K ? r : TOPK_MAX_K;
+      sel[dst] = (key[u] & 0xFFFFFFFF00000000ull) | (uint32_t)li[u];
+      sel_list[dst] = (uint8_t)list_u(u, u * NT_A + tid);
+    }
+    __syncthreads();
+    // the local indices of the numbered entries, alone, for the searches (reuses `lidx`)
+    int32_t* selj = lidx;
+    for (int r = tid; r < take; r += NT_A) selj[r] = (int32_t)(uint32_t)sel[r];
+    // bucket table over the local indices: cum[l (NBK + 1) + b] = list l's selected entries in
+    // buckets below b (then the whole list at b = NBK); it sits in `lidx` past the first
+    // TOPK_MAX_K words
+    const int NBK = TOPK_MAX_K / n_lists;  // n_lists (NBK + 1) <= TOPK_MAX_K + MERGE_FAST_LISTS
+    int* cum = lidx + TOPK_MAX_K;
+    const int ncum = n_lists * (NBK + 1);
+    for (int i = tid; i < ncum; i += NT_A) cum[i] = 0;
+    int jmax = -1;
+    for (int r = tid; r < take; r += NT_A) jmax = max(jmax, (int)(uint32_t)sel[r]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) jmax = max(jmax, __shfl_xor(jmax, o));
+    if (lane == 0) hist2[wave] = jmax;
+    __syncthreads();
+    jmax = -1;
+    for (int w = 0; w < NT_A / 64; ++w) jmax = max(jmax, hist2[w]);
+    const int W = jmax / NBK + 1;  // buckets of W local indices cover [0, jmax]
+    bool on[2];
+    int le[2], own[2], rank[2], bk[2];
+    int32_t je[2];
+    uint64_t ent[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {  // entries tid and tid + 1024 (take <= 2048)
+      const int r = tid + e * NT_A;
+      on[e] = r < take;
+      ent[e] = on[e] ? sel[r] : 0ull;
+      le[e] = on[e] ? sel_list[r] : 0;
+      je[e] = (int32_t)(uint32_t)ent[e];
+      bk[e] = je[e] / W;
+      own[e] = on[e] ? r - lbase[le[e]] : 0;
+      rank[e] = own[e];
+      if (on[e]) atomicAdd(&cum[le[e] * (NBK + 1) + bk[e]], 1);
+    }
+    __syncthreads();
+    {  // exclusive prefix over the whole table (three words per thread); minus the list's start
+      int v[3], loc = 0;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int i = 3 * tid + k;
+        v[k] = i < ncum ? cum[i] : 0;
+        loc += v[k];
+      }
+      int pre = block_incl_scan<NT_A>(loc, red) - loc;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const int i = 3 * tid + k;
+        if (i < ncum) cum[i] = pre - lbase[i / (NBK + 1)];
+        pre += v[k];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (!on[e]) continue;
+      for (int l2 = 0; l2 < n_lists; ++l2) {
+        if (l2 == le[e]) continue;
+        const int32_t tg = l2 < le[e] ? je[e] + 1 : je[e];
+        const int* c2 = cum + l2 * (NBK + 1) + bk[e];
+        const int32_t* s2 = selj + lbase[l2];
+        int cnt = c2[0];
+        for (int x = c2[0]; x < c2[1]; ++x) cnt += s2[x] < tg;
+        rank[e] += cnt;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (!on[e]) continue;
+      if (rank[e] < TOPK_MAX_K)
+        work[rank[e]] = ((uint64_t)(uint32_t)(je[e] * n_lists + le[e]) << 32) | (ent[e] >> 32);
+      if (local_out) local_out[le[e] * local_stride + t * top_k + own[e]] = je[e];
+    }
+    __syncthreads();
+    if (local_out)
+      for (int l = 0; l < n_lists; ++l) {
+        int32_t* lo = local_out + l * local_stride + t * top_k;
+        for (int r = lbase[l + 1] - lbase[l] + tid; r < top_k; r += NT_A) lo[r] = -1;
+      }
+  } else {
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u) mine += u * NT_A + tid < ncand && selected(u * NT_A + tid);
+    int pos = block_incl_scan<NT_A>(mine, red) - mine;
+#pragma unroll
+    for (int u = 0; u < MERGE_PER; ++u)
+      if (u * NT_A + tid < ncand && selected(u * NT_A + tid) && pos < TOPK_MAX_K)
+        work[pos++] = ((uint64_t)(0xFFFFFFFFu - (uint32_t)key[u]) << 32) | (key[u] >> 32);
+    // ascending global index: bitonic sort of the selected (index, score) pairs
+    int m = 1;
+    while (m < take) m <<= 1;
+    __syncthreads();
+    for (int i = take + tid; i < m; i += NT_A) work[i] = ~0ull;
+    __syncthreads();
+    for (int size = 2; size <= m; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < m / 2; i += NT_A) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t a = work[lo], b = work[hi];
+          if ((a > b) == up) {
+            work[lo] = b;
+            work[hi] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if (local_out) {  // each shard's entries of the sorted selection, in order (thread: 2 ranks)
+      const int r0 = 2 * tid;
+      for (int l = 0; l < n_lists; ++l) {
+        const uint32_t g0 = r0 < take ? (uint32_t)(work[r0] >> 32) : 0u;
+        const uint32_t g1 = r0 + 1 < take ? (uint32_t)(work[r0 + 1] >> 32) : 0u;
+        const bool s0 = r0 < take && g0 % (uint32_t)n_lists == (uint32_t)l;
+        const bool s1 = r0 + 1 < take && g1 % (uint32_t)n_lists == (uint32_t)l;
+        const int mc = (int)s0 + (int)s1;
+        const int incl = block_incl_scan<NT_A>(mc, red);
+        const int total = red[NT_A / 64];
+        int32_t* lo = local_out + l * local_stride + t * top_k;
+        int p = incl - mc;
+        if (s0) lo[p++] = (int32_t)(g0 / (uint32_t)n_lists);
+        if (s1) lo[p] = (int32_t)(g1 / (uint32_t)n_lists);
+        for (int r = total + tid; r < top_k; r += NT_A) lo[r] = -1;
+        __syncthreads();  // red is reused by the next shard's scan
+      }
+    }
+  }
   for (int j = tid; j < top_k; j += NT_A) {
     oi[j] = j < take ? (int32_t)(work[j] >> 32) : -1;
     if (os) os[j] = j < take ? (int32_t)(uint32_t)work[j] : pad;
@@ -1056,27 +1269,30 @@ hipError_t launch_topk_t(const smla_batch& b, const int32_t* scores, int32_t top
 }  // namespace
 
 size_t topk_merge_lds_bytes() {
-  return sizeof(uint64_t) * (MERGE_MAX_CAND + TOPK_MAX_K) + sizeof(int) * TOPK_BINS;
+  return 2 * sizeof(uint64_t) * (TOPK_MAX_K + 1) + sizeof(int32_t) * MERGE_MAX_CAND +
+         sizeof(int) * (TOPK_BINS + 1) + sizeof(uint32_t) * MERGE_WORDS + sizeof(int) * (MERGE_WORDS + 1);
 }
 
 hipError_t launch_topk_merge(int32_t total_q, int32_t n_lists, int32_t k_in, const int32_t* idx_lists,
                              const int32_t* score_lists, int64_t list_stride, int32_t top_k,
-                             int32_t* idx, int32_t* score, bool fscores, hipStream_t s) {
+                             int32_t* idx, int32_t* score, int32_t* local_idx, bool fscores,
+                             hipStream_t s) {
+  const int64_t local_stride = (int64_t)total_q * top_k;
   const size_t lds = topk_merge_lds_bytes();
   static const bool lds_set = [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    for (const void* f : {reinterpret_cast<const void*>(&topk_merge_kernel<false, false>),
+                          reinterpret_cast<const void*>(&topk_merge_kernel<false, true>),
+                          reinterpret_cast<const void*>(&topk_merge_kernel<true, false>),
+                          reinterpret_cast<const void*>(&topk_merge_kernel<true, true>)})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     return true;
   }();
   (void)lds_set;
-  if (fscores)
-    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3((unsigned)total_q), dim3(NT_A), lds, s, n_lists,
-                       k_in, idx_lists, score_lists, list_stride, top_k, idx, score);
-  else
-    hipLaunchKernelGGL(topk_merge_kernel<false>, dim3((unsigned)total_q), dim3(NT_A), lds, s, n_lists,
-                       k_in, idx_lists, score_lists, list_stride, top_k, idx, score);
+  const bool al = k_in % NT_A == 0;
+  auto kern = fscores ? (al ? &topk_merge_kernel<true, true> : &topk_merge_kernel<true, false>)
+                      : (al ? &topk_merge_kernel<false, true> : &topk_merge_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)total_q), dim3(NT_A), lds, s, n_lists, k_in, idx_lists,
+                     score_lists, list_stride, top_k, idx, score, local_idx, local_stride);
   return hipGetLastError();
 }
 

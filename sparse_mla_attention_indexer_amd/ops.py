@@ -35,9 +35,10 @@ def _req(t: torch.Tensor, name: str, dtype, shape, device):
 
 class BatchPlan:
     """Device batch table for requests with `n_q[b]` query tokens and `kv_len[b]` cached rows
-    (queries are the last n_q rows of their request). Built once, reused by every call."""
+    (queries are the last n_q rows of their request, unless `positions` [total_q] gives every
+    token's position). Built once, reused by every call."""
 
-    def __init__(self, n_q, kv_len, device="cuda:0"):
+    def __init__(self, n_q, kv_len, device="cuda:0", positions=None):
         self.device = torch.device(device)
         self.n_q = np.ascontiguousarray(n_q, np.int32).reshape(-1)
         self.kv_len = np.ascontiguousarray(kv_len, np.int64).reshape(-1)
@@ -46,21 +47,27 @@ class BatchPlan:
         B = int(self.n_q.size)
         total_q = int(self.n_q.sum())
         max_kv = int(self.kv_len.max())
+        pos = None
+        if positions is not None:
+            pos = np.ascontiguousarray(positions, np.int64).reshape(-1)
+            if pos.size != total_q:
+                raise ValueError("positions must hold one entry per query token")
         nbytes = int(lib().smla_batch_table_bytes(B, total_q, max_kv))
         if nbytes == 0:
             raise ValueError("invalid batch sizes")
         self.table = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.desc = Batch()
         with torch.cuda.device(self.device):
-            check("smla_batch_build",
-                  lib().smla_batch_build(B, self.n_q.ctypes.data, self.kv_len.ctypes.data,
-                                         self.table.data_ptr(), nbytes, _stream(self.device),
-                                         ctypes.byref(self.desc)))
+            check("smla_batch_build_pos",
+                  lib().smla_batch_build_pos(B, self.n_q.ctypes.data, self.kv_len.ctypes.data,
+                                             None if pos is None else pos.ctypes.data,
+                                             self.table.data_ptr(), nbytes, _stream(self.device),
+                                             ctypes.byref(self.desc)))
         self.batch = B
         self.total_q = total_q
         self.total_rows = int(self.kv_len.sum())
         self.max_kv = max_kv
-        self.positions = np.concatenate(
+        self.positions = pos if pos is not None else np.concatenate(
             [np.arange(k - n, k) for n, k in zip(self.n_q, self.kv_len)]).astype(np.int64)
 
     @property
@@ -178,11 +185,13 @@ def indexer_topk_fp8(plan: BatchPlan, q, k, k_scale, w, top_k: int, with_scores=
     return idx, score
 
 
-def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None, float_scores=False):
+def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None, float_scores=False,
+               local=None):
     """DCP top-k merge: idx_lists / score_lists [n_lists, total_q, k_in] int32 (shard l holds the
     tokens l, l + n_lists, ...; local indices, -1 padding; scores as int32, or fp32 bit patterns
     with float_scores) -> the exact global top_k per token, idx [total_q, top_k] ascending (-1
-    padded) and its scores (int32 bit patterns)."""
+    padded) and its scores (int32 bit patterns). local [n_lists, total_q, top_k] (optional): also
+    every shard's part of the selection, as dcp_local_indices gives it."""
     if idx_lists.dim() != 3 or score_lists.shape != idx_lists.shape:
         raise ValueError("idx_lists and score_lists must both be [n_lists, total_q, k_in]")
     n_lists, total_q, k_in = (int(v) for v in idx_lists.shape)
@@ -195,12 +204,32 @@ def topk_merge(idx_lists, score_lists, top_k: int, idx=None, score=None, float_s
         score = torch.empty((total_q, top_k), dtype=torch.int32, device=d)
     _req(idx, "idx", torch.int32, (total_q, top_k), d)
     _req(score, "score", torch.int32, (total_q, top_k), d)
+    if local is not None:
+        _req(local, "local", torch.int32, (n_lists, total_q, top_k), d)
     with torch.cuda.device(d):
         check("smla_topk_merge",
               lib().smla_topk_merge(total_q, n_lists, k_in, idx_lists.data_ptr(), score_lists.data_ptr(),
                                     total_q * k_in, int(bool(float_scores)), top_k, idx.data_ptr(),
-                                    score.data_ptr(), _stream(d)))
+                                    score.data_ptr(), None if local is None else local.data_ptr(),
+                                    _stream(d)))
     return idx, score
+
+
+def dcp_shard_positions(n_q, kv_len, n_shards: int, shard: int):
+    """Round-robin KV sharding ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "DCP"):
+    shard `shard` of n_shards holds rows shard, shard + n, ... of every request. Returns its rows
+    per request and its query tokens' local positions, for
+    BatchPlan(n_q, rows, positions=local): the token at global position P = kv_len - n_q + j sees
+    the local rows j' with j' n + shard <= P, so its local position is floor((P - shard) / n)."""
+    n_q = np.ascontiguousarray(n_q, np.int64).reshape(-1)
+    kv_len = np.ascontiguousarray(kv_len, np.int64).reshape(-1)
+    if n_shards < 1 or not 0 <= shard < n_shards:
+        raise ValueError("need 0 <= shard < n_shards")
+    rows = (kv_len - shard + n_shards - 1) // n_shards
+    P = np.concatenate([np.arange(k - n, k) for n, k in zip(n_q, kv_len)])
+    if (P < shard).any():
+        raise ValueError("a query token sees no row of this shard (position below the shard id)")
+    return rows, (P - shard) // n_shards
 
 
 def dcp_local_indices(idx, n_shards: int, out=None):

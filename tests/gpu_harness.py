@@ -23,13 +23,13 @@ def say(*a):
 
 
 class Dev:
-    def __init__(self, x: W.Inputs, device="cuda:0", n_q=None, kv_len=None):
+    def __init__(self, x: W.Inputs, device="cuda:0", n_q=None, kv_len=None, positions=None):
         self.x = x
         d = x.dims
         self.device = torch.device(device)
         self.n_q = x.n_q if n_q is None else np.asarray(n_q, np.int32)
         self.kv_len = x.kv_len if kv_len is None else np.asarray(kv_len, np.int64)
-        self.plan = ops.BatchPlan(self.n_q, self.kv_len, self.device)
+        self.plan = ops.BatchPlan(self.n_q, self.kv_len, self.device, positions=positions)
         self.q = torch.from_numpy(x.q.view(np.int16)).view(torch.bfloat16).to(self.device)
         if d.kv_format == W.KV_FP8_656:
             self.kv = torch.from_numpy(x.kv).to(self.device)

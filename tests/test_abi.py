@@ -69,6 +69,52 @@ def test_batch_build_rejects_bad_lengths(L):
     assert rc == _lib.SMLA_E_WORKSPACE
 
 
+def test_batch_build_pos_validation(L):
+    # explicit positions: inside [0, kv_len), non-decreasing within a request (repeats allowed)
+    out = _lib.Batch()
+    n_q = np.array([3, 2], np.int32)
+    kv = np.array([10, 6], np.int64)
+
+    def build(pos):
+        p = None if pos is None else np.asarray(pos, np.int64)
+        return L.smla_batch_build_pos(2, n_q.ctypes.data, kv.ctypes.data,
+                                      None if p is None else p.ctypes.data, FAKE, 64, None,
+                                      ctypes.byref(out))
+
+    # every check passes and only the (deliberately small) table is refused
+    assert build([4, 4, 9, 0, 5]) == _lib.SMLA_E_WORKSPACE
+    assert build([0, 0, 0, 5, 5]) == _lib.SMLA_E_WORKSPACE
+    assert build(None) == _lib.SMLA_E_WORKSPACE
+    assert build([4, 3, 9, 0, 5]) == _lib.SMLA_E_INVALID and "request 0 token 1" in _lib.last_error()
+    assert build([4, 4, 10, 0, 5]) == _lib.SMLA_E_INVALID  # position == kv_len
+    assert build([4, 4, 9, -1, 5]) == _lib.SMLA_E_INVALID
+    assert build([4, 4, 9, 5, 6]) == _lib.SMLA_E_INVALID and "request 1 token 1" in _lib.last_error()
+
+
+def test_dcp_shard_positions():
+    # a shard's rows and its tokens' local positions, against counting the shard's rows that
+    # each token sees one by one
+    from sparse_mla_attention_indexer_amd import ops
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        B = int(rng.integers(1, 4))
+        n = int(rng.integers(1, 9))
+        n_q = rng.integers(1, 6, size=B)
+        kv_len = n_q + rng.integers(n, 60, size=B)
+        for s in range(n):
+            rows, pos = ops.dcp_shard_positions(n_q, kv_len, n, s)
+            t = 0
+            for b in range(B):
+                owned = [g for g in range(int(kv_len[b])) if g % n == s]
+                assert rows[b] == len(owned)
+                for j in range(int(n_q[b])):
+                    P = int(kv_len[b] - n_q[b] + j)
+                    assert pos[t] == sum(1 for g in owned if g <= P) - 1
+                    t += 1
+    with pytest.raises(ValueError):
+        ops.dcp_shard_positions([2], [3], 8, 5)  # position 1 sees no row of shard 5
+
+
 def test_table_bytes_bounds(L):
     assert L.smla_batch_table_bytes(0, 1, 1) == 0
     assert L.smla_batch_table_bytes(1, 32768, 32768) > 0
@@ -137,14 +183,18 @@ def test_dcp_merge_validation(L):
     def merge(**kw):
         a = {**ok, **kw}
         return L.smla_topk_merge(a["total_q"], a["n_lists"], a["k_in"], FAKE, FAKE, a["stride"],
-                                 a["flt"], a["top_k"], FAKE, None, None)
+                                 a["flt"], a["top_k"], FAKE, None, a.get("local"), None)
 
     assert merge(n_lists=0) == _lib.SMLA_E_INVALID
     assert merge(n_lists=9) == _lib.SMLA_E_UNSUPPORTED   # 9 x 2048 candidates > 16,384
     assert merge(top_k=2049) == _lib.SMLA_E_UNSUPPORTED
     assert merge(stride=100) == _lib.SMLA_E_INVALID
     assert merge(flt=2) == _lib.SMLA_E_INVALID
-    assert L.smla_topk_merge(4, 8, 2048, None, FAKE, 4 * 2048, 0, 2048, FAKE, None, None) == _lib.SMLA_E_INVALID
+    assert L.smla_topk_merge(4, 8, 2048, None, FAKE, 4 * 2048, 0, 2048, FAKE, None, None,
+                             None) == _lib.SMLA_E_INVALID
+    # the per-shard local lists: aligned, and at most 64 lists
+    assert merge(local=FAKE + 2) == _lib.SMLA_E_INVALID
+    assert merge(n_lists=65, k_in=16, stride=4 * 16, local=FAKE) == _lib.SMLA_E_UNSUPPORTED
     assert L.smla_dcp_local_indices(4, 2049, FAKE, 8, FAKE, None) == _lib.SMLA_E_INVALID
     assert L.smla_dcp_local_indices(4, 2048, FAKE, 0, FAKE, None) == _lib.SMLA_E_INVALID
     assert L.smla_dcp_local_indices(4, 2048, None, 8, FAKE, None) == _lib.SMLA_E_INVALID

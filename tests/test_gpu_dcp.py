@@ -22,24 +22,19 @@ N_SH = 8
 
 
 class Shards:
-    """Shard s of a decode batch (one query token per request): rows g = s, s + 8, ... of each
-    request up to the token's position, uploaded as a batch of its own."""
+    """Shard s of a decode batch: rows g = s, s + 8, ... of each request, uploaded as a batch of
+    its own whose query tokens carry their local positions (with several tokens per request,
+    consecutive global positions give local positions that repeat or step by one)."""
 
     def __init__(self, x, dev: Dev):
-        d = x.dims
-        assert (x.n_q == 1).all()
         self.dev = dev
         self.parts = []
         row0 = np.concatenate([[0], np.cumsum(x.kv_len)[:-1]])
         for s in range(N_SH):
-            lens, rows = [], []
-            for b, kl in enumerate(x.kv_len):
-                p = int(kl) - 1
-                g = np.arange(s, p + 1, N_SH)
-                lens.append(g.size)
-                rows.append(row0[b] + g)
-            rows = np.concatenate(rows)
-            plan = ops.BatchPlan(np.ones(d.batch, np.int32), np.array(lens, np.int64), dev.device)
+            lens, pos = ops.dcp_shard_positions(x.n_q, x.kv_len, N_SH, s)
+            rows = np.concatenate([row0[b] + np.arange(s, int(kl), N_SH) for b, kl in enumerate(x.kv_len)])
+            assert rows.size == lens.sum()
+            plan = ops.BatchPlan(x.n_q, lens, dev.device, positions=pos)
             kv = torch.from_numpy(np.ascontiguousarray(x.kv[rows])).to(dev.device)
             k_idx = torch.from_numpy(np.ascontiguousarray(x.k_idx[rows])).to(dev.device)
             self.parts.append((plan, kv, k_idx))
@@ -53,11 +48,10 @@ class Shards:
                              workspace=ops.topk_workspace(plan, 64, 128, top_k))
         return idx, sc
 
-    def attention(self, merged_idx):
+    def attention(self, local):
         d = self.dev.x.dims
         outs = torch.empty((N_SH, d.total_q, d.H, d.D_v), dtype=torch.bfloat16, device=self.dev.device)
         lses = torch.empty((N_SH, d.total_q, d.H), dtype=torch.float32, device=self.dev.device)
-        local = ops.dcp_local_indices(merged_idx, N_SH)
         for s, (plan, kv, _) in enumerate(self.parts):
             ops.sparse_mla(plan, self.dev.q, kv, d.kv_format, d.D_v, local[s], d.sm_scale, decode=True,
                            out=outs[s], lse=lses[s])
@@ -67,21 +61,24 @@ class Shards:
 def _run(x, label, sample):
     d = x.dims
     dev = Dev(x)
-    say(f"[case] dcp x{N_SH} {label}: B={d.batch} kv_len={int(x.kv_len[0])}")
+    say(f"[case] dcp x{N_SH} {label}: B={d.batch} n_q={int(x.n_q[0])} kv_len={int(x.kv_len[0])}")
     ref_idx, ref_sc = dev.topk()
     sh = Shards(x, dev)
     lists_i, lists_s = sh.topk_lists(d.top_k)
-    idx, sc = ops.topk_merge(lists_i, lists_s, d.top_k)
+    local = torch.empty_like(lists_i)
+    idx, sc = ops.topk_merge(lists_i, lists_s, d.top_k, local=local)
     torch.cuda.synchronize()
     idx_np, sc_np = idx.cpu().numpy(), sc.cpu().numpy()
     assert np.array_equal(idx_np, ref_idx), "merged selection differs from the unsharded one"
     assert np.array_equal(sc_np, ref_sc)
+    # the merge's per-shard lists are what dcp_local_indices cuts out of the merged selection
+    assert np.array_equal(local.cpu().numpy(), ops.dcp_local_indices(idx, N_SH).cpu().numpy())
     li, ls = lists_i.cpu().numpy(), lists_s.cpu().numpy()
     for t in sample:
         oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], d.top_k)
         o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
         assert np.array_equal(idx_np[t], oi[o]) and np.array_equal(sc_np[t], os_[o]), t
-    out, lse = sh.attention(idx)
+    out, lse = sh.attention(local)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_mla(x, ref_idx[sample], sample)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)[sample]
@@ -102,12 +99,56 @@ def test_dcp_decode_batch_full_size():
     _run(x, "decode batch", np.array([0, 17, 31]))
 
 
+def test_dcp_mtp_small():
+    # four query tokens per request (MTP drafts): each shard sees local positions that repeat
+    x = W.generate(W.small_big_dims(batch=2, n_q=4, cached=20000))
+    _run(x, "2 x 4 after 20000", np.arange(8))
+
+
+def test_dcp_mtp_full_size():
+    # the long-context MTP decode: 4 requests x 4 tokens after 1,048,576 cached rows, shards of
+    # 131,072 rows each
+    x = W.generate(W.config_dims(4))
+    _run(x, "4 x 4 after 1048576", np.array([0, 3, 6, 9, 12, 15]))
+
+
+def _local_of(g, n_sh, top_k):
+    """Every shard's part of merged global indices g [top_k]: ascending local indices, then -1."""
+    out = np.full((n_sh, top_k), -1, np.int32)
+    for s in range(n_sh):
+        sel = g[(g >= 0) & (g % n_sh == s)] // n_sh
+        out[s, :sel.size] = sel
+    return out
+
+
+def _check_merge(li, ls, top_k, fp, label):
+    """The library's merge (with its per-shard local lists) against the oracle's merge of the
+    same lists, token by token."""
+    n_sh, total_q, _ = li.shape
+    dv = torch.device("cuda:0")
+    pad = np.float32(-1.0).view(np.int32) if fp else -1
+    local = torch.full((n_sh, total_q, top_k), -7, dtype=torch.int32, device=dv) if n_sh <= 64 else None
+    idx, sc = ops.topk_merge(torch.from_numpy(li).to(dv), torch.from_numpy(ls).to(dv), top_k,
+                             float_scores=fp, local=local)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    loc = None if local is None else local.cpu().numpy()
+    for t in range(total_q):
+        oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], top_k)
+        o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
+        ref_s = np.where(oi[o] < 0, pad, os_[o])
+        assert np.array_equal(idx[t], oi[o]) and np.array_equal(sc[t], ref_s), (label, top_k, t)
+        if loc is not None:
+            assert np.array_equal(loc[:, t], _local_of(oi[o], n_sh, top_k)), (label, top_k, t)
+
+
+@pytest.mark.parametrize("order", ["ascending", "shuffled"])
 @pytest.mark.parametrize("values", [3, 1 << 30, "fp32"])
-def test_topk_merge_against_oracle(values):
-    # random per-shard lists (ascending local indices, scores with heavy ties or none, or fp32
-    # bit patterns), k below, at and above the union's size
+def test_topk_merge_against_oracle(values, order):
+    # random per-shard lists (scores with heavy ties or none, or fp32 bit patterns), k below, at
+    # and above the union's size; ascending lists take the search-based order, shuffled ones the
+    # sort
     fp = values == "fp32"
-    rng = np.random.default_rng(7 if fp else values & 0xFFFF)
+    rng = np.random.default_rng((7 if fp else values & 0xFFFF) + (order == "shuffled"))
     total_q, k_in = 5, 2048
     li = np.full((N_SH, total_q, k_in), -1, np.int32)
     ls = np.full((N_SH, total_q, k_in), -1, np.int32)
@@ -119,17 +160,33 @@ def test_topk_merge_against_oracle(values):
                 ls[s, t, :n] = rng.gamma(2.0, 30.0, size=n).astype(np.float32).view(np.int32)
             else:
                 ls[s, t, :n] = rng.integers(0, values, size=n)
-    dv = torch.device("cuda:0")
-    pad = np.float32(-1.0).view(np.int32) if fp else -1
+            if order == "shuffled":
+                p = rng.permutation(k_in)
+                li[s, t], ls[s, t] = li[s, t, p], ls[s, t, p]
+    say(f"[case] topk_merge values={values} order={order}")
     for top_k in (2048, 1, 100):
-        idx, sc = ops.topk_merge(torch.from_numpy(li).to(dv), torch.from_numpy(ls).to(dv), top_k,
-                                 float_scores=fp)
-        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        _check_merge(li, ls, top_k, fp, f"{values} {order}")
+
+
+@pytest.mark.parametrize("n_sh,k_in", [(7, 1000), (3, 37), (100, 150), (64, 256)])
+def test_topk_merge_shapes(n_sh, k_in):
+    # ragged list lengths (not a multiple of a wave), more lists than the search-based order
+    # takes (100: sorted), and the most it takes (64); one token's lists hold padding in the
+    # middle (taken as unordered, so sorted)
+    rng = np.random.default_rng(n_sh * 1000 + k_in)
+    total_q = 3
+    li = np.full((n_sh, total_q, k_in), -1, np.int32)
+    ls = np.full((n_sh, total_q, k_in), -1, np.int32)
+    for s in range(n_sh):
         for t in range(total_q):
-            oi, os_ = oracle.topk_merge(li[:, t], ls[:, t], top_k)
-            o = np.argsort(np.where(oi < 0, np.iinfo(np.int64).max, oi.astype(np.int64)), kind="stable")
-            ref_s = np.where(oi[o] < 0, pad, os_[o])
-            assert np.array_equal(idx[t], oi[o]) and np.array_equal(sc[t], ref_s), (top_k, t)
+            n = k_in if t != 1 else k_in // 2
+            li[s, t, :n] = np.sort(rng.choice(50000, size=n, replace=False))
+            ls[s, t, :n] = rng.integers(0, 1 << 20, size=n)
+            if t == 2 and s == n_sh // 2 and n > 2:  # a hole: -1 between valid entries
+                li[s, t, n // 2], ls[s, t, n // 2] = -1, -1
+    say(f"[case] topk_merge shapes n_sh={n_sh} k_in={k_in}")
+    for top_k in (2048, 333, 1):
+        _check_merge(li, ls, top_k, False, f"{n_sh}x{k_in}")
 
 
 def test_local_indices_and_lse_merge_small():
