@@ -98,6 +98,62 @@ __device__ __forceinline__ uint32_t relu_weighted_sum(const v16i& acc0, const v1
   return (uint32_t)b[0] + (uint32_t)b[1];
 }
 
+// With the weights folded into the queries: the lane's key score is the plain sum over its 32
+// heads of ReLU(dot), plus the other lane half's; one max per value and one three-input add per
+// two values.
+__device__ __forceinline__ uint32_t relu_sum(const v16i& acc0, const v16i& acc1) {
+  uint32_t ps[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    ps[r & 3] = (uint32_t)max(acc0[r], 0) + (uint32_t)max(acc1[r], 0) + ps[r & 3];
+  const uint32_t sum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  const auto b = __builtin_amdgcn_permlane32_swap(sum, sum, false, false);
+  return (uint32_t)b[0] + (uint32_t)b[1];
+}
+
+// The weights folded into a lane's query fragments (heads col and 32 + col; wown = their
+// weights): w_h ReLU(q_h . k) = ReLU((w_h q_h) . k) exactly when w_h >= 0 and every w_h q_h[d]
+// fits int8, and then the epilogue needs no multiplies. Returns whether that holds for the whole
+// wave (one query token), and then leaves the folded fragments in qa; otherwise qa is unchanged.
+// The check keeps each head's smallest and largest byte; the fold multiplies the bytes two at a
+// time in 16-bit halves and keeps each product's low byte (the same for signed and unsigned).
+typedef unsigned short fold_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bool fold_weights(v4i (&qa)[2][4], const int (&wown)[2]) {
+  bool ok = true;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    int mx = -128, mn = 127;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = (uint32_t)qa[mt][j][e];
+        const int b0 = (int)(x << 24) >> 24, b1 = (int)(x << 16) >> 24;
+        const int b2 = (int)(x << 8) >> 24, b3 = (int)x >> 24;
+        mx = max(mx, max(max(b0, b1), max(b2, b3)));
+        mn = min(mn, min(min(b0, b1), min(b2, b3)));
+      }
+    const int w = wown[mt];
+    ok = ok && w >= 0 && w * mx <= 127 && w * mn >= -128;
+  }
+  if (!__all(ok)) return false;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const fold_u16x2 w2 = {(unsigned short)wown[mt], (unsigned short)wown[mt]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = (uint32_t)qa[mt][j][e];
+        const fold_u16x2 ev = __builtin_bit_cast(fold_u16x2, x & 0x00FF00FFu) * w2;
+        const fold_u16x2 od = __builtin_bit_cast(fold_u16x2, (x >> 8) & 0x00FF00FFu) * w2;
+        qa[mt][j][e] = (int)((__builtin_bit_cast(uint32_t, ev) & 0x00FF00FFu) |
+                             ((__builtin_bit_cast(uint32_t, od) & 0x00FF00FFu) << 8));
+      }
+  }
+  return true;
+}
+
 // FP8 keys: fp32 weights of a lane's heads (same head order as HeadW), per query token.
 struct HeadWF {
   float lo[16], hi[16];
@@ -220,7 +276,8 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
                                              int step, const int8_t* __restrict__ q_idx,
                                              const int8_t* __restrict__ k_idx,
                                              const float* __restrict__ k_scale,
-                                             const HeadW& wl, const float* __restrict__ w_f,
+                                             const HeadW& wl, const int32_t* __restrict__ w_i,
+                                             const float* __restrict__ w_f,
                                              int32_t* __restrict__ out_row,
                                              int* lh, v4i (*ring)[256], float (*scl)[64]) {
   using Acc = std::conditional_t<F8, v16f, v16i>;
@@ -239,8 +296,12 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
   HeadWF wf;
+  int wown[2] = {0, 0};
   if constexpr (F8) wf = load_head_wf(w_f + t * IDX_H);
+  else wown[0] = w_i[col], wown[1] = w_i[32 + col];
   idx_wait_loads();  // the fragments are in before any key load goes out
+  bool fold = false;
+  if constexpr (!F8) fold = fold_weights(qa, wown);
 
   // Scores go out through a buffer resource whose range ends at key `last`: the hardware drops
   // the stores of keys past it, of the upper lane half and of the placeholder stores below, so
@@ -288,10 +349,12 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
     }
   };
   // lane holds key `col`, heads 32*mt + 8*(r/4) + 4*half + r%4
-  auto epilogue = [&](const Acc& acc0, const Acc& acc1, int i) {
+  auto epilogue = [&](auto foldc, const Acc& acc0, const Acc& acc1, int i) {
     uint32_t sum;
     if constexpr (F8)
       sum = __builtin_bit_cast(uint32_t, relu_weighted_sum_f(acc0, acc1, wf) * scl[i % KR][col]);
+    else if constexpr (decltype(foldc)::value)
+      sum = relu_sum(acc0, acc1);
     else
       sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = s_begin + i * step + col;
@@ -312,20 +375,25 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
   dma(2);
   placeholder_store();
   idx_wait_vmcnt<2 * OPS + 1>();  // tile 0: after it, a store, tile 1, a store, tile 2, a store
-  Acc a0[2], a1[2];
-  products(0, a0[0], a1[0]);
+  // the loop is compiled once per epilogue (folded weights or not: uniform per wave)
+  auto run = [&](auto foldc) {
+    Acc a0[2], a1[2];
+    products(0, a0[0], a1[0]);
 #pragma unroll 1
-  for (int i = 0; i < ntile; i += 2) {
-    dma(i + 3);
-    idx_wait_vmcnt<2 * OPS>();
-    if (i + 1 < ntile) products(i + 1, a0[1], a1[1]);
-    epilogue(a0[0], a1[0], i);
-    if (i + 1 >= ntile) break;
-    dma(i + 4);
-    idx_wait_vmcnt<2 * OPS>();
-    if (i + 2 < ntile) products(i + 2, a0[0], a1[0]);
-    epilogue(a0[1], a1[1], i + 1);
-  }
+    for (int i = 0; i < ntile; i += 2) {
+      dma(i + 3);
+      idx_wait_vmcnt<2 * OPS>();
+      if (i + 1 < ntile) products(i + 1, a0[1], a1[1]);
+      epilogue(foldc, a0[0], a1[0], i);
+      if (i + 1 >= ntile) break;
+      dma(i + 4);
+      idx_wait_vmcnt<2 * OPS>();
+      if (i + 2 < ntile) products(i + 2, a0[0], a1[0]);
+      epilogue(foldc, a0[1], a1[1], i + 1);
+    }
+  };
+  if (fold) run(std::true_type{});
+  else run(std::false_type{});
   idx_wait_vmcnt<0>();  // no key load may still be writing this wave's ring when it returns
 }
 
@@ -350,7 +418,8 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
                                                    const int8_t* __restrict__ q_idx,
                                                    const int8_t* __restrict__ k_idx,
                                                    const float* __restrict__ k_scale,
-                                                   const HeadW& wl, const float* __restrict__ w_f,
+                                                   const HeadW& wl, const int32_t* __restrict__ w_i,
+                                                   const float* __restrict__ w_f,
                                                    int32_t* __restrict__ scores, int64_t stride,
                                                    bool hist_on,
                                                    unsigned (*lhist)[TOPK_BINS / 2],
@@ -380,8 +449,12 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
     for (int j = 0; j < 4; ++j)
       qa[mt][j] = *reinterpret_cast<const v4i*>(qbase + (32 * mt + col) * IDX_D + 64 * half + 16 * j);
   HeadWF wf;
+  int wown[2] = {0, 0};
   if constexpr (F8) wf = load_head_wf(w_f + t * IDX_H);
+  else wown[0] = w_i[col], wown[1] = w_i[32 + col];
   idx_wait_loads();  // the fragments are in before any key load goes out
+  bool fold = false;
+  if constexpr (!F8) fold = fold_weights(qa, wown);
 
   // key loads: wave w loads tile SG*g + w of group g; instruction d covers slots 64d .. 64d+63
   const int8_t* kbase = k_idx + tk.row_start * IDX_D + 16 * (2 * 0 + half);
@@ -402,11 +475,13 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
       __builtin_amdgcn_make_buffer_rsrc(out_row, 0, active ? (last + 1) * 4 : 0, 0x00020000);
   unsigned* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
 
-  auto epilogue = [&](const Acc& acc0, const Acc& acc1, int k) {
+  auto epilogue = [&](auto foldc, const Acc& acc0, const Acc& acc1, int k) {
     uint32_t sum;
     if constexpr (F8)
       sum = __builtin_bit_cast(uint32_t, relu_weighted_sum_f(acc0, acc1, wf) *
                                              scl[((k / SG) % SRING) * SG + k % SG][col]);
+    else if constexpr (decltype(foldc)::value)
+      sum = relu_sum(acc0, acc1);
     else
       sum = relu_weighted_sum(acc0, acc1, wl);
     const int key = sg.s0 + 32 * k + col;
@@ -438,34 +513,39 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
       }
     }
   };
-  auto group_tiles = [&](auto ntw, int g, int first, int stride) {
+  auto group_tiles = [&](auto foldc, auto ntw, int g, int first, int stride) {
     constexpr int NTW = decltype(ntw)::value;
     Acc a0[2], a1[2];
     products(g, first, a0[0], a1[0]);
 #pragma unroll
     for (int u = 1; u < NTW; ++u) {
       products(g, first + stride * u, a0[u & 1], a1[u & 1]);
-      epilogue(a0[(u - 1) & 1], a1[(u - 1) & 1], SG * g + first + stride * (u - 1));
+      epilogue(foldc, a0[(u - 1) & 1], a1[(u - 1) & 1], SG * g + first + stride * (u - 1));
     }
-    epilogue(a0[(NTW - 1) & 1], a1[(NTW - 1) & 1], SG * g + first + stride * (NTW - 1));
+    epilogue(foldc, a0[(NTW - 1) & 1], a1[(NTW - 1) & 1], SG * g + first + stride * (NTW - 1));
   };
-
+  // the group loop, compiled once per epilogue (folded weights or not: uniform per wave, and the
+  // two loops need different registers live)
+  auto run = [&](auto foldc) {
 #pragma unroll 1
-  for (int g = 0; g < ngroup; ++g) {
-    // this wave's loads of group g have landed, then everyone's; group g+1 goes into the slots of
-    // group g-1, which every wave has finished
-    idx_wait_vmcnt<0>();
-    idx_lds_barrier();
-    if (g + 1 < ngroup) load_group(g + 1);
-    if (active) {
-      // software pipelined over the wave's tiles of the group: the products of tile u+1 are
-      // issued before the ReLU/weight epilogue of tile u, so the matrix cores and the vector
-      // ALUs work at the same time (tiles past the segment compute on clamped keys; their
-      // stores fall outside the buffer range and are dropped)
-      if (qpw == 1) group_tiles(std::integral_constant<int, SG>{}, g, 0, 1);
-      else group_tiles(std::integral_constant<int, SG / 2>{}, g, par, 2);
+    for (int g = 0; g < ngroup; ++g) {
+      // this wave's loads of group g have landed, then everyone's; group g+1 goes into the slots
+      // of group g-1, which every wave has finished
+      idx_wait_vmcnt<0>();
+      idx_lds_barrier();
+      if (g + 1 < ngroup) load_group(g + 1);
+      if (active) {
+        // software pipelined over the wave's tiles of the group: the products of tile u+1 are
+        // issued before the ReLU/weight epilogue of tile u, so the matrix cores and the vector
+        // ALUs work at the same time (tiles past the segment compute on clamped keys; their
+        // stores fall outside the buffer range and are dropped)
+        if (qpw == 1) group_tiles(foldc, std::integral_constant<int, SG>{}, g, 0, 1);
+        else group_tiles(foldc, std::integral_constant<int, SG / 2>{}, g, par, 2);
+      }
     }
-  }
+  };
+  if (fold) run(std::true_type{});
+  else run(std::false_type{});
   idx_wait_vmcnt<0>();
 }
 
@@ -499,8 +579,8 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
   // the weights of this lane's heads (w < 2^10 by the weight contract; F8: per token, loaded
   // with the token's query)
   HeadW wl;
+  const int32_t* const w_i = F8 ? nullptr : static_cast<const int32_t*>(w);
   if constexpr (!F8) {
-    const int32_t* w_i = static_cast<const int32_t*>(w);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int h = 8 * (r >> 2) + 4 * half + (r & 3);
@@ -522,7 +602,7 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
       __syncthreads();
     }
     if constexpr (MULTI) {
-      indexer_shared_seg<F8>(sg, toks, q_idx, k_idx, k_scale, wl, w_f, scores, stride, hist_on,
+      indexer_shared_seg<F8>(sg, toks, q_idx, k_idx, k_scale, wl, w_i, w_f, scores, stride, hist_on,
                              reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring,
                              scl);
     } else {
@@ -531,7 +611,7 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
       const Tok tk = toks[t];
       int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
       int* lh = hist_on ? lhist_base : nullptr;
-      indexer_wave<F8>(tk, t, sg.s0 + 32 * wave, sg.s1, 128, q_idx, k_idx, k_scale, wl, w_f,
+      indexer_wave<F8>(tk, t, sg.s0 + 32 * wave, sg.s1, 128, q_idx, k_idx, k_scale, wl, w_i, w_f,
                        out_row, lh, ring + KR * wave, scl + KR * wave);
     }
     __syncthreads();  // the ring (and the histograms) are reused by the next segment

@@ -67,6 +67,44 @@ def test_big_shape_scores_full_matrix_mfma():
         assert (s[t, p + 1:] == -1).all()
 
 
+def _fold_edge_queries(x):
+    """Per token, queries on both sides of the weight fold's limit (every w_h q[d] inside int8):
+    t % 3 == 0 one value one past it (that token is scored without folding), t % 3 == 1 the
+    extreme values that still fold, t % 3 == 2 unchanged."""
+    w = x.w.astype(np.int64)
+    for t in range(x.q_idx.shape[0]):
+        if t % 3 == 0:
+            h = (7 * t) % 64
+            x.q_idx[t, h, 3] = min(127, 127 // w[h] + 1)
+        elif t % 3 == 1:
+            x.q_idx[t, :, 0] = (127 // w).astype(np.int8)
+            x.q_idx[t, :, 1] = (-(128 // w)).astype(np.int8)
+
+
+@pytest.mark.parametrize("n_q,batch,cached", [(37, 2, 300), (1, 6, 5000)])
+def test_indexer_weight_fold_limits(n_q, batch, cached):
+    # tokens whose w q fits int8 are scored with the weights folded into the queries, the others
+    # with the weights applied after the ReLU; both must match the oracle exactly, in the
+    # multi-token kernel (n_q = 37) and the single-token one (decode)
+    import oracle
+
+    x = W.generate(W.small_big_dims(batch=batch, n_q=n_q, cached=cached))
+    _fold_edge_queries(x)
+    say(f"[case] weight fold limits B={batch} n_q={n_q} cached={cached}")
+    dev = Dev(x)
+    s = dev.scores()
+    d = x.dims
+    for t in range(d.total_q):
+        b, j = divmod(t, d.n_q)
+        p = d.cached + j
+        keys = x.k_idx[b * d.max_kv: b * d.max_kv + p + 1]
+        assert np.array_equal(s[t, : p + 1], oracle.indexer_scores(x.q_idx[t], keys, x.w)), t
+    tokens = np.arange(d.total_q)
+    idx, sc = dev.topk()
+    ref_idx, ref_sc = oracle_topk(x, tokens)
+    assert_topk_equal(idx, sc, ref_idx, ref_sc, "fold limits")
+
+
 def test_big_shape_prefill_boundary_positions():
     # positions 2000..2299 cross p + 1 = k - 1, k, k + 1
     _full_case(W.generate(W.small_big_dims(n_q=300, cached=2000)), "prefill 300 after 2000")
