@@ -889,27 +889,28 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
 // ---- rows of top_k < n <= TOPK_LDS_MAX: one 512-thread workgroup per row, in registers -------
 // Each of the 8 waves owns a contiguous chunk of 64 V scores of the row (V = 8, 16, 32 or 64, the
 // smallest that covers the row), held in registers; the score histogram is built in LDS from
-// them; then, as for the longer rows, one pass counts the elements above b* and gathers the b*
-// candidates, one wave finds the exact cut among them, and a second pass over the registers
-// writes every selected index at its rank. 40 KB of LDS, so two rows share a CU and hide each
-// other's latencies.
+// them; then one pass counts the elements above b* and gathers the b* candidates, each wave into
+// its own slice of the candidate buffer (a wave-uniform counter, no atomics); one wave finds the
+// exact cut among them, every wave counts its selected candidates, and a second pass over the
+// registers writes every selected index at its rank. The writes are branch-free buffer
+// stores whose offsets fall outside the output row unless the element is selected. 41 KB of
+// LDS, so two rows share a CU and hide each other's latencies.
 constexpr int NT_B = 512;
 constexpr int NW_B = NT_B / 64;
+constexpr int CAND_W = TOPK_CAND_CAP / NW_B;  // candidate slots per wave
 
 template <bool FB, int V>
 __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, int n, int top_k,
                                                int32_t* __restrict__ oi, int32_t* __restrict__ os,
                                                int* hist, uint32_t* klo, uint32_t* khi,
                                                int* hist2, int* red, int* cut, uint64_t* pm,
-                                               int* nk, int* wsel, int* woff) {
+                                               int* wcnt, int* wsel, int* woff) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int ib = wv * (64 * V) + lane;
-  const int rem = n - ib;
-  const bool full = n >= (wv + 1) * (64 * V);
+  const int rem = n - ib;  // this lane's element u is in the row iff 64 u < rem
   uint32_t v[V];
   lane_load<V>(v, row, n, ib, 0);
   for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = 0;
-  if (threadIdx.x == 0) *nk = 0;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < V; ++u)
@@ -920,53 +921,110 @@ __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, 
   const int need = top_k - cut[1];
   const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
   const uint32_t hm1 = bin_hm1<FB>(bstar);
-  const int above = full ? pass_gather<V, true>(v, ib, rem, lo, hm1, klo, khi, nk, TOPK_CAND_CAP)
-                         : pass_gather<V, false>(v, ib, rem, lo, hm1, klo, khi, nk, TOPK_CAND_CAP);
-  if (lane == 0) wsel[wv] = above;
+  // count above b*, gather the b* candidates into this wave's slice
+  const uint64_t below_lane = (1ull << lane) - 1ull;
+  int above = 0, nc = 0;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const uint32_t x = v[u];
+    const bool in = 64 * u < rem;
+    const uint64_t ma = __ballot(in && x > hm1);
+    const bool c = in && x >= lo && x <= hm1;
+    const uint64_t mc = __ballot(c);
+    above += __popcll(ma);
+    if (mc) {  // rare: the b* candidates go to this wave's slice, a wave-uniform count ahead
+      const int slot = nc + __popcll(mc & below_lane);
+      if (c && slot < CAND_W) {
+        klo[wv * CAND_W + slot] = 0xFFFFFFFFu - (uint32_t)(ib + 64 * u);
+        khi[wv * CAND_W + slot] = x;
+      }
+      nc += __popcll(mc);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one element's masks live at a time (SGPR pressure)
+  }
+  if (lane == 0) {
+    wcnt[wv] = nc;
+    wsel[wv] = above;
+  }
   __syncthreads();
-  const int ncand = *nk;
+  int ncand = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int w = 0; w < NW_B; ++w) {
+    ncand += wcnt[w];
+    overflow |= wcnt[w] > CAND_W;
+  }
   uint64_t ck;
-  if (ncand <= TOPK_CAND_CAP) {
-    if (wv == 0) {
+  if (!overflow) {
+    if (wv == 0) {  // candidate i lives in the slice of the wave whose running count passes i
       uint64_t pf, mk;
-      wave_radix_cut([&](int i) { return ((uint64_t)khi[i] << 32) | klo[i]; }, ncand, need, hist2,
-                     &pf, &mk);
+      wave_radix_cut(
+          [&](int i) {
+            int w = 0, base = 0;
+#pragma unroll
+            for (int k = 0; k < NW_B - 1; ++k) {
+              const bool past = i >= base + wcnt[w];
+              base += past ? wcnt[w] : 0;
+              w += past;
+            }
+            const int sl = w * CAND_W + (i - base);
+            return ((uint64_t)khi[sl] << 32) | klo[sl];
+          },
+          ncand, need, hist2, &pf, &mk);
       if (lane == 0) pm[0] = cut_key(pf, lo);
       (void)mk;
     }
     __syncthreads();
     ck = pm[0];
-    // selected candidates per owning wave (the index says which wave holds the score)
-    for (int c = threadIdx.x; c < ncand; c += NT_B) {
-      const uint64_t key = ((uint64_t)khi[c] << 32) | klo[c];
-      if (key >= ck) atomicAdd(&wsel[(int)(0xFFFFFFFFu - klo[c]) / (64 * V)], 1);
+    // every wave counts its selected candidates
+    int sc = 0;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const int sl = wv * CAND_W + c0 + lane;
+      const bool f = c0 + lane < nc && (((uint64_t)khi[sl] << 32) | klo[sl]) >= ck;
+      sc += __popcll(__ballot(f));
     }
+    if (lane == 0) wsel[wv] += sc;
   } else {
-    // more candidates than LDS holds (heavy ties): the exact cut by radix select over the row,
-    // then every wave counts its own selected elements
+    // more candidates than a wave's slice holds (heavy ties): the exact cut by radix select over
+    // the row, then every wave counts its own selected elements
     radix_cut<NT_B>(
         n, need, [&](int i) { return sel_key(row[i], i); },
         [&](int i) { return score_bin<FB>((uint32_t)row[i]) == bstar; }, hist2, red, cut, pm);
     ck = cut_key(pm[0], lo);
-    const int cnt = full ? pass_count<V, true>(v, ib, rem, (uint32_t)(ck >> 32), (uint32_t)ck)
-                         : pass_count<V, false>(v, ib, rem, (uint32_t)(ck >> 32), (uint32_t)ck);
+    const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const uint32_t x = v[u];
+      const bool f = 64 * u < rem && (x > th || (x == th && 0xFFFFFFFFu - (uint32_t)(ib + 64 * u) >= tl));
+      cnt += __popcll(__ballot(f));
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (lane == 0) wsel[wv] = cnt;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < NW_B; ++w) {
-      woff[w] = acc;
-      acc += wsel[w];
-    }
-  }
-  __syncthreads();
+  int pos = 0;
+#pragma unroll
+  for (int w = 0; w < NW_B; ++w) pos += w < wv ? wsel[w] : 0;
+  // write: each selected element's index (and score) at its rank; other lanes' offsets fall
+  // outside the row's range and the hardware drops those stores
   const uint32_t th = (uint32_t)(ck >> 32), tl = (uint32_t)ck;
-  const int pos = __builtin_amdgcn_readfirstlane(woff[wv]);
-  if (full)
-    pass_write<V, true>(v, ib, rem, th, tl, pos, top_k, oi, os);
-  else
-    pass_write<V, false>(v, ib, rem, th, tl, pos, top_k, oi, os);
+  const __amdgpu_buffer_rsrc_t rs_i = __builtin_amdgcn_make_buffer_rsrc(oi, 0, top_k * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_s =
+      __builtin_amdgcn_make_buffer_rsrc(os ? os : oi, 0, os ? top_k * 4 : 0, 0x00020000);
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const uint32_t x = v[u];
+    const int i = ib + 64 * u;
+    const bool f = 64 * u < rem && (x > th || (x == th && 0xFFFFFFFFu - (uint32_t)i >= tl));
+    const uint64_t m = __ballot(f);
+    const int p = pos + __popcll(m & below_lane);
+    const int off = f && p < top_k ? 4 * p : 0x7FFFFFF0;
+    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)i, rs_i, off, 0, 0);
+    if (os) __builtin_amdgcn_raw_buffer_store_b32(x, rs_s, off, 0, 0);
+    pos += __popcll(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <bool FB>
@@ -981,8 +1039,7 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
   __shared__ int red[NW_B + 1];
   __shared__ int cut[2];
   __shared__ uint64_t pm[2];
-  __shared__ int nk;
-  __shared__ int wsel[NW_B], woff[NW_B];
+  __shared__ int wcnt[NW_B], wsel[NW_B], woff[NW_B];
   const int64_t t = blockIdx.x;
   const Tok tk = toks[t];
   const int n = tk.pos + 1;
@@ -999,13 +1056,13 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
   }
   static_assert(NT_B * 64 == TOPK_LDS_MAX, "8 waves x 64 x 64 scores cover the longest short row");
   if (n <= NT_B * 8)
-    topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+    topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else if (n <= NT_B * 16)
-    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else if (n <= NT_B * 32)
-    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else
-    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, &nk, wsel, woff);
+    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
 }
 
 // ---- segmented rows: count / resolve / emit over TOPK_SEG-candidate segments ---------------
