@@ -78,26 +78,35 @@ size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv);
  * Validate a batch and write its device table. n_q (host) [batch], kv_len (host) [batch] with
  * 1 <= n_q[b] <= kv_len[b] < 2^31 and total rows < 2^40. `table` (device, table_bytes from
  * smla_batch_table_bytes) receives the per-request, per-token and indexer work-item tables.
- * Blocking: returns after the table is on the device. `out` is filled on success.
+ * Blocking: returns after the table is on the device (smla_batch_build_pos with a staging
+ * buffer does the same without waiting). `out` is filled on success.
  */
 int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
                      size_t table_bytes, void* stream, smla_batch* out);
 
 /*
- * smla_batch_build with every query token's position given: pos (host) [total_q], token j of
- * request b at pos[Q_b + j] with 0 <= pos < kv_len[b], non-decreasing within a request; the
- * token uses rows s <= pos. With pos = NULL it is smla_batch_build. Under decode context
- * parallelism ("Serving GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "DCP") a shard holds
- * every n-th row, so the consecutive global positions of a request's tokens (MTP drafts) become
- * local positions that repeat or step by one: shard l of n gives global position P the local
- * position floor((P - l) / n), which needs P >= l. Same table size bound and contract otherwise.
+ * smla_batch_build with every query token's position given, and optionally without waiting.
+ * pos (host, optional) [total_q]: token j of request b at pos[Q_b + j] with 0 <= pos <
+ * kv_len[b], non-decreasing within a request; the token uses rows s <= pos (NULL: the default
+ * positions kv_len - n_q + j). Under decode context parallelism ("Serving GLM-5.3 ... PCP, DCP,
+ * Hybrid HiSparse", section "DCP") a shard holds every n-th row, so the consecutive global
+ * positions of a request's tokens (MTP drafts) become local positions that repeat or step by
+ * one: shard l of n gives global position P the local position floor((P - l) / n), which needs
+ * P >= l. host_staging (host, optional, at least table_bytes): the table is assembled there and
+ * copied to `table` on `stream` without waiting (pinned memory makes the copy truly
+ * asynchronous); the caller keeps it unchanged until the stream has run the copy. NULL: the call
+ * uses its own buffer and returns after the copy, as smla_batch_build does. Same table size
+ * bound and contract otherwise.
  */
 int smla_batch_build_pos(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
-                         const int64_t* pos, void* table, size_t table_bytes, void* stream,
-                         smla_batch* out);
+                         const int64_t* pos, void* host_staging, void* table, size_t table_bytes,
+                         void* stream, smla_batch* out);
 
 /*
- * Indexer scores, full matrix (parity and debugging; O(total_q * max_kv) memory).
+ * Indexer scores, full matrix (parity and debugging; O(total_q * max_kv) memory). The indexer
+ * scores every earlier token of every query token ("Serving GLM-5.3 ... PCP, DCP, Hybrid
+ * HiSparse", sections "Why DP8 and TP8 fall short" and "PCP: split tokens, not heads"; the
+ * formula is in the file preamble).
  * q_idx (device) [total_q, H_I, D_I] int8; k_idx (device) [total_rows, D_I] int8;
  * w (device) [H_I] int32 with w_h >= 0 and sum_h w_h * 2^14 * D_I < 2^31 (so no score can
  * overflow; a violation gives wrong scores, never a fault).
@@ -119,7 +128,9 @@ size_t smla_indexer_topk_workspace_bytes(const smla_batch* b, int32_t H_I, int32
                                          int32_t top_k);
 
 /*
- * Indexer scores followed by the exact per-query top-k (same inputs as smla_indexer_scores).
+ * Indexer scores followed by the exact per-query top-k (same inputs as smla_indexer_scores):
+ * the 2,048 best earlier tokens of each query token that sparse MLA attends over ("Serving
+ * GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why DP8 and TP8 fall short").
  * idx (device) [total_q, top_k] int32: the min(top_k, p+1) local row indices with the largest
  * scores, ties to the lower index (all s <= p when p+1 <= top_k), in ascending index order,
  * then -1 padding. score (device, optional) [total_q, top_k] int32: the score of each selected
@@ -253,7 +264,10 @@ size_t smla_sparse_mla_workspace_bytes(const smla_batch* b, int32_t H, int32_t D
                                        int32_t top_k, int32_t decode);
 
 /*
- * Sparse MLA in MQA form: every head attends over the same selected rows.
+ * Sparse MLA in MQA form: every head attends over the same selected rows ("Serving GLM-5.3 ...
+ * PCP, DCP, Hybrid HiSparse", section "Why the numbers work": one latent row serves all 64
+ * heads, QK over 576 dims and PV over 512, BF16 queries and outputs over 656-byte FP8 rows; the
+ * split-KV merge of _decode is the log-sum-exp merge of section "DCP").
  * q (device) [total_q, H, D_qk] bf16; kv (device) [total_rows] rows of `kv_format`;
  * idx (device) [total_q, top_k] int32 local row indices (any order; -1 entries are skipped;
  * indices above the token's position p are treated like -1, so no row past p is ever read);

@@ -83,7 +83,7 @@ def lib():
         L.smla_batch_table_bytes.argtypes = [i32, i32, i64]
         L.smla_batch_table_bytes.restype = sz
         L.smla_batch_build.argtypes = [i32, P, P, P, sz, P, BP]
-        L.smla_batch_build_pos.argtypes = [i32, P, P, P, P, sz, P, BP]
+        L.smla_batch_build_pos.argtypes = [i32, P, P, P, P, P, sz, P, BP]
         L.smla_indexer_scores.argtypes = [BP, P, P, P, i32, i32, P, P]
         L.smla_indexer_topk_workspace_bytes.argtypes = [BP, i32, i32, i32]
         L.smla_indexer_topk_workspace_bytes.restype = sz

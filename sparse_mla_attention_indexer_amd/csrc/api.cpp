@@ -176,12 +176,12 @@ size_t smla_batch_table_bytes(int32_t batch, int32_t total_q, int64_t max_kv) {
 
 int smla_batch_build(int32_t batch, const int32_t* n_q, const int64_t* kv_len, void* table,
                      size_t table_bytes, void* stream, smla_batch* out) {
-  return smla_batch_build_pos(batch, n_q, kv_len, nullptr, table, table_bytes, stream, out);
+  return smla_batch_build_pos(batch, n_q, kv_len, nullptr, nullptr, table, table_bytes, stream, out);
 }
 
 int smla_batch_build_pos(int32_t batch, const int32_t* n_q, const int64_t* kv_len,
-                         const int64_t* pos, void* table, size_t table_bytes, void* stream,
-                         smla_batch* out) {
+                         const int64_t* pos, void* host_staging, void* table, size_t table_bytes,
+                         void* stream, smla_batch* out) {
   g_err.clear();
   if (batch < 1 || !n_q || !kv_len || !table || !out)
     return fail(SMLA_E_INVALID, "batch >= 1 and non-NULL n_q, kv_len, table, out required");
@@ -236,17 +236,27 @@ int smla_batch_build_pos(int32_t batch, const int32_t* n_q, const int64_t* kv_le
   const size_t need = table_layout(batch, (int32_t)total_q, (int64_t)items.size());
   if (table_bytes < need)
     return fail(SMLA_E_WORKSPACE, "table needs %zu bytes, got %zu", need, table_bytes);
-  std::vector<unsigned char> host(need, 0);
+  // the table is assembled in the caller's staging buffer (copied without waiting), or in a
+  // buffer of the call's own (then the call waits for the copy)
+  std::vector<unsigned char> own;
+  unsigned char* host = static_cast<unsigned char*>(host_staging);
+  if (!host) {
+    own.resize(need);
+    host = own.data();
+  }
+  memset(host, 0, need);
   const size_t off_tok = smla::align_up(sizeof(smla::Req) * batch, 256);
   const size_t off_item = off_tok + smla::align_up(sizeof(smla::Tok) * (size_t)total_q, 256);
-  memcpy(host.data(), req.data(), sizeof(smla::Req) * batch);
-  memcpy(host.data() + off_tok, tok.data(), sizeof(smla::Tok) * (size_t)total_q);
-  if (!items.empty()) memcpy(host.data() + off_item, items.data(), sizeof(smla::Item) * items.size());
+  memcpy(host, req.data(), sizeof(smla::Req) * batch);
+  memcpy(host + off_tok, tok.data(), sizeof(smla::Tok) * (size_t)total_q);
+  if (!items.empty()) memcpy(host + off_item, items.data(), sizeof(smla::Item) * items.size());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(table, host.data(), need, hipMemcpyHostToDevice, s);
+  hipError_t e = hipMemcpyAsync(table, host, need, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(batch table)");
-  e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(batch table)");
+  if (!host_staging) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(batch table)");
+  }
   out->batch = batch;
   out->total_q = (int32_t)total_q;
   out->max_q = max_q;

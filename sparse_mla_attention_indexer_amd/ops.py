@@ -60,7 +60,7 @@ class BatchPlan:
         with torch.cuda.device(self.device):
             check("smla_batch_build_pos",
                   lib().smla_batch_build_pos(B, self.n_q.ctypes.data, self.kv_len.ctypes.data,
-                                             None if pos is None else pos.ctypes.data,
+                                             None if pos is None else pos.ctypes.data, None,
                                              self.table.data_ptr(), nbytes, _stream(self.device),
                                              ctypes.byref(self.desc)))
         self.batch = B

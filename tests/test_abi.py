@@ -78,7 +78,7 @@ def test_batch_build_pos_validation(L):
     def build(pos):
         p = None if pos is None else np.asarray(pos, np.int64)
         return L.smla_batch_build_pos(2, n_q.ctypes.data, kv.ctypes.data,
-                                      None if p is None else p.ctypes.data, FAKE, 64, None,
+                                      None if p is None else p.ctypes.data, None, FAKE, 64, None,
                                       ctypes.byref(out))
 
     # every check passes and only the (deliberately small) table is refused

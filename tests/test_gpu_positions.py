@@ -51,3 +51,35 @@ def test_explicit_positions_topk_and_attention():
             ro, rl = oracle.attend(q_tok, rows, d.kv_format, d.D_v, idx[t], d.sm_scale)
             assert_attn_close(out[t][None], ro[None], lse[t][None], rl[None],
                               f"token {t} p={p} decode={decode}")
+
+
+def test_batch_table_built_without_waiting():
+    # a table assembled in pinned staging memory and copied on the stream without a wait gives
+    # the same selection as the blocking build
+    import ctypes
+    import torch
+    from sparse_mla_attention_indexer_amd import _lib, ops
+
+    x = W.generate(W.small_big_dims(batch=2, n_q=5, cached=3000))
+    d = x.dims
+    say("[case] batch table through pinned staging, no wait")
+    dev = Dev(x)
+    ref_idx, ref_sc = dev.topk()
+    nbytes = dev.plan.table.numel()
+    staging = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    table = torch.empty(nbytes, dtype=torch.uint8, device=dev.device)
+    desc = _lib.Batch()
+    n_q = np.ascontiguousarray(x.n_q, np.int32)
+    kv_len = np.ascontiguousarray(x.kv_len, np.int64)
+    stream = torch.cuda.current_stream(dev.device).cuda_stream
+    _lib.check("smla_batch_build_pos",
+               _lib.lib().smla_batch_build_pos(d.batch, n_q.ctypes.data, kv_len.ctypes.data, None,
+                                               staging.data_ptr(), table.data_ptr(), nbytes, stream,
+                                               ctypes.byref(desc)))
+    plan = ops.BatchPlan.__new__(ops.BatchPlan)
+    plan.__dict__.update(dev.plan.__dict__)
+    plan.table, plan.desc = table, desc
+    idx, sc = ops.indexer_topk(plan, dev.q_idx, dev.k_idx, dev.w, d.top_k,
+                               workspace=ops.topk_workspace(plan, d.H_I, d.D_I, d.top_k))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ref_idx) and np.array_equal(sc.cpu().numpy(), ref_sc)
