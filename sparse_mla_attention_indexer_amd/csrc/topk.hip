@@ -902,7 +902,8 @@ constexpr int CAND_W = TOPK_CAND_CAP / NW_B;  // candidate slots per wave
 template <bool FB, int V>
 __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, int n, int top_k,
                                                int32_t* __restrict__ oi, int32_t* __restrict__ os,
-                                               int* hist, uint32_t* klo, uint32_t* khi,
+                                               int* hist, uint32_t (*whist)[TOPK_BINS / 2],
+                                               uint32_t* klo, uint32_t* khi,
                                                int* hist2, int* red, int* cut, uint64_t* pm,
                                                int* wcnt, int* wsel, int* woff) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -910,28 +911,63 @@ __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, 
   const int rem = n - ib;  // this lane's element u is in the row iff 64 u < rem
   uint32_t v[V];
   lane_load<V>(v, row, n, ib, 0);
-  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = 0;
-  __syncthreads();
+  {  // this wave's histogram: 16-bit counts, two bins per word (a wave holds at most 4,096)
+    uint4* wz = reinterpret_cast<uint4*>(whist[wv]);
+#pragma unroll
+    for (int i = lane; i < TOPK_BINS / 8; i += 64) wz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int u = 0; u < V; ++u)
-    if (64 * u < rem) atomicAdd(&hist[score_bin<FB>(v[u])], 1);
+    if (64 * u < rem) {
+      const int b = score_bin<FB>(v[u]);
+      atomicAdd(&whist[wv][b >> 1], 1u << (16 * (b & 1)));
+    }
+  __syncthreads();
+  {  // the row's histogram: thread t sums bins 4t .. 4t + 3 over the waves
+    uint32_t s01 = 0, s23 = 0;  // two packed 16-bit sums each (a row holds at most 32,768)
+#pragma unroll
+    for (int w = 0; w < NW_B; ++w) {
+      const uint2 p = reinterpret_cast<const uint2*>(whist[w])[threadIdx.x];
+      s01 += p.x;
+      s23 += p.y;
+    }
+    reinterpret_cast<int4*>(hist)[threadIdx.x] =
+        make_int4((int)(s01 & 0xFFFFu), (int)(s01 >> 16), (int)(s23 & 0xFFFFu), (int)(s23 >> 16));
+  }
   __syncthreads();
   find_cut<NT_B>(hist, TOPK_BINS, top_k, red, cut);
   const int bstar = cut[0];
   const int need = top_k - cut[1];
   const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
   const uint32_t hm1 = bin_hm1<FB>(bstar);
-  // count above b*, gather the b* candidates into this wave's slice
+  // this wave's elements above b*: its histogram's bins past b* (lane: bins 32 lane .. +31)
+  int above = 0;
+  {
+    const uint4* wq = reinterpret_cast<const uint4*>(whist[wv]) + 4 * lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 q = wq[k];
+      const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b0 = 32 * lane + 8 * k + 2 * e;
+        above += (b0 > bstar ? (int)(wd[e] & 0xFFFFu) : 0) + (b0 + 1 > bstar ? (int)(wd[e] >> 16) : 0);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
+  }
+  // gather the b* candidates into this wave's slice
   const uint64_t below_lane = (1ull << lane) - 1ull;
-  int above = 0, nc = 0;
+  const uint32_t span = hm1 - lo;
+  int nc = 0;
 #pragma unroll
   for (int u = 0; u < V; ++u) {
     const uint32_t x = v[u];
-    const bool in = 64 * u < rem;
-    const uint64_t ma = __ballot(in && x > hm1);
-    const bool c = in && x >= lo && x <= hm1;
+    const bool c = 64 * u < rem && x - lo <= span;
     const uint64_t mc = __ballot(c);
-    above += __popcll(ma);
     if (mc) {  // rare: the b* candidates go to this wave's slice, a wave-uniform count ahead
       const int slot = nc + __popcll(mc & below_lane);
       if (c && slot < CAND_W) {
@@ -1033,7 +1069,8 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
                                                           int top_k, int32_t* __restrict__ idx_out,
                                                           int32_t* __restrict__ score_out,
                                                           int32_t pad_score) {
-  __shared__ int hist[TOPK_BINS];
+  __shared__ __align__(16) int hist[TOPK_BINS];
+  __shared__ __align__(16) uint32_t whist[NW_B][TOPK_BINS / 2];  // per-wave packed histograms
   __shared__ uint32_t klo[TOPK_CAND_CAP], khi[TOPK_CAND_CAP];
   __shared__ int hist2[256];
   __shared__ int red[NW_B + 1];
@@ -1056,13 +1093,13 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
   }
   static_assert(NT_B * 64 == TOPK_LDS_MAX, "8 waves x 64 x 64 scores cover the longest short row");
   if (n <= NT_B * 8)
-    topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+    topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else if (n <= NT_B * 16)
-    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else if (n <= NT_B * 32)
-    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else
-    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
 }
 
 // ---- segmented rows: count / resolve / emit over TOPK_SEG-candidate segments ---------------
