@@ -10,8 +10,10 @@ after 65,536), the 2,048-token chunk after 65,536 and the million-token MTP deco
 1,048,576) run beside it as legs, each with its own roofline.
 
 Steps are timed cold: before each step, outside its timed span, a 1 GiB buffer is written so that
-neither the L2 caches nor the 256 MB last-level cache hold anything of the previous step; each
-step's span is taken with HIP events on the stream the library launches on. Decode legs also
+neither the L2 caches nor the 256 MB last-level cache hold anything of the previous step, and then
+512 MB of another buffer are read, so that the write's dirty lines go back to HBM before the step
+rather than during it (the caches then hold clean data the step never touches); each step's span
+is taken with HIP events on the stream the library launches on. Decode legs also
 rotate among four seeded query sets, so consecutive steps select different rows. The warm figure
 (steps back to back, no scrub) is reported beside the cold one.
 
@@ -47,6 +49,7 @@ DECODE_CONFIGS = (1, 4)
 HEADLINE_CONFIG = 3
 SIDE_LEGS = (1, 2, 4)
 SCRUB_BYTES = 1 << 30        # written between timed steps: > 4 x the 256 MB last-level cache
+DRAIN_BYTES = 1 << 29        # then read: > 2 x that cache, so none of the write stays dirty
 ROTATIONS = 4                # seeded query sets a decode leg cycles through
 # file-name tags of the workloads in profiles/
 WORKLOAD_TAGS = {0: "tiny_1x512", 1: "decode_32x65536", 2: "chunk_2048after65536",
@@ -684,6 +687,7 @@ class Leg:
 
 
 def time_leg(leg, steps, warmup, scrub, log):
+    """scrub: (write buffer, drain buffer); see the module docstring."""
     """Cold per-step spans (the reported figures), cold per-stage kernel times, and the warm rate
     of steps back to back."""
     import numpy as np
@@ -693,8 +697,11 @@ def time_leg(leg, steps, warmup, scrub, log):
         leg.step(k)
     torch.cuda.synchronize()
 
+    wbuf, drain = scrub
+
     def cold(k):
-        scrub.fill_(k & 0x7F)
+        wbuf.fill_(k & 0x7F)
+        drain.max()  # a read of other data: the write's dirty lines leave the caches first
 
     log(f"timing {steps} cold steps")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -803,7 +810,8 @@ def main():
     meta = run_metadata()
     log("measuring copy and GEMM rates")
     meta["measured_peaks"] = measured_peaks(dev)
-    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev)
+    scrub = (torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev),
+             torch.zeros(DRAIN_BYTES // 4, dtype=torch.int32, device=dev))
 
     leg = Leg(args.config, dev, log)
     d = leg.d
@@ -819,7 +827,7 @@ def main():
                                 "softmax; PV in fp16 (bf16 fallback), fp32 accumulate"},
         "data": "synthetic",
         "config": head["config"],
-        "timing": "cold: 1 GiB scrub before each step, outside its HIP-event span"
+        "timing": "cold: 1 GiB written, then 512 MB of other data read, before each step, outside its HIP-event span"
                   + ("; 4 rotating query sets" if leg.decode else ""),
         "median_ms": head["median_ms"], "min_ms": head["min_ms"], "warm": head["warm"],
         "stages_ms": head["stages_ms"],
