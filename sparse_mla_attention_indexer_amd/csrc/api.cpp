@@ -90,8 +90,9 @@ int check_mla_args(const smla_batch* b, const void* q, const void* kv, int32_t f
 }
 
 // Indexer work plan: query tiles of up to QT tokens, tile i paired with tile n-1-i, each pair's
-// combined key range (front tile's keys, then back tile's) cut into C-key items. pos: every
-// token's position (non-decreasing within a request).
+// combined key range (front tile's keys, then back tile's) cut into C-key items; a remainder
+// under C / 4 keys joins the item before it. pos: every token's position (non-decreasing within a
+// request).
 void plan_items_chunk(int32_t batch, const int32_t* n_q, const std::vector<int32_t>& pos,
                       const std::vector<int32_t>& q_start, int64_t C, std::vector<smla::Item>* items) {
   using smla::Item;
@@ -112,8 +113,9 @@ void plan_items_chunk(int32_t batch, const int32_t* n_q, const std::vector<int32
       tile(i, &ea, &qa, &na);
       if (j != i) tile(j, &eb, &qb, &nb);
       const int64_t E = ea + eb;
-      for (int64_t c0 = 0; c0 < E; c0 += C) {
-        const int64_t c1 = std::min(E, c0 + C);
+      for (int64_t c0 = 0; c0 < E;) {
+        int64_t c1 = std::min(E, c0 + C);
+        if (E - c1 < C / 4) c1 = E;  // a short remainder joins this item instead of its own
         Seg segs[2];
         int ns = 0;
         if (c0 < ea) segs[ns++] = Seg{qa, na, (int32_t)c0, (int32_t)std::min(c1, ea)};
@@ -123,6 +125,7 @@ void plan_items_chunk(int32_t batch, const int32_t* n_q, const std::vector<int32
         it.a = segs[0];
         it.b = ns > 1 ? segs[1] : Seg{0, 0, 0, 0};
         items->push_back(it);
+        c0 = c1;
       }
     }
   }

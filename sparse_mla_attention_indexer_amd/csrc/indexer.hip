@@ -404,7 +404,8 @@ __device__ __forceinline__ void indexer_wave(const Tok& tk, int64_t t, int s_beg
 // issued right after the barrier that opens group g (every wave has then finished group g-1,
 // whose slots they take). The ring and histograms fit 48 KB, so three workgroups share a CU and
 // hide each other's latencies. The LDS histograms count in 16 bits, two bins per word (a
-// workgroup scores at most KEY_CHUNK keys per token and segment, so a count stays below 2^16).
+// workgroup scores at most 1.25 KEY_CHUNK keys per token and segment, so a count stays below
+// 2^16).
 constexpr int SG = 4;      // key tiles per group
 constexpr int SRING = 2;   // groups in the ring
 
