@@ -39,7 +39,10 @@
 // their V codes are zeroed before the products, so a padding row's bytes (which may be NaN)
 // never reach an output.
 // The reduction of tile t and the products of tile t-1 share one phase between barriers, so the
-// matrix cores and the vector ALUs overlap across the two waves of each SIMD.
+// matrix cores and the vector ALUs overlap across the two waves of each SIMD. In each phase the
+// wave that issues the matrix instructions runs at a raised wave priority (s_setprio), so that
+// its products and the conversions feeding them are not queued behind the other wave's vector
+// work.
 // Decode splits a token's rows across workgroups and merges bf16 partials by log-sum-exp.
 #include <mutex>
 #include <type_traits>
@@ -424,6 +427,10 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
         v4f acc[2][4];
         if (t < ntiles) {
           if (t >= 2 && t + 2 < ntiles) gather_go(t + 2, gix);  // its slot held tile t - 2, done with
+          // the products go out at a raised priority: the PV wave on the same SIMD issues the
+          // reduction's vector instructions meanwhile, and a product waiting behind them idles the
+          // matrix core
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -443,6 +450,8 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
               for (int i = 0; i < 4; ++i) acc[h][ht][i] *= sb[h][i];
               acc[h][ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kr[h], qr[ht], acc[h][ht], 0, 0, 0);
             }
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(0);
           // tile t + 1 must have landed before phase 2 reads it; later tiles may still be in flight
           if (t + 1 < ntiles) {
             const int last_issued = min(ntiles - 1, max(NRAW - 1, t + 2));
@@ -592,7 +601,12 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
         }
         lds_barrier();  // P' of tile u visible; the partials of tile u read
         if (t >= 1) {
-          // PV of tile u: dims 128 b + 16 dt + 4 G + i of every head
+          // PV of tile u: dims 128 b + 16 dt + 4 G + i of every head. The wave's priority is raised
+          // until its products are issued: the QK wave on the same SIMD (older, so preferred at
+          // equal priority) converts K meanwhile, and its vector instructions would otherwise
+          // delay the conversions and products here. (Raised for the products alone, the phase is
+          // 2% longer: the conversions before them are on its critical path too.)
+          __builtin_amdgcn_s_setprio(2);
           const unsigned vb = (vm_u >> (8 * G)) & 0xFFu;
           const unsigned mlo = byte_mask4(vb), mhi = byte_mask4(vb >> 4);
           v4u pb[4];
@@ -618,6 +632,8 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
               else
                 o[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], __builtin_bit_cast(v8bf, pb[ht]), o[dt][ht], 0, 0, 0);
             }
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_setprio(0);
         }
         lds_barrier();
       }
