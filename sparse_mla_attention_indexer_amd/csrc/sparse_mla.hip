@@ -77,6 +77,7 @@ constexpr int U_OFF = TILE * RB;              // 20992
 constexpr int RAW_INSTR = 21;                 // load instructions per tile (64 chunks each)
 constexpr int RAW_SLOT = RAW_INSTR * 1024;    // 21504 bytes: the rows, then the u table
 constexpr int NRAW = 4;                       // tile slots: two computed on, two in flight
+constexpr int Q_BYTES = MLA_H * MLA_DQK * 2;  // one token's Q, staged in the tile slots first
 constexpr float LOG2E = 1.4426950408889634f;
 // Softmax reference (log2 units): P = 2^(logit - ref) with ref fixed for the whole split, so the
 // output accumulators are only ever touched by the matrix cores. The first tile with a valid row
@@ -100,6 +101,7 @@ struct __align__(16) MlaSmem {
 };
 static_assert(sizeof(MlaSmem) <= 160 * 1024 - 64, "LDS budget");
 static_assert(MLA_H * MLA_DV * 2 <= sizeof(MlaSmem::raw), "output staging");
+static_assert(Q_BYTES % 4096 == 0 && Q_BYTES <= sizeof(MlaSmem::raw), "Q staging");
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   v2f x = {a, b};
@@ -218,6 +220,17 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 
   const int32_t* idx_row = idx + t_tok * top_k;
 
+  // The QK team copies the token's Q (64 heads x 576 bf16 values, 73,728 bytes, as given) into
+  // the tile slots by the load-to-LDS path, so that it travels together with the index list
+  // below instead of after it; the slots are idle until the first gathers.
+  if (qk_team) {
+    const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(q + t_tok * (int64_t)(MLA_H * MLA_DQK));
+    unsigned char* qdst = &sm.raw[0][0];
+#pragma unroll
+    for (int j = 0; j < Q_BYTES / 4096; ++j)
+      lds_load16(qsrc + 1024 * (b + 4 * j) + 16 * lane, qdst + 1024 * (b + 4 * j));
+  }
+
   // The split's indices. First guess, right for a list whose last entry is valid: the splits share
   // all of the list's tiles. The last entry is loaded with them to check.
   __shared__ int last_all, last_valid, logit_over, scale_over;
@@ -276,6 +289,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     }
     if (lv >= 0) atomicMax(&last_valid, lv);
   }
+  if (qk_team) wait_vmcnt<0>();  // this wave's part of the Q copy has landed
   __syncthreads();
   const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
 
@@ -333,14 +347,16 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const bool split_out = part_o != nullptr;
   unsigned char* stage = &sm.raw[0][0];
   if (qk_team) {
-  // The QK team's Q fragments go out with the indices (bf16 as given): head tile ht, head
-    // 16 ht + l16; code k-step ks: dims 128 b + 64 (ks >> 1) + 16 G + 8 (ks & 1) .. +8 (the order
-    // in which the K fragments hold them); rope: dims 512 + 16 b + 4 G .. +4 (a 16-deep k-step
-    // covers the block's share of the 64 rope dims).
+    // The QK team's Q fragments, read from the copy in LDS: head tile ht, head 16 ht + l16; code
+    // k-step ks: dims 128 b + 64 (ks >> 1) + 16 G + 8 (ks & 1) .. +8 (the order in which the K
+    // fragments hold them); rope: dims 512 + 16 b + 4 G .. +4 (a 16-deep k-step covers the
+    // block's share of the 64 rope dims). Reading Q from LDS (not from global memory) also keeps
+    // the compiler from adding waits of its own for Q inside the tile loop, where the
+    // vector-memory counter counts the gathers too.
     v8bf qc[4][4];
     v4s qr[4];
     {
-      const __bf16* qt = q + t_tok * (int64_t)(MLA_H * MLA_DQK);
+      const __bf16* qt = reinterpret_cast<const __bf16*>(&sm.raw[0][0]);
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         const __bf16* qh = qt + (16 * ht + l16) * MLA_DQK;
@@ -349,11 +365,8 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
           qc[ht][ks] = *reinterpret_cast<const v8bf*>(qh + 128 * b + 64 * (ks >> 1) + 16 * G + 8 * (ks & 1));
         qr[ht] = *reinterpret_cast<const v4s*>(qh + 512 + 16 * b + 4 * G);
       }
-      // Q is in before the first gather goes out, visibly to the compiler: it then adds no waits
-      // of its own for these loads inside the tile loop, where the vector-memory counter also
-      // counts the gathers (a compiler wait there would drain gathers still in flight)
-      wait_vmcnt<0>();
     }
+    lds_barrier();  // every QK wave holds its Q before the gathers reuse the slots
   // ---- QK team: one pass over the split's tiles. Phase 1 of iteration t issues only the
     // products of tile t (its K fragments were read and converted in the phase before); phase 2
     // stores the partials, then reads and converts tile t + 1 and writes its block's column of
@@ -494,6 +507,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     float lsum = 0.f;        // this lane's share of the head's softmax denominator
     v4f o[8][4];             // O^T [dim tile][head tile] for dims 128 b + 16 dt + 4 G + i
     bool over = false;       // a logit above ref + REF_HEADROOM
+    lds_barrier();           // pairs with the QK team's barrier after its Q reads
   // ---- PV team: one pass over the split's tiles, one tile behind the QK team
     auto pv_pass = [&](auto f16_tag, bool have_ref) {
       constexpr bool F16 = decltype(f16_tag)::value;
