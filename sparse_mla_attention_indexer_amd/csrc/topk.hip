@@ -1063,6 +1063,151 @@ __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, 
   }
 }
 
+// Rows of more than 2,048 NT_B / 256 candidates first try a threshold taken from a sample: the
+// elements of one register in eight (index i with i mod 512 < 64, about n / 8 of them) fill the
+// histogram, and the bin of the sample's k_s-th largest score, k_s = k f + 4 sqrt(k f) + 16 with
+// f the sampled fraction, bounds the selection from below. One compare-and-ballot pass counts
+// the elements at or above that bin's lowest score, a second writes them to LDS in index order
+// (about 2,700 for k = 2,048), and the exact cut and the ranks are then found among those
+// candidates only, so the histogram atomics and the rank pass no longer touch every element.
+// Every element outside the candidates scores below every candidate, so the k largest keys are
+// among them whenever there are at least k. With fewer than k, or more than the buffer holds
+// (heavy ties), the row returns false and the full-row path runs instead; the result is exact
+// either way.
+template <bool FB, int V>
+__device__ __forceinline__ bool topk_short_row_sampled(const int32_t* __restrict__ row, int n,
+                                                       int top_k, int32_t* __restrict__ oi,
+                                                       int32_t* __restrict__ os, int* hist,
+                                                       uint32_t (*whist)[TOPK_BINS / 2],
+                                                       uint32_t* klo, uint32_t* khi, int* hist2,
+                                                       int* red, int* cut, uint64_t* pm, int* wcnt,
+                                                       int* wsel) {
+  static_assert(V >= 16 && V % 8 == 0, "a wave's chunk is a multiple of 1,024 elements");
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ib = wv * (64 * V) + lane;
+  const int rem = n - ib;  // this lane's element u is in the row iff 64 u < rem
+  uint32_t v[V];
+  lane_load<V>(v, row, n, ib, 0);
+  {  // this wave's histogram of its sampled registers (at most 64 V / 8 per wave: 16-bit counts)
+    uint4* wz = reinterpret_cast<uint4*>(whist[wv]);
+#pragma unroll
+    for (int i = lane; i < TOPK_BINS / 8; i += 64) wz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int u = 0; u < V; u += 8)
+    if (64 * u < rem) {
+      const int b = score_bin<FB>(v[u]);
+      atomicAdd(&whist[wv][b >> 1], 1u << (16 * (b & 1)));
+    }
+  __syncthreads();
+  {  // the sample's histogram: thread t sums bins 4t .. 4t + 3 over the waves
+    uint32_t s01 = 0, s23 = 0;
+#pragma unroll
+    for (int w = 0; w < NW_B; ++w) {
+      const uint2 q = reinterpret_cast<const uint2*>(whist[w])[threadIdx.x];
+      s01 += q.x;
+      s23 += q.y;
+    }
+    reinterpret_cast<int4*>(hist)[threadIdx.x] =
+        make_int4((int)(s01 & 0xFFFFu), (int)(s01 >> 16), (int)(s23 & 0xFFFFu), (int)(s23 >> 16));
+  }
+  __syncthreads();
+  // sampled elements: index i < n with i mod 512 < 64 (a wave's chunk starts at a multiple of
+  // 1,024, and register u = 8 j adds 512 j)
+  const int ns = 64 * (n / 512) + min(n % 512, 64);
+  const float kf = (float)top_k * (float)ns / (float)n;
+  const int ks = min(ns, (int)ceilf(kf + 4.0f * sqrtf(kf)) + 16);
+  find_cut<NT_B>(hist, TOPK_BINS, ks, red, cut);
+  const uint32_t thr = (uint32_t)bin_lo<FB>(cut[0]);
+  // count the candidates (score >= thr), then place them in index order: wave w's after those of
+  // the waves before it. Loads past the row's end returned 0, so with thr > 0 no element outside
+  // the row is ever a candidate and the passes need no range mask (thr == 0: the full-row path).
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    cnt += __popcll(__ballot(v[u] >= thr));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (lane == 0) wcnt[wv] = cnt;
+  __syncthreads();
+  int nc = 0, off = 0;
+#pragma unroll
+  for (int w = 0; w < NW_B; ++w) {
+    off += w < wv ? wcnt[w] : 0;
+    nc += wcnt[w];
+  }
+  if (thr == 0 || nc < top_k || nc > TOPK_CAND_CAP) {  // uniform: the full-row path takes the row
+    __syncthreads();
+    return false;
+  }
+  const uint64_t below_lane = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const uint32_t x = v[u];
+    const bool c = x >= thr;
+    const uint64_t mc = __ballot(c);
+    if (mc) {
+      if (c) {
+        const int slot = off + __popcll(mc & below_lane);
+        klo[slot] = 0xFFFFFFFFu - (uint32_t)(ib + 64 * u);
+        khi[slot] = x;
+      }
+      off += __popcll(mc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the candidates' histogram, exact this time
+  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_B) hist[i] = 0;
+  if (threadIdx.x == 0) wsel[0] = 0;
+  __syncthreads();
+  for (int c = threadIdx.x; c < nc; c += NT_B) atomicAdd(&hist[score_bin<FB>(khi[c])], 1);
+  __syncthreads();
+  find_cut<NT_B>(hist, TOPK_BINS, top_k, red, cut);
+  const int bstar = cut[0];
+  const int need = top_k - cut[1];
+  const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
+  // b*'s members (keys) into the sample histograms' space, which is free now
+  uint32_t* mlo = &whist[0][0];
+  uint32_t* mhi = mlo + TOPK_CAND_CAP;
+  static_assert(2 * TOPK_CAND_CAP <= NW_B * (TOPK_BINS / 2), "member keys fit the histograms");
+  for (int c = threadIdx.x; c < nc; c += NT_B) {
+    const uint32_t x = khi[c];
+    if (score_bin<FB>(x) == bstar) {
+      const int m = atomicAdd(&wsel[0], 1);
+      mlo[m] = klo[c];
+      mhi[m] = x;
+    }
+  }
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t pf, mk;
+    wave_radix_cut([&](int i) { return ((uint64_t)mhi[i] << 32) | mlo[i]; }, wsel[0], need, hist2,
+                   &pf, &mk);
+    if (lane == 0) pm[0] = cut_key(pf, lo);
+    (void)mk;
+  }
+  __syncthreads();
+  const uint64_t ck = pm[0];
+  // ranks: thread t takes a run of consecutive candidates, so a block scan of its count of
+  // selected ones gives its first output position
+  const int per = (nc + NT_B - 1) / NT_B;
+  const int c0 = min(nc, (int)threadIdx.x * per), c1 = min(nc, c0 + per);
+  int sc = 0;
+  for (int c = c0; c < c1; ++c) sc += (((uint64_t)khi[c] << 32) | klo[c]) >= ck;
+  int pos = block_incl_scan<NT_B>(sc, red) - sc;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t x = khi[c], l = klo[c];
+    if ((((uint64_t)x << 32) | l) >= ck && pos < top_k) {
+      oi[pos] = (int32_t)(0xFFFFFFFFu - l);
+      if (os) os[pos] = (int32_t)x;
+      ++pos;
+    }
+  }
+  return true;
+}
+
 template <bool FB>
 __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restrict__ toks,
                                                           const int32_t* __restrict__ scores,
@@ -1092,14 +1237,21 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
     return;
   }
   static_assert(NT_B * 64 == TOPK_LDS_MAX, "8 waves x 64 x 64 scores cover the longest short row");
+  // rows of more than 2,048 NT_B / 256 candidates (k at most a quarter of the row, for k <=
+  // 2,048) try the sampled threshold first
+  const bool sample = top_k * 4 <= n && n > NT_B * 8;
   if (n <= NT_B * 8)
     topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
-  else if (n <= NT_B * 16)
-    topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
-  else if (n <= NT_B * 32)
-    topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
-  else
-    topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+  else if (n <= NT_B * 16) {
+    if (!sample || !topk_short_row_sampled<FB, 16>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel))
+      topk_short_row<FB, 16>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+  } else if (n <= NT_B * 32) {
+    if (!sample || !topk_short_row_sampled<FB, 32>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel))
+      topk_short_row<FB, 32>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+  } else {
+    if (!sample || !topk_short_row_sampled<FB, 64>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel))
+      topk_short_row<FB, 64>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
+  }
 }
 
 // ---- segmented rows: count / resolve / emit over TOPK_SEG-candidate segments ---------------

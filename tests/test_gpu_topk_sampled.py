@@ -1,0 +1,81 @@
+"""GPU parity of the short-row top-k where it first tries a threshold taken from a sample of the
+row (rows of 2,049 to 32,768 candidates with k at most a quarter of the row).
+
+The indexer keeps the k earlier tokens with the largest scores, ties to the lower index ("Serving
+GLM-5.3 ... PCP, DCP, Hybrid HiSparse", section "Why DP8 and TP8 fall short"). The sampled path
+must give exactly that set whatever the scores look like, so each case below is compared with the
+oracle on every query token:
+
+- random scores: the sample's threshold holds, the select runs over the candidates only;
+- 50 distinct score values: the cut falls inside a run of equal scores, decided by the index;
+- scores that are non-zero only where the sample looks (row index mod 512 < 64): the threshold
+  admits fewer than k candidates and the row falls back to the full-row select;
+- all-equal and three-valued scores: zero threshold or an overfull candidate buffer, fallback.
+
+Rows of 6,002, 9,002 and 20,004 candidates take the three register widths (16, 32 and 64
+scores per lane), with k = 2,048, 1,000 and 1. The same shapes with FP8 keys check the fp32-score
+variant against the oracle's top-k of the library's own scores.
+"""
+import numpy as np
+import pytest
+
+from sparse_mla_attention_indexer_amd import workload as W
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import Dev, assert_topk_equal, oracle_topk, say  # noqa: E402
+from test_gpu_fp8_indexer import Fp8Dev, _check_topk_on_own_scores, _token_rows  # noqa: E402
+
+N_Q = np.array([4, 2, 2], np.int32)
+KV_LEN = np.array([20004, 9002, 6002], np.int64)
+
+
+def _inputs(pattern):
+    d = W.small_big_dims(batch=1, n_q=int(N_Q.sum()), cached=int(KV_LEN.sum() - N_Q.sum()),
+                         seed=0x5EED3400)
+    x = W.generate(d)
+    rng = np.random.default_rng(0x34)
+    if pattern == "random":
+        return x
+    # score(s) = (sum_h w_h) * ReLU(k[s, 0]): only dim 0 of the queries is non-zero
+    x.q_idx[:] = 0
+    x.q_idx[:, :, 0] = 1
+    x.k_idx[:] = 0
+    if pattern == "steps":
+        x.k_idx[:, 0] = rng.integers(0, 50, size=x.k_idx.shape[0])
+    elif pattern == "sampled_only":
+        starts = np.concatenate([[0], np.cumsum(KV_LEN)[:-1]])
+        for r0, n in zip(starts, KV_LEN):
+            local = np.arange(n)
+            hot = r0 + local[local % 512 < 64]
+            x.k_idx[hot, 0] = rng.integers(1, 100, size=hot.size)
+    elif pattern == "few_values":
+        x.k_idx[:, 0] = rng.integers(0, 3, size=x.k_idx.shape[0])
+    elif pattern != "zeros":
+        raise ValueError(pattern)
+    return x
+
+
+@pytest.mark.parametrize("pattern", ["random", "steps", "sampled_only", "zeros", "few_values"])
+def test_sampled_threshold_rows_against_oracle(pattern):
+    x = _inputs(pattern)
+    say(f"[case] sampled top-k rows {pattern}", N_Q.tolist(), KV_LEN.tolist())
+    dev = Dev(x, n_q=N_Q, kv_len=KV_LEN)
+    tokens = np.arange(int(N_Q.sum()))
+    for top_k in (2048, 1000, 1):
+        idx, sc = dev.topk(top_k)
+        ref_idx, ref_sc = oracle_topk(x, tokens, top_k=top_k, n_q=N_Q, kv_len=KV_LEN)
+        assert_topk_equal(idx, sc, ref_idx, ref_sc, f"{pattern} k={top_k}")
+        say(f"  {pattern} k={top_k}: {len(tokens)} rows equal to the oracle")
+
+
+def test_sampled_threshold_rows_fp8_scores():
+    d = W.small_big_dims(batch=1, n_q=int(N_Q.sum()), cached=int(KV_LEN.sum() - N_Q.sum()))
+    x = W.fp8_indexer_inputs(d, seed=0x5EED3500)
+    say("[case] sampled top-k rows, FP8 keys", N_Q.tolist(), KV_LEN.tolist())
+    dev = Fp8Dev(N_Q, KV_LEN, x.q, x.k, x.k_scale, x.w)
+    full = dev.scores()
+    toks = _token_rows(N_Q, KV_LEN)
+    for top_k in (2048, 1000, 1):
+        idx, sc = dev.topk(top_k)
+        _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"fp8 k={top_k}")
