@@ -1063,7 +1063,7 @@ __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, 
   }
 }
 
-// Rows of more than 2,048 NT_B / 256 candidates first try a threshold taken from a sample: the
+// Rows of more than 8 NT_B candidates with k <= n / 2 first try a threshold taken from a sample: the
 // elements of one register in eight (index i with i mod 512 < 64, about n / 8 of them) fill the
 // histogram, and the bin of the sample's k_s-th largest score, k_s = k f + 4 sqrt(k f) + 16 with
 // f the sampled fraction, bounds the selection from below. One compare-and-ballot pass counts
@@ -1237,9 +1237,9 @@ __global__ __launch_bounds__(NT_B, 4) void topk_short_kernel(const Tok* __restri
     return;
   }
   static_assert(NT_B * 64 == TOPK_LDS_MAX, "8 waves x 64 x 64 scores cover the longest short row");
-  // rows of more than 2,048 NT_B / 256 candidates (k at most a quarter of the row, for k <=
-  // 2,048) try the sampled threshold first
-  const bool sample = top_k * 4 <= n && n > NT_B * 8;
+  // rows of more than 8 NT_B candidates with k at most half the row try the sampled threshold
+  // first (for k = 2,048 it admits about 2,700 candidates, which the buffer holds)
+  const bool sample = top_k * 2 <= n && n > NT_B * 8;
   if (n <= NT_B * 8)
     topk_short_row<FB, 8>(row, n, top_k, oi, os, hist, whist, klo, khi, hist2, red, cut, pm, wcnt, wsel, woff);
   else if (n <= NT_B * 16) {
