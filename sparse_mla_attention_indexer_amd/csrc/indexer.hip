@@ -422,7 +422,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
                                                    const HeadW& wl, const int32_t* __restrict__ w_i,
                                                    const float* __restrict__ w_f,
                                                    int32_t* __restrict__ scores, int64_t stride,
-                                                   bool hist_on,
+                                                   bool hist_on, int hist_min_n,
                                                    unsigned (*lhist)[TOPK_BINS / 2],
                                                    v4i (*ring)[256], float (*scl)[64]) {
   using Acc = std::conditional_t<F8, v16f, v16i>;
@@ -474,7 +474,7 @@ __device__ __forceinline__ void indexer_shared_seg(const Seg& sg, const Tok* __r
   int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
   const __amdgpu_buffer_rsrc_t out_rs =
       __builtin_amdgcn_make_buffer_rsrc(out_row, 0, active ? (last + 1) * 4 : 0, 0x00020000);
-  unsigned* lh = active && hist_on && tk.pos + 1 > TOPK_LDS_MAX ? lhist[qi] : nullptr;
+  unsigned* lh = active && hist_on && tk.pos + 1 > hist_min_n ? lhist[qi] : nullptr;
 
   auto epilogue = [&](auto foldc, const Acc& acc0, const Acc& acc1, int k) {
     uint32_t sum;
@@ -559,7 +559,7 @@ template <bool MULTI, bool F8>
 __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
     const Item* __restrict__ items, const Tok* __restrict__ toks, const int8_t* __restrict__ q_idx,
     const int8_t* __restrict__ k_idx, const float* __restrict__ k_scale, const void* __restrict__ w,
-    int32_t* __restrict__ scores, int64_t stride, int* __restrict__ hist) {
+    int32_t* __restrict__ scores, int64_t stride, int* __restrict__ hist, int hist_min_n) {
   // LDS: the key ring, then the histograms (QT packed ones, or one of int counters), then (F8)
   // one slot of 64 key scales per ring tile
   constexpr int TILE_INTS = 256 * 4;
@@ -594,9 +594,9 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
   for (int sgi = 0; sgi < 2; ++sgi) {
     const Seg sg = sgi == 0 ? it.a : it.b;
     if (sg.nq <= 0) continue;  // uniform over the workgroup
-    // rows longer than the LDS top-k path also get their score histogram (the last token of the
-    // tile has the longest row)
-    const bool hist_on = hist != nullptr && toks[sg.q0 + sg.nq - 1].pos + 1 > TOPK_LDS_MAX;
+    // rows whose top-k reads the indexer's histogram get it (the last token of the tile has the
+    // longest row)
+    const bool hist_on = hist != nullptr && toks[sg.q0 + sg.nq - 1].pos + 1 > hist_min_n;
     constexpr int HIST_WORDS = MULTI ? TOPK_BINS / 2 : TOPK_BINS;  // per token
     if (hist_on) {
       for (int i = threadIdx.x; i < sg.nq * HIST_WORDS; i += 256) lhist_base[i] = 0;
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
     }
     if constexpr (MULTI) {
       indexer_shared_seg<F8>(sg, toks, q_idx, k_idx, k_scale, wl, w_i, w_f, scores, stride, hist_on,
-                             reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring,
+                             hist_min_n, reinterpret_cast<unsigned (*)[TOPK_BINS / 2]>(lhist_base), ring,
                              scl);
     } else {
       // one token: the 4 waves split its key tiles, each through its own part of the ring
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(256, MULTI ? 3 : 2) void indexer_mfma_kernel(
     if (hist_on) {
       for (int q = 0; q < sg.nq; ++q) {
         const int64_t t = sg.q0 + q;
-        if (toks[t].pos + 1 <= TOPK_LDS_MAX) continue;
+        if (toks[t].pos + 1 <= hist_min_n) continue;
         int* g = hist + t * TOPK_BINS;
         const int* lq = lhist_base + q * HIST_WORDS;
         for (int i = threadIdx.x; i < HIST_WORDS; i += 256) {
@@ -644,7 +644,8 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restr
                                                               const int32_t* __restrict__ w,
                                                               int H_I, int D_I,
                                                               int32_t* __restrict__ scores,
-                                                              int64_t stride, int* __restrict__ hist) {
+                                                              int64_t stride, int* __restrict__ hist,
+                                                              int hist_min_n) {
   __shared__ int qs[16 * 64];
   __shared__ int ws[16];
   const int64_t t = blockIdx.x;
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(const Tok* __restr
   }
   int32_t* out_row = scores + (stride ? t * stride : tk.cand_off);
   out_row[s] = (int32_t)score;
-  if (hist && tk.pos + 1 > TOPK_LDS_MAX) atomicAdd(&hist[t * TOPK_BINS + topk_hist_slot(topk_bin(score))], 1);
+  if (hist && tk.pos + 1 > hist_min_n) atomicAdd(&hist[t * TOPK_BINS + topk_hist_slot(topk_bin(score))], 1);
 }
 
 }  // namespace
@@ -678,10 +679,12 @@ hipError_t launch_indexer_mfma(const smla_batch& b, const int8_t* q_idx, const i
   const int64_t stride = compact ? 0 : b.max_kv;
   if (b.max_q <= 1)
     hipLaunchKernelGGL((indexer_mfma_kernel<false, false>), dim3(b.n_items), dim3(256), 0, s,
-                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist);
+                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist,
+                       topk_hist_min_n(b.total_q));
   else
     hipLaunchKernelGGL((indexer_mfma_kernel<true, false>), dim3(b.n_items), dim3(256), 0, s,
-                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist);
+                       tv.item, tv.tok, q_idx, k_idx, nullptr, w, scores, stride, hist,
+                       topk_hist_min_n(b.total_q));
   return hipGetLastError();
 }
 
@@ -695,10 +698,12 @@ hipError_t launch_indexer_fp8(const smla_batch& b, const uint8_t* q, const uint8
   const int8_t* ki = reinterpret_cast<const int8_t*>(k);
   if (b.max_q <= 1)
     hipLaunchKernelGGL((indexer_mfma_kernel<false, true>), dim3(b.n_items), dim3(256), 0, s,
-                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist);
+                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist,
+                       topk_hist_min_n(b.total_q));
   else
     hipLaunchKernelGGL((indexer_mfma_kernel<true, true>), dim3(b.n_items), dim3(256), 0, s,
-                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist);
+                       tv.item, tv.tok, qi, ki, k_scale, w, scores, stride, hist,
+                       topk_hist_min_n(b.total_q));
   return hipGetLastError();
 }
 
@@ -709,7 +714,8 @@ hipError_t launch_indexer_generic(const smla_batch& b, const int8_t* q_idx, cons
   const int64_t stride = compact ? 0 : b.max_kv;
   dim3 grid((unsigned)b.total_q, (unsigned)((b.max_kv + 255) / 256));
   hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), 0, s, tv.tok, q_idx, k_idx, w, H_I,
-                     D_I, scores, stride, hist);
+                     D_I, scores, stride, hist,
+                       topk_hist_min_n(b.total_q));
   return hipGetLastError();
 }
 

@@ -53,6 +53,13 @@ constexpr int TOPK_ROW_MAX = 73728;  // 1024 threads x 72 scores in registers
 constexpr int TOPK_SEG = 4096;       // 256 threads x 16 scores in registers
 constexpr int TOPK_SEG_MAX = 2048;   // segments per row: rows of up to 8,388,608 candidates
 constexpr int TOPK_SEG_ALL_MAX_Q = 160;  // up to this many query tokens, all long rows segmented
+// Rows whose selection reads the score histogram the indexer fills while scoring: the segmented
+// top-k takes every row longer than TOPK_LDS_MAX in batches of at most TOPK_SEG_ALL_MAX_Q query
+// tokens, and otherwise only rows longer than TOPK_ROW_MAX (shorter rows take their threshold
+// from a sample of their own scores). The indexer histograms rows of more candidates than this.
+inline int topk_hist_min_n(int64_t total_q) {
+  return total_q <= TOPK_SEG_ALL_MAX_Q ? TOPK_LDS_MAX : TOPK_ROW_MAX;
+}
 constexpr int TOPK_BINS = 2048;
 constexpr int TOPK_CAND_CAP = 4096;
 // per row: [0] candidate counter, [1] b*, [2] count above b*, [4..5] cut key (low, high word)

@@ -752,31 +752,36 @@ __device__ void hist_cut(const int* __restrict__ gh, int k, int* red, int* out) 
 }
 
 // ---- rows of TOPK_LDS_MAX < n <= TOPK_ROW_MAX: one 1024-thread workgroup per row ----------
-// For batches with many long rows. The score histogram comes from the indexer, so b* is known at
-// once. Each of the 16 waves owns a contiguous chunk of the row and holds it in registers (72
-// scores per lane); a first pass counts the elements above b* and gathers the b* candidates in
-// LDS, one wave resolves the exact cut among them, the selected candidates are credited to the
-// waves that hold them, and a second pass (reloading the chunk, by then in L2) writes every
-// selected index at its rank. The row's histogram is cleared once read.
+// For batches with many long rows. Each of the 16 waves owns a contiguous chunk of the row and
+// holds it in registers (72 scores per lane). As for the shorter rows, a threshold from a sample
+// comes first: one register in eight fills the histogram, the bin of the sample's k_s-th largest
+// score bounds the selection from below, two compare-and-ballot passes count and compact the
+// candidates in index order, and the exact cut and the ranks are found among them. Without at
+// least k candidates that fit the buffer, the row's whole histogram is built in LDS: a pass counts
+// the elements above its cut bin b* and gathers the b* candidates, one wave resolves the exact cut,
+// the selected candidates are credited to the waves that hold them, and a second pass (reloading
+// the chunk, by then in L2) writes every selected index at its rank.
 constexpr int NT_R = 1024;
 constexpr int NW_R = NT_R / 64;
 constexpr int V_R = TOPK_ROW_MAX / NT_R;  // scores per lane
+static_assert((64 * V_R) % 512 == 0, "a wave's chunk is a whole number of 512-element blocks");
 
 template <bool FB>
 __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ toks,
                                                         const int32_t* __restrict__ scores,
-                                                        int top_k, TopkWs ws,
-                                                        int32_t* __restrict__ idx_out,
+                                                        int top_k, int32_t* __restrict__ idx_out,
                                                         int32_t* __restrict__ score_out) {
   // candidate keys as two planes (low words: ~index, high words: score) so the compiler never
-  // pairs a score with an index into a 64-bit register
+  // pairs a score with an index into a 64-bit register; then the members of the cut bin
   __shared__ uint32_t klo[TOPK_CAND_CAP], khi[TOPK_CAND_CAP];
+  __shared__ uint32_t mlo[TOPK_CAND_CAP], mhi[TOPK_CAND_CAP];
+  __shared__ int hist[TOPK_BINS];
   __shared__ int hist2[256];
   __shared__ int red[NT_R / 64 + 1];
   __shared__ int cut[2];
   __shared__ uint64_t pm[2];
   __shared__ int nk;
-  __shared__ int wsel[NW_R], woff[NW_R];
+  __shared__ int wsel[NW_R], woff[NW_R], wcnt[NW_R];
   const int64_t t = blockIdx.x;
   const Tok tk = toks[t];
   const int n = tk.pos + 1;
@@ -788,32 +793,126 @@ __global__ __launch_bounds__(NT_R) void topk_row_kernel(const Tok* __restrict__ 
   const bool full = n >= (wv + 1) * (64 * V_R);
   int32_t* oi = idx_out + t * top_k;
   int32_t* os = score_out ? score_out + t * top_k : nullptr;
-  int* gh = ws.hist + t * TOPK_BINS;
-  int need, bstar;
-  uint32_t lo;
   {
     uint32_t v[V_R];
     lane_load<V_R>(v, row, n, ib, 0);
+    for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) hist[i] = 0;
     if (threadIdx.x == 0) nk = 0;
-    hist_cut<NT_R>(gh, top_k, red, cut);  // while the row is in flight
-    bstar = cut[0];
-    need = top_k - cut[1];
-    lo = (uint32_t)bin_lo<FB>(bstar);
+    __syncthreads();
+    // the sample: registers u = 8 j, index i with i mod 512 < 64 (ns of them inside the row; the
+    // slots past the row's end read 0 and are taken back out of zero's bin)
+    const int ns = 64 * (n / 512) + min(n % 512, 64);
+#pragma unroll
+    for (int u = 0; u < V_R; u += 8) atomicAdd(&hist[score_bin<FB>(v[u])], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) hist[score_bin<FB>(0u)] -= NT_R * (V_R / 8) - ns;
+    __syncthreads();
+    const float kf = (float)top_k * (float)ns / (float)n;
+    const int ks = min(ns, (int)ceilf(kf + 4.0f * sqrtf(kf)) + 16);
+    find_cut<NT_R>(hist, TOPK_BINS, ks, red, cut);
+    const uint32_t thr = (uint32_t)bin_lo<FB>(cut[0]);
+    // loads past the row's end read 0: with thr > 0 no such element is a candidate
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < V_R; ++u) {
+      cnt += __popcll(__ballot(v[u] >= thr));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (lane == 0) wcnt[wv] = cnt;
+    __syncthreads();
+    int nc = 0, off = 0;
+#pragma unroll
+    for (int w = 0; w < NW_R; ++w) {
+      off += w < wv ? wcnt[w] : 0;
+      nc += wcnt[w];
+    }
+    if (thr > 0 && nc >= top_k && nc <= TOPK_CAND_CAP) {  // uniform
+      const uint64_t below_lane = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int u = 0; u < V_R; ++u) {
+        const uint32_t x = v[u];
+        const bool c = x >= thr;
+        const uint64_t mc = __ballot(c);
+        if (mc) {
+          if (c) {
+            const int slot = off + __popcll(mc & below_lane);
+            klo[slot] = 0xFFFFFFFFu - (uint32_t)(ib + 64 * u);
+            khi[slot] = x;
+          }
+          off += __popcll(mc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) hist[i] = 0;
+      __syncthreads();
+      for (int c = threadIdx.x; c < nc; c += NT_R) atomicAdd(&hist[score_bin<FB>(khi[c])], 1);
+      __syncthreads();
+      find_cut<NT_R>(hist, TOPK_BINS, top_k, red, cut);
+      const int bstar = cut[0];
+      const int need = top_k - cut[1];
+      const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
+      for (int c = threadIdx.x; c < nc; c += NT_R) {
+        const uint32_t x = khi[c];
+        if (score_bin<FB>(x) == bstar) {
+          const int m = atomicAdd(&nk, 1);
+          mlo[m] = klo[c];
+          mhi[m] = x;
+        }
+      }
+      __syncthreads();
+      if (wv == 0) {
+        uint64_t pf, mk;
+        wave_radix_cut([&](int i) { return ((uint64_t)mhi[i] << 32) | mlo[i]; }, nk, need, hist2,
+                       &pf, &mk);
+        if (lane == 0) pm[0] = cut_key(pf, lo);
+        (void)mk;
+      }
+      __syncthreads();
+      const uint64_t ck = pm[0];
+      const int per = (nc + NT_R - 1) / NT_R;
+      const int c0 = min(nc, (int)threadIdx.x * per), c1 = min(nc, c0 + per);
+      int sc = 0;
+      for (int c = c0; c < c1; ++c) sc += (((uint64_t)khi[c] << 32) | klo[c]) >= ck;
+      int pos = block_incl_scan<NT_R>(sc, red) - sc;
+      for (int c = c0; c < c1; ++c) {
+        const uint32_t x = khi[c], l = klo[c];
+        if ((((uint64_t)x << 32) | l) >= ck && pos < top_k) {
+          oi[pos] = (int32_t)(0xFFFFFFFFu - l);
+          if (os) os[pos] = (int32_t)x;
+          ++pos;
+        }
+      }
+      return;
+    }
+    // the row's whole histogram; the slots past the row's end read 0 and are taken back out of
+    // zero's bin, so no per-element range mask is needed
+    for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < V_R; ++u) atomicAdd(&hist[score_bin<FB>(v[u])], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) hist[score_bin<FB>(0u)] -= NT_R * V_R - n;
+    __syncthreads();
+    find_cut<NT_R>(hist, TOPK_BINS, top_k, red, cut);
+  }
+  const int bstar = cut[0];
+  const int need = top_k - cut[1];
+  const uint32_t lo = (uint32_t)bin_lo<FB>(bstar);
+  {
+    uint32_t v[V_R];
+    lane_load<V_R>(v, row, n, ib, 1);  // glc: a distinct load the compiler cannot merge with the first
     const uint32_t hm1 = bin_hm1<FB>(bstar);
     const int above = full ? pass_gather<V_R, true>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP)
                            : pass_gather<V_R, false>(v, ib, rem, lo, hm1, klo, khi, &nk, TOPK_CAND_CAP);
     if (lane == 0) wsel[wv] = above;
   }
-  // the histogram was read by every thread before hist_cut's last barrier: clear it for the next
-  // call
-  for (int i = threadIdx.x; i < TOPK_BINS; i += NT_R) gh[i] = 0;
   __syncthreads();
 
   const int ncand = nk;
   if (ncand <= TOPK_CAND_CAP) {
     // pass 2's loads go out before the cut so their latency hides behind it
     uint32_t v[V_R];
-    lane_load<V_R>(v, row, n, ib, 1);  // glc: a distinct load the compiler cannot merge with pass 1
+    lane_load<V_R>(v, row, n, ib, 1);
     if (wv == 0) {
       uint64_t pf, mk;
       wave_radix_cut([&](int i) { return ((uint64_t)khi[i] << 32) | klo[i]; }, ncand, need, hist2,
@@ -1496,7 +1595,7 @@ hipError_t launch_topk_t(const smla_batch& b, const int32_t* scores, int32_t top
   const int seg_min_n = seg_all ? TOPK_LDS_MAX : TOPK_ROW_MAX;
   if (!seg_all) {
     hipLaunchKernelGGL(topk_row_kernel<FB>, dim3(b.total_q), dim3(NT_R), 0, s, tv.tok, scores, top_k,
-                       w, idx, score);
+                       idx, score);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (b.max_kv <= seg_min_n) return e;

@@ -79,3 +79,63 @@ def test_sampled_threshold_rows_fp8_scores():
     for top_k in (2048, 1000, 1):
         idx, sc = dev.topk(top_k)
         _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"fp8 k={top_k}")
+
+
+# Rows of 32,769 to 73,728 candidates in a batch of more than 160 query tokens: one 1,024-thread
+# workgroup per row (72 scores per lane), which takes the sampled threshold too and otherwise
+# builds the row's whole histogram itself. 176 tokens after 40,000 cached rows; a spread of
+# tokens (the first, the last, and both ends of every 4-token tile seam it samples) against the
+# oracle, properties on every row.
+ROW_NQ, ROW_CACHED = 176, 40000
+ROW_TOKENS = np.array([0, 1, 3, 4, 57, 88, 131, 174, 175])
+
+
+def _row_inputs(pattern):
+    d = W.small_big_dims(n_q=ROW_NQ, cached=ROW_CACHED, seed=0x5EED3600)
+    x = W.generate(d)
+    rng = np.random.default_rng(0x36)
+    if pattern == "random":
+        return d, x
+    x.q_idx[:] = 0
+    x.q_idx[:, :, 0] = 1
+    x.k_idx[:] = 0
+    local = np.arange(x.k_idx.shape[0])
+    if pattern == "steps":
+        x.k_idx[:, 0] = rng.integers(0, 50, size=local.size)
+    elif pattern == "sampled_only":
+        hot = local[local % 512 < 64]
+        x.k_idx[hot, 0] = rng.integers(1, 100, size=hot.size)
+    elif pattern != "zeros":
+        raise ValueError(pattern)
+    return d, x
+
+
+@pytest.mark.parametrize("pattern", ["random", "steps", "sampled_only", "zeros"])
+def test_sampled_threshold_long_rows_one_workgroup_per_row(pattern):
+    d, x = _row_inputs(pattern)
+    say(f"[case] sampled top-k long rows {pattern}: {ROW_NQ} tokens after {ROW_CACHED}")
+    dev = Dev(x)
+    for top_k in (2048, 1000):
+        idx, sc = dev.topk(top_k)
+        ref_idx, ref_sc = oracle_topk(x, ROW_TOKENS, top_k=top_k)
+        assert_topk_equal(idx[ROW_TOKENS], sc[ROW_TOKENS], ref_idx, ref_sc, f"long rows {pattern} k={top_k}")
+        pos = dev.plan.positions
+        assert (idx >= 0).all() and (idx <= pos[:, None]).all()
+        assert (np.diff(idx, axis=1) > 0).all()
+        if pattern == "zeros":
+            assert (idx == np.arange(top_k)[None, :]).all()
+        say(f"  long rows {pattern} k={top_k}: {len(ROW_TOKENS)} rows equal to the oracle")
+
+
+def test_sampled_threshold_long_rows_fp8_scores():
+    n_q = np.array([ROW_NQ], np.int32)
+    kv_len = np.array([ROW_NQ + ROW_CACHED], np.int64)
+    d = W.small_big_dims(n_q=ROW_NQ, cached=ROW_CACHED)
+    x = W.fp8_indexer_inputs(d, seed=0x5EED3700)
+    say("[case] sampled top-k long rows, FP8 keys")
+    dev = Fp8Dev(n_q, kv_len, x.q, x.k, x.k_scale, x.w)
+    full = dev.scores()
+    toks = [r for r in _token_rows(n_q, kv_len) if r[0] in set(ROW_TOKENS.tolist())]
+    for top_k in (2048, 1000):
+        idx, sc = dev.topk(top_k)
+        _check_topk_on_own_scores(idx, sc, full, toks, top_k, f"fp8 long rows k={top_k}")
