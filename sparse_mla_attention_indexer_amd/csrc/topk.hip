@@ -624,6 +624,22 @@ __device__ __forceinline__ void lane_load(uint32_t (&v)[V], const int32_t* base,
   }
 }
 
+// The wave's elements at or above thr (wave-uniform): a count per lane on the vector unit, then a
+// butterfly over the wave, instead of a ballot and a scalar population count per register.
+template <int V>
+__device__ __forceinline__ int wave_count_ge(const uint32_t (&v)[V], uint32_t thr) {
+  // an opaque copy of the threshold: the compiler would otherwise keep these compares (one
+  // register each) alive for the placement pass that repeats them
+  uint32_t t = thr;
+  asm volatile("" : "+v"(t));
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < V; ++u) c += v[u] >= t ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  return c;
+}
+
 // Counts the lane-group's elements above bin b* = [lo, hm1] (returned, wave-uniform) and appends
 // the keys of the b* candidates to klo/khi (slots from *nk, at most cap). FULL: no range mask.
 template <int V, bool FULL>
@@ -1165,8 +1181,8 @@ __device__ __forceinline__ void topk_short_row(const int32_t* __restrict__ row, 
 // Rows of more than 8 NT_B candidates with k <= n / 2 first try a threshold taken from a sample: the
 // elements of one register in eight (index i with i mod 512 < 64, about n / 8 of them) fill the
 // histogram, and the bin of the sample's k_s-th largest score, k_s = k f + 4 sqrt(k f) + 16 with
-// f the sampled fraction, bounds the selection from below. One compare-and-ballot pass counts
-// the elements at or above that bin's lowest score, a second writes them to LDS in index order
+// f the sampled fraction, bounds the selection from below. A count per lane finds how many
+// elements lie at or above that bin's lowest score, a ballot pass writes them to LDS in index order
 // (about 2,700 for k = 2,048), and the exact cut and the ranks are then found among those
 // candidates only, so the histogram atomics and the rank pass no longer touch every element.
 // Every element outside the candidates scores below every candidate, so the k largest keys are
@@ -1223,12 +1239,7 @@ __device__ __forceinline__ bool topk_short_row_sampled(const int32_t* __restrict
   // count the candidates (score >= thr), then place them in index order: wave w's after those of
   // the waves before it. Loads past the row's end returned 0, so with thr > 0 no element outside
   // the row is ever a candidate and the passes need no range mask (thr == 0: the full-row path).
-  int cnt = 0;
-#pragma unroll
-  for (int u = 0; u < V; ++u) {
-    cnt += __popcll(__ballot(v[u] >= thr));
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  const int cnt = wave_count_ge<V>(v, thr);
   if (lane == 0) wcnt[wv] = cnt;
   __syncthreads();
   int nc = 0, off = 0;
