@@ -77,7 +77,7 @@ constexpr int U_OFF = TILE * RB;              // 20992
 constexpr int RAW_INSTR = 21;                 // load instructions per tile (64 chunks each)
 constexpr int RAW_SLOT = RAW_INSTR * 1024;    // 21504 bytes: the rows, then the u table
 constexpr int NRAW = 4;                       // tile slots: two computed on, two in flight
-constexpr int Q_BYTES = MLA_H * MLA_DQK * 2;  // one token's Q, staged in the tile slots first
+constexpr int Q_BYTES = MLA_H * MLA_DQK * 2;  // one token's Q, staged from the last tile slot on
 constexpr float LOG2E = 1.4426950408889634f;
 // Softmax reference (log2 units): P = 2^(logit - ref) with ref fixed for the whole split, so the
 // output accumulators are only ever touched by the matrix cores. The first tile with a valid row
@@ -94,6 +94,7 @@ struct __align__(16) MlaSmem {
   unsigned char raw[NRAW][RAW_SLOT];  // tiles as gathered (row r at 656 r), then their u tables
   v4f part[2][4][4][64];              // [row half][head tile][block][lane]: partial logits
   v4u pp[4][4][4][16];                // [block][head tile][row group][head]: 8 rows of P'
+  unsigned char qtail[Q_BYTES - RAW_SLOT - 32768 - 16384];  // Q's last bytes (see below)
   int idx[TOPK_MAX_K];                // the split's row indices (-1: skip)
   float xmax[2][MLA_H];               // per row half: logit maxima of each head
   float xsum[2][MLA_H];               // per row half: softmax denominators of each head
@@ -101,7 +102,16 @@ struct __align__(16) MlaSmem {
 };
 static_assert(sizeof(MlaSmem) <= 160 * 1024 - 64, "LDS budget");
 static_assert(MLA_H * MLA_DV * 2 <= sizeof(MlaSmem::raw), "output staging");
-static_assert(Q_BYTES % 4096 == 0 && Q_BYTES <= sizeof(MlaSmem::raw), "Q staging");
+// The token's Q is staged in raw[3], part, pp and qtail, one contiguous range that the first
+// three tiles' slots (and the index list) do not touch, so those tiles can be gathered while the
+// Q copy is still in flight.
+static_assert(Q_BYTES % 4096 == 0, "Q staging: four waves of 1 KB instructions");
+static_assert(offsetof(MlaSmem, part) == offsetof(MlaSmem, raw) + NRAW * RAW_SLOT &&
+                  offsetof(MlaSmem, pp) == offsetof(MlaSmem, part) + sizeof(MlaSmem::part) &&
+                  offsetof(MlaSmem, qtail) == offsetof(MlaSmem, pp) + sizeof(MlaSmem::pp) &&
+                  offsetof(MlaSmem, qtail) + sizeof(MlaSmem::qtail) ==
+                      offsetof(MlaSmem, raw) + (NRAW - 1) * RAW_SLOT + Q_BYTES,
+              "Q staging range");
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   v2f x = {a, b};
@@ -220,17 +230,6 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 
   const int32_t* idx_row = idx + t_tok * top_k;
 
-  // The QK team copies the token's Q (64 heads x 576 bf16 values, 73,728 bytes, as given) into
-  // the tile slots by the load-to-LDS path, so that it travels together with the index list
-  // below instead of after it; the slots are idle until the first gathers.
-  if (qk_team) {
-    const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(q + t_tok * (int64_t)(MLA_H * MLA_DQK));
-    unsigned char* qdst = &sm.raw[0][0];
-#pragma unroll
-    for (int j = 0; j < Q_BYTES / 4096; ++j)
-      lds_load16(qsrc + 1024 * (b + 4 * j) + 16 * lane, qdst + 1024 * (b + 4 * j));
-  }
-
   // The split's indices. First guess, right for a list whose last entry is valid: the splits share
   // all of the list's tiles. The last entry is loaded with them to check.
   __shared__ int last_all, last_valid, logit_over, scale_over;
@@ -289,8 +288,22 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     }
     if (lv >= 0) atomicMax(&last_valid, lv);
   }
-  if (qk_team) wait_vmcnt<0>();  // this wave's part of the Q copy has landed
-  __syncthreads();
+  // The QK team copies the token's Q (64 heads x 576 bf16 values, 73,728 bytes) by the
+  // load-to-LDS path, once its index-list loads have been used: the compiler's waits for those
+  // would otherwise wait for the copy too. Head h's 72 sixteen-byte pieces sit at
+  // qs + 1,152 h, piece p at slot p ^ (h & 7), so that the 16 heads a fragment read touches
+  // fall on different banks.
+  unsigned char* const qs = &sm.raw[NRAW - 1][0];
+  if (qk_team) {
+    const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(q + t_tok * (int64_t)(MLA_H * MLA_DQK));
+#pragma unroll
+    for (int j = 0; j < Q_BYTES / 4096; ++j) {
+      const int pc = 64 * (b + 4 * j) + lane;  // the LDS piece this lane fills
+      const int h = pc / 72, sl = pc - 72 * h;
+      lds_load16(qsrc + 16 * (72 * h + (sl ^ (h & 7))), qs + 1024 * (b + 4 * j));
+    }
+  }
+  lds_barrier();  // the index list and last_valid are visible; the Q copy may still fly
   const int ntiles = (last_valid + TILE) / TILE;  // trailing invalid tiles are skipped
 
   // Gather plan (QK team): instruction gq = b + 4 j (j < 6, gq <= 20) loads the tile's chunks
@@ -353,25 +366,31 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     // block's share of the 64 rope dims). Reading Q from LDS (not from global memory) also keeps
     // the compiler from adding waits of its own for Q inside the tile loop, where the
     // vector-memory counter counts the gathers too.
+    // the first three tiles go out now, beside the Q copy (their slots hold no part of Q)
+    const int early = min(ntiles, NRAW - 1);
+    for (int u = 0; u < early; ++u) gather(u);
+    wait_tiles_but(early, b);  // this wave's part of the Q copy has landed
+    lds_barrier();             // every QK wave's part has
     v8bf qc[4][4];
     v4s qr[4];
-    {
-      const __bf16* qt = reinterpret_cast<const __bf16*>(&sm.raw[0][0]);
 #pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const __bf16* qh = qt + (16 * ht + l16) * MLA_DQK;
+    for (int ht = 0; ht < 4; ++ht) {
+      const int h = 16 * ht + l16;
+      const unsigned char* qh = qs + 1152 * h;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          qc[ht][ks] = *reinterpret_cast<const v8bf*>(qh + 128 * b + 64 * (ks >> 1) + 16 * G + 8 * (ks & 1));
-        qr[ht] = *reinterpret_cast<const v4s*>(qh + 512 + 16 * b + 4 * G);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int pc = 16 * b + 8 * (ks >> 1) + 2 * G + (ks & 1);
+        qc[ht][ks] = *reinterpret_cast<const v8bf*>(qh + 16 * (pc ^ (h & 7)));
       }
+      const int pr = 64 + 2 * b + (G >> 1);
+      qr[ht] = *reinterpret_cast<const v4s*>(qh + 16 * (pr ^ (h & 7)) + 8 * (G & 1));
     }
-    lds_barrier();  // every QK wave holds its Q before the gathers reuse the slots
+    lds_barrier();  // every QK wave holds its Q before the gathers reuse its range
   // ---- QK team: one pass over the split's tiles. Phase 1 of iteration t issues only the
     // products of tile t (its K fragments were read and converted in the phase before); phase 2
     // stores the partials, then reads and converts tile t + 1 and writes its block's column of
     // tile t + 1's u table, so the conversions run beside the PV team's products.
-    auto qk_pass = [&](auto f16_tag) {
+    auto qk_pass = [&](auto f16_tag, bool first_pass) {
       constexpr bool F16 = decltype(f16_tag)::value;
       bool have_e = false;
       int e_b = 0;  // E_b of this wave's block
@@ -427,7 +446,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
         }
       };
       const int first = min(ntiles, NRAW);
-      for (int u = 0; u < first; ++u) gather(u);
+      for (int u = first_pass ? early : 0; u < first; ++u) gather(u);  // tiles 0..2 went out early
       if (ntiles > 0) wait_tiles_but(first - 1, b);
       lds_barrier();  // every wave's part of tile 0 has landed
       if (ntiles > 0) {
@@ -492,8 +511,8 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
 
 #pragma unroll 1
     for (int pass = 0;; ++pass) {
-      if (f16) qk_pass(std::true_type{});
-      else qk_pass(std::false_type{});
+      if (f16) qk_pass(std::true_type{}, pass == 0);
+      else qk_pass(std::false_type{}, pass == 0);
       if (__any(u_out)) scale_over = 1;
       __syncthreads();
       if (!(logit_over || scale_over) || pass == 1) break;
@@ -507,6 +526,7 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
     float lsum = 0.f;        // this lane's share of the head's softmax denominator
     v4f o[8][4];             // O^T [dim tile][head tile] for dims 128 b + 16 dt + 4 G + i
     bool over = false;       // a logit above ref + REF_HEADROOM
+    lds_barrier();           // pairs with the QK team's barrier once Q has landed
     lds_barrier();           // pairs with the QK team's barrier after its Q reads
   // ---- PV team: one pass over the split's tiles, one tile behind the QK team
     auto pv_pass = [&](auto f16_tag, bool have_ref) {
