@@ -203,11 +203,12 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
 // time, so that one team's matrix instructions run while the other's vector instructions do:
 //  - the QK team (waves 0..3, wave b = FP8 block b) computes the partial logits of tile t,
 //    holds them in registers across the middle barrier and then stores them; it also issues
-//    every gather, and its last wave writes each tile's u table;
+//    every gather, and wave b writes block b's column of each tile's u table;
 //  - the PV team (waves 4..7, wave b) reduces head tile b of tile t - 1 (all 32 rows, so the
 //    softmax state of heads 16b..16b+15 stays inside the wave), writes P', and after the middle
 //    barrier accumulates O for block b's 128 dims of all 64 heads.
-// Per iteration: [QK(t) | reduce(t-1)] barrier [store partials(t), u table(t) | PV(t-1)] barrier.
+// Per iteration: [QK(t) | reduce(t-1)] barrier [store partials(t), K and u column of tile t+1 |
+// PV(t-1)] barrier.
 __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ toks,
                                                         const __bf16* __restrict__ q,
                                                         const unsigned char* __restrict__ kv,
