@@ -777,7 +777,9 @@ def main():
                     help="headline workload 0..4 (default 3: the 32,768-token prefill)")
     ap.add_argument("--legs", default=",".join(map(str, SIDE_LEGS)),
                     help="comma-separated side workloads, or 'none'")
-    ap.add_argument("--leg-steps", type=int, default=20)
+    ap.add_argument("--leg-steps", type=int, default=50,
+                    help="timed steps of each side workload (decode steps take ~0.1-0.25 ms)")
+    ap.add_argument("--leg-warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the cache-append, DCP, hybrid-offload and FP8-key measurements")
@@ -852,11 +854,11 @@ def main():
     result["legs"] = {}
     for c in legs:
         lg = Leg(c, dev, log)
-        tl = time_leg(lg, args.leg_steps, 3, scrub, log)
-        r = leg_result(lg, tl, args.leg_steps, 3)
+        tl = time_leg(lg, args.leg_steps, args.leg_warmup, scrub, log)
+        r = leg_result(lg, tl, args.leg_steps, args.leg_warmup)
         if extras and lg.decode and lg.d.kv_format == W.KV_FP8_656:
             log("DCP simulation")
-            r["dcp_sim"] = dcp_measurement(dev, lg.x, lg.d, args.leg_steps, 3)
+            r["dcp_sim"] = dcp_measurement(dev, lg.x, lg.d, args.leg_steps, args.leg_warmup)
         if extras and lg.decode and (lg.x.n_q == 1).all() and lg.d.kv_format == W.KV_FP8_656:
             log("hybrid offload resolve")
 
@@ -866,7 +868,8 @@ def main():
                 return lg.idx
 
             hot = hot_resolve_measurement(dev, lg.x, lg.d, lg.plan, lg.q[0], select,
-                                          lambda sel, kv_h: lg.attend(sel, kv_h), args.leg_steps, 3)
+                                          lambda sel, kv_h: lg.attend(sel, kv_h), args.leg_steps,
+                                          args.leg_warmup)
             if hot is not None:
                 r["hot_resolve"] = hot
         result["legs"][WORKLOAD_TAGS[c]] = r
