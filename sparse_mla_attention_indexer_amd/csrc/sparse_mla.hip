@@ -361,17 +361,17 @@ __global__ __launch_bounds__(NT, 1) void mla_fp8_kernel(const Tok* __restrict__ 
   const bool split_out = part_o != nullptr;
   unsigned char* stage = &sm.raw[0][0];
   if (qk_team) {
+    // the first three tiles go out now, beside the Q copy (their slots hold no part of Q)
+    const int early = min(ntiles, NRAW - 1);
+    for (int u = 0; u < early; ++u) gather(u);
+    wait_tiles_but(early, b);  // this wave's part of the Q copy has landed
+    lds_barrier();             // every QK wave's part has
     // The QK team's Q fragments, read from the copy in LDS: head tile ht, head 16 ht + l16; code
     // k-step ks: dims 128 b + 64 (ks >> 1) + 16 G + 8 (ks & 1) .. +8 (the order in which the K
     // fragments hold them); rope: dims 512 + 16 b + 4 G .. +4 (a 16-deep k-step covers the
     // block's share of the 64 rope dims). Reading Q from LDS (not from global memory) also keeps
     // the compiler from adding waits of its own for Q inside the tile loop, where the
     // vector-memory counter counts the gathers too.
-    // the first three tiles go out now, beside the Q copy (their slots hold no part of Q)
-    const int early = min(ntiles, NRAW - 1);
-    for (int u = 0; u < early; ++u) gather(u);
-    wait_tiles_but(early, b);  // this wave's part of the Q copy has landed
-    lds_barrier();             // every QK wave's part has
     v8bf qc[4][4];
     v4s qr[4];
 #pragma unroll
